@@ -1,0 +1,251 @@
+"""ctypes marshalling for the C oracle in zx_oracle.c (test infrastructure only).
+
+Every computation happens in the C file.  This module only converts between numpy
+arrays and the C structures.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BF16 = 0
+FP8 = 1
+BLOCK = 65536
+CHUNK_BITS = 128
+SEG_CHUNKS = 64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "zx_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile zx_oracle.c with gcc into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-shared", "-fPIC",
+                               "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _CContainer(C.Structure):
+    _fields_ = [
+        ("dtype", C.c_int32), ("per_block", C.c_int32),
+        ("n", C.c_uint64), ("nblocks", C.c_uint64), ("ncb", C.c_uint64), ("nsegs", C.c_uint64),
+        ("total_bits", C.c_uint64), ("stream_words", C.c_uint64), ("signmant_bytes", C.c_uint64),
+        ("lengths", C.POINTER(C.c_uint8)), ("degenerate", C.POINTER(C.c_uint16)),
+        ("signmant", C.POINTER(C.c_uint8)), ("stream", C.POINTER(C.c_uint32)),
+        ("block_bitoff", C.POINTER(C.c_uint64)), ("block_seg", C.POINTER(C.c_uint32)),
+        ("seg_desc", C.POINTER(C.c_uint32)), ("gaps", C.POINTER(C.c_uint8)),
+    ]
+
+
+def load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = C.CDLL(_LIB)
+        if lib.zxo_sizeof_container() != C.sizeof(_CContainer):
+            raise RuntimeError("oracle struct layout mismatch; rebuild oracle")
+        P = C.c_void_p
+        lib.zxo_split.argtypes = [C.c_int, P, C.c_uint64, P, P]
+        lib.zxo_histogram.argtypes = [P, C.c_uint64, C.c_uint32, P]
+        lib.zxo_huffman_lengths.argtypes = [P, C.c_int, P]
+        lib.zxo_package_merge.argtypes = [P, C.c_int, C.c_int, P]
+        lib.zxo_code_lengths.argtypes = [P, C.c_int, C.c_int, P, P]
+        lib.zxo_canonical_codes.argtypes = [P, C.c_int, P]
+        lib.zxo_stream_words.argtypes = [C.c_uint64]
+        lib.zxo_stream_words.restype = C.c_uint64
+        lib.zxo_encode.argtypes = [C.c_int, P, C.c_uint64, C.c_int, C.c_int, C.POINTER(_CContainer)]
+        lib.zxo_decode.argtypes = [C.POINTER(_CContainer), P]
+        lib.zxo_free.argtypes = [C.POINTER(_CContainer)]
+        _lib = lib
+    return _lib
+
+
+def _alphabet(dtype: int) -> int:
+    return 256 if dtype == BF16 else 16
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(C.c_void_p)
+
+
+@dataclass
+class Container:
+    """One compressed tensor in container v1 layout (all arrays are numpy)."""
+    dtype: int
+    per_block: int
+    n: int
+    lengths: np.ndarray        # uint8 [ncb, A]
+    degenerate: np.ndarray     # uint16 [ncb]
+    signmant: np.ndarray       # uint8 [n] or [ceil(n/2)]
+    stream: np.ndarray         # uint32 [stream_words]
+    block_bitoff: np.ndarray   # uint64 [nblocks+1]
+    block_seg: np.ndarray      # uint32 [nblocks+1]
+    seg_desc: np.ndarray       # uint32 [nsegs, 2]
+    gaps: np.ndarray           # uint8 [nsegs, 64]
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def nblocks(self) -> int:
+        return (self.n + BLOCK - 1) // BLOCK
+
+    @property
+    def nsegs(self) -> int:
+        return int(self.block_seg[-1])
+
+    @property
+    def total_bits(self) -> int:
+        return int(self.block_bitoff[-1])
+
+    def nbytes(self) -> int:
+        """All container bytes: every array plus a 64-byte header."""
+        return int(64 + self.lengths.nbytes + self.degenerate.nbytes + self.signmant.nbytes
+                   + self.stream.nbytes + self.block_bitoff.nbytes + self.block_seg.nbytes
+                   + self.seg_desc.nbytes + self.gaps.nbytes)
+
+
+def split(dtype: int, x: np.ndarray):
+    lib = load()
+    x = np.ascontiguousarray(x)
+    n = x.size
+    exps = np.empty(max(n, 1), np.uint8)
+    sm = np.empty(max(n if dtype == BF16 else (n + 1) // 2, 1), np.uint8)
+    lib.zxo_split(dtype, _p(x), n, _p(exps), _p(sm))
+    return exps[:n], sm[: (n if dtype == BF16 else (n + 1) // 2)]
+
+
+def histogram(exps: np.ndarray, alphabet: int) -> np.ndarray:
+    lib = load()
+    exps = np.ascontiguousarray(exps, dtype=np.uint8)
+    h = np.zeros(alphabet, np.uint64)
+    lib.zxo_histogram(_p(exps), exps.size, alphabet, _p(h))
+    return h
+
+
+def huffman_lengths(hist) -> np.ndarray:
+    lib = load()
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    ln = np.zeros(h.size, np.uint8)
+    lib.zxo_huffman_lengths(_p(h), h.size, _p(ln))
+    return ln
+
+
+def package_merge(hist, L: int) -> np.ndarray:
+    lib = load()
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    ln = np.zeros(h.size, np.uint8)
+    if lib.zxo_package_merge(_p(h), h.size, int(L), _p(ln)) < 0:
+        raise ValueError("package-merge infeasible")
+    return ln
+
+
+def code_lengths(hist, max_len: int):
+    """(lengths uint8[A], degenerate symbol or 0xFFFF)."""
+    lib = load()
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    ln = np.zeros(h.size, np.uint8)
+    d = np.zeros(1, np.uint16)
+    if lib.zxo_code_lengths(_p(h), h.size, int(max_len), _p(ln), _p(d)) < 0:
+        raise ValueError("length limit infeasible")
+    return ln, int(d[0])
+
+
+def canonical_codes(lengths) -> np.ndarray:
+    lib = load()
+    ln = np.ascontiguousarray(lengths, dtype=np.uint8)
+    code = np.zeros(ln.size, np.uint32)
+    lib.zxo_canonical_codes(_p(ln), ln.size, _p(code))
+    return code
+
+
+def stream_words(total_bits: int) -> int:
+    return int(load().zxo_stream_words(int(total_bits)))
+
+
+def _arr(ptr, count, dtype):
+    if count == 0:
+        return np.zeros(0, dtype)
+    return np.ctypeslib.as_array(ptr, shape=(int(count),)).copy().astype(dtype, copy=False)
+
+
+def encode(dtype: int, x: np.ndarray, per_block: bool = False, max_len: int = 32) -> Container:
+    """Encode raw bits (uint16 for BF16, uint8 for FP8) into a container."""
+    lib = load()
+    x = np.ascontiguousarray(x).reshape(-1)
+    want = np.uint16 if dtype == BF16 else np.uint8
+    if x.dtype != want:
+        x = x.view(want)
+    cc = _CContainer()
+    rc = lib.zxo_encode(dtype, _p(x) if x.size else None, x.size, int(per_block), int(max_len), C.byref(cc))
+    if rc != 0:
+        raise ValueError(f"oracle encode failed rc={rc}")
+    try:
+        A = _alphabet(dtype)
+        ncb = int(cc.ncb)
+        c = Container(
+            dtype=dtype, per_block=int(per_block), n=int(cc.n),
+            lengths=_arr(cc.lengths, ncb * A, np.uint8).reshape(ncb, A),
+            degenerate=_arr(cc.degenerate, ncb, np.uint16),
+            signmant=_arr(cc.signmant, cc.signmant_bytes, np.uint8),
+            stream=_arr(cc.stream, cc.stream_words, np.uint32),
+            block_bitoff=_arr(cc.block_bitoff, cc.nblocks + 1, np.uint64),
+            block_seg=_arr(cc.block_seg, cc.nblocks + 1, np.uint32),
+            seg_desc=_arr(cc.seg_desc, 2 * cc.nsegs, np.uint32).reshape(-1, 2),
+            gaps=_arr(cc.gaps, SEG_CHUNKS * cc.nsegs, np.uint8).reshape(-1, SEG_CHUNKS),
+        )
+    finally:
+        lib.zxo_free(C.byref(cc))
+    return c
+
+
+def decode(c: Container) -> np.ndarray:
+    """Decode a container (from the oracle or from anywhere else); raises on any
+    inconsistency the oracle's checks find."""
+    lib = load()
+    A = _alphabet(c.dtype)
+    keep = [np.ascontiguousarray(a) for a in (c.lengths.reshape(-1), c.degenerate, c.signmant, c.stream,
+                                               c.block_bitoff, c.block_seg, c.seg_desc.reshape(-1),
+                                               c.gaps.reshape(-1))]
+    ln, dg, sm, st, bo, bs, sd, gp = keep
+    assert ln.dtype == np.uint8 and dg.dtype == np.uint16 and sm.dtype == np.uint8 and st.dtype == np.uint32
+    assert bo.dtype == np.uint64 and bs.dtype == np.uint32 and sd.dtype == np.uint32 and gp.dtype == np.uint8
+    nb = (c.n + BLOCK - 1) // BLOCK
+    cc = _CContainer()
+    cc.dtype = c.dtype
+    cc.per_block = int(c.per_block)
+    cc.n = c.n
+    cc.nblocks = nb
+    cc.ncb = ln.size // A
+    cc.nsegs = int(bs[-1])
+    cc.total_bits = int(bo[-1])
+    cc.stream_words = st.size
+    cc.signmant_bytes = sm.size
+
+    def ptr(a, t):
+        if a.size == 0:
+            a = np.zeros(1, a.dtype)
+            keep.append(a)
+        return a.ctypes.data_as(C.POINTER(t))
+
+    cc.lengths = ptr(ln, C.c_uint8)
+    cc.degenerate = ptr(dg, C.c_uint16)
+    cc.signmant = ptr(sm, C.c_uint8)
+    cc.stream = ptr(st, C.c_uint32)
+    cc.block_bitoff = ptr(bo, C.c_uint64)
+    cc.block_seg = ptr(bs, C.c_uint32)
+    cc.seg_desc = ptr(sd, C.c_uint32)
+    cc.gaps = ptr(gp, C.c_uint8)
+    out = np.empty(max(c.n, 1), np.uint16 if c.dtype == BF16 else np.uint8)
+    rc = lib.zxo_decode(C.byref(cc), _p(out))
+    if rc != 0:
+        raise ValueError(f"oracle decode rejected the container rc={rc}")
+    return out[: c.n]
