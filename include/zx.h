@@ -1,0 +1,186 @@
+/*
+ * zx.h -- C ABI of libzx: lossless canonical-Huffman coding of the exponent field
+ * of BF16 and FP8-E4M3FN tensors on AMD MI355X (gfx950).
+ *
+ * Method (from the pages this library follows):
+ *   - each float is split into its exponent field and the raw sign+mantissa bits;
+ *     only the exponent is entropy coded, with Huffman coding
+ *     (Intel paper summary "Lossless Compression of Neural Network Components:
+ *      Weights, Checkpoints, and K/V Caches in Low-Precision Formats", sections
+ *      方法论 / 方法详解 and the English abstract);
+ *   - the Huffman tree comes from the exponent distribution; coded exponents are
+ *     tightly bit-packed into one byte array (EncodedExponent) and sign+mantissa go
+ *     into a separate byte array (PackedSignMantissa)
+ *     (DFloat11 article "70% Size, 100% Accuracy ...", section 方法介绍, Fig. 2);
+ *   - a tensor is coded in fixed-size blocks (Intel summary, section 实验设计);
+ *   - the GPU decoder uses small lookup tables, a two-phase kernel whose auxiliary
+ *     variables tell each thread where to read and write, and block-level decode
+ *     (DFloat11 article, 方法介绍: three components);
+ *   - decoding is lossless bit for bit (DFloat11 article, 实验结果).
+ *
+ * Container v1 (all multi-byte values little-endian; every array is device memory):
+ *   block      65536 elements; block b = elements [65536 b, min(65536 (b+1), n)).
+ *   codebook   one per tensor (per_block = 0) or one per block (per_block = 1);
+ *              stored as code lengths only (lengths[cb][A], A = 256 for BF16,
+ *              16 for FP8), 0 = symbol absent.  A scope with a single exponent
+ *              value has all lengths 0 and degenerate[cb] = that value (0 bits per
+ *              element); otherwise degenerate[cb] = 0xFFFF.
+ *   lengths    Huffman lengths by two-queue merging (leaf queue in (count, symbol)
+ *              order wins weight ties), redone with package-merge when deeper than
+ *              max_len; canonical codes in (length, symbol) order (RFC 1951 3.2.2).
+ *   signmant   BF16: byte i = sign<<7 | mantissa7 of element i (n bytes).
+ *              FP8: nibble sign<<3 | mantissa3; element i in the low nibble of
+ *              byte i/2 when i is even, high nibble when odd (ceil(n/2) bytes).
+ *   stream     codes of all elements in order, MSB first; stream bit j is bit
+ *              31 - j%32 of u32 word j/32; blocks follow each other with no gap;
+ *              stream_words = round_up(ceil(total_bits/32), 4) + 4, zero padded.
+ *   block_bitoff[nblocks+1]  u64 stream bit where block b starts; last = total_bits.
+ *   block_seg[nblocks+1]     u32 first segment of block b; last = nsegs.
+ *              A block's bits are cut into 128-bit chunks (block-relative),
+ *              64 chunks per segment; a block has max(1, ceil(chunks/64)) segments.
+ *   seg_desc[nsegs][2]       u32 {block, index (in the block) of the first element
+ *              whose code starts at or after the segment's first bit}.
+ *   gaps[nsegs][64]          u8 per chunk: offset of the first code starting in the
+ *              chunk, 0xFF if none starts there or the chunk does not exist.
+ *
+ * Conventions for every entry point:
+ *   - every pointer argument is a device pointer unless stated otherwise; the
+ *     caller owns and allocates all memory (the library allocates nothing);
+ *   - device pointers must be 16-byte aligned;
+ *   - work is enqueued on `stream` and the call returns without synchronising;
+ *   - argument errors are detected on the host and returned synchronously before
+ *     anything is enqueued; data errors found on the device are written to the
+ *     optional device word `err` (first error wins, 0 = no error; the caller
+ *     clears it);
+ *   - the library keeps no global mutable state; calls on different streams may
+ *     run concurrently.
+ */
+#ifndef ZX_H
+#define ZX_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZX_BLOCK_ELEMS 65536u
+#define ZX_CHUNK_BITS 128u
+#define ZX_SEG_CHUNKS 64u
+#define ZX_MAX_CODE_LEN 32u
+#define ZX_NO_DEGENERATE 0xFFFFu
+#define ZX_NO_GAP 0xFFu
+
+typedef enum {
+    ZX_OK = 0,
+    ZX_E_INVAL = 1,        /* bad argument (null, misaligned, size out of range)   */
+    ZX_E_UNSUPPORTED = 2,  /* unknown dtype                                        */
+    ZX_E_CODEBOOK = 3,     /* max_len infeasible, or data/codebook mismatch        */
+    ZX_E_CORRUPT = 4,      /* container inconsistent (device-detected)             */
+    ZX_E_HIP = 5           /* a HIP launch failed                                  */
+} zx_status;
+
+typedef enum {
+    ZX_BF16 = 0,           /* 8-bit exponent, alphabet 256 */
+    ZX_FP8_E4M3FN = 1      /* 4-bit exponent, alphabet 16  */
+} zx_dtype;
+
+/* One compressed tensor (a host struct holding device pointers). */
+typedef struct zx_container {
+    int32_t dtype;                 /* zx_dtype                                          */
+    int32_t per_block;             /* 0: one codebook, 1: one codebook per block        */
+    uint64_t n;                    /* elements                                          */
+    uint64_t nsegs;                /* block_seg[nblocks]                                */
+    uint64_t total_bits;           /* block_bitoff[nblocks]                             */
+    uint64_t stream_words;         /* length of `stream` in u32 words                   */
+    const uint8_t *lengths;        /* [ncb][A]                                          */
+    const uint16_t *degenerate;    /* [ncb]                                             */
+    const uint8_t *signmant;       /* [n] (BF16) or [ceil(n/2)] (FP8)                   */
+    const uint32_t *stream;        /* [stream_words]                                    */
+    const uint64_t *block_bitoff;  /* [nblocks+1]                                       */
+    const uint32_t *block_seg;     /* [nblocks+1]                                       */
+    const uint32_t *seg_desc;      /* [nsegs][2]                                        */
+    const uint8_t *gaps;           /* [nsegs][64]                                       */
+    const uint32_t *dtab;          /* per_block = 0: decode table from
+                                      zx_build_decode_table (required); per_block = 1:
+                                      ignored (tables are built in the kernel)          */
+} zx_container;
+
+/* Exponent histogram (Intel summary, 方法论: the exponent distribution is what makes
+ * it compressible; DFloat11, 方法介绍: the tree is built from that distribution).
+ *   in           n elements: BF16 as u16 bits, FP8 as u8 bits.
+ *   tensor_hist  u32[A] or NULL: counts over the whole tensor (requires n < 2^32).
+ *   block_hist   u32[nblocks][A] or NULL: counts per 65536-element block.
+ * At least one output must be given. */
+zx_status zx_histogram(zx_dtype dtype, const void *in, uint64_t n,
+                       uint32_t *tensor_hist, uint32_t *block_hist, hipStream_t stream);
+
+/* Code lengths for n_codebooks histograms (DFloat11, 方法介绍: Huffman tree from the
+ * exponent distribution; the length limit and tie rules are container v1).
+ *   hist        u32[n_codebooks][A]
+ *   max_len     length limit, 8..32 for BF16, 4..32 for FP8 (else ZX_E_CODEBOOK)
+ *   lengths     u8[n_codebooks][A] out;  degenerate u16[n_codebooks] out. */
+zx_status zx_build_codebook(zx_dtype dtype, const uint32_t *hist, uint32_t n_codebooks,
+                            uint32_t max_len, uint8_t *lengths, uint16_t *degenerate,
+                            hipStream_t stream);
+
+/* Block geometry for encoding: per-block stream bits and segment counts, scanned.
+ * (Auxiliary read/write positions: DFloat11, 方法介绍, second component.)
+ *   lengths      u8[ncb][A] (ncb = 1, or nblocks when per_block)
+ *   block_hist   u32[nblocks][A] from zx_histogram, or NULL to read `in` instead
+ *   block_bitoff u64[nblocks+1] out;  block_seg u32[nblocks+1] out
+ *   totals       u64[2] out: {total_bits, nsegs}; the caller reads these back to
+ *                size the stream (zx_stream_words) and the segment arrays. */
+zx_status zx_encode_size(zx_dtype dtype, const void *in, uint64_t n, int per_block,
+                         const uint8_t *lengths, const uint32_t *block_hist,
+                         uint64_t *block_bitoff, uint32_t *block_seg, uint64_t *totals,
+                         hipStream_t stream);
+
+/* Encode: split fields, bit-pack exponent codes, write gaps and segment table
+ * (Intel summary, 方法论; DFloat11, 方法介绍 Fig. 2).
+ *   in, n, per_block, lengths, degenerate   as above
+ *   block_bitoff, block_seg                  from zx_encode_size
+ *   total_bits, nsegs                        the totals read back
+ *   signmant   u8 out [n] (BF16) or [ceil(n/2)] (FP8)
+ *   stream     u32 out [zx_stream_words(total_bits)]
+ *   seg_desc   u32 out [nsegs][2];  gaps  u8 out [nsegs][64]
+ *   err        optional: ZX_E_CODEBOOK if an element's exponent has no code. */
+zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int per_block,
+                    const uint8_t *lengths, const uint16_t *degenerate,
+                    const uint64_t *block_bitoff, const uint32_t *block_seg,
+                    uint64_t total_bits, uint64_t nsegs,
+                    uint8_t *signmant, uint32_t *stream, uint32_t *seg_desc, uint8_t *gaps,
+                    uint32_t *err, hipStream_t stream_);
+
+/* Decode table for one codebook (per-tensor scope): the small lookup tables the
+ * decoder keeps in LDS (DFloat11, 方法介绍: one large prefix-free table split into
+ * compact tables that fit on-chip memory).
+ *   lengths  u8[A];  dtab  out, zx_decode_table_bytes() bytes. */
+zx_status zx_build_decode_table(zx_dtype dtype, const uint8_t *lengths, uint32_t *dtab,
+                                hipStream_t stream);
+size_t zx_decode_table_bytes(void);
+
+/* Decode one container into out (n u16 BF16 bits, or n u8 FP8 bits): count pass,
+ * wavefront prefix scan of output positions, fused write pass (DFloat11, 方法介绍:
+ * two-phase kernel).  err: optional device word, ZX_E_CORRUPT on inconsistency;
+ * out is never written outside [0, n). */
+zx_status zx_decode(const zx_container *c, void *out, uint32_t *err, hipStream_t stream);
+
+/* Decode `count` containers (host array) into outs[i] (host array of device
+ * pointers) with one kernel launch: block-level decode of a group of tensors such
+ * as one transformer layer (DFloat11, 方法介绍: decompression at transformer-block
+ * level; 消融研究: its cost does not depend on batch size).  count <= 16. */
+zx_status zx_decode_block_batch(const zx_container *cs, void *const *outs, uint32_t count,
+                                uint32_t *err, hipStream_t stream);
+
+/* Stream length in u32 words for a given number of code bits. */
+uint64_t zx_stream_words(uint64_t total_bits);
+const char *zx_status_string(zx_status s);
+const char *zx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZX_H */

@@ -1,0 +1,185 @@
+// zx_common.h -- device-side helpers shared by the libzx kernels (gfx950, wave64).
+//
+// Canonical code tables are rebuilt on the device from code lengths alone, which
+// is all the container stores (DFloat11 article, 方法介绍: the Huffman tree comes
+// from the exponent distribution; container v1 keeps only its lengths).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zx.h"
+
+namespace zxk {
+
+constexpr uint32_t kBlock = 65536;       // elements per block
+constexpr uint32_t kChunkBits = 128;     // stream bits per decode chunk
+constexpr uint32_t kSegChunks = 64;      // chunks per segment (one wavefront lane each)
+constexpr uint32_t kSegBits = kChunkBits * kSegChunks;
+constexpr uint32_t kMaxLen = 32;
+constexpr int kWave = 64;
+
+// Decode lookup table index width: the primary table maps the next kLutBits
+// stream bits to up to two symbols.
+constexpr int kLutBits = 11;
+constexpr uint32_t kLutSize = 1u << kLutBits;
+
+__host__ __device__ constexpr uint32_t alphabet_of(int dtype) { return dtype == ZX_BF16 ? 256u : 16u; }
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+__device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
+
+__device__ __forceinline__ void report(uint32_t *err, uint32_t code)
+{
+    if (err) atomicCAS(err, 0u, code);
+}
+
+// Exclusive prefix sum across the 64 lanes of a wavefront; `total` gets the sum.
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t &total)
+{
+    uint32_t x = v;
+    const uint32_t lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        uint32_t y = __shfl_up(x, d, kWave);
+        if (lane >= (uint32_t)d) x += y;
+    }
+    total = __shfl(x, kWave - 1, kWave);
+    return x - v;
+}
+
+// Canonical-code description of one codebook, built in LDS by a whole workgroup.
+// Codes of length L are the consecutive integers first[L] .. first[L]+count[L]-1,
+// assigned to symbols in (length, symbol) order (RFC 1951, section 3.2.2).
+struct Canon {
+    uint32_t count[kMaxLen + 1];
+    uint32_t first[kMaxLen + 1];
+    uint32_t offset[kMaxLen + 1];       // position of the first length-L symbol in `sym`
+    uint32_t wcnt[16][kMaxLen + 1];     // per-wave symbol counts by length
+    uint64_t lim[kMaxLen + 2];          // (first[L]+count[L]) << (32-L), left-justified
+    uint32_t code[256];
+    uint8_t len[256];
+    uint8_t sym[256];
+    uint32_t nsym;
+    uint32_t maxlen;
+    uint32_t ok;                        // 1 if the lengths form a complete prefix code
+};
+
+// Build `c` from lengths_g[0..A).  Every thread of the workgroup must call it;
+// blockDim.x must be a multiple of 64, >= A and <= 1024.
+__device__ inline void canon_build(const uint8_t *__restrict__ lengths_g, uint32_t A, Canon &c)
+{
+    const uint32_t tid = threadIdx.x;
+    const uint32_t wave = tid / kWave;
+    const uint32_t nwaves = blockDim.x / kWave;
+    uint32_t l = 0;
+    if (tid < A) l = lengths_g[tid];
+    if (tid < A) c.len[tid] = (uint8_t)l;
+    // per-wave count and in-wave rank of each symbol among symbols of its length
+    uint32_t rank = 0;
+    const uint64_t lt = lanemask_lt();
+    for (uint32_t L = 1; L <= kMaxLen; ++L) {
+        uint64_t m = __ballot(tid < A && l == L);
+        if (l == L) rank = (uint32_t)__popcll(m & lt);
+        if (lane_id() == 0) c.wcnt[wave][L] = (uint32_t)__popcll(m);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t code = 0, idx = 0, maxlen = 0;
+        uint64_t kraft = 0;
+        for (uint32_t L = 1; L <= kMaxLen; ++L) {
+            uint32_t cnt = 0;
+            for (uint32_t w = 0; w < nwaves; ++w) cnt += c.wcnt[w][L];
+            c.count[L] = cnt;
+            c.first[L] = code;
+            c.offset[L] = idx;
+            uint64_t lim = ((uint64_t)code + cnt) << (kMaxLen - L);
+            c.lim[L] = lim;
+            if (cnt) maxlen = L;
+            kraft += (uint64_t)cnt << (kMaxLen - L);
+            // the next length starts right after this one's codes, one bit longer
+            // (a wrap here implies an over-full code, which the Kraft test rejects)
+            code = (uint32_t)(((uint64_t)code + cnt) << 1);
+            idx += cnt;
+        }
+        c.lim[kMaxLen + 1] = ~0ull;
+        c.count[0] = 0;
+        c.nsym = idx;
+        c.maxlen = maxlen;
+        c.ok = (idx >= 2 && kraft == (1ull << 32)) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (tid < A) {
+        uint32_t code = 0;
+        if (l) {
+            uint32_t r = rank;
+            for (uint32_t w = 0; w < wave; ++w) r += c.wcnt[w][l];
+            code = c.first[l] + r;
+            c.sym[c.offset[l] + r] = (uint8_t)tid;
+        }
+        c.code[tid] = code;
+    }
+    __syncthreads();
+}
+
+// Length of the code at the front of a left-justified 32-bit window, searching
+// lengths from `from` upward; returns kMaxLen+1 when nothing matches.
+__device__ __forceinline__ uint32_t canon_len(const uint64_t *lim, uint32_t v, uint32_t from)
+{
+    uint32_t L = from;
+    while (L <= kMaxLen && (uint64_t)v >= lim[L]) ++L;
+    return L;
+}
+
+// Decoder tables kept in LDS.  lut[x] for the next kLutBits bits x:
+//   bits  0..7  first symbol            bits  8..15 second symbol
+//   bits 16..19 first code length       bits 20..23 length of both codes
+//   bits 24..25 number of whole codes inside the window (0: longer than kLutBits)
+struct __align__(16) DTab {
+    uint32_t lut[kLutSize];
+    uint64_t lim[kMaxLen + 2];
+    int32_t base[kMaxLen + 1];          // offset[L] - first[L]
+    uint8_t sym[256];
+    uint32_t ok;
+    uint32_t nsym;
+    uint32_t maxlen;
+    uint32_t pad_;
+};
+static_assert(sizeof(DTab) % 16 == 0, "DTab must copy in 16-byte pieces");
+
+// Fill a DTab from a built Canon; every thread of the workgroup calls it.
+__device__ inline void dtab_fill(const Canon &c, DTab &t)
+{
+    const uint32_t tid = threadIdx.x;
+    for (uint32_t i = tid; i < kMaxLen + 2; i += blockDim.x) t.lim[i] = (i == 0) ? 0ull : c.lim[i];
+    for (uint32_t i = tid; i <= kMaxLen; i += blockDim.x) t.base[i] = (int32_t)c.offset[i] - (int32_t)c.first[i];
+    for (uint32_t i = tid; i < 256; i += blockDim.x) t.sym[i] = c.sym[i];
+    if (tid == 0) {
+        t.ok = c.ok;
+        t.nsym = c.nsym;
+        t.maxlen = c.maxlen;
+        t.pad_ = 0;
+    }
+    for (uint32_t x = tid; x < kLutSize; x += blockDim.x) {
+        uint32_t e = 0;
+        if (c.ok) {
+            uint32_t v = x << (32 - kLutBits);
+            uint32_t L1 = canon_len(c.lim, v, 1);
+            if (L1 <= (uint32_t)kLutBits) {
+                uint32_t s0 = c.sym[c.offset[L1] + ((v >> (32 - L1)) - c.first[L1])];
+                uint32_t rem = kLutBits - L1;
+                uint32_t v2 = v << L1;   // the bits after the first code, zero filled
+                uint32_t L2 = canon_len(c.lim, v2, 1);
+                if (L2 <= rem) {
+                    uint32_t s1 = c.sym[c.offset[L2] + ((v2 >> (32 - L2)) - c.first[L2])];
+                    e = s0 | (s1 << 8) | (L1 << 16) | ((L1 + L2) << 20) | (2u << 24);
+                } else {
+                    e = s0 | (L1 << 16) | (L1 << 20) | (1u << 24);
+                }
+            }
+        }
+        t.lut[x] = e;
+    }
+}
+
+}  // namespace zxk

@@ -1,0 +1,384 @@
+// zx_encode.hip -- field split, exponent bit-packing and the decoder's auxiliary
+// arrays, one workgroup per 65536-element block.
+//
+// Method: sign+mantissa stay raw in their own byte array, exponents are replaced by
+// their canonical Huffman codes, tightly bit-packed (DFloat11 article, 方法介绍,
+// Fig. 2; Intel summary, 方法论), tensor processed in fixed-size blocks (Intel
+// summary, 实验设计).  Fast online encode matters for K/V caches (ZipFloat page,
+// section 4.2; Intel summary, 局限性), so the whole encode runs on the GPU.
+//
+// Positions come from prefix sums, never from atomics: per-block bit counts are
+// scanned into block offsets, and inside a block each round of 2048 elements scans
+// its per-thread code lengths.  Codes are ORed into an LDS staging area aligned to
+// global stream words; whole words are then written with plain stores.  The only
+// words two blocks can share are a block's first and last word; those are cleared
+// beforehand and combined with atomicOr, which gives the same bytes in any order.
+#include "zx_common.h"
+
+namespace zxk {
+
+constexpr int kEncThreads = 256;
+constexpr uint32_t kEncPerThread = 8;
+constexpr uint32_t kRound = kEncThreads * kEncPerThread;   // 2048 elements per round
+constexpr uint32_t kStageWords = kRound + 2;               // up to 32 bits per element + carry
+
+// -------------------------------------------------------------------- block sizes
+template <int DT>
+__global__ __launch_bounds__(kEncThreads) void k_block_bits(const void *__restrict__ in, uint64_t n, int per_block,
+                                                            const uint8_t *__restrict__ lengths,
+                                                            const uint32_t *__restrict__ block_hist,
+                                                            uint64_t *__restrict__ block_bitoff,
+                                                            uint32_t *__restrict__ block_seg)
+{
+    constexpr uint32_t A = alphabet_of(DT);
+    __shared__ uint8_t len[256];
+    __shared__ uint32_t part[kEncThreads / kWave];
+    const uint32_t tid = threadIdx.x;
+    const uint64_t b = blockIdx.x;
+    const uint64_t cb = per_block ? b : 0;
+    if (tid < A) len[tid] = lengths[cb * A + tid];
+    __syncthreads();
+    uint32_t bits = 0;
+    if (block_hist) {
+        if (tid < A) bits = block_hist[b * A + tid] * (uint32_t)len[tid];
+    } else {
+        const uint64_t lo = b * kBlock;
+        const uint64_t hi = (lo + kBlock < n) ? lo + kBlock : n;
+        for (uint64_t i = lo + tid; i < hi; i += kEncThreads) {
+            uint32_t e;
+            if (DT == ZX_BF16)
+                e = (reinterpret_cast<const uint16_t *>(in)[i] >> 7) & 0xFFu;
+            else
+                e = (reinterpret_cast<const uint8_t *>(in)[i] >> 3) & 0xFu;
+            bits += len[e];
+        }
+    }
+    uint32_t tot;
+    wave_excl_scan(bits, tot);
+    if (lane_id() == 0) part[tid / kWave] = tot;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t s = 0;
+        for (uint32_t w = 0; w < kEncThreads / kWave; ++w) s += part[w];
+        const uint32_t nch = (s + kChunkBits - 1) / kChunkBits;
+        uint32_t nseg = (nch + kSegChunks - 1) / kSegChunks;
+        if (nseg == 0) nseg = 1;
+        block_bitoff[b + 1] = s;   // raw counts; k_scan_blocks turns them into offsets
+        block_seg[b + 1] = nseg;
+    }
+}
+
+// In-place inclusive scan over [1..nblocks] of both arrays; one workgroup.
+__global__ __launch_bounds__(1024) void k_scan_blocks(uint64_t nblocks, uint64_t *__restrict__ block_bitoff,
+                                                      uint32_t *__restrict__ block_seg, uint64_t *__restrict__ totals)
+{
+    __shared__ uint64_t wb[16];
+    __shared__ uint32_t ws[16];
+    const uint32_t tid = threadIdx.x;
+    const uint64_t per = (nblocks + 1023) / 1024;
+    const uint64_t lo = 1 + tid * per;
+    const uint64_t hi = (lo + per <= nblocks + 1) ? lo + per : nblocks + 1;
+    uint64_t sb = 0;
+    uint32_t ss = 0;
+    for (uint64_t i = lo; i < hi; ++i) {
+        sb += block_bitoff[i];
+        ss += block_seg[i];
+    }
+    // exclusive scan of (sb, ss) over the workgroup
+    uint64_t xb = sb;
+    uint32_t xs = ss;
+    const uint32_t lane = lane_id();
+    for (int d = 1; d < kWave; d <<= 1) {
+        uint64_t yb = __shfl_up(xb, d, kWave);
+        uint32_t ys = __shfl_up(xs, d, kWave);
+        if (lane >= (uint32_t)d) { xb += yb; xs += ys; }
+    }
+    if (lane == kWave - 1) { wb[tid / kWave] = xb; ws[tid / kWave] = xs; }
+    __syncthreads();
+    uint64_t ob = 0;
+    uint32_t os = 0;
+    for (uint32_t w = 0; w < tid / kWave; ++w) { ob += wb[w]; os += ws[w]; }
+    ob += xb - sb;
+    os += xs - ss;
+    for (uint64_t i = lo; i < hi; ++i) {
+        ob += block_bitoff[i];
+        os += block_seg[i];
+        block_bitoff[i] = ob;
+        block_seg[i] = os;
+    }
+    if (tid == 0) { block_bitoff[0] = 0; block_seg[0] = 0; }
+    __syncthreads();
+    if (tid == 1023) {
+        uint64_t tb = 0;
+        uint32_t ts = 0;
+        for (uint32_t w = 0; w < 16; ++w) { tb += wb[w]; ts += ws[w]; }
+        totals[0] = tb;
+        totals[1] = ts;
+    }
+}
+
+// Clear every stream word two blocks may share, and the tail padding.
+__global__ void k_clear_shared_words(uint64_t nblocks, const uint64_t *__restrict__ block_bitoff, uint64_t total_bits,
+                                     uint64_t stream_words, uint32_t *__restrict__ stream)
+{
+    const uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x;
+    if (i < nblocks) {
+        const uint64_t g0 = block_bitoff[i], g1 = block_bitoff[i + 1];
+        if (g1 > g0 && g1 <= total_bits) {
+            stream[g0 >> 5] = 0;
+            stream[(g1 - 1) >> 5] = 0;
+        }
+    }
+    const uint64_t tail = total_bits >> 5;
+    for (uint64_t w = tail + i; w < stream_words; w += (uint64_t)gridDim.x * blockDim.x) stream[w] = 0;
+}
+
+// -------------------------------------------------------------------- bit packing
+template <int DT>
+__global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__ in, uint64_t n, int per_block,
+                                                        const uint8_t *__restrict__ lengths,
+                                                        const uint16_t *__restrict__ degenerate,
+                                                        const uint64_t *__restrict__ block_bitoff,
+                                                        const uint32_t *__restrict__ block_seg,
+                                                        uint8_t *__restrict__ signmant, uint32_t *__restrict__ stream,
+                                                        uint32_t *__restrict__ seg_desc, uint8_t *__restrict__ gaps,
+                                                        uint64_t total_bits, uint64_t nsegs, uint32_t *__restrict__ err)
+{
+    constexpr uint32_t A = alphabet_of(DT);
+    __shared__ Canon c;
+    __shared__ uint32_t stage[kStageWords];
+    __shared__ uint32_t part[kEncThreads / kWave];
+    __shared__ uint32_t s_bad;
+
+    const uint32_t tid = threadIdx.x;
+    const uint64_t b = blockIdx.x;
+    const uint64_t cb = per_block ? b : 0;
+    canon_build(lengths + cb * A, A, c);
+    const uint32_t degen = degenerate[cb];
+    const uint64_t G = block_bitoff[b];
+    const uint64_t bits = block_bitoff[b + 1] - G;
+    const uint32_t s0 = block_seg[b];
+    const uint32_t nsb = block_seg[b + 1] - s0;
+    const uint64_t lo = b * kBlock;
+    const uint32_t nb = (uint32_t)(((lo + kBlock < n) ? lo + kBlock : n) - lo);
+    const uint32_t nch = (uint32_t)((bits + kChunkBits - 1) / kChunkBits);
+    // the geometry must be the one zx_encode_size produced for these sizes
+    if (block_bitoff[b + 1] < G || block_bitoff[b + 1] > total_bits || block_seg[b + 1] < s0 || block_seg[b + 1] > nsegs ||
+        bits > (uint64_t)nb * kMaxLen || (uint64_t)nsb * kSegChunks < nch || nsb == 0) {
+        if (tid == 0) report(err, ZX_E_CORRUPT);
+        return;
+    }
+    const uint64_t w_first = G >> 5;
+    const uint64_t w_last = bits ? (G + bits - 1) >> 5 : w_first;
+
+    if (tid == 0) {
+        s_bad = 0;
+        seg_desc[2 * (uint64_t)s0] = (uint32_t)b;
+        seg_desc[2 * (uint64_t)s0 + 1] = 0;
+    }
+    // chunks past the block's last chunk, in its last segment
+    for (uint32_t ch = nch + tid; ch < nsb * kSegChunks; ch += kEncThreads) gaps[(uint64_t)s0 * kSegChunks + ch] = (uint8_t)ZX_NO_GAP;
+    for (uint32_t i = tid; i < kStageWords; i += kEncThreads) stage[i] = 0;
+    __syncthreads();
+
+    uint32_t a0 = (uint32_t)(G & 31);   // stage bit of the round's first code
+    uint64_t W = G >> 5;                // global word held by stage[0]
+    uint32_t P = 0;                     // block-relative bit of the round's first code
+    bool bad = false;
+    const uint32_t nrounds = (nb + kRound - 1) / kRound;
+    for (uint32_t r = 0; r < nrounds; ++r) {
+        const uint32_t i0 = r * kRound + tid * kEncPerThread;   // block-relative element
+        const uint32_t have = (i0 < nb) ? ((nb - i0 < kEncPerThread) ? nb - i0 : kEncPerThread) : 0;
+        uint32_t u[kEncPerThread];
+        // ---- load and split
+        if (DT == ZX_BF16) {
+            const uint16_t *src = reinterpret_cast<const uint16_t *>(in) + lo + i0;
+            if (have == kEncPerThread) {
+                const uint4 q = *reinterpret_cast<const uint4 *>(src);
+                const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (uint32_t k = 0; k < kEncPerThread; ++k) u[k] = (wv[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+                uint64_t smv = 0;
+#pragma unroll
+                for (uint32_t k = 0; k < kEncPerThread; ++k) smv |= (uint64_t)(((u[k] >> 8) & 0x80u) | (u[k] & 0x7Fu)) << (8 * k);
+                *reinterpret_cast<uint64_t *>(signmant + lo + i0) = smv;
+            } else {
+#pragma unroll
+                for (uint32_t k = 0; k < kEncPerThread; ++k) {
+                    u[k] = 0;
+                    if (k < have) {
+                        u[k] = src[k];
+                        signmant[lo + i0 + k] = (uint8_t)(((u[k] >> 8) & 0x80u) | (u[k] & 0x7Fu));
+                    }
+                }
+            }
+        } else {
+            const uint8_t *src = reinterpret_cast<const uint8_t *>(in) + lo + i0;
+            if (have == kEncPerThread) {
+                const uint2 q = *reinterpret_cast<const uint2 *>(src);
+                const uint32_t wv[2] = {q.x, q.y};
+#pragma unroll
+                for (uint32_t k = 0; k < kEncPerThread; ++k) u[k] = (wv[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+                uint32_t nib = 0;
+#pragma unroll
+                for (uint32_t k = 0; k < kEncPerThread; ++k) nib |= (((u[k] >> 4) & 0x8u) | (u[k] & 0x7u)) << (4 * k);
+                *reinterpret_cast<uint32_t *>(signmant + (lo + i0) / 2) = nib;
+            } else {
+#pragma unroll
+                for (uint32_t k = 0; k < kEncPerThread; ++k) u[k] = (k < have) ? src[k] : 0u;
+                for (uint32_t k = 0; k < have; k += 2) {
+                    uint32_t lo_n = ((u[k] >> 4) & 0x8u) | (u[k] & 0x7u);
+                    uint32_t hi_n = (k + 1 < have) ? (((u[k + 1] >> 4) & 0x8u) | (u[k + 1] & 0x7u)) : 0u;
+                    signmant[(lo + i0 + k) / 2] = (uint8_t)(lo_n | (hi_n << 4));
+                }
+            }
+        }
+        // ---- code lengths of this thread's elements
+        uint32_t sym[kEncPerThread];
+        uint32_t tb = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < kEncPerThread; ++k) {
+            sym[k] = (DT == ZX_BF16) ? ((u[k] >> 7) & 0xFFu) : ((u[k] >> 3) & 0xFu);
+            if (k < have) {
+                const uint32_t l = c.len[sym[k]];
+                if (bits ? (l == 0) : (sym[k] != degen)) bad = true;
+                tb += l;
+            }
+        }
+        // ---- workgroup exclusive scan of code bits
+        uint32_t wtot;
+        uint32_t o = wave_excl_scan(tb, wtot);
+        if (lane_id() == 0) part[tid / kWave] = wtot;
+        __syncthreads();
+        uint32_t R = 0;
+        for (uint32_t w = 0; w < kEncThreads / kWave; ++w) {
+            const uint32_t pw = part[w];
+            if (w < tid / kWave) o += pw;
+            R += pw;
+        }
+        // ---- place codes, write gaps and segment entries
+        uint32_t q = a0 + o;     // stage bit
+        uint32_t p = P + o;      // block-relative stream bit
+#pragma unroll
+        for (uint32_t k = 0; k < kEncPerThread; ++k) {
+            if (k >= have) break;
+            const uint32_t l = c.len[sym[k]];
+            if (l == 0) continue;
+            const uint32_t cd = (p + kChunkBits - 1) / kChunkBits;   // first chunk boundary >= p
+            if (cd * kChunkBits < p + l) {
+                // this code covers the first bit of chunk cd
+                uint32_t gap;
+                if (cd * kChunkBits == p)
+                    gap = 0;
+                else
+                    gap = (p + l < bits) ? p + l - cd * kChunkBits : ZX_NO_GAP;
+                const uint64_t seg = s0 + cd / kSegChunks;
+                gaps[seg * kSegChunks + (cd % kSegChunks)] = (uint8_t)gap;
+                if (cd % kSegChunks == 0 && cd > 0) {
+                    seg_desc[2 * seg] = (uint32_t)b;
+                    seg_desc[2 * seg + 1] = (cd * kChunkBits == p) ? (i0 + k) : (i0 + k + 1);
+                }
+            }
+            const uint32_t code = c.code[sym[k]];
+            const uint32_t sh = q & 31;
+            const uint64_t x = (uint64_t)code << (64 - l - sh);
+            atomicOr(&stage[q >> 5], (uint32_t)(x >> 32));
+            if (sh + l > 32) atomicOr(&stage[(q >> 5) + 1], (uint32_t)x);
+            q += l;
+            p += l;
+        }
+        __syncthreads();
+        // ---- flush whole words, keep the partial last word as the next carry
+        const uint32_t nw = (a0 + R) >> 5;
+        for (uint32_t i = tid; i < nw; i += kEncThreads) {
+            const uint64_t gw = W + i;
+            const uint32_t val = stage[i];
+            if (gw == w_first || gw == w_last)
+                atomicOr(&stream[gw], val);
+            else
+                stream[gw] = val;
+        }
+        const uint32_t carry = stage[nw];
+        __syncthreads();
+        for (uint32_t i = tid; i < kStageWords; i += kEncThreads) stage[i] = (i == 0) ? carry : 0u;
+        __syncthreads();
+        W += nw;
+        a0 = (a0 + R) & 31;
+        P += R;
+    }
+    if (tid == 0 && bits && a0) atomicOr(&stream[W], stage[0]);
+    if (bad) s_bad = 1;
+    __syncthreads();
+    if (tid == 0 && s_bad) report(err, ZX_E_CODEBOOK);
+}
+
+}  // namespace zxk
+
+using namespace zxk;
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+extern "C" uint64_t zx_stream_words(uint64_t total_bits)
+{
+    uint64_t w = (total_bits + 31) / 32;
+    w = (w + 3) / 4 * 4;
+    return w + 4;
+}
+
+extern "C" zx_status zx_encode_size(zx_dtype dtype, const void *in, uint64_t n, int per_block,
+                                    const uint8_t *lengths, const uint32_t *block_hist,
+                                    uint64_t *block_bitoff, uint32_t *block_seg, uint64_t *totals,
+                                    hipStream_t stream)
+{
+    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    if (!block_bitoff || !block_seg || !totals) return ZX_E_INVAL;
+    const uint64_t nblocks = (n + kBlock - 1) / kBlock;
+    if (nblocks > 0x7FFFFFFFull) return ZX_E_INVAL;
+    if (nblocks && (!lengths || (!block_hist && !in))) return ZX_E_INVAL;
+    if (!aligned16(in) || !aligned16(block_hist)) return ZX_E_INVAL;
+    if (nblocks) {
+        if (dtype == ZX_BF16)
+            hipLaunchKernelGGL(k_block_bits<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream, in, n, per_block, lengths,
+                               block_hist, block_bitoff, block_seg);
+        else
+            hipLaunchKernelGGL(k_block_bits<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream, in, n, per_block,
+                               lengths, block_hist, block_bitoff, block_seg);
+        if (hipGetLastError() != hipSuccess) return ZX_E_HIP;
+    }
+    hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(1024), 0, stream, nblocks, block_bitoff, block_seg, totals);
+    return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}
+
+extern "C" zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int per_block,
+                               const uint8_t *lengths, const uint16_t *degenerate,
+                               const uint64_t *block_bitoff, const uint32_t *block_seg,
+                               uint64_t total_bits, uint64_t nsegs,
+                               uint8_t *signmant, uint32_t *stream, uint32_t *seg_desc, uint8_t *gaps,
+                               uint32_t *err, hipStream_t stream_)
+{
+    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    const uint64_t nblocks = (n + kBlock - 1) / kBlock;
+    if (nblocks > 0x7FFFFFFFull || nsegs > 0xFFFFFFFFull) return ZX_E_INVAL;
+    if (!stream || !block_bitoff) return ZX_E_INVAL;
+    if (nblocks && (!in || !lengths || !degenerate || !block_seg || !signmant || !seg_desc || !gaps)) return ZX_E_INVAL;
+    if (!aligned16(in) || !aligned16(signmant) || !aligned16(stream)) return ZX_E_INVAL;
+    if (nsegs < nblocks) return ZX_E_INVAL;
+    const uint64_t words = zx_stream_words(total_bits);
+    {
+        const uint32_t threads = 256;
+        uint64_t grid = (nblocks + threads - 1) / threads;
+        if (grid == 0) grid = 1;
+        if (grid > 65535) grid = 65535;
+        hipLaunchKernelGGL(k_clear_shared_words, dim3((uint32_t)grid), dim3(threads), 0, stream_, nblocks, block_bitoff, total_bits,
+                           words, stream);
+        if (hipGetLastError() != hipSuccess) return ZX_E_HIP;
+    }
+    if (nblocks == 0) return ZX_OK;
+    if (dtype == ZX_BF16)
+        hipLaunchKernelGGL(k_encode<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream_, in, n, per_block, lengths,
+                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, err);
+    else
+        hipLaunchKernelGGL(k_encode<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream_, in, n, per_block, lengths,
+                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, err);
+    return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}

@@ -1,0 +1,118 @@
+// zx_hist.hip -- exponent histogram with wavefront-ballot aggregation.
+//
+// The exponent distribution is what the Huffman tree is built from (DFloat11
+// article, 方法介绍; Intel summary, 方法论).  Exponents of weights and K/V values
+// cluster on a few values (ZipFloat page, section 2, Tables 1-2), so within one
+// wavefront most lanes share a handful of values: each round the wavefront picks
+// the value of its first unfinished lane, ballots the lanes holding that value and
+// adds the popcount with a single LDS atomic.  The number of rounds is the number
+// of distinct values among the 64 lanes, not 64.
+#include "zx_common.h"
+
+namespace zxk {
+
+constexpr int kHistThreads = 256;
+
+// Add one exponent per lane (valid lanes only) into the LDS histogram.
+__device__ __forceinline__ void ballot_add(uint32_t *h, uint32_t e, bool valid)
+{
+    bool todo = valid;
+    while (true) {
+        uint64_t act = __ballot(todo);
+        if (act == 0) break;
+        const int leader = __ffsll((long long)act) - 1;
+        const uint32_t v = __shfl(e, leader, kWave);
+        const uint64_t same = __ballot(todo && e == v);
+        if (lane_id() == (uint32_t)leader) atomicAdd(&h[v], (uint32_t)__popcll(same));
+        if (e == v) todo = false;
+    }
+}
+
+// One workgroup per 65536-element block.
+template <int DT>
+__global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restrict__ in, uint64_t n,
+                                                            uint32_t *__restrict__ tensor_hist,
+                                                            uint32_t *__restrict__ block_hist)
+{
+    constexpr uint32_t A = alphabet_of(DT);
+    __shared__ uint32_t h[256];
+    const uint32_t tid = threadIdx.x;
+    const uint64_t b = blockIdx.x;
+    for (uint32_t i = tid; i < A; i += blockDim.x) h[i] = 0;
+    __syncthreads();
+    const uint64_t lo = b * kBlock;
+    const uint64_t hi = (lo + kBlock < n) ? lo + kBlock : n;
+    const uint32_t nb = (uint32_t)(hi - lo);
+    // 16 bytes per lane per step: 8 BF16 or 16 FP8 elements
+    constexpr uint32_t EPV = DT == ZX_BF16 ? 8 : 16;
+    const uint32_t nvec = (nb + EPV - 1) / EPV;
+    const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(in) + lo * (DT == ZX_BF16 ? 2 : 1));
+    for (uint32_t v = tid; v < (nvec + kHistThreads - 1) / kHistThreads * kHistThreads; v += kHistThreads) {
+        uint32_t words[4] = {0, 0, 0, 0};
+        uint32_t have = 0;  // valid elements in this vector
+        if (v < nvec) {
+            const uint32_t first = v * EPV;
+            have = (nb - first < EPV) ? nb - first : EPV;
+            if (have == EPV) {
+                uint4 q = src[v];
+                words[0] = q.x; words[1] = q.y; words[2] = q.z; words[3] = q.w;
+            } else {
+                const uint8_t *bytes = reinterpret_cast<const uint8_t *>(src) + (uint64_t)first * (DT == ZX_BF16 ? 2 : 1);
+                const uint32_t nbytes = have * (DT == ZX_BF16 ? 2 : 1);
+                for (uint32_t k = 0; k < nbytes; ++k) words[k >> 2] |= (uint32_t)bytes[k] << (8 * (k & 3));
+            }
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < EPV; ++k) {
+            uint32_t e;
+            if (DT == ZX_BF16) {
+                const uint32_t u = (words[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+                e = (u >> 7) & 0xFFu;
+            } else {
+                const uint32_t u = (words[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+                e = (u >> 3) & 0xFu;
+            }
+            ballot_add(h, e, k < have);
+        }
+    }
+    __syncthreads();
+    for (uint32_t i = tid; i < A; i += blockDim.x) {
+        const uint32_t c = h[i];
+        if (block_hist) block_hist[b * A + i] = c;
+        if (tensor_hist && c) atomicAdd(&tensor_hist[i], c);
+    }
+}
+
+__global__ void k_zero_u32(uint32_t *p, uint64_t count)
+{
+    for (uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; i < count; i += (uint64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+}  // namespace zxk
+
+using namespace zxk;
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+extern "C" zx_status zx_histogram(zx_dtype dtype, const void *in, uint64_t n, uint32_t *tensor_hist,
+                                  uint32_t *block_hist, hipStream_t stream)
+{
+    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    if (!tensor_hist && !block_hist) return ZX_E_INVAL;
+    if (n && !in) return ZX_E_INVAL;
+    if (!aligned16(in) || !aligned16(tensor_hist) || !aligned16(block_hist)) return ZX_E_INVAL;
+    if (tensor_hist && n >= (1ull << 32)) return ZX_E_INVAL;
+    const uint32_t A = alphabet_of(dtype);
+    const uint64_t nblocks = (n + kBlock - 1) / kBlock;
+    if (nblocks > 0x7FFFFFFFull) return ZX_E_INVAL;
+    if (tensor_hist) {
+        hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(256), 0, stream, tensor_hist, (uint64_t)A);
+        if (hipGetLastError() != hipSuccess) return ZX_E_HIP;
+    }
+    if (nblocks == 0) return ZX_OK;
+    if (dtype == ZX_BF16)
+        hipLaunchKernelGGL(k_histogram<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, tensor_hist, block_hist);
+    else
+        hipLaunchKernelGGL(k_histogram<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, tensor_hist, block_hist);
+    return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}

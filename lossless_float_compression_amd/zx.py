@@ -1,0 +1,278 @@
+"""Python binding of libzx (ctypes).
+
+This is argument marshalling only.  Every step of the codec runs in the HIP kernels
+behind the C ABI in include/zx.h.  PyTorch supplies device memory and the current
+stream.  If libzx.so is missing, this module raises: there is no CPU fallback.
+
+Low-level names mirror the C ABI (zx_histogram, zx_build_codebook, zx_encode_size,
+zx_encode, zx_build_decode_table, zx_decode, zx_decode_block_batch).  `compress`,
+`decompress` and `decompress_batch` chain them and allocate the outputs.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+BF16 = 0
+FP8_E4M3FN = 1
+BLOCK_ELEMS = 65536
+SEG_CHUNKS = 64
+MAX_BATCH = 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzx.so")
+_lib = None
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype", 3: "codebook error",
+           4: "corrupt container", 5: "HIP launch failure"}
+
+
+class ZxError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {_STATUS.get(status, status)} ({status})")
+        self.status = status
+
+
+class zx_container(C.Structure):
+    _fields_ = [
+        ("dtype", C.c_int32), ("per_block", C.c_int32),
+        ("n", C.c_uint64), ("nsegs", C.c_uint64), ("total_bits", C.c_uint64), ("stream_words", C.c_uint64),
+        ("lengths", C.c_void_p), ("degenerate", C.c_void_p), ("signmant", C.c_void_p), ("stream", C.c_void_p),
+        ("block_bitoff", C.c_void_p), ("block_seg", C.c_void_p), ("seg_desc", C.c_void_p), ("gaps", C.c_void_p),
+        ("dtab", C.c_void_p),
+    ]
+
+
+EXPORTS = ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
+           "zx_decode_table_bytes", "zx_decode", "zx_decode_block_batch", "zx_stream_words",
+           "zx_status_string", "zx_version")
+
+
+def lib():
+    """Load libzx.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                               "`python -m lossless_float_compression_amd._build` (there is no fallback)")
+        L = C.CDLL(LIB_PATH)
+        P, U64, U32, I = C.c_void_p, C.c_uint64, C.c_uint32, C.c_int
+        L.zx_histogram.argtypes = [I, P, U64, P, P, P]
+        L.zx_build_codebook.argtypes = [I, P, U32, U32, P, P, P]
+        L.zx_encode_size.argtypes = [I, P, U64, I, P, P, P, P, P, P]
+        L.zx_encode.argtypes = [I, P, U64, I, P, P, P, P, U64, U64, P, P, P, P, P, P]
+        L.zx_build_decode_table.argtypes = [I, P, P, P]
+        L.zx_decode_table_bytes.argtypes = []
+        L.zx_decode_table_bytes.restype = C.c_size_t
+        L.zx_decode.argtypes = [C.POINTER(zx_container), P, P, P]
+        L.zx_decode_block_batch.argtypes = [C.POINTER(zx_container), C.POINTER(C.c_void_p), U32, P, P]
+        L.zx_stream_words.argtypes = [U64]
+        L.zx_stream_words.restype = U64
+        L.zx_status_string.argtypes = [I]
+        L.zx_status_string.restype = C.c_char_p
+        L.zx_version.restype = C.c_char_p
+        for f in ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
+                  "zx_decode", "zx_decode_block_batch"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise ZxError(fn, st)
+
+
+def alphabet(dtype: int) -> int:
+    return 256 if dtype == BF16 else 16
+
+
+def nblocks_of(n: int) -> int:
+    return (n + BLOCK_ELEMS - 1) // BLOCK_ELEMS
+
+
+# ----------------------------------------------------------------- C ABI mirrors
+
+def zx_histogram(dtype, inp, n, tensor_hist=None, block_hist=None, stream=None):
+    _check("zx_histogram", lib().zx_histogram(dtype, _ptr(inp), n, _ptr(tensor_hist), _ptr(block_hist), _stream(stream)))
+
+
+def zx_build_codebook(dtype, hist, n_codebooks, max_len, lengths, degenerate, stream=None):
+    _check("zx_build_codebook", lib().zx_build_codebook(dtype, _ptr(hist), n_codebooks, max_len, _ptr(lengths),
+                                                        _ptr(degenerate), _stream(stream)))
+
+
+def zx_encode_size(dtype, inp, n, per_block, lengths, block_hist, block_bitoff, block_seg, totals, stream=None):
+    _check("zx_encode_size", lib().zx_encode_size(dtype, _ptr(inp), n, int(per_block), _ptr(lengths), _ptr(block_hist),
+                                                  _ptr(block_bitoff), _ptr(block_seg), _ptr(totals), _stream(stream)))
+
+
+def zx_encode(dtype, inp, n, per_block, lengths, degenerate, block_bitoff, block_seg, total_bits, nsegs,
+              signmant, stream_words, seg_desc, gaps, err=None, stream=None):
+    _check("zx_encode", lib().zx_encode(dtype, _ptr(inp), n, int(per_block), _ptr(lengths), _ptr(degenerate),
+                                        _ptr(block_bitoff), _ptr(block_seg), total_bits, nsegs, _ptr(signmant),
+                                        _ptr(stream_words), _ptr(seg_desc), _ptr(gaps), _ptr(err), _stream(stream)))
+
+
+def zx_build_decode_table(dtype, lengths, dtab, stream=None):
+    _check("zx_build_decode_table", lib().zx_build_decode_table(dtype, _ptr(lengths), _ptr(dtab), _stream(stream)))
+
+
+def zx_decode_table_bytes() -> int:
+    return int(lib().zx_decode_table_bytes())
+
+
+def zx_stream_words(total_bits: int) -> int:
+    return int(lib().zx_stream_words(int(total_bits)))
+
+
+def zx_decode(container: zx_container, out, err=None, stream=None):
+    _check("zx_decode", lib().zx_decode(C.byref(container), _ptr(out), _ptr(err), _stream(stream)))
+
+
+def zx_decode_block_batch(containers: Sequence[zx_container], outs: Sequence[torch.Tensor], err=None, stream=None):
+    k = len(containers)
+    arr = (zx_container * k)(*containers)
+    optrs = (C.c_void_p * k)(*[o.data_ptr() for o in outs])
+    _check("zx_decode_block_batch", lib().zx_decode_block_batch(arr, optrs, k, _ptr(err), _stream(stream)))
+
+
+# ----------------------------------------------------------------- compressed tensor
+
+@dataclass
+class Compressed:
+    """A compressed tensor: container v1 arrays as device tensors."""
+    dtype: int
+    per_block: int
+    n: int
+    shape: tuple
+    total_bits: int
+    nsegs: int
+    lengths: torch.Tensor      # uint8 [ncb, A]
+    degenerate: torch.Tensor   # int16 (u16 bits) [ncb]
+    signmant: torch.Tensor     # uint8
+    stream: torch.Tensor       # int32 (u32 bits) [stream_words]
+    block_bitoff: torch.Tensor # int64 (u64 bits) [nblocks+1]
+    block_seg: torch.Tensor    # int32 (u32 bits) [nblocks+1]
+    seg_desc: torch.Tensor     # int32 (u32 bits) [nsegs, 2]
+    gaps: torch.Tensor         # uint8 [nsegs, 64]
+    dtab: Optional[torch.Tensor] = None  # uint8 decode table (per-tensor scope)
+    fp8_scale: Optional[float] = None    # carried raw for FP8 tensors, never applied
+
+    def container(self) -> zx_container:
+        c = zx_container()
+        c.dtype, c.per_block, c.n = self.dtype, self.per_block, self.n
+        c.nsegs, c.total_bits, c.stream_words = self.nsegs, self.total_bits, self.stream.numel()
+        c.lengths, c.degenerate = self.lengths.data_ptr(), self.degenerate.data_ptr()
+        c.signmant, c.stream = self.signmant.data_ptr(), self.stream.data_ptr()
+        c.block_bitoff, c.block_seg = self.block_bitoff.data_ptr(), self.block_seg.data_ptr()
+        c.seg_desc, c.gaps = self.seg_desc.data_ptr(), self.gaps.data_ptr()
+        c.dtab = self.dtab.data_ptr() if self.dtab is not None else None
+        return c
+
+    def nbytes(self) -> int:
+        """All container bytes (arrays + a 64-byte header), excluding the decode
+        table, which is derived from the lengths."""
+        return int(64 + sum(t.numel() * t.element_size() for t in (
+            self.lengths, self.degenerate, self.signmant, self.stream, self.block_bitoff,
+            self.block_seg, self.seg_desc, self.gaps)))
+
+    def raw_bytes(self) -> int:
+        return self.n * (2 if self.dtype == BF16 else 1)
+
+
+def _as_bits(x: torch.Tensor):
+    """(dtype code, flat raw-bit view) of a bf16 / float8_e4m3fn / int16 / uint8 tensor."""
+    if x.dtype in (torch.bfloat16, torch.int16):
+        return BF16, x.reshape(-1).view(torch.int16)
+    if x.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return FP8_E4M3FN, x.reshape(-1).view(torch.uint8)
+    raise TypeError(f"unsupported dtype {x.dtype}")
+
+
+def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_scale: Optional[float] = None,
+             stream=None) -> Compressed:
+    """Encode a device tensor (bf16 or int16 bits -> BF16; float8_e4m3fn or uint8 bits -> FP8).
+
+    Runs histogram -> codebook -> block sizes, reads back the two totals (the single
+    host synchronisation) to size the outputs, then encodes."""
+    dtype, flat = _as_bits(x)
+    if not flat.is_cuda:
+        raise ValueError("compress expects a device tensor")
+    flat = flat.contiguous()
+    dev = flat.device
+    n = flat.numel()
+    A = alphabet(dtype)
+    nb = nblocks_of(n)
+    ncb = nb if per_block else 1
+    u8 = dict(dtype=torch.uint8, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    block_hist = torch.empty((max(nb, 1), A), **i32)
+    tensor_hist = None if per_block else torch.empty(A, **i32)
+    lengths = torch.empty((max(ncb, 1), A), **u8)
+    degenerate = torch.empty(max(ncb, 1), dtype=torch.int16, device=dev)
+    block_bitoff = torch.empty(nb + 1, dtype=torch.int64, device=dev)
+    block_seg = torch.empty(nb + 1, **i32)
+    totals = torch.empty(2, dtype=torch.int64, device=dev)
+    zx_histogram(dtype, flat, n, tensor_hist, block_hist, stream)
+    zx_build_codebook(dtype, block_hist if per_block else tensor_hist, ncb, max_len, lengths, degenerate, stream)
+    if per_block and nb == 0:
+        lengths = lengths[:0]
+        degenerate = degenerate[:0]
+    zx_encode_size(dtype, flat, n, per_block, lengths, block_hist, block_bitoff, block_seg, totals, stream)
+    total_bits, nsegs = (int(v) for v in totals.cpu().tolist())
+    signmant = torch.empty(n if dtype == BF16 else (n + 1) // 2, **u8)
+    words = torch.empty(zx_stream_words(total_bits), **i32)
+    seg_desc = torch.empty((nsegs, 2), **i32)
+    gaps = torch.empty((nsegs, SEG_CHUNKS), **u8)
+    err = torch.zeros(1, **i32)
+    zx_encode(dtype, flat, n, per_block, lengths, degenerate, block_bitoff, block_seg, total_bits, nsegs,
+              signmant, words, seg_desc, gaps, err, stream)
+    dtab = None
+    if not per_block:
+        dtab = torch.empty(zx_decode_table_bytes(), **u8)
+        zx_build_decode_table(dtype, lengths, dtab, stream)
+    c = Compressed(dtype=dtype, per_block=int(per_block), n=n, shape=tuple(x.shape), total_bits=total_bits,
+                   nsegs=nsegs, lengths=lengths, degenerate=degenerate, signmant=signmant, stream=words,
+                   block_bitoff=block_bitoff, block_seg=block_seg, seg_desc=seg_desc, gaps=gaps, dtab=dtab,
+                   fp8_scale=fp8_scale)
+    c._err = err  # device word set by the encoder on a data/codebook mismatch
+    return c
+
+
+def empty_output(c: Compressed, device=None) -> torch.Tensor:
+    dev = device if device is not None else c.signmant.device
+    if c.dtype == BF16:
+        return torch.empty(c.shape, dtype=torch.bfloat16, device=dev)
+    return torch.empty(c.shape, dtype=torch.float8_e4m3fn, device=dev)
+
+
+def decompress(c: Compressed, out: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None, stream=None):
+    """Decode into `out` (allocated when None).  `err` is an optional int32 device
+    word that receives 4 (corrupt) if the decoder finds an inconsistency."""
+    if out is None:
+        out = empty_output(c)
+    zx_decode(c.container(), out, err, stream)
+    return out
+
+
+def decompress_batch(cs: Sequence[Compressed], outs: Optional[List[torch.Tensor]] = None,
+                     err: Optional[torch.Tensor] = None, stream=None):
+    """Decode up to 16 tensors (e.g. one transformer layer) with one kernel launch."""
+    if outs is None:
+        outs = [empty_output(c) for c in cs]
+    zx_decode_block_batch([c.container() for c in cs], outs, err, stream)
+    return outs

@@ -1,0 +1,81 @@
+"""Host-only checks of the C-ABI library: it loads, exports every entry point that
+include/zx.h declares, and rejects bad arguments before touching a GPU."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zx.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zx_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def zx():
+    import lossless_float_compression_amd as m
+    return m
+
+
+def test_header_lists_the_api():
+    names = declared_functions()
+    for f in ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
+              "zx_decode", "zx_decode_block_batch", "zx_stream_words", "zx_status_string", "zx_version"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(zx):
+    lib = zx.lib()
+    for f in declared_functions():
+        assert hasattr(lib, f), f
+    assert b"container v1" in lib.zx_version()
+
+
+def test_stream_words_rule(zx):
+    # round_up(ceil(bits/32), 4) + 4
+    for bits, want in [(0, 4), (1, 8), (32, 8), (128, 8), (129, 12), (1000, 36)]:
+        assert zx.zx_stream_words(bits) == want
+
+
+def test_status_strings(zx):
+    lib = zx.lib()
+    for s in range(6):
+        assert lib.zx_status_string(s)
+
+
+def test_argument_errors_return_before_any_launch(zx):
+    lib = zx.lib()
+    P = C.c_void_p
+    # unknown dtype
+    assert lib.zx_histogram(7, None, 0, P(16), None, None) == 2
+    # no output at all
+    assert lib.zx_histogram(0, None, 0, None, None, None) == 1
+    # misaligned pointer
+    assert lib.zx_histogram(0, P(0x1001), 10, P(0x2000), None, None) == 1
+    # tensor scope limited to n < 2^32
+    assert lib.zx_histogram(0, P(0x1000), 1 << 32, P(0x2000), None, None) == 1
+    # max_len below log2(alphabet) or above 32
+    assert lib.zx_build_codebook(0, P(0x1000), 1, 7, P(0x2000), P(0x3000), None) == 3
+    assert lib.zx_build_codebook(1, P(0x1000), 1, 3, P(0x2000), P(0x3000), None) == 3
+    assert lib.zx_build_codebook(0, P(0x1000), 1, 33, P(0x2000), P(0x3000), None) == 3
+    # decode: null container, too many tensors in a batch
+    assert lib.zx_decode(None, P(0x1000), None, None) == 1
+    arr = (zx.zx.zx_container * 17)()
+    outs = (C.c_void_p * 17)()
+    assert lib.zx_decode_block_batch(arr, outs, 17, None, None) == 1
+    # per-tensor container without its decode table
+    c = zx.zx.zx_container()
+    c.dtype, c.per_block, c.n, c.nsegs, c.total_bits, c.stream_words = 0, 0, 10, 1, 20, 8
+    for f in ("lengths", "degenerate", "signmant", "stream", "block_bitoff", "block_seg", "seg_desc", "gaps"):
+        setattr(c, f, 0x10000)
+    c.dtab = None
+    assert lib.zx_decode(C.byref(c), P(0x20000), None, None) == 1
+    # stream length must follow the padding rule
+    c.dtab = 0x30000
+    c.stream_words = 5
+    assert lib.zx_decode(C.byref(c), P(0x20000), None, None) == 1
