@@ -131,19 +131,27 @@ __device__ __forceinline__ uint32_t canon_len(const uint64_t *lim, uint32_t v, u
     return L;
 }
 
-// Decoder tables kept in LDS.  lut[x] for the next kLutBits bits x:
-//   bits  0..7  first symbol            bits  8..15 second symbol
-//   bits 16..19 first code length       bits 20..23 length of both codes
-//   bits 24..25 number of whole codes inside the window (0: longer than kLutBits)
+// Decoder tables kept in LDS.
+//   lut[x], x = the next kLutBits stream bits: up to three whole codes that fit in
+//   the window, decoded in order:
+//     bits  0..7 / 8..15 / 16..23  first / second / third symbol
+//     bits 24..27                   bits taken by those codes (<= kLutBits)
+//     bits 28..29                   number of codes (0: the first code is longer
+//                                   than the window; use the length limits)
+//   first_len[x]: length of the first code in the window, 0 if longer.
+//   lim/base/sym: canonical description for codes longer than the window.
+constexpr uint32_t kLutSymMax = 3;
+
 struct __align__(16) DTab {
     uint32_t lut[kLutSize];
+    uint8_t first_len[kLutSize];
     uint64_t lim[kMaxLen + 2];
     int32_t base[kMaxLen + 1];          // offset[L] - first[L]
     uint8_t sym[256];
     uint32_t ok;
     uint32_t nsym;
     uint32_t maxlen;
-    uint32_t pad_;
+    uint32_t pad_[3];
 };
 static_assert(sizeof(DTab) % 16 == 0, "DTab must copy in 16-byte pieces");
 
@@ -158,27 +166,28 @@ __device__ inline void dtab_fill(const Canon &c, DTab &t)
         t.ok = c.ok;
         t.nsym = c.nsym;
         t.maxlen = c.maxlen;
-        t.pad_ = 0;
+        t.pad_[0] = t.pad_[1] = t.pad_[2] = 0;
     }
     for (uint32_t x = tid; x < kLutSize; x += blockDim.x) {
-        uint32_t e = 0;
+        uint32_t e = 0, first = 0;
         if (c.ok) {
-            uint32_t v = x << (32 - kLutBits);
-            uint32_t L1 = canon_len(c.lim, v, 1);
-            if (L1 <= (uint32_t)kLutBits) {
-                uint32_t s0 = c.sym[c.offset[L1] + ((v >> (32 - L1)) - c.first[L1])];
-                uint32_t rem = kLutBits - L1;
-                uint32_t v2 = v << L1;   // the bits after the first code, zero filled
-                uint32_t L2 = canon_len(c.lim, v2, 1);
-                if (L2 <= rem) {
-                    uint32_t s1 = c.sym[c.offset[L2] + ((v2 >> (32 - L2)) - c.first[L2])];
-                    e = s0 | (s1 << 8) | (L1 << 16) | ((L1 + L2) << 20) | (2u << 24);
-                } else {
-                    e = s0 | (L1 << 16) | (L1 << 20) | (1u << 24);
-                }
+            uint32_t v = x << (32 - kLutBits);   // window, left-justified, zero filled
+            uint32_t used = 0, ns = 0, syms = 0;
+            while (ns < kLutSymMax) {
+                // a code is fully inside the window if its length fits in the bits left
+                const uint32_t L = canon_len(c.lim, v, 1);
+                if (L > kLutBits - used) break;
+                const uint32_t sy = c.sym[c.offset[L] + ((v >> (32 - L)) - c.first[L])];
+                if (ns == 0) first = L;
+                syms |= sy << (8 * ns);
+                used += L;
+                ++ns;
+                v <<= L;
             }
+            if (ns) e = syms | (used << 24) | (ns << 28);
         }
         t.lut[x] = e;
+        t.first_len[x] = (uint8_t)first;
     }
 }
 

@@ -23,7 +23,12 @@ namespace zxk {
 
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * kWave;
-constexpr uint32_t kStageBytes = kSegChunks * kChunkBits + 16;   // <= 8192 codes + alignment slack
+constexpr uint32_t kStageBytes = 4096;   // exponent stage per wavefront
+// A segment whose exponents do not fit the stage at once (mean code length under
+// two bits) is written in rounds of kRoundElems output positions.
+constexpr uint32_t kRoundElems = 4064;
+constexpr int kDecWgPerCu = 3;
+constexpr int kDecMinWavesPerSimd = kDecWgPerCu * kDecWaves / 4;
 constexpr int kMaxBatch = 16;
 
 struct DecTensor {
@@ -53,40 +58,43 @@ struct DecBatch {
     uint32_t count;
 };
 
-// Left-aligned 64-bit bit buffer over the stream: bit 63 is the next stream bit.
-struct BitReader {
-    uint64_t buf;
-    uint32_t nbits;
-    uint64_t next;
-    const uint32_t *s;
-    uint64_t wmax;
-    __device__ __forceinline__ void init(const uint32_t *stream, uint64_t words, uint64_t pos)
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// Stream words of one segment staged in LDS: word k holds stream word W0 + k, where
+// W0 is the word holding the segment's first bit.  A segment spans 8192 bits from
+// an offset below 32, so 257 words cover it and a 64-bit window past its end.
+constexpr uint32_t kSegWords = 264;
+
+struct SegWords {
+    const uint32_t *w;   // LDS
+    // 64 bits starting at staged bit p, left-aligned
+    __device__ __forceinline__ uint64_t win(uint32_t p) const
     {
-        s = stream;
-        wmax = words - 1;
-        const uint64_t w = pos >> 5;
-        const uint32_t off = (uint32_t)(pos & 31);
-        const uint64_t w0 = s[w < wmax ? w : wmax];
-        const uint64_t w1 = s[w + 1 < wmax ? w + 1 : wmax];
-        buf = ((w0 << 32) | w1) << off;
-        nbits = 64 - off;
-        next = w + 2;
-    }
-    __device__ __forceinline__ void refill()
-    {
-        if (nbits < 32) {
-            const uint64_t wd = s[next < wmax ? next : wmax];
-            buf |= wd << (32 - nbits);
-            nbits += 32;
-            ++next;
-        }
-    }
-    __device__ __forceinline__ void skip(uint32_t k)
-    {
-        buf <<= k;
-        nbits -= k;
+        const uint32_t k = p >> 5;
+        return ((((uint64_t)w[k]) << 32) | w[k + 1]) << (p & 31);
     }
 };
+
+// Copy stream words [W0, W0 + 260) into the wavefront's LDS area (zero past the end).
+__device__ __forceinline__ void stage_words(uint32_t *sw, const uint32_t *stream, uint64_t words, uint64_t W0)
+{
+    const uint32_t lane = lane_id();
+    const uint64_t k = W0 + 4ull * lane;
+    u32x4_a4 v;
+    if (k + 4 <= words) {
+        v = *reinterpret_cast<const u32x4_a4 *>(stream + k);
+    } else {
+        v.x = k < words ? stream[k] : 0u;
+        v.y = k + 1 < words ? stream[k + 1] : 0u;
+        v.z = k + 2 < words ? stream[k + 2] : 0u;
+        v.w = k + 3 < words ? stream[k + 3] : 0u;
+    }
+    reinterpret_cast<uint4 *>(sw)[lane] = make_uint4(v.x, v.y, v.z, v.w);
+    if (lane < 4) {
+        const uint64_t t = W0 + 256 + lane;
+        sw[256 + lane] = t < words ? stream[t] : 0u;
+    }
+}
 
 __device__ __forceinline__ uint32_t fuse2_bf16(uint32_t s16, uint32_t e16)
 {
@@ -103,11 +111,143 @@ __device__ __forceinline__ uint32_t fuse4_fp8(uint32_t nib16, uint32_t e4)
     return ((x & 0x08080808u) << 4) | (x & 0x07070707u) | (e4 << 3);
 }
 
+// Codes longer than the lookup window: canonical length limits, kept out of line.
+__device__ __forceinline__ uint32_t slow_len(const DTab &tab, uint32_t v)
+{
+    uint32_t L = kLutBits + 1;
+#pragma unroll 1
+    while (L <= kMaxLen && (uint64_t)v >= tab.lim[L]) ++L;
+    return L;
+}
+
+__device__ __forceinline__ uint32_t slow_sym(const DTab &tab, uint32_t v, uint32_t L)
+{
+    return tab.sym[(uint32_t)(tab.base[L] + (int32_t)(v >> (32 - L))) & 0xFFu];
+}
+
+// Write pass pieces: 8 BF16 or 16 FP8 elements per lane per step, i.e. 8 bytes of
+// sign/mantissa in and one 16-byte store out.
+template <int DT>
+struct Piece {
+    static constexpr uint32_t kElems = DT == ZX_BF16 ? 8 : 16;
+};
+
+template <int DT>
+__device__ __forceinline__ uint2 load_sm(const uint8_t *sm_block, uint32_t i)
+{
+    return *reinterpret_cast<const uint2 *>(sm_block + (DT == ZX_BF16 ? i : i / 2));
+}
+
+// Exponents of one piece, from the stage or a 0-bit block's single symbol.
+template <int DT>
+__device__ __forceinline__ uint4 piece_exps(const uint8_t *ex, bool degen, uint32_t dsplat)
+{
+    if (degen) return make_uint4(dsplat, dsplat, dsplat, dsplat);
+    if (DT == ZX_BF16) {
+        const uint2 e = *reinterpret_cast<const uint2 *>(ex);
+        return make_uint4(e.x, e.y, 0, 0);
+    }
+    return *reinterpret_cast<const uint4 *>(ex);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_piece(void *out_block, uint32_t i, uint2 smv, uint4 e)
+{
+    if (DT == ZX_BF16) {
+        uint4 r;
+        r.x = fuse2_bf16(smv.x & 0xFFFFu, e.x & 0xFFFFu);
+        r.y = fuse2_bf16(smv.x >> 16, e.x >> 16);
+        r.z = fuse2_bf16(smv.y & 0xFFFFu, e.y & 0xFFFFu);
+        r.w = fuse2_bf16(smv.y >> 16, e.y >> 16);
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out_block) + i) = r;
+    } else {
+        uint4 r;
+        r.x = fuse4_fp8(smv.x & 0xFFFFu, e.x);
+        r.y = fuse4_fp8(smv.x >> 16, e.y);
+        r.z = fuse4_fp8(smv.y & 0xFFFFu, e.z);
+        r.w = fuse4_fp8(smv.y >> 16, e.w);
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(out_block) + i) = r;
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_one(void *out_block, const uint8_t *sm_block, uint32_t ii, uint32_t ex)
+{
+    if (DT == ZX_BF16) {
+        reinterpret_cast<uint16_t *>(out_block)[ii] = (uint16_t)(fuse2_bf16(sm_block[ii], ex) & 0xFFFFu);
+    } else {
+        const uint32_t nb2 = sm_block[ii / 2];
+        const uint32_t nn = (ii & 1) ? (nb2 >> 4) : (nb2 & 0xFu);
+        reinterpret_cast<uint8_t *>(out_block)[ii] = (uint8_t)(fuse4_fp8(nn, ex) & 0xFFu);
+    }
+}
+
+
+// One piece of the write pass: a whole piece is fused and stored with one 16-byte
+// store; a piece cut by the range ends is written element by element.
+template <int DT>
+__device__ __forceinline__ void write_piece(void *out_block, const uint8_t *sm_block, uint32_t q, uint32_t i_begin,
+                                            uint32_t i_end, const uint8_t *stage, uint32_t sbase, bool degen,
+                                            uint32_t degen_sym, bool have_sm, uint2 smv)
+{
+    constexpr uint32_t P = Piece<DT>::kElems;
+    const uint32_t i = q * P;
+    if (i >= i_begin && i + P <= i_end) {
+        if (!have_sm) smv = load_sm<DT>(sm_block, i);
+        store_piece<DT>(out_block, i, smv, piece_exps<DT>(stage + (i - sbase), degen, degen_sym * 0x01010101u));
+    } else {
+#pragma unroll 1
+        for (uint32_t t = 0; t < P; ++t) {
+            const uint32_t ii = i + t;
+            if (ii >= i_begin && ii < i_end) store_one<DT>(out_block, sm_block, ii, degen ? degen_sym : stage[ii - sbase]);
+        }
+    }
+}
+
+constexpr int kWriteBatch = 4;   // pieces per lane whose loads are issued together
+
+// Write block elements [i_begin, i_end); the exponent of element i is stage[i - sbase]
+// (or `degen_sym` for a 0-bit block).  Sign/mantissa loads of kWriteBatch pieces
+// per lane are issued before any of them is used.
+template <int DT>
+__device__ __forceinline__ void write_range(void *out_block, const uint8_t *sm_block, uint32_t i_begin, uint32_t i_end,
+                                            const uint8_t *stage, uint32_t sbase, bool degen, uint32_t degen_sym)
+{
+    constexpr uint32_t P = Piece<DT>::kElems;
+    const uint32_t lane = lane_id();
+    const uint32_t q_begin = i_begin / P;
+    const uint32_t q_end = (i_end + P - 1) / P;
+    for (uint32_t qb = q_begin; qb < q_end; qb += kWave * kWriteBatch) {
+        uint2 smv[kWriteBatch];
+#pragma unroll
+        for (int k = 0; k < kWriteBatch; ++k) {
+            const uint32_t q = qb + lane + k * kWave;
+            const uint32_t i = q * P;
+            smv[k] = make_uint2(0, 0);
+            if (q < q_end && i >= i_begin && i + P <= i_end) smv[k] = load_sm<DT>(sm_block, i);
+        }
+#pragma unroll
+        for (int k = 0; k < kWriteBatch; ++k) {
+            const uint32_t q = qb + lane + k * kWave;
+            if (q < q_end) write_piece<DT>(out_block, sm_block, q, i_begin, i_end, stage, sbase, degen, degen_sym, true, smv[k]);
+        }
+    }
+}
+
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Decode one segment with one wavefront.
 template <int DT>
-__device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t s, uint32_t *err)
+__device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *swords, uint32_t s,
+                               uint32_t *err)
 {
     constexpr uint32_t A = alphabet_of(DT);
+    constexpr uint32_t P = Piece<DT>::kElems;
     const uint32_t lane = lane_id();
     const uint32_t b = T.seg_desc[2 * (uint64_t)s];
     const uint32_t e0 = T.seg_desc[2 * (uint64_t)s + 1];
@@ -126,174 +266,177 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
     const uint32_t j = s - sb;
     const uint32_t e_end = (s + 1 < sbn) ? T.seg_desc[2 * (uint64_t)(s + 1) + 1] : nb;
     if (e0 > e_end || e_end > nb) { report(err, ZX_E_CORRUPT); return; }
+    const uint8_t *sm_block = T.signmant + (DT == ZX_BF16 ? lo : lo / 2);
+    void *out_block = reinterpret_cast<uint8_t *>(T.out) + lo * (DT == ZX_BF16 ? 2 : 1);
+    const uint32_t sbase = e0 & ~15u;   // 16-aligned element that stage byte 0 stands for
 
-    uint32_t total = 0;
-    uint32_t degen_sym = 0;
-    const bool degen = (bits == 0);
-    if (degen) {
+    if (bits == 0) {
         const uint32_t d = T.degenerate[T.per_block ? b : 0];
         if (d >= A || e0 != 0 || e_end != nb) { report(err, ZX_E_CORRUPT); return; }
-        degen_sym = d;
-        total = nb;
-    } else {
-        if (!tab.ok) { report(err, ZX_E_CORRUPT); return; }
-        const uint32_t nch = (bits + kChunkBits - 1) / kChunkBits;
-        const uint32_t ch = j * kSegChunks + lane;
-        const uint32_t gap = (ch < nch) ? T.gaps[(uint64_t)s * kSegChunks + lane] : ZX_NO_GAP;
-        bool work = gap != ZX_NO_GAP;
-        bool lane_bad = false;
-        if (work && gap >= kMaxLen) { work = false; lane_bad = true; }
-        const uint64_t start = G + (uint64_t)ch * kChunkBits + gap;
-        const uint64_t cend = (uint64_t)ch * kChunkBits + kChunkBits;
-        const uint64_t end = G + (cend < bits ? cend : bits);
-        if (work && start >= end) { work = false; lane_bad = true; }
-        // ---- count pass
-        uint32_t cnt = 0;
-        uint64_t pos_end = start;
-        if (work) {
-            BitReader br;
-            br.init(T.stream, T.stream_words, start);
-            uint64_t pos = start;
-            while (pos < end) {
-                br.refill();
-                const uint32_t e = tab.lut[br.buf >> (64 - kLutBits)];
-                const uint32_t ns = e >> 24;
-                uint32_t adv;
-                if (ns == 0) {
-                    const uint32_t L = canon_len(tab.lim, (uint32_t)(br.buf >> 32), kLutBits + 1);
-                    if (L > kMaxLen) { lane_bad = true; break; }
-                    adv = L;
-                    cnt += 1;
-                } else {
-                    const uint32_t L0 = (e >> 16) & 0xFu;
-                    const bool two = (ns == 2) && (pos + L0 < end);
-                    adv = two ? ((e >> 20) & 0xFu) : L0;
-                    cnt += two ? 2u : 1u;
-                    if (L0 == 0 || adv < L0) { lane_bad = true; break; }   // a damaged table must not stall
-                }
-                br.skip(adv);
-                pos += adv;
-            }
-            pos_end = pos;
-        }
-        // codes of one chunk must end exactly where the next chunk's first code
-        // starts (or at the block end), as the stored gaps claim
-        uint32_t gap_next = __shfl_down(gap, 1, kWave);
-        if (lane == kWave - 1) gap_next = (ch + 1 < nch) ? T.gaps[(uint64_t)(s + 1) * kSegChunks] : ZX_NO_GAP;
-        if (work && !lane_bad) {
-            const uint64_t expect = (ch + 1 < nch && gap_next != ZX_NO_GAP) ? G + (uint64_t)(ch + 1) * kChunkBits + gap_next
-                                                                              : G + bits;
-            if (pos_end != expect) lane_bad = true;
-        }
-        uint32_t off = wave_excl_scan(cnt, total);
-        if (__ballot(lane_bad) != 0 || e0 + total != e_end) { report(err, ZX_E_CORRUPT); return; }
-        // ---- decode pass: exponents into the stage, in output order
-        if (work) {
-            BitReader br;
-            br.init(T.stream, T.stream_words, start);
-            uint64_t pos = start;
-            uint32_t wp = (e0 & 7u) + off;
-            while (pos < end) {
-                br.refill();
-                const uint32_t e = tab.lut[br.buf >> (64 - kLutBits)];
-                const uint32_t ns = e >> 24;
-                uint32_t adv;
-                if (ns == 0) {
-                    const uint32_t v = (uint32_t)(br.buf >> 32);
-                    const uint32_t L = canon_len(tab.lim, v, kLutBits + 1);
-                    adv = L;
-                    stage[wp++] = tab.sym[(uint32_t)(tab.base[L] + (int32_t)(v >> (32 - L))) & 0xFFu];
-                } else {
-                    const uint32_t L0 = (e >> 16) & 0xFu;
-                    const bool two = (ns == 2) && (pos + L0 < end);
-                    stage[wp++] = (uint8_t)e;
-                    if (two) stage[wp++] = (uint8_t)(e >> 8);
-                    adv = two ? ((e >> 20) & 0xFu) : L0;
-                }
-                br.skip(adv);
-                pos += adv;
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        write_range<DT>(out_block, sm_block, e0, e_end, stage, sbase, true, d);
+        return;
     }
-    // ---- write pass over block elements [e0, e_end)
-    const uint32_t sbase = e0 & ~7u;   // stage byte k holds element sbase + k
-    const uint32_t g_begin = e0 >> 3;
-    const uint32_t g_end = (e_end + 7) >> 3;
-    const uint32_t dsplat = degen_sym * 0x01010101u;
-    if (DT == ZX_BF16) {
-        uint16_t *out = reinterpret_cast<uint16_t *>(T.out) + lo;
-        const uint8_t *sm = T.signmant + lo;
-        for (uint32_t g = g_begin + lane; g < g_end; g += kWave) {
-            const uint32_t i = g * 8;
-            if (i >= e0 && i + 8 <= e_end) {
-                const uint2 s8 = *reinterpret_cast<const uint2 *>(sm + i);
-                uint32_t ea, eb;
-                if (degen) {
-                    ea = eb = dsplat;
-                } else {
-                    const uint2 e8 = *reinterpret_cast<const uint2 *>(stage + (i - sbase));
-                    ea = e8.x;
-                    eb = e8.y;
-                }
-                uint4 o;
-                o.x = fuse2_bf16(s8.x & 0xFFFFu, ea & 0xFFFFu);
-                o.y = fuse2_bf16(s8.x >> 16, ea >> 16);
-                o.z = fuse2_bf16(s8.y & 0xFFFFu, eb & 0xFFFFu);
-                o.w = fuse2_bf16(s8.y >> 16, eb >> 16);
-                *reinterpret_cast<uint4 *>(out + i) = o;
-            } else {
-                for (uint32_t k = 0; k < 8; ++k) {
-                    const uint32_t ii = i + k;
-                    if (ii >= e0 && ii < e_end) {
-                        const uint32_t ex = degen ? degen_sym : stage[ii - sbase];
-                        out[ii] = (uint16_t)(fuse2_bf16(sm[ii], ex) & 0xFFFFu);
-                    }
-                }
+    if (!tab.ok) { report(err, ZX_E_CORRUPT); return; }
+
+    const uint32_t nch = (bits + kChunkBits - 1) / kChunkBits;
+    const uint32_t ch = j * kSegChunks + lane;
+    const uint32_t gap = (ch < nch) ? T.gaps[(uint64_t)s * kSegChunks + lane] : ZX_NO_GAP;
+    bool work = gap != ZX_NO_GAP;
+    bool lane_bad = false;
+    if (work && gap >= kMaxLen) { work = false; lane_bad = true; }
+    // chunk-relative end: the lane decodes the codes starting in [gap, cend)
+    const uint32_t cend = (ch * kChunkBits + kChunkBits < bits) ? kChunkBits : bits - ch * kChunkBits;
+    if (work && gap >= cend) { work = false; lane_bad = true; }
+    const uint64_t segbit = G + (uint64_t)j * kSegBits;
+    stage_words(swords, T.stream, T.stream_words, segbit >> 5);
+    wave_sync();
+    const SegWords sw{swords};
+    // staged-bit coordinates: chunk start = (segbit & 31) + 128 lane
+    const uint32_t cbase = (uint32_t)(segbit & 31) + lane * kChunkBits;
+    const uint32_t start = cbase + gap;
+    const uint32_t lim = work ? cbase + cend : 0;
+
+    // ---- count pass.  Main loop: while a whole window lies inside the chunk, every
+    //      code the table returns starts inside it.  Tail: one code at a time.
+    uint32_t cnt = 0;
+    uint32_t pos = work ? start : 0;
+    while (__ballot(pos + kLutBits <= lim) != 0) {
+        const bool act = pos + kLutBits <= lim;
+        const uint64_t x = sw.win(pos);
+        const uint32_t e = tab.lut[(uint32_t)(x >> (64 - kLutBits))];
+        uint32_t ns = e >> 28;
+        uint32_t adv = (e >> 24) & 0xFu;
+        if (__ballot(act && ns == 0) != 0) {
+            if (act && ns == 0) {
+                adv = slow_len(tab, (uint32_t)(x >> 32));
+                ns = 1;
+                if (adv > kMaxLen) { lane_bad = true; adv = lim - pos; }
             }
         }
-    } else {
-        uint8_t *out = reinterpret_cast<uint8_t *>(T.out) + lo;
-        const uint8_t *nib = T.signmant + lo / 2;
-        for (uint32_t g = g_begin + lane; g < g_end; g += kWave) {
-            const uint32_t i = g * 8;
-            if (i >= e0 && i + 8 <= e_end) {
-                const uint32_t n8 = *reinterpret_cast<const uint32_t *>(nib + i / 2);
-                uint32_t ea, eb;
-                if (degen) {
-                    ea = eb = dsplat;
-                } else {
-                    const uint2 e8 = *reinterpret_cast<const uint2 *>(stage + (i - sbase));
-                    ea = e8.x;
-                    eb = e8.y;
-                }
-                uint2 o;
-                o.x = fuse4_fp8(n8 & 0xFFFFu, ea);
-                o.y = fuse4_fp8(n8 >> 16, eb);
-                *reinterpret_cast<uint2 *>(out + i) = o;
-            } else {
-                for (uint32_t k = 0; k < 8; ++k) {
-                    const uint32_t ii = i + k;
-                    if (ii >= e0 && ii < e_end) {
-                        const uint32_t nb2 = nib[ii / 2];
-                        const uint32_t nn = (ii & 1) ? (nb2 >> 4) : (nb2 & 0xFu);
-                        const uint32_t ex = degen ? degen_sym : stage[ii - sbase];
-                        out[ii] = (uint8_t)(fuse4_fp8(nn, ex) & 0xFFu);
-                    }
+        if (act && adv == 0) { lane_bad = true; adv = lim - pos; }   // a damaged table must not stall
+        cnt += act ? ns : 0u;
+        pos += act ? adv : 0u;
+    }
+    while (__ballot(pos < lim) != 0) {
+        const bool act = pos < lim;
+        const uint64_t x = sw.win(pos);
+        uint32_t L = tab.first_len[(uint32_t)(x >> (64 - kLutBits))];
+        if (__ballot(act && L == 0) != 0) {
+            if (act && L == 0) {
+                L = slow_len(tab, (uint32_t)(x >> 32));
+                if (L > kMaxLen) { lane_bad = true; L = lim - pos; }
+            }
+        }
+        cnt += act ? 1u : 0u;
+        pos += act ? L : 0u;
+    }
+    // codes of one chunk must end exactly where the next chunk's first code
+    // starts (or at the block end), as the stored gaps claim
+    uint32_t gap_next = __shfl_down(gap, 1, kWave);
+    if (lane == kWave - 1) gap_next = (ch + 1 < nch) ? T.gaps[(uint64_t)(s + 1) * kSegChunks] : ZX_NO_GAP;
+    if (work && !lane_bad) {
+        const uint32_t expect = (ch + 1 < nch && gap_next != ZX_NO_GAP) ? cbase + kChunkBits + gap_next : cbase + (bits - ch * kChunkBits);
+        if (pos != expect) lane_bad = true;
+    }
+    uint32_t total;
+    const uint32_t off = wave_excl_scan(cnt, total);
+    if (__ballot(lane_bad) != 0 || e0 + total != e_end) { report(err, ZX_E_CORRUPT); return; }
+
+    const uint32_t t0 = e0 - sbase;   // stage position of the segment's first element
+    if (t0 + total + 2 <= kStageBytes) {
+        // ---- decode pass, one round: each lookup stores all its symbols; a lane's
+        //      last lookup may spill up to two bytes onto the next lanes' first
+        //      positions, which those lanes restore right after
+        uint32_t wp = t0 + off;
+        uint32_t done = 0;
+        pos = start;
+        while (__ballot(done < cnt) != 0) {
+            const bool act = done < cnt;
+            const uint64_t x = sw.win(pos);
+            uint32_t e = tab.lut[(uint32_t)(x >> (64 - kLutBits))];
+            uint32_t ns = e >> 28;
+            uint32_t adv = (e >> 24) & 0xFu;
+            if (__ballot(act && ns == 0) != 0) {
+                if (act && ns == 0) {
+                    const uint32_t v = (uint32_t)(x >> 32);
+                    adv = slow_len(tab, v);
+                    e = slow_sym(tab, v, adv);
+                    ns = 1;
                 }
             }
+            if (act) {
+                stage[wp] = (uint8_t)e;
+                stage[wp + 1] = (uint8_t)(e >> 8);
+                stage[wp + 2] = (uint8_t)(e >> 16);
+                wp += ns;
+                done += ns;
+                pos += adv;
+            }
+        }
+        wave_sync();
+        if (cnt) {
+            uint32_t p = start;
+            const uint32_t first = cnt < 2 ? cnt : 2;
+            for (uint32_t k = 0; k < first; ++k) {
+                const uint64_t x = sw.win(p);
+                const uint32_t idx = (uint32_t)(x >> (64 - kLutBits));
+                uint32_t L = tab.first_len[idx];
+                uint32_t sy;
+                if (L) {
+                    sy = tab.lut[idx] & 0xFFu;
+                } else {
+                    const uint32_t v = (uint32_t)(x >> 32);
+                    L = slow_len(tab, v);
+                    sy = slow_sym(tab, v, L);
+                }
+                stage[t0 + off + k] = (uint8_t)sy;
+                p += L;
+            }
+        }
+        wave_sync();
+        write_range<DT>(out_block, sm_block, e0, e_end, stage, sbase, false, 0);
+    } else {
+        // ---- several rounds of kRoundElems stage positions; exact writes
+        for (uint32_t r0 = 0; r0 < t0 + total; r0 += kRoundElems) {
+            const uint32_t r1 = r0 + kRoundElems;
+            if (cnt) {
+                uint32_t p = start;
+                uint32_t t = t0 + off;
+                uint32_t done = 0;
+                while (done < cnt && t < r1) {
+                    const uint64_t x = sw.win(p);
+                    const uint32_t idx = (uint32_t)(x >> (64 - kLutBits));
+                    uint32_t L = tab.first_len[idx];
+                    uint32_t sy;
+                    if (L) {
+                        sy = tab.lut[idx] & 0xFFu;
+                    } else {
+                        const uint32_t v = (uint32_t)(x >> 32);
+                        L = slow_len(tab, v);
+                        sy = slow_sym(tab, v, L);
+                    }
+                    if (t >= r0) stage[t - r0] = (uint8_t)sy;
+                    p += L;
+                    ++t;
+                    ++done;
+                }
+            }
+            wave_sync();
+            const uint32_t ib = sbase + (r0 > t0 ? r0 : t0);
+            const uint32_t ie = sbase + (r1 < t0 + total ? r1 : t0 + total);
+            write_range<DT>(out_block, sm_block, ib, ie, stage, sbase + r0, false, 0);
+            wave_sync();
         }
     }
 }
 
 template <int DT>
-__global__ __launch_bounds__(kDecThreads) void k_decode(const DecBatch batch, uint32_t *err)
+__global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(const DecBatch batch, uint32_t *err)
 {
     constexpr uint32_t A = alphabet_of(DT);
     __shared__ DTab tab;
     __shared__ __align__(16) uint8_t stage_all[kDecWaves * kStageBytes];
+    __shared__ __align__(16) uint32_t words_all[kDecWaves * kSegWords];
     static_assert(sizeof(Canon) <= sizeof(stage_all), "Canon is built inside the stage area");
 
     const uint32_t g = blockIdx.x;
@@ -323,7 +466,8 @@ __global__ __launch_bounds__(kDecThreads) void k_decode(const DecBatch batch, ui
     }
     const uint32_t wave = tid / kWave;
     uint8_t *stage = stage_all + wave * kStageBytes;
-    for (uint32_t s = s_begin + wave; s < s_end; s += kDecWaves) decode_segment<DT>(T, tab, stage, s, err);
+    uint32_t *swords = words_all + wave * kSegWords;
+    for (uint32_t s = s_begin + wave; s < s_end; s += kDecWaves) decode_segment<DT>(T, tab, stage, swords, s, err);
 }
 
 __global__ __launch_bounds__(256) void k_build_dtab(const uint8_t *__restrict__ lengths, uint32_t A, DTab *__restrict__ out)
@@ -379,7 +523,7 @@ extern "C" zx_status zx_decode_block_batch(const zx_container *cs, void *const *
     }
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const uint64_t slots = (uint64_t)cus * 2;   // two 512-thread workgroups fit a CU's LDS
+    const uint64_t slots = (uint64_t)cus * kDecWgPerCu;   // resident 512-thread workgroups per CU
     uint64_t seg_total = 0;
     for (uint32_t i = 0; i < count; ++i)
         if (!cs[i].per_block) seg_total += cs[i].nsegs;

@@ -17,14 +17,16 @@
 
 namespace zxk {
 
-constexpr int kEncThreads = 256;
+constexpr int kEncThreads = 1024;
 constexpr uint32_t kEncPerThread = 8;
-constexpr uint32_t kRound = kEncThreads * kEncPerThread;   // 2048 elements per round
+constexpr uint32_t kRound = kEncThreads * kEncPerThread;   // 8192 elements per round
 constexpr uint32_t kStageWords = kRound + 2;               // up to 32 bits per element + carry
 
 // -------------------------------------------------------------------- block sizes
+constexpr int kSizeThreads = 256;
+
 template <int DT>
-__global__ __launch_bounds__(kEncThreads) void k_block_bits(const void *__restrict__ in, uint64_t n, int per_block,
+__global__ __launch_bounds__(kSizeThreads) void k_block_bits(const void *__restrict__ in, uint64_t n, int per_block,
                                                             const uint8_t *__restrict__ lengths,
                                                             const uint32_t *__restrict__ block_hist,
                                                             uint64_t *__restrict__ block_bitoff,
@@ -32,7 +34,7 @@ __global__ __launch_bounds__(kEncThreads) void k_block_bits(const void *__restri
 {
     constexpr uint32_t A = alphabet_of(DT);
     __shared__ uint8_t len[256];
-    __shared__ uint32_t part[kEncThreads / kWave];
+    __shared__ uint32_t part[kSizeThreads / kWave];
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x;
     const uint64_t cb = per_block ? b : 0;
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(kEncThreads) void k_block_bits(const void *__restri
     } else {
         const uint64_t lo = b * kBlock;
         const uint64_t hi = (lo + kBlock < n) ? lo + kBlock : n;
-        for (uint64_t i = lo + tid; i < hi; i += kEncThreads) {
+        for (uint64_t i = lo + tid; i < hi; i += kSizeThreads) {
             uint32_t e;
             if (DT == ZX_BF16)
                 e = (reinterpret_cast<const uint16_t *>(in)[i] >> 7) & 0xFFu;
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(kEncThreads) void k_block_bits(const void *__restri
     __syncthreads();
     if (tid == 0) {
         uint32_t s = 0;
-        for (uint32_t w = 0; w < kEncThreads / kWave; ++w) s += part[w];
+        for (uint32_t w = 0; w < kSizeThreads / kWave; ++w) s += part[w];
         const uint32_t nch = (s + kChunkBits - 1) / kChunkBits;
         uint32_t nseg = (nch + kSegChunks - 1) / kSegChunks;
         if (nseg == 0) nseg = 1;
@@ -186,18 +188,36 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
     uint32_t P = 0;                     // block-relative bit of the round's first code
     bool bad = false;
     const uint32_t nrounds = (nb + kRound - 1) / kRound;
+    // raw 16 (BF16) or 8 (FP8) input bytes of this thread, loaded one round ahead
+    constexpr uint32_t RW = DT == ZX_BF16 ? 4 : 2;
+    auto load_raw = [&](uint32_t r, uint32_t (&w)[RW]) {
+        const uint32_t i0 = r * kRound + tid * kEncPerThread;
+        if (i0 + kEncPerThread <= nb) {
+            if (DT == ZX_BF16) {
+                const uint4 q = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(in) + lo + i0);
+                w[0] = q.x; w[1] = q.y; w[2 % RW] = q.z; w[3 % RW] = q.w;
+            } else {
+                const uint2 q = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(in) + lo + i0);
+                w[0] = q.x; w[1] = q.y;
+            }
+        }
+    };
+    uint32_t nxt[RW];
+    if (nrounds) load_raw(0, nxt);
     for (uint32_t r = 0; r < nrounds; ++r) {
         const uint32_t i0 = r * kRound + tid * kEncPerThread;   // block-relative element
         const uint32_t have = (i0 < nb) ? ((nb - i0 < kEncPerThread) ? nb - i0 : kEncPerThread) : 0;
+        uint32_t cur[RW];
+#pragma unroll
+        for (uint32_t k = 0; k < RW; ++k) cur[k] = nxt[k];
+        if (r + 1 < nrounds) load_raw(r + 1, nxt);
         uint32_t u[kEncPerThread];
-        // ---- load and split
+        // ---- split
         if (DT == ZX_BF16) {
             const uint16_t *src = reinterpret_cast<const uint16_t *>(in) + lo + i0;
             if (have == kEncPerThread) {
-                const uint4 q = *reinterpret_cast<const uint4 *>(src);
-                const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-                for (uint32_t k = 0; k < kEncPerThread; ++k) u[k] = (wv[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+                for (uint32_t k = 0; k < kEncPerThread; ++k) u[k] = (cur[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
                 uint64_t smv = 0;
 #pragma unroll
                 for (uint32_t k = 0; k < kEncPerThread; ++k) smv |= (uint64_t)(((u[k] >> 8) & 0x80u) | (u[k] & 0x7Fu)) << (8 * k);
@@ -215,10 +235,8 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
         } else {
             const uint8_t *src = reinterpret_cast<const uint8_t *>(in) + lo + i0;
             if (have == kEncPerThread) {
-                const uint2 q = *reinterpret_cast<const uint2 *>(src);
-                const uint32_t wv[2] = {q.x, q.y};
 #pragma unroll
-                for (uint32_t k = 0; k < kEncPerThread; ++k) u[k] = (wv[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+                for (uint32_t k = 0; k < kEncPerThread; ++k) u[k] = (cur[k >> 2] >> (8 * (k & 3))) & 0xFFu;
                 uint32_t nib = 0;
 #pragma unroll
                 for (uint32_t k = 0; k < kEncPerThread; ++k) nib |= (((u[k] >> 4) & 0x8u) | (u[k] & 0x7u)) << (4 * k);
@@ -338,10 +356,10 @@ extern "C" zx_status zx_encode_size(zx_dtype dtype, const void *in, uint64_t n, 
     if (!aligned16(in) || !aligned16(block_hist)) return ZX_E_INVAL;
     if (nblocks) {
         if (dtype == ZX_BF16)
-            hipLaunchKernelGGL(k_block_bits<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream, in, n, per_block, lengths,
+            hipLaunchKernelGGL(k_block_bits<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kSizeThreads), 0, stream, in, n, per_block, lengths,
                                block_hist, block_bitoff, block_seg);
         else
-            hipLaunchKernelGGL(k_block_bits<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream, in, n, per_block,
+            hipLaunchKernelGGL(k_block_bits<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kSizeThreads), 0, stream, in, n, per_block,
                                lengths, block_hist, block_bitoff, block_seg);
         if (hipGetLastError() != hipSuccess) return ZX_E_HIP;
     }

@@ -11,7 +11,8 @@
 
 namespace zxk {
 
-constexpr int kHistThreads = 256;
+constexpr int kHistThreads = 1024;
+constexpr uint32_t kHistUnroll = 4;   // 16-byte loads in flight per lane
 
 // Add one exponent per lane (valid lanes only) into the LDS histogram.
 __device__ __forceinline__ void ballot_add(uint32_t *h, uint32_t e, bool valid)
@@ -21,7 +22,7 @@ __device__ __forceinline__ void ballot_add(uint32_t *h, uint32_t e, bool valid)
         uint64_t act = __ballot(todo);
         if (act == 0) break;
         const int leader = __ffsll((long long)act) - 1;
-        const uint32_t v = __shfl(e, leader, kWave);
+        const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)e, leader);
         const uint64_t same = __ballot(todo && e == v);
         if (lane_id() == (uint32_t)leader) atomicAdd(&h[v], (uint32_t)__popcll(same));
         if (e == v) todo = false;
@@ -47,32 +48,43 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restri
     constexpr uint32_t EPV = DT == ZX_BF16 ? 8 : 16;
     const uint32_t nvec = (nb + EPV - 1) / EPV;
     const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(in) + lo * (DT == ZX_BF16 ? 2 : 1));
-    for (uint32_t v = tid; v < (nvec + kHistThreads - 1) / kHistThreads * kHistThreads; v += kHistThreads) {
-        uint32_t words[4] = {0, 0, 0, 0};
-        uint32_t have = 0;  // valid elements in this vector
-        if (v < nvec) {
-            const uint32_t first = v * EPV;
-            have = (nb - first < EPV) ? nb - first : EPV;
-            if (have == EPV) {
-                uint4 q = src[v];
-                words[0] = q.x; words[1] = q.y; words[2] = q.z; words[3] = q.w;
-            } else {
-                const uint8_t *bytes = reinterpret_cast<const uint8_t *>(src) + (uint64_t)first * (DT == ZX_BF16 ? 2 : 1);
-                const uint32_t nbytes = have * (DT == ZX_BF16 ? 2 : 1);
-                for (uint32_t k = 0; k < nbytes; ++k) words[k >> 2] |= (uint32_t)bytes[k] << (8 * (k & 3));
+    constexpr uint32_t kStep = kHistThreads * kHistUnroll;
+    for (uint32_t base = 0; base < nvec; base += kStep) {
+        uint32_t words[kHistUnroll][4];
+        uint32_t have[kHistUnroll];
+        // issue every load of this step before counting
+#pragma unroll
+        for (uint32_t u = 0; u < kHistUnroll; ++u) {
+            const uint32_t v = base + u * kHistThreads + tid;
+            words[u][0] = words[u][1] = words[u][2] = words[u][3] = 0;
+            have[u] = 0;
+            if (v < nvec) {
+                const uint32_t first = v * EPV;
+                have[u] = (nb - first < EPV) ? nb - first : EPV;
+                if (have[u] == EPV) {
+                    const uint4 q = src[v];
+                    words[u][0] = q.x; words[u][1] = q.y; words[u][2] = q.z; words[u][3] = q.w;
+                } else {
+                    const uint8_t *bytes = reinterpret_cast<const uint8_t *>(src) + (uint64_t)first * (DT == ZX_BF16 ? 2 : 1);
+                    const uint32_t nbytes = have[u] * (DT == ZX_BF16 ? 2 : 1);
+                    for (uint32_t k = 0; k < nbytes; ++k) words[u][k >> 2] |= (uint32_t)bytes[k] << (8 * (k & 3));
+                }
             }
         }
 #pragma unroll
-        for (uint32_t k = 0; k < EPV; ++k) {
-            uint32_t e;
-            if (DT == ZX_BF16) {
-                const uint32_t u = (words[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-                e = (u >> 7) & 0xFFu;
-            } else {
-                const uint32_t u = (words[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                e = (u >> 3) & 0xFu;
+        for (uint32_t u = 0; u < kHistUnroll; ++u) {
+#pragma unroll
+            for (uint32_t k = 0; k < EPV; ++k) {
+                uint32_t e;
+                if (DT == ZX_BF16) {
+                    const uint32_t x = (words[u][k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+                    e = (x >> 7) & 0xFFu;
+                } else {
+                    const uint32_t x = (words[u][k >> 2] >> (8 * (k & 3))) & 0xFFu;
+                    e = (x >> 3) & 0xFu;
+                }
+                ballot_add(h, e, k < have[u]);
             }
-            ballot_add(h, e, k < have);
         }
     }
     __syncthreads();
