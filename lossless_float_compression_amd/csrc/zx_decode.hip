@@ -96,21 +96,6 @@ __device__ __forceinline__ void stage_words(uint32_t *sw, const uint32_t *stream
     }
 }
 
-__device__ __forceinline__ uint32_t fuse2_bf16(uint32_t s16, uint32_t e16)
-{
-    // element a in the low half, b in the high half: sign -> bit 15, exponent -> bits 7..14
-    const uint32_t s2 = (s16 & 0xFFu) | ((s16 & 0xFF00u) << 8);
-    const uint32_t e2 = (e16 & 0xFFu) | ((e16 & 0xFF00u) << 8);
-    return ((s2 * 0x0101u) & 0x807F807Fu) | (e2 << 7);
-}
-
-__device__ __forceinline__ uint32_t fuse4_fp8(uint32_t nib16, uint32_t e4)
-{
-    // four sign|mantissa nibbles (element k at bits 4k..4k+3) and four exponent bytes
-    const uint32_t x = (nib16 & 0xFu) | ((nib16 & 0xF0u) << 4) | ((nib16 & 0xF00u) << 8) | ((nib16 & 0xF000u) << 12);
-    return ((x & 0x08080808u) << 4) | (x & 0x07070707u) | (e4 << 3);
-}
-
 // Codes longer than the lookup window: canonical length limits, kept out of line.
 __device__ __forceinline__ uint32_t slow_len(const DTab &tab, uint32_t v)
 {
@@ -150,88 +135,107 @@ __device__ __forceinline__ uint4 piece_exps(const uint8_t *ex, bool degen, uint3
     return *reinterpret_cast<const uint4 *>(ex);
 }
 
+// BF16: from sign/mantissa bytes S and exponent bytes E (4 elements each) make the
+// two output words of elements (2h, 2h+1): byte-permute S into [s,s] per element
+// (sign lands on bit 15, mantissa on bits 0..6 after the mask) and E into
+// [0,e] per element, shifted to bits 7..14.
+__device__ __forceinline__ uint32_t fuse_bf16_pair(uint32_t S, uint32_t E, uint32_t sel_s, uint32_t sel_e)
+{
+    const uint32_t sd = __builtin_amdgcn_perm(0u, S, sel_s);
+    const uint32_t ed = __builtin_amdgcn_perm(0u, E, sel_e);
+    return (sd & 0x807F807Fu) | (ed << 7);
+}
+
+// FP8: four sign|mantissa nibbles N (element k at bits 4k..4k+3) and four exponent
+// bytes E.  Each output byte is (sign << 7) | (exp << 3) | mant.
+__device__ __forceinline__ uint32_t fuse_fp8_quad(uint32_t N, uint32_t E)
+{
+    const uint32_t t = __builtin_amdgcn_perm(0u, N, 0x01010000u);       // [n23, n23, n01, n01]
+    const uint32_t x = (t & 0x000F000Fu) | ((t >> 4) & 0x0F000F00u);    // one nibble per byte
+    return x + (x & 0x08080808u) * 15u + (E << 3);                       // sign bit 3 -> bit 7
+}
+
 template <int DT>
 __device__ __forceinline__ void store_piece(void *out_block, uint32_t i, uint2 smv, uint4 e)
 {
     if (DT == ZX_BF16) {
         uint4 r;
-        r.x = fuse2_bf16(smv.x & 0xFFFFu, e.x & 0xFFFFu);
-        r.y = fuse2_bf16(smv.x >> 16, e.x >> 16);
-        r.z = fuse2_bf16(smv.y & 0xFFFFu, e.y & 0xFFFFu);
-        r.w = fuse2_bf16(smv.y >> 16, e.y >> 16);
+        r.x = fuse_bf16_pair(smv.x, e.x, 0x01010000u, 0x0C010C00u);
+        r.y = fuse_bf16_pair(smv.x, e.x, 0x03030202u, 0x0C030C02u);
+        r.z = fuse_bf16_pair(smv.y, e.y, 0x01010000u, 0x0C010C00u);
+        r.w = fuse_bf16_pair(smv.y, e.y, 0x03030202u, 0x0C030C02u);
         *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out_block) + i) = r;
     } else {
         uint4 r;
-        r.x = fuse4_fp8(smv.x & 0xFFFFu, e.x);
-        r.y = fuse4_fp8(smv.x >> 16, e.y);
-        r.z = fuse4_fp8(smv.y & 0xFFFFu, e.z);
-        r.w = fuse4_fp8(smv.y >> 16, e.w);
+        r.x = fuse_fp8_quad(smv.x & 0xFFFFu, e.x);
+        r.y = fuse_fp8_quad(smv.x >> 16, e.y);
+        r.z = fuse_fp8_quad(smv.y & 0xFFFFu, e.z);
+        r.w = fuse_fp8_quad(smv.y >> 16, e.w);
         *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(out_block) + i) = r;
     }
 }
 
-template <int DT>
-__device__ __forceinline__ void store_one(void *out_block, const uint8_t *sm_block, uint32_t ii, uint32_t ex)
-{
-    if (DT == ZX_BF16) {
-        reinterpret_cast<uint16_t *>(out_block)[ii] = (uint16_t)(fuse2_bf16(sm_block[ii], ex) & 0xFFFFu);
-    } else {
-        const uint32_t nb2 = sm_block[ii / 2];
-        const uint32_t nn = (ii & 1) ? (nb2 >> 4) : (nb2 & 0xFu);
-        reinterpret_cast<uint8_t *>(out_block)[ii] = (uint8_t)(fuse4_fp8(nn, ex) & 0xFFu);
-    }
-}
 
 
-// One piece of the write pass: a whole piece is fused and stored with one 16-byte
-// store; a piece cut by the range ends is written element by element.
+// Elements of the cut pieces at the two range ends, one element per lane: lane t
+// (< P) takes element t of the head piece, lane P + t element t of the tail piece.
 template <int DT>
-__device__ __forceinline__ void write_piece(void *out_block, const uint8_t *sm_block, uint32_t q, uint32_t i_begin,
-                                            uint32_t i_end, const uint8_t *stage, uint32_t sbase, bool degen,
-                                            uint32_t degen_sym, bool have_sm, uint2 smv)
+__device__ __forceinline__ void write_cut_pieces(void *out_block, const uint8_t *sm_block, uint32_t i_begin, uint32_t i_end,
+                                                 const uint8_t *stage, uint32_t sbase, bool degen, uint32_t degen_sym)
 {
     constexpr uint32_t P = Piece<DT>::kElems;
-    const uint32_t i = q * P;
-    if (i >= i_begin && i + P <= i_end) {
-        if (!have_sm) smv = load_sm<DT>(sm_block, i);
-        store_piece<DT>(out_block, i, smv, piece_exps<DT>(stage + (i - sbase), degen, degen_sym * 0x01010101u));
-    } else {
-#pragma unroll 1
-        for (uint32_t t = 0; t < P; ++t) {
-            const uint32_t ii = i + t;
-            if (ii >= i_begin && ii < i_end) store_one<DT>(out_block, sm_block, ii, degen ? degen_sym : stage[ii - sbase]);
+    const uint32_t lane = lane_id();
+    const uint32_t q_head = i_begin / P;
+    const uint32_t q_tail = (i_end - 1) / P;
+    const bool head_cut = (i_begin % P) != 0 || (q_head == q_tail && (i_end % P) != 0);
+    const bool tail_cut = (i_end % P) != 0 && q_tail != q_head;
+    uint32_t ii = ~0u;
+    if (lane < P && head_cut) ii = q_head * P + lane;
+    if (lane >= P && lane < 2 * P && tail_cut) ii = q_tail * P + (lane - P);
+    if (ii != ~0u && ii >= i_begin && ii < i_end) {
+        const uint32_t smb = sm_block[DT == ZX_BF16 ? ii : ii / 2];
+        const uint32_t ex = degen ? degen_sym : stage[ii - sbase];
+        if (DT == ZX_BF16) {
+            reinterpret_cast<uint16_t *>(out_block)[ii] = (uint16_t)fuse_bf16_pair(smb, ex, 0x0C0C0000u, 0x0C0C0C00u);
+        } else {
+            const uint32_t nn = (ii & 1) ? (smb >> 4) : (smb & 0xFu);
+            reinterpret_cast<uint8_t *>(out_block)[ii] = (uint8_t)(fuse_fp8_quad(nn, ex) & 0xFFu);
         }
     }
 }
 
-constexpr int kWriteBatch = 4;   // pieces per lane whose loads are issued together
+constexpr int kWriteBatch = 4;   // whole pieces per lane whose loads are issued together
 
 // Write block elements [i_begin, i_end); the exponent of element i is stage[i - sbase]
-// (or `degen_sym` for a 0-bit block).  Sign/mantissa loads of kWriteBatch pieces
-// per lane are issued before any of them is used.
+// (or `degen_sym` for a 0-bit block).  Whole pieces: kWriteBatch sign/mantissa
+// loads per lane are issued before any is used, then each piece is fused and
+// written with one 16-byte store.  The (at most two) cut pieces at the range ends
+// are written one element per lane.
 template <int DT>
 __device__ __forceinline__ void write_range(void *out_block, const uint8_t *sm_block, uint32_t i_begin, uint32_t i_end,
                                             const uint8_t *stage, uint32_t sbase, bool degen, uint32_t degen_sym)
 {
     constexpr uint32_t P = Piece<DT>::kElems;
+    if (i_begin >= i_end) return;
     const uint32_t lane = lane_id();
-    const uint32_t q_begin = i_begin / P;
-    const uint32_t q_end = (i_end + P - 1) / P;
-    for (uint32_t qb = q_begin; qb < q_end; qb += kWave * kWriteBatch) {
+    const uint32_t qf_begin = (i_begin + P - 1) / P;   // first whole piece
+    const uint32_t qf_end = i_end / P;                 // one past the last whole piece
+    const uint32_t dsplat = degen_sym * 0x01010101u;
+    for (uint32_t qb = qf_begin; qb < qf_end; qb += kWave * kWriteBatch) {
         uint2 smv[kWriteBatch];
 #pragma unroll
         for (int k = 0; k < kWriteBatch; ++k) {
             const uint32_t q = qb + lane + k * kWave;
-            const uint32_t i = q * P;
             smv[k] = make_uint2(0, 0);
-            if (q < q_end && i >= i_begin && i + P <= i_end) smv[k] = load_sm<DT>(sm_block, i);
+            if (q < qf_end) smv[k] = load_sm<DT>(sm_block, q * P);
         }
 #pragma unroll
         for (int k = 0; k < kWriteBatch; ++k) {
             const uint32_t q = qb + lane + k * kWave;
-            if (q < q_end) write_piece<DT>(out_block, sm_block, q, i_begin, i_end, stage, sbase, degen, degen_sym, true, smv[k]);
+            if (q < qf_end) store_piece<DT>(out_block, q * P, smv[k], piece_exps<DT>(stage + (q * P - sbase), degen, dsplat));
         }
     }
+    write_cut_pieces<DT>(out_block, sm_block, i_begin, i_end, stage, sbase, degen, degen_sym);
 }
 
 __device__ __forceinline__ void wave_sync()
