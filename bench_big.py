@@ -1,0 +1,166 @@
+"""Large workloads for bench.py (--config c3 | c5).
+
+c3: Llama-3-8B-shaped BF16 weight set (32 layers x {q,k,v,o,gate,up,down} + lm_head),
+    one codebook per tensor; a step decodes the whole set as 33 calls, one
+    zx_decode_block_batch per transformer layer (7 tensors) and one for the lm_head.
+c5: BF16 K/V cache [2, 32, 8, 32768, 128] (2^31 elements), one codebook per
+    65536-element block; a step decodes the whole cache.
+
+Inputs are drawn on the GPU with seeded generators (workloads.py), compressed once
+(the encode is timed separately on a subset), then decoded repeatedly.  The
+decoded outputs are compared with the inputs on the device after timing.
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import torch
+
+import workloads
+import lossless_float_compression_amd as zx
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "decode GB/s (BF16 out) and % HBM roofline; encode GB/s; compression ratio"
+
+
+def _alg_bytes(c) -> int:
+    read = (c.signmant.numel() + c.total_bits // 8 + c.gaps.numel() + c.seg_desc.numel() * 4
+            + c.block_bitoff.numel() * 8 + c.block_seg.numel() * 4 + c.lengths.numel() + c.degenerate.numel() * 2)
+    return int(read + c.raw_bytes())
+
+
+def _events(n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def run_c3(args):
+    names = workloads.c3_names()
+    n_layers = workloads.C3_LAYERS
+    per_layer = len(workloads.C3_SHAPES)
+    t0 = time.time()
+    comps, raw_total, enc_ms = [], 0, []
+    e = _events(2)
+    for i, (name, shape) in enumerate(names):
+        x = workloads.c3_tensor(i)
+        raw_total += x.numel() * 2
+        if i < per_layer:  # time the encode of layer 0 (its 7 tensors)
+            torch.cuda.synchronize()
+            e[0].record()
+            c = zx.compress(x)
+            e[1].record()
+            torch.cuda.synchronize()
+            enc_ms.append((e[0].elapsed_time(e[1]), x.numel() * 2))
+        else:
+            c = zx.compress(x)
+        comps.append(c)
+        del x
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    groups = [comps[l * per_layer:(l + 1) * per_layer] for l in range(n_layers)] + [[comps[-1]]]
+    outs = [[zx.empty_output(c) for c in groups[0]], [zx.empty_output(c) for c in groups[0]]]
+    out_head = zx.empty_output(comps[-1])
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step(evs=None):
+        for g, grp in enumerate(groups):
+            o = [out_head] if g == n_layers else outs[g % 2]
+            if evs is not None:
+                evs[g][0].record()
+            zx.decompress_batch(grp, o, err=err)
+            if evs is not None:
+                evs[g][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[_events(2) for _ in groups] for _ in range(args.steps)]
+    t1 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    layer_ms = np.array([[ev[g][0].elapsed_time(ev[g][1]) for g in range(n_layers)] for ev in evs])
+    head_ms = np.array([ev[n_layers][0].elapsed_time(ev[n_layers][1]) for ev in evs])
+    assert int(err.item()) == 0
+    # correctness: decode every tensor again and compare with a regenerated input
+    for i, c in enumerate(comps):
+        y = zx.decompress(c)
+        assert torch.equal(y.view(torch.int16), workloads.c3_tensor(i)), f"tensor {i} did not round-trip"
+        del y
+    dec_ms = float(layer_ms.sum(1).mean() + head_ms.mean())
+    layer_alg = sum(_alg_bytes(c) for c in groups[0])
+    layer_raw = sum(c.raw_bytes() for c in groups[0])
+    lay_avg = float(layer_ms.mean())
+    achieved = layer_alg / (lay_avg * 1e-3) / 1e9
+    comp_bytes = sum(c.nbytes() for c in comps)
+    enc_t = sum(m for m, _ in enc_ms)
+    enc_b = sum(b for _, b in enc_ms)
+    return {
+        "metric": METRIC, "value": round(raw_total / (dec_ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": {"workload": "c3: Llama-3-8B-shaped BF16 weights, one codebook per tensor, one batched call per layer",
+                   "elements": int(raw_total // 2), "raw_bytes": int(raw_total), "calls_per_step": len(groups)},
+        "decode_ms": round(dec_ms, 4), "layer_decode_ms": round(lay_avg, 5), "lm_head_decode_ms": round(float(head_ms.mean()), 5),
+        "layer_decode_GBps": round(layer_raw / (lay_avg * 1e-3) / 1e9, 2),
+        "encode_GBps_layer0": round(enc_b / (enc_t * 1e-3) / 1e9, 2),
+        "ratio": round(comp_bytes / raw_total, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_decode (one layer call)",
+                     "alg_bytes_per_launch": int(layer_alg)},
+        "setup_s": round(setup_s, 1),
+    }
+
+
+def run_c5(args):
+    t0 = time.time()
+    x = workloads.c5()
+    raw = x.numel() * 2
+    torch.cuda.synchronize()
+    e = _events(2)
+    e[0].record()
+    c = zx.compress(x, per_block=True)
+    e[1].record()
+    torch.cuda.synchronize()
+    enc_ms = e[0].elapsed_time(e[1])
+    setup_s = time.time() - t0
+    out = zx.empty_output(c)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(args.warmup):
+        zx.decompress(c, out=out, err=err)
+    torch.cuda.synchronize()
+    evs = [_events(2) for _ in range(args.steps)]
+    t1 = time.perf_counter()
+    for k in range(args.steps):
+        evs[k][0].record()
+        zx.decompress(c, out=out, err=err)
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    dec = np.array([a.elapsed_time(b) for a, b in evs])
+    assert int(err.item()) == 0
+    assert torch.equal(out.view(torch.int16), x), "K/V cache did not round-trip"
+    dec_ms = float(dec.mean())
+    alg = _alg_bytes(c)
+    achieved = alg / (dec_ms * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": round(raw / (dec_ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": {"workload": "c5: BF16 K/V [2,32,8,32768,128], 0.5*t(5) with 4/128 channels x20, one codebook per 64K block",
+                   "elements": int(x.numel()), "raw_bytes": int(raw)},
+        "decode_ms": round(dec_ms, 4), "encode_ms": round(enc_ms, 4),
+        "encode_GBps": round(raw / (enc_ms * 1e-3) / 1e9, 2),
+        "ratio": round(c.nbytes() / raw, 5), "exponent_bits_per_element": round(c.total_bits / c.n, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_decode (per-block codebooks)",
+                     "alg_bytes_per_launch": int(alg)},
+        "setup_s": round(setup_s, 1),
+    }
+
+
+def run(args):
+    if args.config == "c3":
+        return run_c3(args)
+    return run_c5(args)

@@ -21,7 +21,7 @@ constexpr int kWave = 64;
 
 // Decode lookup table index width: the primary table maps the next kLutBits
 // stream bits to up to two symbols.
-constexpr int kLutBits = 11;
+constexpr int kLutBits = 10;
 constexpr uint32_t kLutSize = 1u << kLutBits;
 
 __host__ __device__ constexpr uint32_t alphabet_of(int dtype) { return dtype == ZX_BF16 ? 256u : 16u; }
@@ -142,9 +142,10 @@ __device__ __forceinline__ uint32_t canon_len(const uint64_t *lim, uint32_t v, u
 //   lim/base/sym: canonical description for codes longer than the window.
 constexpr uint32_t kLutSymMax = 3;
 
+// Index kLutSize is a zero entry: lanes that are done look it up and stay put.
 struct __align__(16) DTab {
-    uint32_t lut[kLutSize];
-    uint8_t first_len[kLutSize];
+    uint32_t lut[kLutSize + 4];
+    uint8_t first_len[kLutSize + 16];
     uint64_t lim[kMaxLen + 2];
     int32_t base[kMaxLen + 1];          // offset[L] - first[L]
     uint8_t sym[256];
@@ -189,6 +190,8 @@ __device__ inline void dtab_fill(const Canon &c, DTab &t)
         t.lut[x] = e;
         t.first_len[x] = (uint8_t)first;
     }
+    if (tid < 4) t.lut[kLutSize + tid] = 0;
+    if (tid < 16) t.first_len[kLutSize + tid] = 0;
 }
 
 }  // namespace zxk

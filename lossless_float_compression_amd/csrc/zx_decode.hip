@@ -23,10 +23,10 @@ namespace zxk {
 
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * kWave;
-constexpr uint32_t kStageBytes = 4096;   // exponent stage per wavefront
+constexpr uint32_t kStageBytes = 4000;   // exponent stage per wavefront
 // A segment whose exponents do not fit the stage at once (mean code length under
 // two bits) is written in rounds of kRoundElems output positions.
-constexpr uint32_t kRoundElems = 4064;
+constexpr uint32_t kRoundElems = 3968;
 constexpr int kDecWgPerCu = 3;
 constexpr int kDecMinWavesPerSimd = kDecWgPerCu * kDecWaves / 4;
 constexpr int kMaxBatch = 16;
@@ -60,23 +60,29 @@ struct DecBatch {
 
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
-// Stream words of one segment staged in LDS: word k holds stream word W0 + k, where
-// W0 is the word holding the segment's first bit.  A segment spans 8192 bits from
-// an offset below 32, so 257 words cover it and a 64-bit window past its end.
-constexpr uint32_t kSegWords = 264;
+// Stream words of a lane's chunk, staged in LDS one column per lane: word t of
+// lane l (the t-th word from the one holding the chunk's first bit) sits at
+// 64 t + l.  In every window read each lane then hits its own bank.  A chunk
+// starts less than 32 bits into its first word and a lane reads at most a 64-bit
+// window starting inside its chunk, so 7 words per lane suffice.
+constexpr uint32_t kLaneWords = 7;
+constexpr uint32_t kSegWords = kLaneWords * 64;
 
 struct SegWords {
-    const uint32_t *w;   // LDS
-    // 64 bits starting at staged bit p, left-aligned
+    const uint32_t *w;   // LDS, this lane's column
+    // 64 bits starting at chunk-relative bit p (counted from the first word's MSB)
     __device__ __forceinline__ uint64_t win(uint32_t p) const
     {
-        const uint32_t k = p >> 5;
-        return ((((uint64_t)w[k]) << 32) | w[k + 1]) << (p & 31);
+        const uint32_t t = p >> 5;
+        const uint64_t v = ((uint64_t)w[t * 64] << 32) | w[(t + 1) * 64];
+        return v << (p & 31);
     }
 };
 
-// Copy stream words [W0, W0 + 260) into the wavefront's LDS area (zero past the end).
-__device__ __forceinline__ void stage_words(uint32_t *sw, const uint32_t *stream, uint64_t words, uint64_t W0)
+// Stage the segment's words: the wavefront loads stream words [W0, W0 + 260) with
+// one coalesced 16-byte load per lane (plus the tail words), and each word goes to
+// the lanes that need it: lane l needs words 4 l .. 4 l + 6.
+__device__ __forceinline__ void stage_seg_words(uint32_t *sw, const uint32_t *stream, uint64_t words, uint64_t W0)
 {
     const uint32_t lane = lane_id();
     const uint64_t k = W0 + 4ull * lane;
@@ -89,10 +95,15 @@ __device__ __forceinline__ void stage_words(uint32_t *sw, const uint32_t *stream
         v.z = k + 2 < words ? stream[k + 2] : 0u;
         v.w = k + 3 < words ? stream[k + 3] : 0u;
     }
-    reinterpret_cast<uint4 *>(sw)[lane] = make_uint4(v.x, v.y, v.z, v.w);
-    if (lane < 4) {
+    uint32_t *own = sw + lane;                    // words 4l .. 4l+3 are this lane's 0..3
+    own[0] = v.x; own[64] = v.y; own[128] = v.z; own[192] = v.w;
+    if (lane > 0) {                               // and the previous lane's 4..6
+        uint32_t *prev = sw + lane - 1;
+        prev[256] = v.x; prev[320] = v.y; prev[384] = v.z;
+    }
+    if (lane < 3) {                               // words 256..258 finish lane 63
         const uint64_t t = W0 + 256 + lane;
-        sw[256 + lane] = t < words ? stream[t] : 0u;
+        sw[64 * (4 + lane) + 63] = t < words ? stream[t] : 0u;
     }
 }
 
@@ -204,13 +215,15 @@ __device__ __forceinline__ void write_cut_pieces(void *out_block, const uint8_t 
     }
 }
 
-constexpr int kWriteBatch = 4;   // whole pieces per lane whose loads are issued together
+constexpr int kWriteBatch = 7;   // whole pieces per lane whose loads are issued together
+// Whole pieces of [i_begin, i_end) for this lane: q = qf_begin + lane + 64 k.
+__device__ __forceinline__ uint32_t first_whole(uint32_t i_begin, uint32_t P) { return (i_begin + P - 1) / P; }
 
 // Write block elements [i_begin, i_end); the exponent of element i is stage[i - sbase]
-// (or `degen_sym` for a 0-bit block).  Whole pieces: kWriteBatch sign/mantissa
-// loads per lane are issued before any is used, then each piece is fused and
-// written with one 16-byte store.  The (at most two) cut pieces at the range ends
-// are written one element per lane.
+// (or `degen_sym` for a 0-bit block).  Whole pieces: sign/mantissa loads of
+// kWriteBatch pieces per lane are issued before any is used, then each piece is
+// fused and written with one 16-byte store.  The (at most two) cut pieces at the
+// range ends are written one element per lane.
 template <int DT>
 __device__ __forceinline__ void write_range(void *out_block, const uint8_t *sm_block, uint32_t i_begin, uint32_t i_end,
                                             const uint8_t *stage, uint32_t sbase, bool degen, uint32_t degen_sym)
@@ -218,8 +231,8 @@ __device__ __forceinline__ void write_range(void *out_block, const uint8_t *sm_b
     constexpr uint32_t P = Piece<DT>::kElems;
     if (i_begin >= i_end) return;
     const uint32_t lane = lane_id();
-    const uint32_t qf_begin = (i_begin + P - 1) / P;   // first whole piece
-    const uint32_t qf_end = i_end / P;                 // one past the last whole piece
+    const uint32_t qf_begin = first_whole(i_begin, P);
+    const uint32_t qf_end = i_end / P;
     const uint32_t dsplat = degen_sym * 0x01010101u;
     for (uint32_t qb = qf_begin; qb < qf_end; qb += kWave * kWriteBatch) {
         uint2 smv[kWriteBatch];
@@ -291,55 +304,68 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
     // chunk-relative end: the lane decodes the codes starting in [gap, cend)
     const uint32_t cend = (ch * kChunkBits + kChunkBits < bits) ? kChunkBits : bits - ch * kChunkBits;
     if (work && gap >= cend) { work = false; lane_bad = true; }
-    const uint64_t segbit = G + (uint64_t)j * kSegBits;
-    stage_words(swords, T.stream, T.stream_words, segbit >> 5);
+    // chunk-relative bit coordinates from the MSB of the word holding the chunk's
+    // first bit: the chunk starts at b0 < 32
+    const uint64_t cbit = G + (uint64_t)ch * kChunkBits;
+    const uint32_t b0 = (uint32_t)(cbit & 31);
+    stage_seg_words(swords, T.stream, T.stream_words, (G >> 5) + (uint64_t)j * (kSegBits / 32));
     wave_sync();
-    const SegWords sw{swords};
-    // staged-bit coordinates: chunk start = (segbit & 31) + 128 lane
-    const uint32_t cbase = (uint32_t)(segbit & 31) + lane * kChunkBits;
-    const uint32_t start = cbase + gap;
-    const uint32_t lim = work ? cbase + cend : 0;
+    const SegWords sw{swords + lane};
+    const uint32_t start = work ? b0 + gap : 0;
+    const uint32_t lim = work ? b0 + cend : 0;
 
-    // ---- count pass.  Main loop: while a whole window lies inside the chunk, every
-    //      code the table returns starts inside it.  Tail: one code at a time.
+    // ---- count pass.  Main phase: while a whole window lies inside the chunk, every
+    //      code the table returns starts inside it.  Tail phase: one code at a time.
+    //      A code longer than the window reads as a zero entry, so its lane stalls;
+    //      the inner loops run while some lane progresses, then stalled lanes take
+    //      their long code from the canonical length limits.
     uint32_t cnt = 0;
     uint32_t pos = work ? start : 0;
-    while (__ballot(pos + kLutBits <= lim) != 0) {
-        const bool act = pos + kLutBits <= lim;
-        const uint64_t x = sw.win(pos);
-        const uint32_t e = tab.lut[(uint32_t)(x >> (64 - kLutBits))];
-        uint32_t ns = e >> 28;
-        uint32_t adv = (e >> 24) & 0xFu;
-        if (__ballot(act && ns == 0) != 0) {
-            if (act && ns == 0) {
-                adv = slow_len(tab, (uint32_t)(x >> 32));
-                ns = 1;
-                if (adv > kMaxLen) { lane_bad = true; adv = lim - pos; }
-            }
+    for (;;) {
+        bool act = pos + kLutBits <= lim;
+        if (__ballot(act) == 0) break;
+        bool progress;
+        do {
+            const uint32_t idx = act ? (uint32_t)(sw.win(pos) >> (64 - kLutBits)) : kLutSize;
+            const uint32_t e = tab.lut[idx];
+            const uint32_t adv = (e >> 24) & 0xFu;
+            progress = adv != 0;   // a zero advance (long code, or a damaged table) stalls
+            cnt += e >> 28;
+            pos += adv;
+            act = pos + kLutBits <= lim;
+        } while (__ballot(progress && act) != 0);
+        if (act && !progress) {   // stalled at a long code
+            uint32_t L = slow_len(tab, (uint32_t)(sw.win(pos) >> 32));
+            if (L > kMaxLen) { lane_bad = true; L = lim - pos; }
+            cnt += 1;
+            pos += L;
         }
-        if (act && adv == 0) { lane_bad = true; adv = lim - pos; }   // a damaged table must not stall
-        cnt += act ? ns : 0u;
-        pos += act ? adv : 0u;
     }
-    while (__ballot(pos < lim) != 0) {
-        const bool act = pos < lim;
-        const uint64_t x = sw.win(pos);
-        uint32_t L = tab.first_len[(uint32_t)(x >> (64 - kLutBits))];
-        if (__ballot(act && L == 0) != 0) {
-            if (act && L == 0) {
-                L = slow_len(tab, (uint32_t)(x >> 32));
-                if (L > kMaxLen) { lane_bad = true; L = lim - pos; }
-            }
+    for (;;) {
+        bool act = pos < lim;
+        if (__ballot(act) == 0) break;
+        bool progress;
+        do {
+            const uint32_t idx = act ? (uint32_t)(sw.win(pos) >> (64 - kLutBits)) : kLutSize;
+            const uint32_t L = tab.first_len[idx];
+            progress = L != 0;
+            cnt += progress ? 1u : 0u;
+            pos += L;
+            act = pos < lim;
+        } while (__ballot(progress && act) != 0);
+        if (act && !progress) {
+            uint32_t L = slow_len(tab, (uint32_t)(sw.win(pos) >> 32));
+            if (L > kMaxLen) { lane_bad = true; L = lim - pos; }
+            cnt += 1;
+            pos += L;
         }
-        cnt += act ? 1u : 0u;
-        pos += act ? L : 0u;
     }
     // codes of one chunk must end exactly where the next chunk's first code
     // starts (or at the block end), as the stored gaps claim
     uint32_t gap_next = __shfl_down(gap, 1, kWave);
     if (lane == kWave - 1) gap_next = (ch + 1 < nch) ? T.gaps[(uint64_t)(s + 1) * kSegChunks] : ZX_NO_GAP;
     if (work && !lane_bad) {
-        const uint32_t expect = (ch + 1 < nch && gap_next != ZX_NO_GAP) ? cbase + kChunkBits + gap_next : cbase + (bits - ch * kChunkBits);
+        const uint32_t expect = (ch + 1 < nch && gap_next != ZX_NO_GAP) ? b0 + kChunkBits + gap_next : b0 + (bits - ch * kChunkBits);
         if (pos != expect) lane_bad = true;
     }
     uint32_t total;
@@ -347,34 +373,40 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
     if (__ballot(lane_bad) != 0 || e0 + total != e_end) { report(err, ZX_E_CORRUPT); return; }
 
     const uint32_t t0 = e0 - sbase;   // stage position of the segment's first element
-    if (t0 + total + 2 <= kStageBytes) {
+    if (t0 + total + 2 <= kStageBytes - 4) {   // the last 4 bytes are the dummy store slot
         // ---- decode pass, one round: each lookup stores all its symbols; a lane's
         //      last lookup may spill up to two bytes onto the next lanes' first
         //      positions, which those lanes restore right after
         uint32_t wp = t0 + off;
         uint32_t done = 0;
         pos = start;
-        while (__ballot(done < cnt) != 0) {
-            const bool act = done < cnt;
-            const uint64_t x = sw.win(pos);
-            uint32_t e = tab.lut[(uint32_t)(x >> (64 - kLutBits))];
-            uint32_t ns = e >> 28;
-            uint32_t adv = (e >> 24) & 0xFu;
-            if (__ballot(act && ns == 0) != 0) {
-                if (act && ns == 0) {
-                    const uint32_t v = (uint32_t)(x >> 32);
-                    adv = slow_len(tab, v);
-                    e = slow_sym(tab, v, adv);
-                    ns = 1;
-                }
-            }
-            if (act) {
-                stage[wp] = (uint8_t)e;
-                stage[wp + 1] = (uint8_t)(e >> 8);
-                stage[wp + 2] = (uint8_t)(e >> 16);
+        uint8_t *const dummy = stage + kStageBytes - 4;   // where lanes that are done store
+        for (;;) {
+            bool act = done < cnt;
+            if (__ballot(act) == 0) break;
+            bool progress;
+            do {
+                const uint32_t idx = act ? (uint32_t)(sw.win(pos) >> (64 - kLutBits)) : kLutSize;
+                const uint32_t e = tab.lut[idx];
+                uint8_t *const d = act ? stage + wp : dummy;
+                d[0] = (uint8_t)e;
+                d[1] = (uint8_t)(e >> 8);
+                d[2] = (uint8_t)(e >> 16);
+                const uint32_t adv = (e >> 24) & 0xFu;
+                progress = adv != 0;
+                const uint32_t ns = e >> 28;
                 wp += ns;
                 done += ns;
                 pos += adv;
+                act = done < cnt;
+            } while (__ballot(progress && act) != 0);
+            if (act && !progress) {
+                const uint32_t v = (uint32_t)(sw.win(pos) >> 32);
+                const uint32_t L = slow_len(tab, v);
+                stage[wp] = (uint8_t)slow_sym(tab, v, L);
+                wp += 1;
+                done += 1;
+                pos += L;
             }
         }
         wave_sync();
@@ -441,6 +473,8 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
     __shared__ DTab tab;
     __shared__ __align__(16) uint8_t stage_all[kDecWaves * kStageBytes];
     __shared__ __align__(16) uint32_t words_all[kDecWaves * kSegWords];
+    // three workgroups of this size were measured to fit a CU; 54 KB ones were not
+    static_assert(sizeof(DTab) + sizeof(stage_all) + sizeof(words_all) <= 52224, "decode workgroup LDS budget");
     static_assert(sizeof(Canon) <= sizeof(stage_all), "Canon is built inside the stage area");
 
     const uint32_t g = blockIdx.x;
