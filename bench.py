@@ -12,6 +12,8 @@ R copies of the input and its containers (>= 1 GiB of traffic in flight): step i
 encodes copy i % R and decodes copy (i + R/2) % R, which was encoded half a
 rotation earlier and has been evicted since.
 
+After the K steps, K decodes run back to back over the rotation between two
+events; their average launch time is `decode_ms`, the time the roofline uses.
 The JSON line reports decode throughput (BF16 bytes out / decode time) as `value`,
 with encode throughput, compression ratio, the decode kernel's HBM roofline and
 the CPU oracle's decode throughput on the host as extra fields.
@@ -43,7 +45,57 @@ def parse():
     p.add_argument("--copies", type=int, default=0, help="rotation depth (0 = enough for 1 GiB)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run plain device copies of 256 MiB (reference for HBM byte counters)")
     return p.parse_args()
+
+
+DECODE_SOURCES = ("lossless_float_compression_amd/csrc/zx_decode.hip", "lossless_float_compression_amd/csrc/zx_common.h")
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+# workload names used in the committed profile summaries
+WORKLOAD_SLUG = {"c1": "bf16_1024x1024", "c2": "bf16_4096x4096", "c3": "llama3_8b_shaped_layer",
+                 "c4": "fp8_e4m3_8192x8192", "c5": "bf16_kv_cache"}
+
+
+def profiled_traffic(cfg: str):
+    """HBM bytes per decode launch (FETCH_SIZE and WRITE_SIZE counters scaled by a plain
+    copy of known size) from the committed counter summary, or None when there is none
+    or the decode kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"k_decode_{WORKLOAD_SLUG[cfg]}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != decode_source_hash():
+        return None
+    try:
+        return int(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    """Plain device-to-device copies of exactly 256 MiB (read 256 MiB, write 256 MiB)."""
+    import torch
+    a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("copied 5 x 268435456 bytes", flush=True)
 
 
 def decode_alg_bytes(c) -> int:
@@ -126,15 +178,25 @@ def bench_single(args):
         step(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    dec_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    step_dec_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     enc_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    # decode launches back to back over the rotation (each copy cold in the caches),
+    # two events around all of them: the per-launch average without event overhead
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    d0.record(stream)
+    for i in range(args.steps):
+        k = i % R
+        zx.decompress(cs[k], out=outs[k], err=err)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    dec_avg = d0.elapsed_time(d1) / args.steps
     # correctness at full size, outside the timed region
     assert int(err.item()) == 0, "decoder reported a corrupt container"
     for k in range(R):
         y = zx.decompress(cs[k])
         assert torch.equal(y.reshape(-1).view(x0.dtype), xs[k].reshape(-1)), f"copy {k} did not round-trip"
     c = cs[0]
-    dec_avg = float(dec_ms.mean())
     alg = decode_alg_bytes(c)
     achieved = alg / (dec_avg * 1e-3) / 1e9
     res = {
@@ -152,13 +214,13 @@ def bench_single(args):
         "data": "synthetic",
         "config": {"workload": desc, "elements": c.n, "raw_bytes": raw_bytes, "rotation_copies": R},
         "decode_ms": round(dec_avg, 5),
-        "decode_ms_median": round(float(np.median(dec_ms)), 5),
+        "decode_ms_in_step": round(float(step_dec_ms.mean()), 5),
         "encode_ms": round(float(enc_ms.mean()), 5),
         "encode_GBps": round(raw_bytes / (float(enc_ms.mean()) * 1e-3) / 1e9, 2),
         "ratio": round(c.nbytes() / raw_bytes, 5),
         "exponent_bits_per_element": round(c.total_bits / c.n, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(args.config),
                      "kernel": "k_decode", "alg_bytes_per_launch": alg},
     }
     if not args.no_cpu:
@@ -175,6 +237,9 @@ def main():
               "(the codec needs no collectives: each GPU decodes its own shard)", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)

@@ -30,6 +30,11 @@ def _alg_bytes(c) -> int:
     return int(read + c.raw_bytes())
 
 
+def _traffic(cfg):
+    from bench import profiled_traffic
+    return profiled_traffic(cfg)
+
+
 def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
@@ -107,7 +112,7 @@ def run_c3(args):
         "encode_GBps_layer0": round(enc_b / (enc_t * 1e-3) / 1e9, 2),
         "ratio": round(comp_bytes / raw_total, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_decode (one layer call)",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": _traffic("c3"), "kernel": "k_decode (one layer call)",
                      "alg_bytes_per_launch": int(layer_alg)},
         "setup_s": round(setup_s, 1),
     }
@@ -154,7 +159,7 @@ def run_c5(args):
         "encode_GBps": round(raw / (enc_ms * 1e-3) / 1e9, 2),
         "ratio": round(c.nbytes() / raw, 5), "exponent_bits_per_element": round(c.total_bits / c.n, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_decode (per-block codebooks)",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": _traffic("c5"), "kernel": "k_decode (per-block codebooks)",
                      "alg_bytes_per_launch": int(alg)},
         "setup_s": round(setup_s, 1),
     }
