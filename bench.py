@@ -54,10 +54,16 @@ DECODE_SOURCES = ("lossless_float_compression_amd/csrc/zx_decode.hip", "lossless
 
 
 def decode_source_hash() -> str:
+    """Hash of the decode kernel's sources with comments and blank space removed, so
+    that only a change of the code itself invalidates counters taken on it."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in DECODE_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        src = open(os.path.join(ROOT, f), encoding="utf-8").read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

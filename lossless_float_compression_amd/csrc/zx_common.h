@@ -20,7 +20,7 @@ constexpr uint32_t kMaxLen = 32;
 constexpr int kWave = 64;
 
 // Decode lookup table index width: the primary table maps the next kLutBits
-// stream bits to up to two symbols.
+// stream bits to up to three symbols.
 constexpr int kLutBits = 10;
 constexpr uint32_t kLutSize = 1u << kLutBits;
 

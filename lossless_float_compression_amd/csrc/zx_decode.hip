@@ -6,8 +6,8 @@
 // decode of a whole transformer block per call.  The gfx950 design here:
 //   * one wavefront decodes one segment: 64 chunks of 128 stream bits, lane l owns
 //     chunk l and starts at the chunk's stored gap (the first code starting in it);
-//   * lookup: the next 11 stream bits index a 2048-entry LDS table that yields up to
-//     two whole codes; longer codes fall back to the canonical length limits;
+//   * lookup: the next 10 stream bits index a 1024-entry LDS table that yields up to
+//     three whole codes; longer codes fall back to the canonical length limits;
 //   * count pass, then a wavefront prefix scan of per-lane counts gives each lane
 //     its output offset (the segment's first element is stored in the container);
 //   * the lane decodes again, dropping exponents into a wavefront-private LDS stage
