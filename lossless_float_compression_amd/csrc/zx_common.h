@@ -35,17 +35,21 @@ __device__ __forceinline__ void report(uint32_t *err, uint32_t code)
 }
 
 // Exclusive prefix sum across the 64 lanes of a wavefront; `total` gets the sum.
+// Data-parallel-primitive lane moves: shifts by 1, 2, 4, 8 inside each row of 16
+// lanes, then the last lane of each row is broadcast into the following rows.  No
+// address registers are needed, unlike a permute-based scan.
 __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t &total)
 {
-    uint32_t x = v;
-    const uint32_t lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        uint32_t y = __shfl_up(x, d, kWave);
-        if (lane >= (uint32_t)d) x += y;
-    }
-    total = __shfl(x, kWave - 1, kWave);
-    return x - v;
+    // dpp_ctrl encodings: row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143
+    int x = (int)v;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+    total = (uint32_t)__builtin_amdgcn_readlane(x, kWave - 1);
+    return (uint32_t)x - v;
 }
 
 // Canonical-code description of one codebook, built in LDS by a whole workgroup.
@@ -131,24 +135,41 @@ __device__ __forceinline__ uint32_t canon_len(const uint64_t *lim, uint32_t v, u
     return L;
 }
 
-// Decoder tables kept in LDS.
-//   lut[x], x = the next kLutBits stream bits: up to three whole codes that fit in
-//   the window, decoded in order:
-//     bits  0..7 / 8..15 / 16..23  first / second / third symbol
-//     bits 24..27                   bits taken by those codes (<= kLutBits)
-//     bits 28..29                   number of codes (0: the first code is longer
-//                                   than the window; use the length limits)
-//   first_len[x]: length of the first code in the window, 0 if longer.
+// Form in which the decoder stages an exponent symbol for the write pass.
+//   BF16: the 8-bit exponent rotated right by one bit.  Bit 7 is then the exponent's
+//         low bit, which belongs in the low byte of the BF16 value next to the 7
+//         mantissa bits, and bits 0..6 are the exponent's upper seven bits, which
+//         belong in the high byte next to the sign: one bit-select per byte pair.
+//   FP8:  the 4-bit exponent already shifted to its place, bits 3..6.
+__host__ __device__ constexpr uint32_t stage_form(uint32_t A, uint32_t e)
+{
+    return A == 16u ? (e << 3) : (((e >> 1) | (e << 7)) & 0xFFu);
+}
+
+// Decoder tables kept in LDS.  For every value x of the next kLutBits stream bits:
+//   lo[x]  bits  0..3   bits taken by the whole codes that fit in the window (adv)
+//          bits 16..23  number of those codes, at most three (ns)
+//          bits 24..27  length of the first code
+//          bits 28..31  length of the first two codes together
+//          lo[x] == 0   the first code is longer than the window
+//   hi[x]  bytes 0..2   stage forms of the decoded symbols, in stream order
+//          byte  3      ns again
+// The fields of lo are placed so that a lane can keep its bit position in the low
+// byte and its code count in bits 16..23 of one register and subtract whole entries
+// from it, and so that the low five bits of lo are exactly the shift that consumes
+// the entry from a 32-bit window.  Entry kLutSize is all zero.
 //   lim/base/sym: canonical description for codes longer than the window.
+//   lim_short: the largest left-justified 32-bit window that starts with a code of at
+//   most kLutBits bits (canonical codes of length <= L fill [0, lim[L]) in order).
 constexpr uint32_t kLutSymMax = 3;
 
-// Index kLutSize is a zero entry: lanes that are done look it up and stay put.
 struct __align__(16) DTab {
-    uint32_t lut[kLutSize + 4];
-    uint8_t first_len[kLutSize + 16];
+    uint32_t lo[kLutSize + 4];
+    uint32_t hi[kLutSize + 4];
     uint64_t lim[kMaxLen + 2];
     int32_t base[kMaxLen + 1];          // offset[L] - first[L]
-    uint8_t sym[256];
+    uint8_t sym[256];                   // stage form by canonical index
+    uint32_t lim_short;
     uint32_t ok;
     uint32_t nsym;
     uint32_t maxlen;
@@ -156,42 +177,50 @@ struct __align__(16) DTab {
 };
 static_assert(sizeof(DTab) % 16 == 0, "DTab must copy in 16-byte pieces");
 
-// Fill a DTab from a built Canon; every thread of the workgroup calls it.
-__device__ inline void dtab_fill(const Canon &c, DTab &t)
+// Fill a DTab for alphabet size A from a built Canon; every thread of the workgroup calls it.
+__device__ inline void dtab_fill(const Canon &c, uint32_t A, DTab &t)
 {
     const uint32_t tid = threadIdx.x;
     for (uint32_t i = tid; i < kMaxLen + 2; i += blockDim.x) t.lim[i] = (i == 0) ? 0ull : c.lim[i];
     for (uint32_t i = tid; i <= kMaxLen; i += blockDim.x) t.base[i] = (int32_t)c.offset[i] - (int32_t)c.first[i];
-    for (uint32_t i = tid; i < 256; i += blockDim.x) t.sym[i] = c.sym[i];
+    for (uint32_t i = tid; i < 256; i += blockDim.x) t.sym[i] = (uint8_t)stage_form(A, c.sym[i]);
     if (tid == 0) {
         t.ok = c.ok;
         t.nsym = c.nsym;
         t.maxlen = c.maxlen;
+        const uint64_t l = c.lim[kLutBits];
+        t.lim_short = l == 0 ? 0u : (l >= (1ull << 32) ? 0xFFFFFFFFu : (uint32_t)(l - 1));
         t.pad_[0] = t.pad_[1] = t.pad_[2] = 0;
     }
     for (uint32_t x = tid; x < kLutSize; x += blockDim.x) {
-        uint32_t e = 0, first = 0;
+        uint32_t lo = 0, hi = 0;
         if (c.ok) {
             uint32_t v = x << (32 - kLutBits);   // window, left-justified, zero filled
-            uint32_t used = 0, ns = 0, syms = 0;
+            uint32_t used = 0, ns = 0, syms = 0, l1 = 0, l12 = 0;
             while (ns < kLutSymMax) {
                 // a code is fully inside the window if its length fits in the bits left
                 const uint32_t L = canon_len(c.lim, v, 1);
                 if (L > kLutBits - used) break;
                 const uint32_t sy = c.sym[c.offset[L] + ((v >> (32 - L)) - c.first[L])];
-                if (ns == 0) first = L;
-                syms |= sy << (8 * ns);
+                syms |= stage_form(A, sy) << (8 * ns);
                 used += L;
                 ++ns;
+                if (ns == 1) l1 = used;
+                if (ns == 2) l12 = used;
                 v <<= L;
             }
-            if (ns) e = syms | (used << 24) | (ns << 28);
+            if (ns) {
+                lo = used | (ns << 16) | (l1 << 24) | (l12 << 28);
+                hi = syms | (ns << 24);
+            }
         }
-        t.lut[x] = e;
-        t.first_len[x] = (uint8_t)first;
+        t.lo[x] = lo;
+        t.hi[x] = hi;
     }
-    if (tid < 4) t.lut[kLutSize + tid] = 0;
-    if (tid < 16) t.first_len[kLutSize + tid] = 0;
+    if (tid < 4) {
+        t.lo[kLutSize + tid] = 0;
+        t.hi[kLutSize + tid] = 0;
+    }
 }
 
 }  // namespace zxk

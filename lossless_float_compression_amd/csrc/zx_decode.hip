@@ -6,13 +6,17 @@
 // decode of a whole transformer block per call.  The gfx950 design here:
 //   * one wavefront decodes one segment: 64 chunks of 128 stream bits, lane l owns
 //     chunk l and starts at the chunk's stored gap (the first code starting in it);
-//   * lookup: the next 10 stream bits index a 1024-entry LDS table that yields up to
-//     three whole codes; longer codes fall back to the canonical length limits;
-//   * count pass, then a wavefront prefix scan of per-lane counts gives each lane
-//     its output offset (the segment's first element is stored in the container);
-//   * the lane decodes again, dropping exponents into a wavefront-private LDS stage
-//     in output order; the write pass then streams sign/mantissa bytes, fuses them
-//     with the staged exponents and issues 16-byte coalesced stores.
+//   * count pass: a lane refreshes a 32-bit window from its LDS word rows with one
+//     funnel shift, then takes three lookups from it; each lookup indexes a
+//     1024-entry LDS table with the next 10 bits and yields up to three symbols.
+//     The entries stay in registers.  A running "256 - position" value gives the
+//     funnel-shift amount and the word row directly, and accumulates the code count;
+//   * a wavefront prefix scan of the per-lane counts, plus the segment's stored first
+//     element, gives each lane its output offset;
+//   * replay: the register entries are dropped into a wavefront-private LDS stage in
+//     output order; the write pass then fuses the staged exponents with the
+//     sign/mantissa bytes, which were requested before the decode started, into
+//     16-byte coalesced stores.
 // Per-tensor codebooks load a prepared table; per-block codebooks (one workgroup
 // per block) build theirs in LDS from the block's code lengths.
 #include <cstring>
@@ -23,13 +27,24 @@ namespace zxk {
 
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * kWave;
-constexpr uint32_t kStageBytes = 4000;   // exponent stage per wavefront
-// A segment whose exponents do not fit the stage at once (mean code length under
-// two bits) is written in rounds of kRoundElems output positions.
-constexpr uint32_t kRoundElems = 3968;
 constexpr int kDecWgPerCu = 3;
 constexpr int kDecMinWavesPerSimd = kDecWgPerCu * kDecWaves / 4;
 constexpr int kMaxBatch = 16;
+
+// Per-wavefront LDS: the lanes' stream words and the exponent stage.
+constexpr uint32_t kSlots = 7;                 // word slots per lane
+constexpr uint32_t kSegWords = kSlots * kWave;
+constexpr uint32_t kStageBytes = 3616;         // one byte per output position, 16-byte multiple
+// A segment whose exponents do not fit the stage at once (mean code length under
+// about 2.3 bits) is written in rounds of kRoundElems output positions.
+constexpr uint32_t kRoundElems = 3584;
+// Register path: up to kRounds rounds of three lookups per lane.
+constexpr int kRounds = 8;
+constexpr int kEnt = 3 * kRounds;
+constexpr int kWriteBatch = 7;                 // write-pass pieces per lane whose loads go out together
+// Bit positions within a lane's rows: row r holds bits [32 r, 32 r + 32); row 1 is
+// the word holding the chunk's first bit, so the chunk starts at kPosBase + b0.
+constexpr uint32_t kPosBase = 32;
 
 struct DecTensor {
     const uint8_t *signmant;
@@ -60,33 +75,44 @@ struct DecBatch {
 
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
-// Stream words of a lane's chunk, staged in LDS one column per lane: word t of
-// lane l (the t-th word from the one holding the chunk's first bit) sits at
-// 64 t + l.  In every window read each lane then hits its own bank.  A chunk
-// starts less than 32 bits into its first word and a lane reads at most a 64-bit
-// window starting inside its chunk, so 7 words per lane suffice.
-constexpr uint32_t kLaneWords = 7;
-constexpr uint32_t kSegWords = kLaneWords * 64;
-
-struct SegWords {
-    const uint32_t *w;   // LDS, this lane's column
-    // 64 bits starting at chunk-relative bit p (counted from the first word's MSB)
-    __device__ __forceinline__ uint64_t win(uint32_t p) const
-    {
-        const uint32_t t = p >> 5;
-        const uint64_t v = ((uint64_t)w[t * 64] << 32) | w[(t + 1) * 64];
-        return v << (p & 31);
-    }
-};
-
-// Stage the segment's words: the wavefront loads stream words [W0, W0 + 260) with
-// one coalesced 16-byte load per lane (plus the tail words), and each word goes to
-// the lanes that need it: lane l needs words 4 l .. 4 l + 6.
-__device__ __forceinline__ void stage_seg_words(uint32_t *sw, const uint32_t *stream, uint64_t words, uint64_t W0)
+// Lane index computed where it is used.  The segment loop runs each wavefront over
+// many segments; if the lane index were a plain value the compiler would hoist every
+// lane-derived address out of that loop and keep them all live across it, which
+// costs more registers than recomputing them per segment.
+__device__ __forceinline__ uint32_t lane_now()
 {
-    const uint32_t lane = lane_id();
+    uint32_t r;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+    return r;
+}
+
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t lds_word(const uint32_t *base, uint32_t byte_off)
+{
+    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(base) + byte_off);
+}
+
+// ---- stream words of the lanes' chunks --------------------------------------
+//
+// Lane l needs the six words w0(l) .. w0(l)+5 from the one holding its chunk's first
+// bit: the chunk starts less than 32 bits into w0 and the lane never reads a window
+// starting at or past the chunk end.  They are its rows 1..6; row r sits in slot
+// 7 - r, i.e. at sw[(6 - r) * 64 + l], one column per lane so that every window read
+// of the wavefront hits 64 distinct banks.  Row 0 is never stored: it is read only
+// with a zero funnel shift, which takes the other word whole.
+
+// 16 bytes of stream words per lane (the lane's rows 1..4, the previous lane's rows 5
+// and 6) plus, in lanes 0 and 1, lane 63's rows 5 and 6.
+__device__ __forceinline__ void rows_load(const uint32_t *stream, uint64_t words, uint64_t W0, uint32_t lane,
+                                          u32x4_a4 &v, uint32_t &tail)
+{
     const uint64_t k = W0 + 4ull * lane;
-    u32x4_a4 v;
     if (k + 4 <= words) {
         v = *reinterpret_cast<const u32x4_a4 *>(stream + k);
     } else {
@@ -95,16 +121,46 @@ __device__ __forceinline__ void stage_seg_words(uint32_t *sw, const uint32_t *st
         v.z = k + 2 < words ? stream[k + 2] : 0u;
         v.w = k + 3 < words ? stream[k + 3] : 0u;
     }
-    uint32_t *own = sw + lane;                    // words 4l .. 4l+3 are this lane's 0..3
-    own[0] = v.x; own[64] = v.y; own[128] = v.z; own[192] = v.w;
-    if (lane > 0) {                               // and the previous lane's 4..6
-        uint32_t *prev = sw + lane - 1;
-        prev[256] = v.x; prev[320] = v.y; prev[384] = v.z;
+    tail = 0;
+    const uint64_t t = W0 + 256 + lane;
+    if (lane < 2 && t < words) tail = stream[t];
+}
+
+__device__ __forceinline__ void rows_store(uint32_t *sw, uint32_t lane, const u32x4_a4 &v, uint32_t tail)
+{
+    sw[5 * 64 + lane] = v.x;
+    sw[4 * 64 + lane] = v.y;
+    sw[3 * 64 + lane] = v.z;
+    sw[2 * 64 + lane] = v.w;
+    if (lane > 0) {
+        sw[1 * 64 + lane - 1] = v.x;
+        sw[0 * 64 + lane - 1] = v.y;
     }
-    if (lane < 3) {                               // words 256..258 finish lane 63
-        const uint64_t t = W0 + 256 + lane;
-        sw[64 * (4 + lane) + 63] = t < words ? stream[t] : 0u;
-    }
+    if (lane < 2) sw[(1 - lane) * 64 + 63] = tail;
+}
+
+// The 32 stream bits starting at position p of this lane's rows, given q with low
+// byte 256 - p; p must lie in [32, 190].  Slot (q >> 5) & 7 holds the row with the
+// window's first bit (or, when p is a multiple of 32, the row before it, which a
+// zero funnel shift then drops), the next slot down holds the row after it, and the
+// low five bits of q are the funnel shift.
+// `col` is window_col(): the LDS address two slots below this lane's slot 0 column,
+// kept opaque to the compiler so that both words come from one two-address LDS read
+// with immediate offsets.
+typedef __attribute__((address_space(3))) const uint32_t lds_cu32;
+
+__device__ __forceinline__ uint32_t window(lds_cu32 *col, uint32_t q)
+{
+    lds_cu32 *w = col + (((q >> 5) & 7u) << 6);
+    return __builtin_amdgcn_alignbit(w[64], w[0], q & 31u);
+}
+
+__device__ __forceinline__ lds_cu32 *window_col(uint32_t *sw, uint32_t lane)
+{
+    lds_cu32 *p = (lds_cu32 *)(sw + lane);
+    uint32_t a = (uint32_t)(uintptr_t)p - 2u * 64u * 4u;
+    asm volatile("" : "+v"(a));
+    return (lds_cu32 *)(uintptr_t)a;
 }
 
 // Codes longer than the lookup window: canonical length limits, kept out of line.
@@ -121,8 +177,24 @@ __device__ __forceinline__ uint32_t slow_sym(const DTab &tab, uint32_t v, uint32
     return tab.sym[(uint32_t)(tab.base[L] + (int32_t)(v >> (32 - L))) & 0xFFu];
 }
 
-// Write pass pieces: 8 BF16 or 16 FP8 elements per lane per step, i.e. 8 bytes of
-// sign/mantissa in and one 16-byte store out.
+// Length and stage form of the code at the front of window v.
+__device__ __forceinline__ uint32_t one_code(const DTab &tab, uint32_t v, uint32_t &sym)
+{
+    const uint32_t x = v >> (32 - kLutBits);
+    const uint32_t lo = tab.lo[x];
+    if (lo != 0) {
+        sym = tab.hi[x] & 0xFFu;
+        return (lo >> 24) & 0xFu;
+    }
+    const uint32_t L = slow_len(tab, v);
+    sym = L <= kMaxLen ? slow_sym(tab, v, L) : 0u;
+    return L;
+}
+
+// ---- write pass ---------------------------------------------------------------
+
+// 8 BF16 or 16 FP8 elements per lane per piece: 8 bytes of sign/mantissa in and one
+// 16-byte store out.
 template <int DT>
 struct Piece {
     static constexpr uint32_t kElems = DT == ZX_BF16 ? 8 : 16;
@@ -134,7 +206,25 @@ __device__ __forceinline__ uint2 load_sm(const uint8_t *sm_block, uint32_t i)
     return *reinterpret_cast<const uint2 *>(sm_block + (DT == ZX_BF16 ? i : i / 2));
 }
 
-// Exponents of one piece, from the stage or a 0-bit block's single symbol.
+// Sign/mantissa bytes of the first batch of whole pieces of [i_begin, i_end):
+// piece q = first + lane + 64 k.
+template <int DT>
+__device__ __forceinline__ void prefetch_sm(const uint8_t *sm_block, uint32_t i_begin, uint32_t i_end,
+                                            uint2 (&smv)[kWriteBatch])
+{
+    constexpr uint32_t P = Piece<DT>::kElems;
+    const uint32_t lane = lane_now();
+    const uint32_t qf_begin = (i_begin + P - 1) / P;
+    const uint32_t qf_end = i_end / P;
+#pragma unroll
+    for (int k = 0; k < kWriteBatch; ++k) {
+        const uint32_t q = qf_begin + lane + k * kWave;
+        smv[k] = make_uint2(0, 0);
+        if (q < qf_end) smv[k] = load_sm<DT>(sm_block, q * P);
+    }
+}
+
+// Staged exponents of one piece, or a 0-bit block's single symbol.
 template <int DT>
 __device__ __forceinline__ uint4 piece_exps(const uint8_t *ex, bool degen, uint32_t dsplat)
 {
@@ -146,38 +236,40 @@ __device__ __forceinline__ uint4 piece_exps(const uint8_t *ex, bool degen, uint3
     return *reinterpret_cast<const uint4 *>(ex);
 }
 
-// BF16: from sign/mantissa bytes S and exponent bytes E (4 elements each) make the
-// two output words of elements (2h, 2h+1): byte-permute S into [s,s] per element
-// (sign lands on bit 15, mantissa on bits 0..6 after the mask) and E into
-// [0,e] per element, shifted to bits 7..14.
-__device__ __forceinline__ uint32_t fuse_bf16_pair(uint32_t S, uint32_t E, uint32_t sel_s, uint32_t sel_e)
+// BF16: from four sign/mantissa bytes S and four staged exponents E (each rotated
+// right by one bit) make the output word of two elements: byte-permute into
+// [e, s, e, s] and [s, e, s, e], then take bit 7 of each byte from the first and
+// bits 0..6 from the second.  Low byte: exponent bit 0 | mantissa; high byte:
+// sign | exponent bits 7..1.
+__device__ __forceinline__ uint32_t fuse_bf16_pair(uint32_t S, uint32_t E, uint32_t sel_a, uint32_t sel_b)
 {
-    const uint32_t sd = __builtin_amdgcn_perm(0u, S, sel_s);
-    const uint32_t ed = __builtin_amdgcn_perm(0u, E, sel_e);
-    return (sd & 0x807F807Fu) | (ed << 7);
+    const uint32_t a = __builtin_amdgcn_perm(E, S, sel_a);
+    const uint32_t b = __builtin_amdgcn_perm(E, S, sel_b);
+    return (a & 0x80808080u) | (b & 0x7F7F7F7Fu);
 }
+constexpr uint32_t kSelA01 = 0x01050004u, kSelB01 = 0x05010400u;   // elements 0, 1
+constexpr uint32_t kSelA23 = 0x03070206u, kSelB23 = 0x07030602u;   // elements 2, 3
 
-// FP8: four sign|mantissa nibbles N (element k at bits 4k..4k+3) and four exponent
-// bytes E.  Each output byte is (sign << 7) | (exp << 3) | mant.
-__device__ __forceinline__ uint32_t fuse_fp8_quad(uint32_t N, uint32_t E)
+// FP8: four sign|mantissa nibbles N (element k at bits 4k..4k+3) and four staged
+// exponents E3 (already at bits 3..6).  Each output byte is sign << 7 | exp << 3 | mant.
+__device__ __forceinline__ uint32_t fuse_fp8_quad(uint32_t N, uint32_t E3)
 {
-    const uint32_t t = __builtin_amdgcn_perm(0u, N, 0x01010000u);       // [n23, n23, n01, n01]
+    const uint32_t t = __builtin_amdgcn_perm(0u, N, 0x01010000u);       // [n01, n01, n23, n23]
     const uint32_t x = (t & 0x000F000Fu) | ((t >> 4) & 0x0F000F00u);    // one nibble per byte
-    return x + (x & 0x08080808u) * 15u + (E << 3);                       // sign bit 3 -> bit 7
+    return x + (x & 0x08080808u) * 15u + E3;                             // sign bit 3 -> bit 7
 }
 
 template <int DT>
 __device__ __forceinline__ void store_piece(void *out_block, uint32_t i, uint2 smv, uint4 e)
 {
+    uint4 r;
     if (DT == ZX_BF16) {
-        uint4 r;
-        r.x = fuse_bf16_pair(smv.x, e.x, 0x01010000u, 0x0C010C00u);
-        r.y = fuse_bf16_pair(smv.x, e.x, 0x03030202u, 0x0C030C02u);
-        r.z = fuse_bf16_pair(smv.y, e.y, 0x01010000u, 0x0C010C00u);
-        r.w = fuse_bf16_pair(smv.y, e.y, 0x03030202u, 0x0C030C02u);
+        r.x = fuse_bf16_pair(smv.x, e.x, kSelA01, kSelB01);
+        r.y = fuse_bf16_pair(smv.x, e.x, kSelA23, kSelB23);
+        r.z = fuse_bf16_pair(smv.y, e.y, kSelA01, kSelB01);
+        r.w = fuse_bf16_pair(smv.y, e.y, kSelA23, kSelB23);
         *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out_block) + i) = r;
     } else {
-        uint4 r;
         r.x = fuse_fp8_quad(smv.x & 0xFFFFu, e.x);
         r.y = fuse_fp8_quad(smv.x >> 16, e.y);
         r.z = fuse_fp8_quad(smv.y & 0xFFFFu, e.z);
@@ -186,16 +278,27 @@ __device__ __forceinline__ void store_piece(void *out_block, uint32_t i, uint2 s
     }
 }
 
-
+template <int DT>
+__device__ __forceinline__ void store_batch(void *out_block, uint32_t qb, uint32_t qf_end, const uint2 (&smv)[kWriteBatch],
+                                            const uint8_t *stage, uint32_t sbase, bool degen, uint32_t dsplat)
+{
+    constexpr uint32_t P = Piece<DT>::kElems;
+    const uint32_t lane = lane_now();
+#pragma unroll
+    for (int k = 0; k < kWriteBatch; ++k) {
+        const uint32_t q = qb + lane + k * kWave;
+        if (q < qf_end) store_piece<DT>(out_block, q * P, smv[k], piece_exps<DT>(stage + (q * P - sbase), degen, dsplat));
+    }
+}
 
 // Elements of the cut pieces at the two range ends, one element per lane: lane t
 // (< P) takes element t of the head piece, lane P + t element t of the tail piece.
 template <int DT>
 __device__ __forceinline__ void write_cut_pieces(void *out_block, const uint8_t *sm_block, uint32_t i_begin, uint32_t i_end,
-                                                 const uint8_t *stage, uint32_t sbase, bool degen, uint32_t degen_sym)
+                                                 const uint8_t *stage, uint32_t sbase, bool degen, uint32_t dform)
 {
     constexpr uint32_t P = Piece<DT>::kElems;
-    const uint32_t lane = lane_id();
+    const uint32_t lane = lane_now();
     const uint32_t q_head = i_begin / P;
     const uint32_t q_tail = (i_end - 1) / P;
     const bool head_cut = (i_begin % P) != 0 || (q_head == q_tail && (i_end % P) != 0);
@@ -205,9 +308,9 @@ __device__ __forceinline__ void write_cut_pieces(void *out_block, const uint8_t 
     if (lane >= P && lane < 2 * P && tail_cut) ii = q_tail * P + (lane - P);
     if (ii != ~0u && ii >= i_begin && ii < i_end) {
         const uint32_t smb = sm_block[DT == ZX_BF16 ? ii : ii / 2];
-        const uint32_t ex = degen ? degen_sym : stage[ii - sbase];
+        const uint32_t ex = degen ? dform : stage[ii - sbase];
         if (DT == ZX_BF16) {
-            reinterpret_cast<uint16_t *>(out_block)[ii] = (uint16_t)fuse_bf16_pair(smb, ex, 0x0C0C0000u, 0x0C0C0C00u);
+            reinterpret_cast<uint16_t *>(out_block)[ii] = (uint16_t)fuse_bf16_pair(smb, ex, kSelA01, kSelB01);
         } else {
             const uint32_t nn = (ii & 1) ? (smb >> 4) : (smb & 0xFu);
             reinterpret_cast<uint8_t *>(out_block)[ii] = (uint8_t)(fuse_fp8_quad(nn, ex) & 0xFFu);
@@ -215,26 +318,28 @@ __device__ __forceinline__ void write_cut_pieces(void *out_block, const uint8_t 
     }
 }
 
-constexpr int kWriteBatch = 7;   // whole pieces per lane whose loads are issued together
-// Whole pieces of [i_begin, i_end) for this lane: q = qf_begin + lane + 64 k.
-__device__ __forceinline__ uint32_t first_whole(uint32_t i_begin, uint32_t P) { return (i_begin + P - 1) / P; }
-
-// Write block elements [i_begin, i_end); the exponent of element i is stage[i - sbase]
-// (or `degen_sym` for a 0-bit block).  Whole pieces: sign/mantissa loads of
-// kWriteBatch pieces per lane are issued before any is used, then each piece is
-// fused and written with one 16-byte store.  The (at most two) cut pieces at the
-// range ends are written one element per lane.
-template <int DT>
+// Write block elements [i_begin, i_end); the staged exponent of element i is
+// stage[i - sbase] (or `dform` for a 0-bit block).  Whole pieces go in batches of
+// kWriteBatch per lane, whose sign/mantissa loads are all issued before any is used;
+// with kPre the first batch's bytes are `smv0`, loaded by prefetch_sm on the same
+// range.  The (at most two) cut pieces at the range ends go one element per lane.
+template <int DT, bool kPre>
 __device__ __forceinline__ void write_range(void *out_block, const uint8_t *sm_block, uint32_t i_begin, uint32_t i_end,
-                                            const uint8_t *stage, uint32_t sbase, bool degen, uint32_t degen_sym)
+                                            const uint8_t *stage, uint32_t sbase, bool degen, uint32_t dform,
+                                            const uint2 (&smv0)[kWriteBatch])
 {
     constexpr uint32_t P = Piece<DT>::kElems;
     if (i_begin >= i_end) return;
-    const uint32_t lane = lane_id();
-    const uint32_t qf_begin = first_whole(i_begin, P);
+    const uint32_t lane = lane_now();
+    const uint32_t qf_begin = (i_begin + P - 1) / P;
     const uint32_t qf_end = i_end / P;
-    const uint32_t dsplat = degen_sym * 0x01010101u;
-    for (uint32_t qb = qf_begin; qb < qf_end; qb += kWave * kWriteBatch) {
+    const uint32_t dsplat = dform * 0x01010101u;
+    uint32_t qb = qf_begin;
+    if (kPre && qb < qf_end) {
+        store_batch<DT>(out_block, qb, qf_end, smv0, stage, sbase, degen, dsplat);
+        qb += kWave * kWriteBatch;
+    }
+    for (; qb < qf_end; qb += kWave * kWriteBatch) {
         uint2 smv[kWriteBatch];
 #pragma unroll
         for (int k = 0; k < kWriteBatch; ++k) {
@@ -242,30 +347,98 @@ __device__ __forceinline__ void write_range(void *out_block, const uint8_t *sm_b
             smv[k] = make_uint2(0, 0);
             if (q < qf_end) smv[k] = load_sm<DT>(sm_block, q * P);
         }
-#pragma unroll
-        for (int k = 0; k < kWriteBatch; ++k) {
-            const uint32_t q = qb + lane + k * kWave;
-            if (q < qf_end) store_piece<DT>(out_block, q * P, smv[k], piece_exps<DT>(stage + (q * P - sbase), degen, dsplat));
+        store_batch<DT>(out_block, qb, qf_end, smv, stage, sbase, degen, dsplat);
+    }
+    write_cut_pieces<DT>(out_block, sm_block, i_begin, i_end, stage, sbase, degen, dform);
+}
+
+// ---- fallback passes, one code at a time ------------------------------------
+
+// Count the codes starting in [start, lim): whole lookups while the window lies
+// inside the chunk, single codes near its end.
+__device__ uint32_t count_generic(const DTab &tab, lds_cu32 *col, uint32_t start, uint32_t lim, bool work,
+                                  bool &lane_bad, uint32_t &pos_out)
+{
+    uint32_t cnt = 0;
+    uint32_t p = start;
+    if (work) {
+        while (p < lim) {
+            const uint32_t v = window(col, 256u - p);
+            const uint32_t lo = tab.lo[v >> (32 - kLutBits)];
+            if (lo != 0 && p + kLutBits <= lim) {
+                cnt += (lo >> 16) & 0xFFu;
+                p += lo & 0xFFu;
+            } else if (lo != 0) {
+                cnt += 1;
+                p += (lo >> 24) & 0xFu;
+            } else {
+                const uint32_t L = slow_len(tab, v);
+                if (L > kMaxLen) { lane_bad = true; break; }
+                cnt += 1;
+                p += L;
+            }
         }
     }
-    write_cut_pieces<DT>(out_block, sm_block, i_begin, i_end, stage, sbase, degen, degen_sym);
+    pos_out = p;
+    return cnt;
 }
 
-__device__ __forceinline__ void wave_sync()
+// Store this lane's `cnt` symbols, decoded again from `start`, at stage[wp ...].
+__device__ void store_generic(const DTab &tab, lds_cu32 *col, uint8_t *stage, uint32_t start, uint32_t cnt, uint32_t wp)
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint32_t p = start;
+    for (uint32_t i = 0; i < cnt; ++i) {
+        uint32_t sy;
+        p += one_code(tab, window(col, 256u - p), sy);
+        stage[wp + i] = (uint8_t)sy;
+    }
 }
 
-// Decode one segment with one wavefront.
+// Segments whose exponents do not fit the stage: rounds of kRoundElems stage
+// positions, one code per step, exact writes.
 template <int DT>
-__device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *swords, uint32_t s,
+__device__ void write_rounds(const DTab &tab, lds_cu32 *col, uint8_t *stage, uint32_t start, uint32_t cnt,
+                             uint32_t off, uint32_t t0, uint32_t total, void *out_block, const uint8_t *sm_block,
+                             uint32_t sbase, const uint2 (&none)[kWriteBatch])
+{
+    for (uint32_t r0 = 0; r0 < t0 + total; r0 += kRoundElems) {
+        const uint32_t r1 = r0 + kRoundElems;
+        uint32_t p = start;
+        uint32_t t = t0 + off;
+        for (uint32_t i = 0; i < cnt && t < r1; ++i, ++t) {
+            uint32_t sy;
+            p += one_code(tab, window(col, 256u - p), sy);
+            if (t >= r0) stage[t - r0] = (uint8_t)sy;
+        }
+        wave_sync();
+        const uint32_t ib = sbase + (r0 > t0 ? r0 : t0);
+        const uint32_t ie = sbase + (r1 < t0 + total ? r1 : t0 + total);
+        write_range<DT, false>(out_block, sm_block, ib, ie, stage, sbase + r0, false, 0, none);
+        wave_sync();
+    }
+}
+
+// ---- one segment per wavefront ------------------------------------------------
+
+// One table lookup at the front of `win` for the lanes in `a`; the others read the
+// zero entry and keep their state.
+#define ZX_LOOKUP(a, slot, extra)                                                        \
+    do {                                                                                 \
+        const uint32_t x_ = (a) ? ((win >> 20) & 0xFFCu) : (kLutSize * 4u);              \
+        const uint32_t lo_ = lds_word(tab.lo, x_);                                       \
+        const uint32_t hi_ = lds_word(tab.hi, x_);                                       \
+        win <<= (lo_ & 31u);                                                             \
+        Bprev = (a) ? B : Bprev;                                                         \
+        B -= lo_;                                                                        \
+        ent[slot] = hi_ | (extra);                                                       \
+    } while (0)
+
+template <int DT>
+__device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *sw, uint32_t s,
                                uint32_t *err)
 {
     constexpr uint32_t A = alphabet_of(DT);
-    constexpr uint32_t P = Piece<DT>::kElems;
-    const uint32_t lane = lane_id();
+    const uint32_t lane = lane_now();
     const uint32_t b = T.seg_desc[2 * (uint64_t)s];
     const uint32_t e0 = T.seg_desc[2 * (uint64_t)s + 1];
     if (b >= T.nblocks) { report(err, ZX_E_CORRUPT); return; }
@@ -287,184 +460,158 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
     void *out_block = reinterpret_cast<uint8_t *>(T.out) + lo * (DT == ZX_BF16 ? 2 : 1);
     const uint32_t sbase = e0 & ~15u;   // 16-aligned element that stage byte 0 stands for
 
+    // requests first: the lanes' stream words, their gap bytes, and the sign/mantissa
+    // bytes of the first write batch, which arrive while the lanes decode
+    const uint32_t nch = (bits + kChunkBits - 1) / kChunkBits;
+    const uint32_t ch = j * kSegChunks + lane;
+    u32x4_a4 rv = {0u, 0u, 0u, 0u};
+    uint32_t rtail = 0;
+    if (bits != 0) rows_load(T.stream, T.stream_words, (G >> 5) + (uint64_t)j * (kSegBits / 32), lane, rv, rtail);
+    const uint32_t gap = (bits != 0 && ch < nch) ? T.gaps[(uint64_t)s * kSegChunks + lane] : ZX_NO_GAP;
+    uint32_t gap_next = (lane == kWave - 1 && ch + 1 < nch) ? T.gaps[(uint64_t)(s + 1) * kSegChunks] : ZX_NO_GAP;
+    uint2 smv[kWriteBatch];
+    prefetch_sm<DT>(sm_block, e0, e_end, smv);
+
     if (bits == 0) {
         const uint32_t d = T.degenerate[T.per_block ? b : 0];
         if (d >= A || e0 != 0 || e_end != nb) { report(err, ZX_E_CORRUPT); return; }
-        write_range<DT>(out_block, sm_block, e0, e_end, stage, sbase, true, d);
+        write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, true, stage_form(A, d), smv);
         return;
     }
     if (!tab.ok) { report(err, ZX_E_CORRUPT); return; }
 
-    const uint32_t nch = (bits + kChunkBits - 1) / kChunkBits;
-    const uint32_t ch = j * kSegChunks + lane;
-    const uint32_t gap = (ch < nch) ? T.gaps[(uint64_t)s * kSegChunks + lane] : ZX_NO_GAP;
+    {
+        const uint32_t gn = __shfl_down(gap, 1, kWave);
+        if (lane != kWave - 1) gap_next = gn;
+    }
     bool work = gap != ZX_NO_GAP;
     bool lane_bad = false;
     if (work && gap >= kMaxLen) { work = false; lane_bad = true; }
-    // chunk-relative end: the lane decodes the codes starting in [gap, cend)
     const uint32_t cend = (ch * kChunkBits + kChunkBits < bits) ? kChunkBits : bits - ch * kChunkBits;
     if (work && gap >= cend) { work = false; lane_bad = true; }
-    // chunk-relative bit coordinates from the MSB of the word holding the chunk's
-    // first bit: the chunk starts at b0 < 32
-    const uint64_t cbit = G + (uint64_t)ch * kChunkBits;
-    const uint32_t b0 = (uint32_t)(cbit & 31);
-    stage_seg_words(swords, T.stream, T.stream_words, (G >> 5) + (uint64_t)j * (kSegBits / 32));
+    const uint32_t b0 = (uint32_t)(G & 31);
+    // codes of one chunk must end exactly where the next chunk's first code starts
+    // (or at the block end), as the stored gaps claim
+    const uint32_t expect = (ch + 1 < nch && gap_next != ZX_NO_GAP) ? kPosBase + b0 + kChunkBits + gap_next
+                                                                    : kPosBase + b0 + (bits - ch * kChunkBits);
+    rows_store(sw, lane, rv, rtail);
     wave_sync();
-    const SegWords sw{swords + lane};
-    const uint32_t start = work ? b0 + gap : 0;
-    const uint32_t lim = work ? b0 + cend : 0;
+    lds_cu32 *col = window_col(sw, lane);
+    const uint32_t start = kPosBase + b0 + gap;
+    const uint32_t lim = kPosBase + b0 + cend;
+    // B: low byte 256 - position, bits 16..23 minus the code count; a lane is active
+    // while its position is below lim, i.e. while B's low byte exceeds thr
+    const uint32_t thr = work ? 256u - lim : 255u;
+    constexpr uint32_t kIdleQ = 256u - kPosBase;   // a harmless window for idle lanes
+    uint32_t B = work ? 256u - start : kIdleQ;
+    uint32_t Bprev = B;
+    bool ok = work;
+    const uint32_t lim_short = tab.lim_short;
 
-    // ---- count pass.  Main phase: while a whole window lies inside the chunk, every
-    //      code the table returns starts inside it.  Tail phase: one code at a time.
-    //      A code longer than the window reads as a zero entry, so its lane stalls;
-    //      the inner loops run while some lane progresses, then stalled lanes take
-    //      their long code from the canonical length limits.
+    // ---- count pass, register path
+    uint32_t ent[kEnt];
+#pragma unroll
+    for (int k = 0; k < kEnt; ++k) ent[k] = 0;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+        bool act = ok && (B & 0xFFu) > thr;
+        if (__ballot(act) == 0) break;
+        uint32_t win = window(col, act ? B : kIdleQ);
+        const bool lng = act && win > lim_short;   // the next code is longer than the table window
+        uint32_t eslow = 0;
+        if (__ballot(lng) != 0) {
+            if (lng) {
+                const uint32_t L = slow_len(tab, win);
+                if (L > kMaxLen) {
+                    ok = false;
+                    lane_bad = true;
+                    act = false;
+                } else {
+                    eslow = slow_sym(tab, win, L) | (1u << 24);
+                    Bprev = B;
+                    B -= L | (1u << 16);
+                    act = (B & 0xFFu) > thr;
+                    win = window(col, act ? B : kIdleQ);
+                }
+            }
+        }
+        const bool a0 = act && !lng;   // a long code took slot 0
+        ZX_LOOKUP(a0, 3 * r, eslow);
+        act = act && (B & 0xFFu) > thr;
+        ZX_LOOKUP(act, 3 * r + 1, 0u);
+        act = act && (B & 0xFFu) > thr;
+        ZX_LOOKUP(act, 3 * r + 2, 0u);
+    }
+    const bool more = __ballot(ok && (B & 0xFFu) > thr) != 0;
+
     uint32_t cnt = 0;
-    uint32_t pos = work ? start : 0;
-    for (;;) {
-        bool act = pos + kLutBits <= lim;
-        if (__ballot(act) == 0) break;
-        bool progress;
-        do {
-            const uint32_t idx = act ? (uint32_t)(sw.win(pos) >> (64 - kLutBits)) : kLutSize;
-            const uint32_t e = tab.lut[idx];
-            const uint32_t adv = (e >> 24) & 0xFu;
-            progress = adv != 0;   // a zero advance (long code, or a damaged table) stalls
-            cnt += e >> 28;
-            pos += adv;
-            act = pos + kLutBits <= lim;
-        } while (__ballot(progress && act) != 0);
-        if (act && !progress) {   // stalled at a long code
-            uint32_t L = slow_len(tab, (uint32_t)(sw.win(pos) >> 32));
-            if (L > kMaxLen) { lane_bad = true; L = lim - pos; }
-            cnt += 1;
-            pos += L;
+    if (!more) {
+        if (ok) {
+            // the last lookup may hold codes that start in the next chunk: drop them
+            const uint32_t el = Bprev - B;
+            const uint32_t pl = 256u - (Bprev & 0xFFu);
+            const uint32_t ns = (el >> 16) & 0xFFu;
+            uint32_t endp = pl + (el & 0xFFu);
+            uint32_t drop = 0;
+            if (ns >= 2 && pl + ((el >> 24) & 0xFu) >= lim) {
+                drop = ns - 1;
+                endp = pl + ((el >> 24) & 0xFu);
+            } else if (ns == 3 && pl + (el >> 28) >= lim) {
+                drop = 1;
+                endp = pl + (el >> 28);
+            }
+            cnt = ((0u - (B >> 16)) & 0xFFu) - drop;
+            if (endp != expect) lane_bad = true;
         }
-    }
-    for (;;) {
-        bool act = pos < lim;
-        if (__ballot(act) == 0) break;
-        bool progress;
-        do {
-            const uint32_t idx = act ? (uint32_t)(sw.win(pos) >> (64 - kLutBits)) : kLutSize;
-            const uint32_t L = tab.first_len[idx];
-            progress = L != 0;
-            cnt += progress ? 1u : 0u;
-            pos += L;
-            act = pos < lim;
-        } while (__ballot(progress && act) != 0);
-        if (act && !progress) {
-            uint32_t L = slow_len(tab, (uint32_t)(sw.win(pos) >> 32));
-            if (L > kMaxLen) { lane_bad = true; L = lim - pos; }
-            cnt += 1;
-            pos += L;
-        }
-    }
-    // codes of one chunk must end exactly where the next chunk's first code
-    // starts (or at the block end), as the stored gaps claim
-    uint32_t gap_next = __shfl_down(gap, 1, kWave);
-    if (lane == kWave - 1) gap_next = (ch + 1 < nch) ? T.gaps[(uint64_t)(s + 1) * kSegChunks] : ZX_NO_GAP;
-    if (work && !lane_bad) {
-        const uint32_t expect = (ch + 1 < nch && gap_next != ZX_NO_GAP) ? b0 + kChunkBits + gap_next : b0 + (bits - ch * kChunkBits);
-        if (pos != expect) lane_bad = true;
+    } else {
+        // some lane needs more lookups than the registers hold: count again, one code at a time near the end
+        uint32_t pos = 0;
+        cnt = count_generic(tab, col, start, lim, work, lane_bad, pos);
+        if (work && !lane_bad && pos != expect) lane_bad = true;
     }
     uint32_t total;
     const uint32_t off = wave_excl_scan(cnt, total);
     if (__ballot(lane_bad) != 0 || e0 + total != e_end) { report(err, ZX_E_CORRUPT); return; }
 
     const uint32_t t0 = e0 - sbase;   // stage position of the segment's first element
-    if (t0 + total + 2 <= kStageBytes - 4) {   // the last 4 bytes are the dummy store slot
-        // ---- decode pass, one round: each lookup stores all its symbols; a lane's
-        //      last lookup may spill up to two bytes onto the next lanes' first
-        //      positions, which those lanes restore right after
-        uint32_t wp = t0 + off;
-        uint32_t done = 0;
-        pos = start;
-        uint8_t *const dummy = stage + kStageBytes - 4;   // where lanes that are done store
-        for (;;) {
-            bool act = done < cnt;
-            if (__ballot(act) == 0) break;
-            bool progress;
-            do {
-                const uint32_t idx = act ? (uint32_t)(sw.win(pos) >> (64 - kLutBits)) : kLutSize;
-                const uint32_t e = tab.lut[idx];
-                uint8_t *const d = act ? stage + wp : dummy;
-                d[0] = (uint8_t)e;
-                d[1] = (uint8_t)(e >> 8);
-                d[2] = (uint8_t)(e >> 16);
-                const uint32_t adv = (e >> 24) & 0xFu;
-                progress = adv != 0;
-                const uint32_t ns = e >> 28;
-                wp += ns;
-                done += ns;
-                pos += adv;
-                act = done < cnt;
-            } while (__ballot(progress && act) != 0);
-            if (act && !progress) {
-                const uint32_t v = (uint32_t)(sw.win(pos) >> 32);
-                const uint32_t L = slow_len(tab, v);
-                stage[wp] = (uint8_t)slow_sym(tab, v, L);
-                wp += 1;
-                done += 1;
-                pos += L;
-            }
-        }
-        wave_sync();
-        if (cnt) {
-            uint32_t p = start;
-            const uint32_t first = cnt < 2 ? cnt : 2;
-            for (uint32_t k = 0; k < first; ++k) {
-                const uint64_t x = sw.win(p);
-                const uint32_t idx = (uint32_t)(x >> (64 - kLutBits));
-                uint32_t L = tab.first_len[idx];
-                uint32_t sy;
-                if (L) {
-                    sy = tab.lut[idx] & 0xFFu;
-                } else {
-                    const uint32_t v = (uint32_t)(x >> 32);
-                    L = slow_len(tab, v);
-                    sy = slow_sym(tab, v, L);
-                }
-                stage[t0 + off + k] = (uint8_t)sy;
-                p += L;
-            }
-        }
-        wave_sync();
-        write_range<DT>(out_block, sm_block, e0, e_end, stage, sbase, false, 0);
-    } else {
-        // ---- several rounds of kRoundElems stage positions; exact writes
-        for (uint32_t r0 = 0; r0 < t0 + total; r0 += kRoundElems) {
-            const uint32_t r1 = r0 + kRoundElems;
-            if (cnt) {
-                uint32_t p = start;
-                uint32_t t = t0 + off;
-                uint32_t done = 0;
-                while (done < cnt && t < r1) {
-                    const uint64_t x = sw.win(p);
-                    const uint32_t idx = (uint32_t)(x >> (64 - kLutBits));
-                    uint32_t L = tab.first_len[idx];
-                    uint32_t sy;
-                    if (L) {
-                        sy = tab.lut[idx] & 0xFFu;
-                    } else {
-                        const uint32_t v = (uint32_t)(x >> 32);
-                        L = slow_len(tab, v);
-                        sy = slow_sym(tab, v, L);
-                    }
-                    if (t >= r0) stage[t - r0] = (uint8_t)sy;
-                    p += L;
-                    ++t;
-                    ++done;
+    if (t0 + total + 2 <= kStageBytes) {
+        if (!more) {
+            // ---- replay the entries into the stage.  Each writes three bytes and
+            //      advances by its symbol count; the bytes past a lane's last symbol
+            //      (at most two) land on the next lane's first positions, which that
+            //      lane rewrites after the barrier from its first two symbols.
+            const uint32_t n0 = ent[0] >> 24;
+            const uint32_t e1 = (ent[1] >> 24) != 0 ? ent[1] : ent[3];
+            const uint32_t first2 = (ent[0] & 0xFFu) | (((n0 >= 2 ? (ent[0] >> 8) : e1) & 0xFFu) << 8);
+            uint32_t wp = t0 + off;
+            int32_t rem = (int32_t)cnt;
+#pragma unroll
+            for (int k = 0; k < kEnt; ++k) {
+                if (__ballot(rem > 0) == 0) break;
+                if (rem > 0) {
+                    const uint32_t e = ent[k];
+                    uint8_t *d = stage + wp;
+                    d[0] = (uint8_t)e;
+                    d[1] = (uint8_t)(e >> 8);
+                    d[2] = (uint8_t)(e >> 16);
+                    const uint32_t ns = e >> 24;
+                    wp += ns;
+                    rem -= (int32_t)ns;
                 }
             }
             wave_sync();
-            const uint32_t ib = sbase + (r0 > t0 ? r0 : t0);
-            const uint32_t ie = sbase + (r1 < t0 + total ? r1 : t0 + total);
-            write_range<DT>(out_block, sm_block, ib, ie, stage, sbase + r0, false, 0);
-            wave_sync();
+            if (cnt >= 1) stage[t0 + off] = (uint8_t)first2;
+            if (cnt >= 2) stage[t0 + off + 1] = (uint8_t)(first2 >> 8);
+        } else {
+            store_generic(tab, col, stage, start, cnt, t0 + off);
         }
+        wave_sync();
+        write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, false, 0, smv);
+        return;
     }
+    write_rounds<DT>(tab, col, stage, start, cnt, off, t0, total, out_block, sm_block, sbase, smv);
 }
+#undef ZX_LOOKUP
 
 template <int DT>
 __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(const DecBatch batch, uint32_t *err)
@@ -491,7 +638,7 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
         if (s_end > T.nsegs || s_begin > s_end) { s_end = s_begin; if (tid == 0) report(err, ZX_E_CORRUPT); }
         Canon &c = *reinterpret_cast<Canon *>(stage_all);
         canon_build(T.lengths + (uint64_t)b * A, A, c);
-        dtab_fill(c, tab);
+        dtab_fill(c, A, tab);
         __syncthreads();
     } else {
         s_begin = lg * T.segs_per_wg;
@@ -512,7 +659,7 @@ __global__ __launch_bounds__(256) void k_build_dtab(const uint8_t *__restrict__ 
 {
     __shared__ Canon c;
     canon_build(lengths, A, c);
-    dtab_fill(c, *out);
+    dtab_fill(c, A, *out);
 }
 
 }  // namespace zxk

@@ -1,12 +1,14 @@
-// zx_hist.hip -- exponent histogram with wavefront-ballot aggregation.
+// zx_hist.hip -- exponent histogram per 65536-element block.
 //
 // The exponent distribution is what the Huffman tree is built from (DFloat11
 // article, 方法介绍; Intel summary, 方法论).  Exponents of weights and K/V values
-// cluster on a few values (ZipFloat page, section 2, Tables 1-2), so within one
-// wavefront most lanes share a handful of values: each round the wavefront picks
-// the value of its first unfinished lane, ballots the lanes holding that value and
-// adds the popcount with a single LDS atomic.  The number of rounds is the number
-// of distinct values among the 64 lanes, not 64.
+// cluster on a few values (ZipFloat page, section 2, Tables 1-2), so lanes of a
+// wavefront mostly hold the same handful of values: a single shared histogram would
+// serialise its atomics on those few bins.  Each lane therefore owns a private copy
+// of the histogram in LDS (shared by the lane of the same index in every wavefront
+// of the workgroup), laid out with a stride of A + 1 words so that lane l's bin v
+// sits in bank (l + v) mod 64: the 64 LDS atomics of one instruction fall in 64
+// distinct banks whatever the values.  The 64 copies are summed at the end.
 #include "zx_common.h"
 
 namespace zxk {
@@ -14,33 +16,20 @@ namespace zxk {
 constexpr int kHistThreads = 1024;
 constexpr uint32_t kHistUnroll = 4;   // 16-byte loads in flight per lane
 
-// Add one exponent per lane (valid lanes only) into the LDS histogram.
-__device__ __forceinline__ void ballot_add(uint32_t *h, uint32_t e, bool valid)
-{
-    bool todo = valid;
-    while (true) {
-        uint64_t act = __ballot(todo);
-        if (act == 0) break;
-        const int leader = __ffsll((long long)act) - 1;
-        const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)e, leader);
-        const uint64_t same = __ballot(todo && e == v);
-        if (lane_id() == (uint32_t)leader) atomicAdd(&h[v], (uint32_t)__popcll(same));
-        if (e == v) todo = false;
-    }
-}
-
-// One workgroup per 65536-element block.
 template <int DT>
 __global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restrict__ in, uint64_t n,
                                                             uint32_t *__restrict__ tensor_hist,
                                                             uint32_t *__restrict__ block_hist)
 {
     constexpr uint32_t A = alphabet_of(DT);
-    __shared__ uint32_t h[256];
+    constexpr uint32_t S = A + 1;                 // copy stride in words
+    __shared__ uint32_t h[kWave * S];
     const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid % kWave;
     const uint64_t b = blockIdx.x;
-    for (uint32_t i = tid; i < A; i += blockDim.x) h[i] = 0;
+    for (uint32_t i = tid; i < kWave * S; i += kHistThreads) h[i] = 0;
     __syncthreads();
+    uint32_t *const mine = h + lane * S;
     const uint64_t lo = b * kBlock;
     const uint64_t hi = (lo + kBlock < n) ? lo + kBlock : n;
     const uint32_t nb = (uint32_t)(hi - lo);
@@ -73,25 +62,39 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restri
         }
 #pragma unroll
         for (uint32_t u = 0; u < kHistUnroll; ++u) {
+            if (have[u] == EPV) {
 #pragma unroll
-            for (uint32_t k = 0; k < EPV; ++k) {
-                uint32_t e;
-                if (DT == ZX_BF16) {
-                    const uint32_t x = (words[u][k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-                    e = (x >> 7) & 0xFFu;
-                } else {
-                    const uint32_t x = (words[u][k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                    e = (x >> 3) & 0xFu;
+                for (uint32_t k = 0; k < EPV; ++k) {
+                    uint32_t e;
+                    if (DT == ZX_BF16) e = (words[u][k >> 1] >> (16 * (k & 1) + 7)) & 0xFFu;
+                    else e = (words[u][k >> 2] >> (8 * (k & 3) + 3)) & 0xFu;
+                    atomicAdd(&mine[e], 1u);
                 }
-                ballot_add(h, e, k < have[u]);
+            } else {
+                for (uint32_t k = 0; k < have[u]; ++k) {
+                    uint32_t e;
+                    if (DT == ZX_BF16) e = (words[u][k >> 1] >> (16 * (k & 1) + 7)) & 0xFFu;
+                    else e = (words[u][k >> 2] >> (8 * (k & 3) + 3)) & 0xFu;
+                    atomicAdd(&mine[e], 1u);
+                }
             }
         }
     }
     __syncthreads();
-    for (uint32_t i = tid; i < A; i += blockDim.x) {
-        const uint32_t c = h[i];
-        if (block_hist) block_hist[b * A + i] = c;
-        if (tensor_hist && c) atomicAdd(&tensor_hist[i], c);
+    // sum the 64 copies: thread t adds copies t/A, t/A + 1024/A, ... of bin t % A
+    constexpr uint32_t kGroups = kHistThreads / A;          // 4 (BF16) or 64 (FP8)
+    const uint32_t bin = tid % A;
+    const uint32_t grp = tid / A;
+    uint32_t c = 0;
+    for (uint32_t cp = grp; cp < kWave; cp += kGroups) c += h[cp * S + bin];
+    __syncthreads();
+    h[grp * S + bin] = c;
+    __syncthreads();
+    if (tid < A) {
+        uint32_t t = 0;
+        for (uint32_t g = 0; g < kGroups; ++g) t += h[g * S + tid];
+        if (block_hist) block_hist[b * A + tid] = t;
+        if (tensor_hist && t) atomicAdd(&tensor_hist[tid], t);
     }
 }
 
