@@ -27,7 +27,7 @@ namespace zxk {
 
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * kWave;
-constexpr int kDecWgPerCu = 3;
+constexpr int kDecWgPerCu = 2;
 constexpr int kDecMinWavesPerSimd = kDecWgPerCu * kDecWaves / 4;
 constexpr int kMaxBatch = 16;
 
@@ -86,6 +86,10 @@ __device__ __forceinline__ uint32_t lane_now()
     return r;
 }
 
+// True if the predicate holds in any lane (the lane mask itself, not a ballot
+// materialised through vector registers).
+__device__ __forceinline__ bool any_lane(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
 __device__ __forceinline__ void wave_sync()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -140,7 +144,9 @@ __device__ __forceinline__ void rows_store(uint32_t *sw, uint32_t lane, const u3
 }
 
 // The 32 stream bits starting at position p of this lane's rows, given q with low
-// byte 256 - p; p must lie in [32, 190].  Slot (q >> 5) & 7 holds the row with the
+// byte 256 - p.  For p in [32, 190] the slots read are this lane's; any p up to 223
+// (a lane past its chunk end after a long code) still reads inside the LDS
+// allocation, one slot below, which only idle lanes do.  Slot (q >> 5) & 7 holds the row with the
 // window's first bit (or, when p is a multiple of 32, the row before it, which a
 // zero funnel shift then drops), the next slot down holds the row after it, and the
 // low five bits of q are the funnel shift.
@@ -151,8 +157,8 @@ typedef __attribute__((address_space(3))) const uint32_t lds_cu32;
 
 __device__ __forceinline__ uint32_t window(lds_cu32 *col, uint32_t q)
 {
-    lds_cu32 *w = col + (((q >> 5) & 7u) << 6);
-    return __builtin_amdgcn_alignbit(w[64], w[0], q & 31u);
+    lds_cu32 *w = col + (__builtin_amdgcn_ubfe(q, 5, 3) << 6);
+    return __builtin_amdgcn_alignbit(w[64], w[0], q);
 }
 
 __device__ __forceinline__ lds_cu32 *window_col(uint32_t *sw, uint32_t lane)
@@ -259,8 +265,9 @@ __device__ __forceinline__ uint32_t fuse_fp8_quad(uint32_t N, uint32_t E3)
     return x + (x & 0x08080808u) * 15u + E3;                             // sign bit 3 -> bit 7
 }
 
+// Output words of one piece.
 template <int DT>
-__device__ __forceinline__ void store_piece(void *out_block, uint32_t i, uint2 smv, uint4 e)
+__device__ __forceinline__ uint4 fuse_piece(uint2 smv, uint4 e)
 {
     uint4 r;
     if (DT == ZX_BF16) {
@@ -268,26 +275,45 @@ __device__ __forceinline__ void store_piece(void *out_block, uint32_t i, uint2 s
         r.y = fuse_bf16_pair(smv.x, e.x, kSelA23, kSelB23);
         r.z = fuse_bf16_pair(smv.y, e.y, kSelA01, kSelB01);
         r.w = fuse_bf16_pair(smv.y, e.y, kSelA23, kSelB23);
-        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out_block) + i) = r;
     } else {
         r.x = fuse_fp8_quad(smv.x & 0xFFFFu, e.x);
         r.y = fuse_fp8_quad(smv.x >> 16, e.y);
         r.z = fuse_fp8_quad(smv.y & 0xFFFFu, e.z);
         r.w = fuse_fp8_quad(smv.y >> 16, e.w);
-        *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(out_block) + i) = r;
     }
+    return r;
 }
 
+template <int DT>
+__device__ __forceinline__ void store_piece(void *out_block, uint32_t i, uint4 r)
+{
+    if (DT == ZX_BF16)
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(out_block) + i) = r;
+    else
+        *reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(out_block) + i) = r;
+}
+
+// One batch of whole pieces.  Every piece is fused before the first store goes out:
+// the stores are conditional, and once one is in flight the outstanding-access
+// count no longer tells when a given load has returned, so any wait after it would
+// have to drain all stores first.
 template <int DT>
 __device__ __forceinline__ void store_batch(void *out_block, uint32_t qb, uint32_t qf_end, const uint2 (&smv)[kWriteBatch],
                                             const uint8_t *stage, uint32_t sbase, bool degen, uint32_t dsplat)
 {
     constexpr uint32_t P = Piece<DT>::kElems;
     const uint32_t lane = lane_now();
+    uint4 r[kWriteBatch];
 #pragma unroll
     for (int k = 0; k < kWriteBatch; ++k) {
         const uint32_t q = qb + lane + k * kWave;
-        if (q < qf_end) store_piece<DT>(out_block, q * P, smv[k], piece_exps<DT>(stage + (q * P - sbase), degen, dsplat));
+        r[k] = make_uint4(0, 0, 0, 0);
+        if (q < qf_end) r[k] = fuse_piece<DT>(smv[k], piece_exps<DT>(stage + (q * P - sbase), degen, dsplat));
+    }
+#pragma unroll
+    for (int k = 0; k < kWriteBatch; ++k) {
+        const uint32_t q = qb + lane + k * kWave;
+        if (q < qf_end) store_piece<DT>(out_block, q * P, r[k]);
     }
 }
 
@@ -418,6 +444,92 @@ __device__ void write_rounds(const DTab &tab, lds_cu32 *col, uint8_t *stage, uin
     }
 }
 
+// ---- segment descriptors and requests issued one segment ahead ---------------
+
+// A segment's descriptor, validated.  Each lane of a wavefront loads the descriptor
+// of one of the wavefront's segments (lane k: its k-th segment), so the dependent
+// loads (segment -> block -> bit offset) are paid once per 64 segments; the values
+// of the segment at hand are then read from that lane.
+struct SegMeta {
+    uint32_t b;          // block
+    uint32_t e0;         // first element, within the block
+    uint32_t e_end;      // end element, within the block
+    uint32_t bits;       // stream bits of the block
+    uint32_t j;          // segment index within the block
+    uint32_t wlo, whi;   // stream word holding the segment's first bit
+    uint32_t b0bad;      // bits 0..4: bit offset of the block start within its word;
+                         // bit 8: the descriptor is inconsistent with the block arrays
+};
+
+__device__ __forceinline__ void load_meta(const DecTensor &T, uint32_t s, bool valid, SegMeta &m)
+{
+    m.b = 0; m.e0 = 0; m.e_end = 0; m.bits = 0; m.j = 0; m.wlo = 0; m.whi = 0;
+    m.b0bad = valid ? 0u : 0x100u;
+    if (!valid) return;
+    const uint32_t b = T.seg_desc[2 * (uint64_t)s];
+    const uint32_t e0 = T.seg_desc[2 * (uint64_t)s + 1];
+    if (b >= T.nblocks) { m.b0bad = 0x100u; return; }
+    const uint64_t G = T.block_bitoff[b];
+    const uint64_t Gn = T.block_bitoff[b + 1];
+    const uint32_t sb = T.block_seg[b];
+    const uint32_t sbn = T.block_seg[b + 1];
+    const uint64_t lo = (uint64_t)b * kBlock;
+    const uint32_t nb = (uint32_t)(((lo + kBlock < T.n) ? lo + kBlock : T.n) - lo);
+    if (Gn < G || Gn > T.total_bits || s < sb || s >= sbn || sbn > T.nsegs || Gn - G > (uint64_t)nb * kMaxLen) {
+        m.b0bad = 0x100u;
+        return;
+    }
+    const uint32_t e_end = (s + 1 < sbn) ? T.seg_desc[2 * (uint64_t)(s + 1) + 1] : nb;
+    if (e0 > e_end || e_end > nb) { m.b0bad = 0x100u; return; }
+    const uint64_t W0 = (G >> 5) + (uint64_t)(s - sb) * (kSegBits / 32);
+    m.b = b;
+    m.e0 = e0;
+    m.e_end = e_end;
+    m.bits = (uint32_t)(Gn - G);
+    m.j = s - sb;
+    m.wlo = (uint32_t)W0;
+    m.whi = (uint32_t)(W0 >> 32);
+    m.b0bad = (uint32_t)(G & 31);
+}
+
+// Descriptor held by lane i, as wavefront-uniform values.
+__device__ __forceinline__ SegMeta meta_at(const SegMeta &m, uint32_t i)
+{
+    SegMeta u;
+    u.b = __builtin_amdgcn_readlane(m.b, i);
+    u.e0 = __builtin_amdgcn_readlane(m.e0, i);
+    u.e_end = __builtin_amdgcn_readlane(m.e_end, i);
+    u.bits = __builtin_amdgcn_readlane(m.bits, i);
+    u.j = __builtin_amdgcn_readlane(m.j, i);
+    u.wlo = __builtin_amdgcn_readlane(m.wlo, i);
+    u.whi = __builtin_amdgcn_readlane(m.whi, i);
+    u.b0bad = __builtin_amdgcn_readlane(m.b0bad, i);
+    return u;
+}
+
+// Loads a segment needs before it can decode: its lanes' stream words and gap bytes
+// (and the next segment's first gap, for lane 63).
+struct SegIn {
+    u32x4_a4 rv;
+    uint32_t rtail;
+    uint32_t gap;
+    uint32_t gapn;
+};
+
+__device__ __forceinline__ void issue_seg(const DecTensor &T, uint32_t s, const SegMeta &m, uint32_t lane, SegIn &in)
+{
+    in.rv = u32x4_a4{0u, 0u, 0u, 0u};
+    in.rtail = 0;
+    in.gap = ZX_NO_GAP;
+    in.gapn = ZX_NO_GAP;
+    if ((m.b0bad & 0x100u) != 0 || m.bits == 0) return;
+    rows_load(T.stream, T.stream_words, ((uint64_t)m.whi << 32) | m.wlo, lane, in.rv, in.rtail);
+    const uint32_t nch = (m.bits + kChunkBits - 1) / kChunkBits;
+    const uint32_t ch = m.j * kSegChunks + lane;
+    if (ch < nch) in.gap = T.gaps[(uint64_t)s * kSegChunks + lane];
+    if (lane == kWave - 1 && ch + 1 < nch) in.gapn = T.gaps[(uint64_t)(s + 1) * kSegChunks];
+}
+
 // ---- one segment per wavefront ------------------------------------------------
 
 // One table lookup at the front of `win` for the lanes in `a`; the others read the
@@ -433,44 +545,37 @@ __device__ void write_rounds(const DTab &tab, lds_cu32 *col, uint8_t *stage, uin
         ent[slot] = hi_ | (extra);                                                       \
     } while (0)
 
+// Decode segment s, whose stream words are already in this wavefront's LDS rows.
+// `in` holds its gap bytes; the next segment's loads are issued into `in` and, once
+// this segment no longer reads its rows, stored to them (`next_pending` cleared).
 template <int DT>
-__device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *sw, uint32_t s,
-                               uint32_t *err)
+__device__ __forceinline__ void decode_segment_body(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *sw,
+                                                    uint32_t s, const SegMeta &m, SegIn &in, bool has_next, uint32_t sn,
+                                                    const SegMeta &mn, uint32_t *err, bool &next_pending)
 {
     constexpr uint32_t A = alphabet_of(DT);
     const uint32_t lane = lane_now();
-    const uint32_t b = T.seg_desc[2 * (uint64_t)s];
-    const uint32_t e0 = T.seg_desc[2 * (uint64_t)s + 1];
-    if (b >= T.nblocks) { report(err, ZX_E_CORRUPT); return; }
-    const uint64_t G = T.block_bitoff[b];
-    const uint64_t Gn = T.block_bitoff[b + 1];
-    const uint32_t sb = T.block_seg[b];
-    const uint32_t sbn = T.block_seg[b + 1];
+    const bool bad = (m.b0bad & 0x100u) != 0;
+    const uint32_t b = m.b;
+    const uint32_t e0 = m.e0;
+    const uint32_t e_end = m.e_end;
+    const uint32_t bits = m.bits;
+    const uint32_t j = m.j;
     const uint64_t lo = (uint64_t)b * kBlock;
     const uint32_t nb = (uint32_t)(((lo + kBlock < T.n) ? lo + kBlock : T.n) - lo);
-    if (Gn < G || Gn > T.total_bits || s < sb || s >= sbn || sbn > T.nsegs || Gn - G > (uint64_t)nb * kMaxLen) {
-        report(err, ZX_E_CORRUPT);
-        return;
-    }
-    const uint32_t bits = (uint32_t)(Gn - G);
-    const uint32_t j = s - sb;
-    const uint32_t e_end = (s + 1 < sbn) ? T.seg_desc[2 * (uint64_t)(s + 1) + 1] : nb;
-    if (e0 > e_end || e_end > nb) { report(err, ZX_E_CORRUPT); return; }
     const uint8_t *sm_block = T.signmant + (DT == ZX_BF16 ? lo : lo / 2);
     void *out_block = reinterpret_cast<uint8_t *>(T.out) + lo * (DT == ZX_BF16 ? 2 : 1);
     const uint32_t sbase = e0 & ~15u;   // 16-aligned element that stage byte 0 stands for
 
-    // requests first: the lanes' stream words, their gap bytes, and the sign/mantissa
-    // bytes of the first write batch, which arrive while the lanes decode
-    const uint32_t nch = (bits + kChunkBits - 1) / kChunkBits;
-    const uint32_t ch = j * kSegChunks + lane;
-    u32x4_a4 rv = {0u, 0u, 0u, 0u};
-    uint32_t rtail = 0;
-    if (bits != 0) rows_load(T.stream, T.stream_words, (G >> 5) + (uint64_t)j * (kSegBits / 32), lane, rv, rtail);
-    const uint32_t gap = (bits != 0 && ch < nch) ? T.gaps[(uint64_t)s * kSegChunks + lane] : ZX_NO_GAP;
-    uint32_t gap_next = (lane == kWave - 1 && ch + 1 < nch) ? T.gaps[(uint64_t)(s + 1) * kSegChunks] : ZX_NO_GAP;
+    // the sign/mantissa bytes of this segment's first write batch and the next
+    // segment's words and gaps are requested first; they arrive while this segment
+    // decodes
+    const uint32_t gap = in.gap;
+    uint32_t gap_next = in.gapn;
     uint2 smv[kWriteBatch];
-    prefetch_sm<DT>(sm_block, e0, e_end, smv);
+    prefetch_sm<DT>(sm_block, bad ? 0 : e0, bad ? 0 : e_end, smv);
+    if (has_next) issue_seg(T, sn, mn, lane, in);
+    if (bad) { report(err, ZX_E_CORRUPT); return; }
 
     if (bits == 0) {
         const uint32_t d = T.degenerate[T.per_block ? b : 0];
@@ -480,6 +585,8 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
     }
     if (!tab.ok) { report(err, ZX_E_CORRUPT); return; }
 
+    const uint32_t nch = (bits + kChunkBits - 1) / kChunkBits;
+    const uint32_t ch = j * kSegChunks + lane;
     {
         const uint32_t gn = __shfl_down(gap, 1, kWave);
         if (lane != kWave - 1) gap_next = gn;
@@ -489,41 +596,43 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
     if (work && gap >= kMaxLen) { work = false; lane_bad = true; }
     const uint32_t cend = (ch * kChunkBits + kChunkBits < bits) ? kChunkBits : bits - ch * kChunkBits;
     if (work && gap >= cend) { work = false; lane_bad = true; }
-    const uint32_t b0 = (uint32_t)(G & 31);
+    const uint32_t b0 = m.b0bad & 31u;
     // codes of one chunk must end exactly where the next chunk's first code starts
     // (or at the block end), as the stored gaps claim
     const uint32_t expect = (ch + 1 < nch && gap_next != ZX_NO_GAP) ? kPosBase + b0 + kChunkBits + gap_next
                                                                     : kPosBase + b0 + (bits - ch * kChunkBits);
-    rows_store(sw, lane, rv, rtail);
     wave_sync();
     lds_cu32 *col = window_col(sw, lane);
     const uint32_t start = kPosBase + b0 + gap;
     const uint32_t lim = kPosBase + b0 + cend;
     // B: low byte 256 - position, bits 16..23 minus the code count; a lane is active
     // while its position is below lim, i.e. while B's low byte exceeds thr
-    const uint32_t thr = work ? 256u - lim : 255u;
+    // (a lane without a chunk, or one found damaged, gets thr = 255: never active)
+    uint32_t thr = work ? 256u - lim : 255u;
     constexpr uint32_t kIdleQ = 256u - kPosBase;   // a harmless window for idle lanes
     uint32_t B = work ? 256u - start : kIdleQ;
     uint32_t Bprev = B;
-    bool ok = work;
     const uint32_t lim_short = tab.lim_short;
 
     // ---- count pass, register path
+    // entries of rounds that do not run are never read: the replay stops once no lane
+    // has symbols left
     uint32_t ent[kEnt];
 #pragma unroll
-    for (int k = 0; k < kEnt; ++k) ent[k] = 0;
+    for (int k = 0; k < kEnt; ++k) ent[k] = __builtin_nondeterministic_value(0u);
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
-        bool act = ok && (B & 0xFFu) > thr;
-        if (__ballot(act) == 0) break;
-        uint32_t win = window(col, act ? B : kIdleQ);
+        bool act = (B & 0xFFu) > thr;
+        const uint64_t am = __builtin_amdgcn_ballot_w64(act);
+        if (am == 0) break;
+        uint32_t win = window(col, B);
         const bool lng = act && win > lim_short;   // the next code is longer than the table window
         uint32_t eslow = 0;
-        if (__ballot(lng) != 0) {
+        if ((__builtin_amdgcn_ballot_w64(win > lim_short) & am) != 0) {
             if (lng) {
                 const uint32_t L = slow_len(tab, win);
                 if (L > kMaxLen) {
-                    ok = false;
+                    thr = 255u;
                     lane_bad = true;
                     act = false;
                 } else {
@@ -531,7 +640,7 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
                     Bprev = B;
                     B -= L | (1u << 16);
                     act = (B & 0xFFu) > thr;
-                    win = window(col, act ? B : kIdleQ);
+                    win = window(col, B);
                 }
             }
         }
@@ -542,11 +651,11 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
         act = act && (B & 0xFFu) > thr;
         ZX_LOOKUP(act, 3 * r + 2, 0u);
     }
-    const bool more = __ballot(ok && (B & 0xFFu) > thr) != 0;
+    const bool more = __builtin_amdgcn_ballot_w64((B & 0xFFu) > thr) != 0;
 
     uint32_t cnt = 0;
     if (!more) {
-        if (ok) {
+        if (work && !lane_bad) {
             // the last lookup may hold codes that start in the next chunk: drop them
             const uint32_t el = Bprev - B;
             const uint32_t pl = 256u - (Bprev & 0xFFu);
@@ -571,37 +680,60 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
     }
     uint32_t total;
     const uint32_t off = wave_excl_scan(cnt, total);
-    if (__ballot(lane_bad) != 0 || e0 + total != e_end) { report(err, ZX_E_CORRUPT); return; }
+    if (any_lane(lane_bad) || e0 + total != e_end) { report(err, ZX_E_CORRUPT); return; }
 
     const uint32_t t0 = e0 - sbase;   // stage position of the segment's first element
-    if (t0 + total + 2 <= kStageBytes) {
+    if (t0 + total + 3 <= kStageBytes) {
         if (!more) {
-            // ---- replay the entries into the stage.  Each writes three bytes and
-            //      advances by its symbol count; the bytes past a lane's last symbol
-            //      (at most two) land on the next lane's first positions, which that
-            //      lane rewrites after the barrier from its first two symbols.
-            const uint32_t n0 = ent[0] >> 24;
-            const uint32_t e1 = (ent[1] >> 24) != 0 ? ent[1] : ent[3];
-            const uint32_t first2 = (ent[0] & 0xFFu) | (((n0 >= 2 ? (ent[0] >> 8) : e1) & 0xFFu) << 8);
-            uint32_t wp = t0 + off;
-            int32_t rem = (int32_t)cnt;
+            // the rows are read no more: the next segment's words go in now, before
+            // this segment's stores are in flight (a later wait for them would have
+            // to drain those stores too)
+            if (next_pending) {
+                rows_store(sw, lane, in.rv, in.rtail);
+                next_pending = false;
+            }
+            // ---- replay the entries into the stage: each entry stores its three symbol
+            //      bytes and advances by its symbol count (byte stores: unaligned dword
+            //      stores to LDS were measured slower).  A lane's last entry may store up
+            //      to two bytes past its end, onto the first positions of the lanes after
+            //      it, so after a barrier every lane rewrites its first three positions.
+            // first three symbols: the first entry's, topped up from the entries after it
+            // (a stalled lookup leaves an empty entry; a long code fills one slot)
+            uint32_t f3 = ent[0];
+            uint32_t nf = ent[0] >> 24;
+            const uint32_t need = cnt < 3u ? cnt : 3u;
+#pragma unroll
+            for (int k = 1; k < 7; ++k) {
+                if (__builtin_amdgcn_ballot_w64(nf < need) == 0) break;
+                if (nf < need) {
+                    f3 = (f3 & ((1u << (8 * nf)) - 1u)) | (ent[k] << (8 * nf));
+                    nf += ent[k] >> 24;
+                }
+            }
+            uint8_t *a = stage + t0 + off;
+            uint8_t *const aend = a + cnt;
 #pragma unroll
             for (int k = 0; k < kEnt; ++k) {
-                if (__ballot(rem > 0) == 0) break;
-                if (rem > 0) {
-                    const uint32_t e = ent[k];
-                    uint8_t *d = stage + wp;
-                    d[0] = (uint8_t)e;
-                    d[1] = (uint8_t)(e >> 8);
-                    d[2] = (uint8_t)(e >> 16);
-                    const uint32_t ns = e >> 24;
-                    wp += ns;
-                    rem -= (int32_t)ns;
+                if (__builtin_amdgcn_ballot_w64(a < aend) == 0) break;
+                if (a < aend) {
+                    a[0] = (uint8_t)ent[k];
+                    a[1] = (uint8_t)(ent[k] >> 8);
+                    a[2] = (uint8_t)(ent[k] >> 16);
+                    a += ent[k] >> 24;
                 }
             }
             wave_sync();
-            if (cnt >= 1) stage[t0 + off] = (uint8_t)first2;
-            if (cnt >= 2) stage[t0 + off + 1] = (uint8_t)(first2 >> 8);
+            uint8_t *const a0 = stage + t0 + off;
+            if (cnt >= 3) {
+                a0[0] = (uint8_t)f3;
+                a0[1] = (uint8_t)(f3 >> 8);
+                a0[2] = (uint8_t)(f3 >> 16);
+            } else if (cnt == 2) {
+                a0[0] = (uint8_t)f3;
+                a0[1] = (uint8_t)(f3 >> 8);
+            } else if (cnt == 1) {
+                a0[0] = (uint8_t)f3;
+            }
         } else {
             store_generic(tab, col, stage, start, cnt, t0 + off);
         }
@@ -612,6 +744,15 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
     write_rounds<DT>(tab, col, stage, start, cnt, off, t0, total, out_block, sm_block, sbase, smv);
 }
 #undef ZX_LOOKUP
+
+template <int DT>
+__device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *sw, uint32_t s,
+                               const SegMeta &m, SegIn &in, bool has_next, uint32_t sn, const SegMeta &mn, uint32_t *err)
+{
+    bool next_pending = has_next;
+    decode_segment_body<DT>(T, tab, stage, sw, s, m, in, has_next, sn, mn, err, next_pending);
+    if (next_pending) rows_store(sw, lane_now(), in.rv, in.rtail);
+}
 
 template <int DT>
 __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(const DecBatch batch, uint32_t *err)
@@ -630,29 +771,63 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
     const DecTensor &T = batch.t[t];
     const uint32_t lg = g - T.wg_begin;
     const uint32_t tid = threadIdx.x;
+    const uint32_t wave = tid / kWave;
+    const uint32_t lane = lane_now();
     uint32_t s_begin, s_end;
     if (T.per_block) {
-        const uint32_t b = lg;
-        s_begin = T.block_seg[b];
-        s_end = T.block_seg[b + 1];
+        s_begin = T.block_seg[lg];
+        s_end = T.block_seg[lg + 1];
         if (s_end > T.nsegs || s_begin > s_end) { s_end = s_begin; if (tid == 0) report(err, ZX_E_CORRUPT); }
-        Canon &c = *reinterpret_cast<Canon *>(stage_all);
-        canon_build(T.lengths + (uint64_t)b * A, A, c);
-        dtab_fill(c, A, tab);
-        __syncthreads();
     } else {
         s_begin = lg * T.segs_per_wg;
         s_end = s_begin + T.segs_per_wg;
         if (s_end > T.nsegs) s_end = T.nsegs;
+    }
+    // the wavefront's segments are s_begin + wave + kDecWaves k, k < nk; lane k holds
+    // the descriptor of the k-th (in groups of 64)
+    const uint32_t s0 = s_begin + wave;
+    const uint32_t nk = s0 < s_end ? (s_end - s0 + kDecWaves - 1) / kDecWaves : 0;
+    SegMeta mine;
+    SegIn in;
+    if (T.per_block) {
+        load_meta(T, s0 + kDecWaves * lane, lane < nk, mine);
+        if (nk) issue_seg(T, s0, meta_at(mine, 0), lane, in);
+        Canon &c = *reinterpret_cast<Canon *>(stage_all);
+        canon_build(T.lengths + (uint64_t)lg * A, A, c);
+        dtab_fill(c, A, tab);
+    } else {
+        // the prepared table is requested first, the descriptors next; the table is
+        // stored to LDS once it arrives
         const uint4 *src = reinterpret_cast<const uint4 *>(T.dtab);
         uint4 *dst = reinterpret_cast<uint4 *>(&tab);
-        for (uint32_t i = tid; i < sizeof(DTab) / 16; i += kDecThreads) dst[i] = src[i];
-        __syncthreads();
+        constexpr uint32_t kTabPieces = sizeof(DTab) / 16;
+        static_assert(kTabPieces <= 2 * kDecThreads, "decode table copy takes two pieces per thread");
+        const uint4 p0 = src[tid];
+        uint4 p1 = make_uint4(0, 0, 0, 0);
+        if (tid + kDecThreads < kTabPieces) p1 = src[tid + kDecThreads];
+        load_meta(T, s0 + kDecWaves * lane, lane < nk, mine);
+        if (nk) issue_seg(T, s0, meta_at(mine, 0), lane, in);
+        dst[tid] = p0;
+        if (tid + kDecThreads < kTabPieces) dst[tid + kDecThreads] = p1;
     }
-    const uint32_t wave = tid / kWave;
     uint8_t *stage = stage_all + wave * kStageBytes;
     uint32_t *swords = words_all + wave * kSegWords;
-    for (uint32_t s = s_begin + wave; s < s_end; s += kDecWaves) decode_segment<DT>(T, tab, stage, swords, s, err);
+    if (nk) rows_store(swords, lane, in.rv, in.rtail);
+    __syncthreads();
+    for (uint32_t k = 0; k < nk; ++k) {
+        const uint32_t i = k & (kWave - 1);
+        const uint32_t s = s0 + kDecWaves * k;
+        const bool has_next = k + 1 < nk && i + 1 < kWave;
+        const SegMeta mu = meta_at(mine, i);
+        const SegMeta mn = meta_at(mine, has_next ? i + 1 : i);
+        decode_segment<DT>(T, tab, stage, swords, s, mu, in, has_next, s + kDecWaves, mn, err);
+        if (i == kWave - 1 && k + 1 < nk) {
+            // next group of 64 descriptors
+            load_meta(T, s + kDecWaves + kDecWaves * lane, k + 1 + lane < nk, mine);
+            issue_seg(T, s + kDecWaves, meta_at(mine, 0), lane, in);
+            rows_store(swords, lane, in.rv, in.rtail);
+        }
+    }
 }
 
 __global__ __launch_bounds__(256) void k_build_dtab(const uint8_t *__restrict__ lengths, uint32_t A, DTab *__restrict__ out)
@@ -707,7 +882,8 @@ extern "C" zx_status zx_decode_block_batch(const zx_container *cs, void *const *
         if (cs[i].dtype != dt) return ZX_E_INVAL;
     }
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
     const uint64_t slots = (uint64_t)cus * kDecWgPerCu;   // resident 512-thread workgroups per CU
     uint64_t seg_total = 0;
     for (uint32_t i = 0; i < count; ++i)
