@@ -212,12 +212,38 @@ __device__ __forceinline__ uint2 load_sm(const uint8_t *sm_block, uint32_t i)
     return *reinterpret_cast<const uint2 *>(sm_block + (DT == ZX_BF16 ? i : i / 2));
 }
 
-// Sign/mantissa bytes of the first batch of whole pieces of [i_begin, i_end):
-// piece q = first + lane + 64 k.
+// The element of [i_begin, i_end) this lane writes in one of the (at most two) cut
+// pieces at the range ends, or ~0u: lane t (< P) takes element t of the head piece,
+// lane P + t element t of the tail piece.
+template <int DT>
+__device__ __forceinline__ uint32_t cut_elem(uint32_t i_begin, uint32_t i_end)
+{
+    constexpr uint32_t P = Piece<DT>::kElems;
+    if (i_begin >= i_end) return ~0u;
+    const uint32_t lane = lane_now();
+    const uint32_t q_head = i_begin / P;
+    const uint32_t q_tail = (i_end - 1) / P;
+    const bool head_cut = (i_begin % P) != 0 || (q_head == q_tail && (i_end % P) != 0);
+    const bool tail_cut = (i_end % P) != 0 && q_tail != q_head;
+    uint32_t ii = ~0u;
+    if (lane < P && head_cut) ii = q_head * P + lane;
+    if (lane >= P && lane < 2 * P && tail_cut) ii = q_tail * P + (lane - P);
+    return (ii != ~0u && ii >= i_begin && ii < i_end) ? ii : ~0u;
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t load_cut_sm(const uint8_t *sm_block, uint32_t ii)
+{
+    return ii != ~0u ? (uint32_t)sm_block[DT == ZX_BF16 ? ii : ii / 2] : 0u;
+}
+
+// Sign/mantissa bytes of the first batch of whole pieces of [i_begin, i_end)
+// (piece q = first + lane + 64 k) and of this lane's cut-piece element.
 template <int DT>
 __device__ __forceinline__ void prefetch_sm(const uint8_t *sm_block, uint32_t i_begin, uint32_t i_end,
-                                            uint2 (&smv)[kWriteBatch])
+                                            uint2 (&smv)[kWriteBatch], uint32_t &smcut)
 {
+    smcut = load_cut_sm<DT>(sm_block, cut_elem<DT>(i_begin, i_end));
     constexpr uint32_t P = Piece<DT>::kElems;
     const uint32_t lane = lane_now();
     const uint32_t qf_begin = (i_begin + P - 1) / P;
@@ -296,7 +322,9 @@ __device__ __forceinline__ void store_piece(void *out_block, uint32_t i, uint4 r
 // One batch of whole pieces.  Every piece is fused before the first store goes out:
 // the stores are conditional, and once one is in flight the outstanding-access
 // count no longer tells when a given load has returned, so any wait after it would
-// have to drain all stores first.
+// have to drain all stores first.  (Fusing and storing piece by piece after one
+// wait for all loads was measured slower: each piece then waits for its own LDS
+// read.)
 template <int DT>
 __device__ __forceinline__ void store_batch(void *out_block, uint32_t qb, uint32_t qf_end, const uint2 (&smv)[kWriteBatch],
                                             const uint8_t *stage, uint32_t sbase, bool degen, uint32_t dsplat)
@@ -317,23 +345,13 @@ __device__ __forceinline__ void store_batch(void *out_block, uint32_t qb, uint32
     }
 }
 
-// Elements of the cut pieces at the two range ends, one element per lane: lane t
-// (< P) takes element t of the head piece, lane P + t element t of the tail piece.
+// This lane's cut-piece element (see cut_elem), from its sign/mantissa byte smb.
 template <int DT>
-__device__ __forceinline__ void write_cut_pieces(void *out_block, const uint8_t *sm_block, uint32_t i_begin, uint32_t i_end,
-                                                 const uint8_t *stage, uint32_t sbase, bool degen, uint32_t dform)
+__device__ __forceinline__ void write_cut_pieces(void *out_block, uint32_t i_begin, uint32_t i_end, const uint8_t *stage,
+                                                 uint32_t sbase, bool degen, uint32_t dform, uint32_t smb)
 {
-    constexpr uint32_t P = Piece<DT>::kElems;
-    const uint32_t lane = lane_now();
-    const uint32_t q_head = i_begin / P;
-    const uint32_t q_tail = (i_end - 1) / P;
-    const bool head_cut = (i_begin % P) != 0 || (q_head == q_tail && (i_end % P) != 0);
-    const bool tail_cut = (i_end % P) != 0 && q_tail != q_head;
-    uint32_t ii = ~0u;
-    if (lane < P && head_cut) ii = q_head * P + lane;
-    if (lane >= P && lane < 2 * P && tail_cut) ii = q_tail * P + (lane - P);
-    if (ii != ~0u && ii >= i_begin && ii < i_end) {
-        const uint32_t smb = sm_block[DT == ZX_BF16 ? ii : ii / 2];
+    const uint32_t ii = cut_elem<DT>(i_begin, i_end);
+    if (ii != ~0u) {
         const uint32_t ex = degen ? dform : stage[ii - sbase];
         if (DT == ZX_BF16) {
             reinterpret_cast<uint16_t *>(out_block)[ii] = (uint16_t)fuse_bf16_pair(smb, ex, kSelA01, kSelB01);
@@ -347,16 +365,18 @@ __device__ __forceinline__ void write_cut_pieces(void *out_block, const uint8_t 
 // Write block elements [i_begin, i_end); the staged exponent of element i is
 // stage[i - sbase] (or `dform` for a 0-bit block).  Whole pieces go in batches of
 // kWriteBatch per lane, whose sign/mantissa loads are all issued before any is used;
-// with kPre the first batch's bytes are `smv0`, loaded by prefetch_sm on the same
-// range.  The (at most two) cut pieces at the range ends go one element per lane.
+// with kPre the first batch's bytes and the cut-piece byte are `smv0` and `smcut0`,
+// loaded by prefetch_sm on the same range.  The (at most two) cut pieces at the range
+// ends go one element per lane; their byte is loaded before any store goes out.
 template <int DT, bool kPre>
 __device__ __forceinline__ void write_range(void *out_block, const uint8_t *sm_block, uint32_t i_begin, uint32_t i_end,
                                             const uint8_t *stage, uint32_t sbase, bool degen, uint32_t dform,
-                                            const uint2 (&smv0)[kWriteBatch])
+                                            const uint2 (&smv0)[kWriteBatch], uint32_t smcut0)
 {
     constexpr uint32_t P = Piece<DT>::kElems;
     if (i_begin >= i_end) return;
     const uint32_t lane = lane_now();
+    const uint32_t smcut = kPre ? smcut0 : load_cut_sm<DT>(sm_block, cut_elem<DT>(i_begin, i_end));
     const uint32_t qf_begin = (i_begin + P - 1) / P;
     const uint32_t qf_end = i_end / P;
     const uint32_t dsplat = dform * 0x01010101u;
@@ -375,7 +395,7 @@ __device__ __forceinline__ void write_range(void *out_block, const uint8_t *sm_b
         }
         store_batch<DT>(out_block, qb, qf_end, smv, stage, sbase, degen, dsplat);
     }
-    write_cut_pieces<DT>(out_block, sm_block, i_begin, i_end, stage, sbase, degen, dform);
+    write_cut_pieces<DT>(out_block, i_begin, i_end, stage, sbase, degen, dform, smcut);
 }
 
 // ---- fallback passes, one code at a time ------------------------------------
@@ -439,7 +459,7 @@ __device__ void write_rounds(const DTab &tab, lds_cu32 *col, uint8_t *stage, uin
         wave_sync();
         const uint32_t ib = sbase + (r0 > t0 ? r0 : t0);
         const uint32_t ie = sbase + (r1 < t0 + total ? r1 : t0 + total);
-        write_range<DT, false>(out_block, sm_block, ib, ie, stage, sbase + r0, false, 0, none);
+        write_range<DT, false>(out_block, sm_block, ib, ie, stage, sbase + r0, false, 0, none, 0u);
         wave_sync();
     }
 }
@@ -516,6 +536,14 @@ struct SegIn {
     uint32_t gapn;
 };
 
+// Put a segment's requested words into the LDS rows and wait for its gap bytes as
+// well, so that no later wait for them has to drain stores issued in between.
+__device__ __forceinline__ void rows_store_in(uint32_t *sw, uint32_t lane, const SegIn &in)
+{
+    rows_store(sw, lane, in.rv, in.rtail);
+    asm volatile("" ::"v"(in.gap), "v"(in.gapn));
+}
+
 __device__ __forceinline__ void issue_seg(const DecTensor &T, uint32_t s, const SegMeta &m, uint32_t lane, SegIn &in)
 {
     in.rv = u32x4_a4{0u, 0u, 0u, 0u};
@@ -573,14 +601,15 @@ __device__ __forceinline__ void decode_segment_body(const DecTensor &T, const DT
     const uint32_t gap = in.gap;
     uint32_t gap_next = in.gapn;
     uint2 smv[kWriteBatch];
-    prefetch_sm<DT>(sm_block, bad ? 0 : e0, bad ? 0 : e_end, smv);
+    uint32_t smcut;
+    prefetch_sm<DT>(sm_block, bad ? 0 : e0, bad ? 0 : e_end, smv, smcut);
     if (has_next) issue_seg(T, sn, mn, lane, in);
     if (bad) { report(err, ZX_E_CORRUPT); return; }
 
     if (bits == 0) {
         const uint32_t d = T.degenerate[T.per_block ? b : 0];
         if (d >= A || e0 != 0 || e_end != nb) { report(err, ZX_E_CORRUPT); return; }
-        write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, true, stage_form(A, d), smv);
+        write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, true, stage_form(A, d), smv, smcut);
         return;
     }
     if (!tab.ok) { report(err, ZX_E_CORRUPT); return; }
@@ -689,7 +718,7 @@ __device__ __forceinline__ void decode_segment_body(const DecTensor &T, const DT
             // this segment's stores are in flight (a later wait for them would have
             // to drain those stores too)
             if (next_pending) {
-                rows_store(sw, lane, in.rv, in.rtail);
+                rows_store_in(sw, lane, in);
                 next_pending = false;
             }
             // ---- replay the entries into the stage: each entry stores its three symbol
@@ -738,7 +767,7 @@ __device__ __forceinline__ void decode_segment_body(const DecTensor &T, const DT
             store_generic(tab, col, stage, start, cnt, t0 + off);
         }
         wave_sync();
-        write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, false, 0, smv);
+        write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, false, 0, smv, smcut);
         return;
     }
     write_rounds<DT>(tab, col, stage, start, cnt, off, t0, total, out_block, sm_block, sbase, smv);
@@ -751,7 +780,7 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
 {
     bool next_pending = has_next;
     decode_segment_body<DT>(T, tab, stage, sw, s, m, in, has_next, sn, mn, err, next_pending);
-    if (next_pending) rows_store(sw, lane_now(), in.rv, in.rtail);
+    if (next_pending) rows_store_in(sw, lane_now(), in);
 }
 
 template <int DT>
@@ -761,8 +790,9 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
     __shared__ DTab tab;
     __shared__ __align__(16) uint8_t stage_all[kDecWaves * kStageBytes];
     __shared__ __align__(16) uint32_t words_all[kDecWaves * kSegWords];
-    // three workgroups of this size were measured to fit a CU; 54 KB ones were not
-    static_assert(sizeof(DTab) + sizeof(stage_all) + sizeof(words_all) <= 52224, "decode workgroup LDS budget");
+    // kDecWgPerCu workgroups share the CU's 160 KB of LDS
+    static_assert(sizeof(DTab) + sizeof(stage_all) + sizeof(words_all) <= 160u * 1024u / kDecWgPerCu - 512u,
+                  "decode workgroup LDS budget");
     static_assert(sizeof(Canon) <= sizeof(stage_all), "Canon is built inside the stage area");
 
     const uint32_t g = blockIdx.x;
@@ -801,18 +831,24 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
         const uint4 *src = reinterpret_cast<const uint4 *>(T.dtab);
         uint4 *dst = reinterpret_cast<uint4 *>(&tab);
         constexpr uint32_t kTabPieces = sizeof(DTab) / 16;
-        static_assert(kTabPieces <= 2 * kDecThreads, "decode table copy takes two pieces per thread");
-        const uint4 p0 = src[tid];
-        uint4 p1 = make_uint4(0, 0, 0, 0);
-        if (tid + kDecThreads < kTabPieces) p1 = src[tid + kDecThreads];
+        constexpr uint32_t kPer = (kTabPieces + kDecThreads - 1) / kDecThreads;
+        uint4 pc[kPer];
+#pragma unroll
+        for (uint32_t k = 0; k < kPer; ++k) {
+            const uint32_t i = tid + k * kDecThreads;
+            pc[k] = i < kTabPieces ? src[i] : make_uint4(0, 0, 0, 0);
+        }
         load_meta(T, s0 + kDecWaves * lane, lane < nk, mine);
         if (nk) issue_seg(T, s0, meta_at(mine, 0), lane, in);
-        dst[tid] = p0;
-        if (tid + kDecThreads < kTabPieces) dst[tid + kDecThreads] = p1;
+#pragma unroll
+        for (uint32_t k = 0; k < kPer; ++k) {
+            const uint32_t i = tid + k * kDecThreads;
+            if (i < kTabPieces) dst[i] = pc[k];
+        }
     }
     uint8_t *stage = stage_all + wave * kStageBytes;
     uint32_t *swords = words_all + wave * kSegWords;
-    if (nk) rows_store(swords, lane, in.rv, in.rtail);
+    if (nk) rows_store_in(swords, lane, in);
     __syncthreads();
     for (uint32_t k = 0; k < nk; ++k) {
         const uint32_t i = k & (kWave - 1);
@@ -825,7 +861,7 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
             // next group of 64 descriptors
             load_meta(T, s + kDecWaves + kDecWaves * lane, k + 1 + lane < nk, mine);
             issue_seg(T, s + kDecWaves, meta_at(mine, 0), lane, in);
-            rows_store(swords, lane, in.rv, in.rtail);
+            rows_store_in(swords, lane, in);
         }
     }
 }
