@@ -88,29 +88,44 @@ __device__ inline void canon_build(const uint8_t *__restrict__ lengths_g, uint32
         if (lane_id() == 0) c.wcnt[wave][L] = (uint32_t)__popcll(m);
     }
     __syncthreads();
-    if (tid == 0) {
-        uint32_t code = 0, idx = 0, maxlen = 0;
-        uint64_t kraft = 0;
-        for (uint32_t L = 1; L <= kMaxLen; ++L) {
-            uint32_t cnt = 0;
+    if (wave == 0) {
+        // lane L (1..32): the number of codes of length L, then by prefix scans its
+        // first canonical code and first symbol index.  Left-justified to 32 bits, the
+        // first code of length L is the sum over shorter lengths j of count[j] << (32 - j)
+        // (each length's codes follow the shorter ones, one bit longer).
+        const uint32_t L = lane_id();
+        const bool isl = L >= 1 && L <= kMaxLen;
+        uint32_t cnt = 0;
+        if (isl)
             for (uint32_t w = 0; w < nwaves; ++w) cnt += c.wcnt[w][L];
-            c.count[L] = cnt;
-            c.first[L] = code;
-            c.offset[L] = idx;
-            uint64_t lim = ((uint64_t)code + cnt) << (kMaxLen - L);
-            c.lim[L] = lim;
-            if (cnt) maxlen = L;
-            kraft += (uint64_t)cnt << (kMaxLen - L);
-            // the next length starts right after this one's codes, one bit longer
-            // (a wrap here implies an over-full code, which the Kraft test rejects)
-            code = (uint32_t)(((uint64_t)code + cnt) << 1);
-            idx += cnt;
+        uint32_t nsym;
+        const uint32_t idx = wave_excl_scan(cnt, nsym);
+        const uint64_t t = isl ? (uint64_t)cnt << (kMaxLen - L) : 0ull;
+        uint64_t x = t;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const uint64_t y = __shfl_up(x, d, kWave);
+            if (L >= (uint32_t)d) x += y;
         }
-        c.lim[kMaxLen + 1] = ~0ull;
-        c.count[0] = 0;
-        c.nsym = idx;
-        c.maxlen = maxlen;
-        c.ok = (idx >= 2 && kraft == (1ull << 32)) ? 1u : 0u;
+        const uint64_t F = x - t;                      // exclusive: left-justified first code
+        const uint64_t kraft = __shfl(x, kWave - 1, kWave);
+        const uint64_t nz = __builtin_amdgcn_ballot_w64(isl && cnt != 0);
+        if (isl) {
+            c.count[L] = cnt;
+            c.first[L] = (uint32_t)(F >> (kMaxLen - L));
+            c.offset[L] = idx;
+            c.lim[L] = F + t;
+        }
+        if (L == 0) {
+            c.lim[kMaxLen + 1] = ~0ull;
+            c.count[0] = 0;
+            c.first[0] = 0;
+            c.offset[0] = 0;
+            c.lim[0] = 0;
+            c.nsym = nsym;
+            c.maxlen = nz ? 63u - (uint32_t)__builtin_clzll(nz) : 0u;
+            c.ok = (nsym >= 2 && kraft == (1ull << 32)) ? 1u : 0u;
+        }
     }
     __syncthreads();
     if (tid < A) {

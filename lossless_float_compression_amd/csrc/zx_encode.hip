@@ -136,6 +136,189 @@ __global__ void k_clear_shared_words(uint64_t nblocks, const uint64_t *__restric
 }
 
 // -------------------------------------------------------------------- bit packing
+// A full block whose bits fit the LDS stage (at most 8192 words: any mean code length
+// up to about 4 bits) is packed in one pass: all of the block's input is requested
+// first; every round stores its sign/mantissa bytes (one unconditional store per
+// thread) and places its codes, gap bytes and segment entries in LDS; the stream
+// words, gaps and segment entries are stored at the end.  Stores count among the
+// outstanding vector-memory accesses, so waiting for a load issued before a store
+// is only cheap when the number of accesses issued after the load is known
+// statically; with every store before the last wait unconditional it is.  Other
+// blocks (the last, partial block of a tensor, or very long codes) take the
+// round-by-round path in k_encode.
+constexpr uint32_t kOnePassBits = (kStageWords - 2) * 32;
+constexpr uint32_t kOnePassChunks = kOnePassBits / kChunkBits;
+constexpr uint32_t kOnePassSegs = kOnePassChunks / kSegChunks;
+constexpr uint32_t kRoundsPerBlock = kBlock / kRound;
+
+template <int DT>
+__device__ __forceinline__ void encode_onepass(const void *__restrict__ in, uint64_t lo, uint32_t nb, uint64_t b, const Canon &c,
+                                               uint32_t degen, uint64_t G, uint32_t bits, uint32_t s0, uint32_t nsb, uint32_t nch,
+                                               uint64_t w_first, uint64_t w_last, uint8_t *__restrict__ signmant,
+                                               uint32_t *__restrict__ stream, uint32_t *__restrict__ seg_desc,
+                                               uint8_t *__restrict__ gaps, uint32_t *__restrict__ err, uint32_t *stage,
+                                               uint8_t *gapbuf, uint32_t *segbuf, uint32_t (*part2)[kEncThreads / kWave],
+                                               uint32_t &s_bad)
+{
+    constexpr uint32_t RW = DT == ZX_BF16 ? 4 : 2;   // input words per thread per round
+    const uint32_t tid = threadIdx.x;
+    // ---- input requested two rounds ahead
+    const uint8_t *src = reinterpret_cast<const uint8_t *>(in) + (lo + tid * kEncPerThread) * (DT == ZX_BF16 ? 2 : 1);
+    auto load_round = [&](uint32_t r, uint32_t (&w)[RW]) {
+        const uint8_t *a = src + (uint64_t)r * kRound * (DT == ZX_BF16 ? 2 : 1);
+        if (DT == ZX_BF16) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(a);
+            w[0] = q.x; w[1] = q.y; w[2 % RW] = q.z; w[3 % RW] = q.w;
+        } else {
+            const uint2 q = *reinterpret_cast<const uint2 *>(a);
+            w[0] = q.x; w[1] = q.y;
+        }
+    };
+    uint32_t nx1[RW], nx2[RW];
+    load_round(0, nx1);
+    load_round(1, nx2);
+    for (uint32_t i = tid; i < kStageWords; i += kEncThreads) stage[i] = 0;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+
+    const uint32_t a0 = (uint32_t)(G & 31);
+    uint32_t P = 0;    // block-relative bit of the round's first code
+    bool bad = false;
+#pragma unroll 1
+    for (uint32_t r = 0; r < kRoundsPerBlock; ++r) {
+        uint32_t raw[RW];
+#pragma unroll
+        for (uint32_t k = 0; k < RW; ++k) {
+            raw[k] = nx1[k];
+            nx1[k] = nx2[k];
+        }
+        if (r + 2 < kRoundsPerBlock) load_round(r + 2, nx2);
+        const uint32_t i0 = r * kRound + tid * kEncPerThread;
+        // ---- split: sign/mantissa bytes (nibbles) stored right away
+        uint32_t sym[kEncPerThread];
+        if (DT == ZX_BF16) {
+            uint32_t t[4];
+#pragma unroll
+            for (uint32_t w = 0; w < 4; ++w) {
+                const uint32_t x = raw[w];
+                t[w] = (x & 0x007F007Fu) | ((x >> 8) & 0x00800080u);   // [sm, 0, sm, 0]
+                sym[2 * w] = (x >> 7) & 0xFFu;
+                sym[2 * w + 1] = (x >> 23) & 0xFFu;
+            }
+            *reinterpret_cast<uint2 *>(signmant + lo + tid * kEncPerThread + (uint64_t)r * kRound) =
+                make_uint2(__builtin_amdgcn_perm(t[1], t[0], 0x06040200u), __builtin_amdgcn_perm(t[3], t[2], 0x06040200u));
+        } else {
+            uint32_t t[2];
+#pragma unroll
+            for (uint32_t w = 0; w < 2; ++w) {
+                const uint32_t x = raw[w];
+                const uint32_t nb4 = (x & 0x07070707u) | ((x >> 4) & 0x08080808u);   // one nibble per byte
+                t[w] = (nb4 | (nb4 >> 4)) & 0x00FF00FFu;                               // two nibbles per half
+#pragma unroll
+                for (uint32_t k = 0; k < 4; ++k) sym[4 * w + k] = (x >> (8 * k + 3)) & 0xFu;
+            }
+            *reinterpret_cast<uint32_t *>(signmant + (lo + tid * kEncPerThread) / 2 + (uint64_t)r * (kRound / 2)) =
+                __builtin_amdgcn_perm(t[1], t[0], 0x06040200u);
+        }
+        // ---- code lengths; codes concatenated; code starts as a bit mask
+        uint32_t lmin = 255;
+        uint32_t tb = 0;
+        uint64_t acc = 0;
+        uint64_t starts = 0;   // bit j: a code starts j bits into this thread's codes (j < 64)
+#pragma unroll
+        for (uint32_t k = 0; k < kEncPerThread; ++k) {
+            const uint32_t lk = c.len[sym[k]];
+            lmin = lk < lmin ? lk : lmin;
+            if (!bits && sym[k] != degen) bad = true;
+            acc = (acc << lk) | c.code[sym[k]];
+            starts |= (tb < 64 ? 1ull : 0ull) << (tb & 63);
+            tb += lk;
+        }
+        if (bits && lmin == 0) bad = true;
+        // ---- workgroup exclusive scan of code bits (partials double-buffered by round)
+        uint32_t wtot;
+        uint32_t o = wave_excl_scan(tb, wtot);
+        if (lane_id() == 0) part2[r & 1][tid / kWave] = wtot;
+        __syncthreads();
+        uint32_t R = 0;
+        for (uint32_t w = 0; w < kEncThreads / kWave; ++w) {
+            const uint32_t pw = part2[r & 1][w];
+            if (w < tid / kWave) o += pw;
+            R += pw;
+        }
+        const uint32_t p0 = P + o;       // block-relative bit of this thread's first code
+        const uint32_t q0 = a0 + p0;     // its stage bit
+        const uint32_t bnd = (p0 + kChunkBits - 1) & ~(kChunkBits - 1);   // first chunk boundary >= p0
+        if (tb <= 64) {
+            // ---- codes into the stage: up to three words, shared with the
+            //      neighbouring threads only at the ends
+            if (tb) {
+                const uint32_t sh = q0 & 31;
+                const uint64_t X = acc << (64 - tb);
+                uint32_t *w = &stage[q0 >> 5];
+                atomicOr(&w[0], (uint32_t)(X >> (32 + sh)));
+                if (sh + tb > 32) atomicOr(&w[1], (uint32_t)(X >> sh));
+                if (sh + tb > 64) atomicOr(&w[2], (uint32_t)(X << (32 - sh)));
+            }
+            // ---- gap byte of the chunk boundary these bits cover, if any: the distance
+            //      to the first code that starts at or after it (the next thread's first
+            //      code starts at tb)
+            if (bnd < p0 + tb) {
+                const uint32_t rel = bnd - p0;
+                const uint64_t after = starts >> rel;
+                const uint32_t m = after ? (uint32_t)__builtin_ctzll(after) : tb - rel;
+                gapbuf[bnd / kChunkBits] = (uint8_t)(bnd + m < bits ? m : ZX_NO_GAP);
+                if (bnd % (kChunkBits * kSegChunks) == 0 && bnd > 0)   // first element of a segment
+                    segbuf[bnd / (kChunkBits * kSegChunks)] = i0 + (uint32_t)__builtin_popcountll(starts & ((1ull << rel) - 1));
+            }
+        } else {
+            // ---- long codes: code by code, recomputed from the input
+            uint32_t pk = p0;
+#pragma unroll
+            for (uint32_t k = 0; k < kEncPerThread; ++k) {
+                const uint32_t lk = c.len[sym[k]];
+                if (lk == 0) continue;
+                const uint32_t q = a0 + pk;
+                const uint32_t sh = q & 31;
+                const uint64_t x = (uint64_t)c.code[sym[k]] << (64 - lk - sh);
+                atomicOr(&stage[q >> 5], (uint32_t)(x >> 32));
+                if (sh + lk > 32) atomicOr(&stage[(q >> 5) + 1], (uint32_t)x);
+                const uint32_t cd = (pk + kChunkBits - 1) / kChunkBits;
+                if (cd * kChunkBits < pk + lk) {
+                    uint32_t gap;
+                    if (cd * kChunkBits == pk)
+                        gap = 0;
+                    else
+                        gap = (pk + lk < bits) ? pk + lk - cd * kChunkBits : ZX_NO_GAP;
+                    gapbuf[cd] = (uint8_t)gap;
+                    if (cd % kSegChunks == 0 && cd > 0) segbuf[cd / kSegChunks] = (cd * kChunkBits == pk) ? (i0 + k) : (i0 + k + 1);
+                }
+                pk += lk;
+            }
+        }
+        P += R;
+    }
+    if (bad) s_bad = 1;
+    __syncthreads();
+    // ---- all stores
+    const uint64_t W0 = G >> 5;
+    const uint32_t nw = bits ? (a0 + bits + 31) >> 5 : 0;
+    for (uint32_t i = tid; i < nw; i += kEncThreads) {
+        const uint64_t gw = W0 + i;
+        if (gw == w_first || gw == w_last)
+            atomicOr(&stream[gw], stage[i]);
+        else
+            stream[gw] = stage[i];
+    }
+    for (uint32_t ch = tid; ch < nsb * kSegChunks; ch += kEncThreads)
+        gaps[(uint64_t)s0 * kSegChunks + ch] = ch < nch ? gapbuf[ch] : (uint8_t)ZX_NO_GAP;
+    for (uint32_t j = tid; j < nsb; j += kEncThreads) {
+        seg_desc[2 * (uint64_t)(s0 + j)] = (uint32_t)b;
+        seg_desc[2 * (uint64_t)(s0 + j) + 1] = j ? segbuf[j] : 0u;
+    }
+    if (tid == 0 && s_bad) report(err, ZX_E_CODEBOOK);
+}
+
 template <int DT>
 __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__ in, uint64_t n, int per_block,
                                                         const uint8_t *__restrict__ lengths,
@@ -151,6 +334,9 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
     __shared__ uint32_t stage[kStageWords];
     __shared__ uint32_t part[kEncThreads / kWave];
     __shared__ uint32_t s_bad;
+    __shared__ uint8_t gapbuf[kOnePassChunks];
+    __shared__ uint32_t segbuf[kOnePassSegs];
+    __shared__ uint32_t part2[2][kEncThreads / kWave];
 
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x;
@@ -172,6 +358,11 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
     }
     const uint64_t w_first = G >> 5;
     const uint64_t w_last = bits ? (G + bits - 1) >> 5 : w_first;
+    if (nb == kBlock && (G & 31) + bits <= kOnePassBits) {
+        encode_onepass<DT>(in, lo, nb, b, c, degen, G, (uint32_t)bits, s0, nsb, nch, w_first, w_last, signmant, stream, seg_desc,
+                           gaps, err, stage, gapbuf, segbuf, part2, s_bad);
+        return;
+    }
 
     if (tid == 0) {
         s_bad = 0;
@@ -277,6 +468,8 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
         // ---- place codes, write gaps and segment entries
         uint32_t q = a0 + o;     // stage bit
         uint32_t p = P + o;      // block-relative stream bit
+        const bool packed = tb <= 64;   // this thread's codes fit one 64-bit register
+        uint64_t acc = 0;
 #pragma unroll
         for (uint32_t k = 0; k < kEncPerThread; ++k) {
             if (k >= have) break;
@@ -298,12 +491,27 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
                 }
             }
             const uint32_t code = c.code[sym[k]];
-            const uint32_t sh = q & 31;
-            const uint64_t x = (uint64_t)code << (64 - l - sh);
-            atomicOr(&stage[q >> 5], (uint32_t)(x >> 32));
-            if (sh + l > 32) atomicOr(&stage[(q >> 5) + 1], (uint32_t)x);
+            if (packed) {
+                acc = (acc << l) | code;
+            } else {
+                const uint32_t sh = q & 31;
+                const uint64_t x = (uint64_t)code << (64 - l - sh);
+                atomicOr(&stage[q >> 5], (uint32_t)(x >> 32));
+                if (sh + l > 32) atomicOr(&stage[(q >> 5) + 1], (uint32_t)x);
+            }
             q += l;
             p += l;
+        }
+        if (packed && tb) {
+            // the thread's tb bits, left-justified, placed at stage bit q0: up to
+            // three words, shared with the neighbouring threads only at the ends
+            const uint32_t q0 = a0 + o;
+            const uint32_t sh = q0 & 31;
+            const uint64_t X = acc << (64 - tb);
+            uint32_t *w = &stage[q0 >> 5];
+            atomicOr(&w[0], (uint32_t)(X >> (32 + sh)));
+            if (sh + tb > 32) atomicOr(&w[1], (uint32_t)(X >> sh));
+            if (sh + tb > 64) atomicOr(&w[2], (uint32_t)(X << (32 - sh)));
         }
         __syncthreads();
         // ---- flush whole words, keep the partial last word as the next carry
