@@ -866,7 +866,7 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
     }
 }
 
-__global__ __launch_bounds__(256) void k_build_dtab(const uint8_t *__restrict__ lengths, uint32_t A, DTab *__restrict__ out)
+__global__ __launch_bounds__(1024) void k_build_dtab(const uint8_t *__restrict__ lengths, uint32_t A, DTab *__restrict__ out)
 {
     __shared__ Canon c;
     canon_build(lengths, A, c);
@@ -885,7 +885,8 @@ extern "C" zx_status zx_build_decode_table(zx_dtype dtype, const uint8_t *length
 {
     if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
     if (!lengths || !dtab || !aligned16(dtab)) return ZX_E_INVAL;
-    hipLaunchKernelGGL(k_build_dtab, dim3(1), dim3(256), 0, stream, lengths, alphabet_of(dtype), reinterpret_cast<DTab *>(dtab));
+    // one table entry per thread
+    hipLaunchKernelGGL(k_build_dtab, dim3(1), dim3(1024), 0, stream, lengths, alphabet_of(dtype), reinterpret_cast<DTab *>(dtab));
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
 }
 
