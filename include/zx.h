@@ -33,7 +33,8 @@
  *              byte i/2 when i is even, high nibble when odd (ceil(n/2) bytes).
  *   stream     codes of all elements in order, MSB first; stream bit j is bit
  *              31 - j%32 of u32 word j/32; blocks follow each other with no gap;
- *              stream_words = round_up(ceil(total_bits/32), 4) + 4, zero padded.
+ *              stream_words = round_up(ceil(total_bits/32), 4) + 260, zero padded
+ *              (a decoder may read a segment's 258 words from any segment start).
  *   block_bitoff[nblocks+1]  u64 stream bit where block b starts; last = total_bits.
  *   block_seg[nblocks+1]     u32 first segment of block b; last = nsegs.
  *              A block's bits are cut into 128-bit chunks (block-relative),

@@ -17,6 +17,10 @@ constexpr uint32_t kChunkBits = 128;     // stream bits per decode chunk
 constexpr uint32_t kSegChunks = 64;      // chunks per segment (one wavefront lane each)
 constexpr uint32_t kSegBits = kChunkBits * kSegChunks;
 constexpr uint32_t kMaxLen = 32;
+// Zero words after the last stream word (a multiple of four): one segment's words
+// and the two a lane's window may reach past them.
+constexpr uint32_t kStreamPadWords = 260;
+static_assert(kStreamPadWords % 4 == 0 && kStreamPadWords >= kSegBits / 32 + 2 + 2, "stream padding");
 constexpr int kWave = 64;
 
 // Decode lookup table index width: the primary table maps the next kLutBits

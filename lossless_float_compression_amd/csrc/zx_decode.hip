@@ -33,7 +33,11 @@ constexpr int kMaxBatch = 16;
 
 // Per-wavefront LDS: the lanes' stream words and the exponent stage.
 constexpr uint32_t kSlots = 7;                 // word slots per lane
-constexpr uint32_t kSegWords = kSlots * kWave;
+// Slot 6 is only ever read as the upper word of a zero-bit shift (a position of
+// exactly kPosBase), so it holds the lanes' gap bytes instead; the word after the
+// slots holds the next segment's first gap.
+constexpr uint32_t kGapSlot = 6;
+constexpr uint32_t kSegWords = kSlots * kWave + 4;
 constexpr uint32_t kStageBytes = 3616;         // one byte per output position, 16-byte multiple
 // A segment whose exponents do not fit the stage at once (mean code length under
 // about 2.3 bits) is written in rounds of kRoundElems output positions.
@@ -112,22 +116,15 @@ __device__ __forceinline__ uint32_t lds_word(const uint32_t *base, uint32_t byte
 // with a zero funnel shift, which takes the other word whole.
 
 // 16 bytes of stream words per lane (the lane's rows 1..4, the previous lane's rows 5
-// and 6) plus, in lanes 0 and 1, lane 63's rows 5 and 6.
-__device__ __forceinline__ void rows_load(const uint32_t *stream, uint64_t words, uint64_t W0, uint32_t lane,
-                                          u32x4_a4 &v, uint32_t &tail)
+// and 6) plus, in lanes 0 and 1, lane 63's rows 5 and 6 (the other lanes load a word
+// they do not use).  W0 is at most the last code word, and the stream has
+// kStreamPadWords zero words after it: every read is in bounds, and none needs a
+// condition.
+__device__ __forceinline__ void rows_load(const uint32_t *stream, uint64_t W0, uint32_t lane, u32x4_a4 &v,
+                                          uint32_t &tail)
 {
-    const uint64_t k = W0 + 4ull * lane;
-    if (k + 4 <= words) {
-        v = *reinterpret_cast<const u32x4_a4 *>(stream + k);
-    } else {
-        v.x = k < words ? stream[k] : 0u;
-        v.y = k + 1 < words ? stream[k + 1] : 0u;
-        v.z = k + 2 < words ? stream[k + 2] : 0u;
-        v.w = k + 3 < words ? stream[k + 3] : 0u;
-    }
-    tail = 0;
-    const uint64_t t = W0 + 256 + lane;
-    if (lane < 2 && t < words) tail = stream[t];
+    v = *reinterpret_cast<const u32x4_a4 *>(stream + W0 + 4u * lane);
+    tail = stream[W0 + 256u + (lane & 1u)];
 }
 
 __device__ __forceinline__ void rows_store(uint32_t *sw, uint32_t lane, const u32x4_a4 &v, uint32_t tail)
@@ -238,12 +235,17 @@ __device__ __forceinline__ uint32_t load_cut_sm(const uint8_t *sm_block, uint32_
 }
 
 // Sign/mantissa bytes of the first batch of whole pieces of [i_begin, i_end)
-// (piece q = first + lane + 64 k) and of this lane's cut-piece element.
+// (piece q = first + lane + 64 k) and of this lane's cut-piece element.  Every load
+// is issued, and nothing else writes its register: a piece (or cut element) the
+// lane does not have reads `dummy` instead, any 16 readable bytes.  (A default
+// value written to the register would first wait for the previous segment's load
+// into it, and so, with one counter for loads and stores, for all its stores.)
 template <int DT>
 __device__ __forceinline__ void prefetch_sm(const uint8_t *sm_block, uint32_t i_begin, uint32_t i_end,
-                                            uint2 (&smv)[kWriteBatch], uint32_t &smcut)
+                                            const uint8_t *dummy, uint2 (&smv)[kWriteBatch], uint32_t &smcut)
 {
-    smcut = load_cut_sm<DT>(sm_block, cut_elem<DT>(i_begin, i_end));
+    const uint32_t ii = cut_elem<DT>(i_begin, i_end);
+    smcut = *(ii != ~0u ? sm_block + (DT == ZX_BF16 ? ii : ii / 2) : dummy);
     constexpr uint32_t P = Piece<DT>::kElems;
     const uint32_t lane = lane_now();
     const uint32_t qf_begin = (i_begin + P - 1) / P;
@@ -251,9 +253,20 @@ __device__ __forceinline__ void prefetch_sm(const uint8_t *sm_block, uint32_t i_
 #pragma unroll
     for (int k = 0; k < kWriteBatch; ++k) {
         const uint32_t q = qf_begin + lane + k * kWave;
-        smv[k] = make_uint2(0, 0);
-        if (q < qf_end) smv[k] = load_sm<DT>(sm_block, q * P);
+        const uint8_t *a = q < qf_end ? sm_block + (DT == ZX_BF16 ? q * P : q * P / 2) : dummy;
+        smv[k] = *reinterpret_cast<const uint2 *>(a);
     }
+}
+
+// Mark the prefetched bytes as used on every path, at a point where they have
+// arrived and no store of the segment is out yet.  A register the loads target
+// that looks still pending on some path would make the next segment's first write
+// to it wait for all memory operations, this segment's stores included.
+__device__ __forceinline__ void settle_sm(const uint2 (&smv)[kWriteBatch], uint32_t smcut)
+{
+#pragma unroll
+    for (int k = 0; k < kWriteBatch; ++k) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
+    asm volatile("" ::"v"(smcut));
 }
 
 // Staged exponents of one piece, or a 0-bit block's single symbol.
@@ -336,6 +349,7 @@ __device__ __forceinline__ void store_batch(void *out_block, uint32_t qb, uint32
     for (int k = 0; k < kWriteBatch; ++k) {
         const uint32_t q = qb + lane + k * kWave;
         r[k] = make_uint4(0, 0, 0, 0);
+        asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
         if (q < qf_end) r[k] = fuse_piece<DT>(smv[k], piece_exps<DT>(stage + (q * P - sbase), degen, dsplat));
     }
 #pragma unroll
@@ -351,6 +365,7 @@ __device__ __forceinline__ void write_cut_pieces(void *out_block, uint32_t i_beg
                                                  uint32_t sbase, bool degen, uint32_t dform, uint32_t smb)
 {
     const uint32_t ii = cut_elem<DT>(i_begin, i_end);
+    asm volatile("" ::"v"(smb));
     if (ii != ~0u) {
         const uint32_t ex = degen ? dform : stage[ii - sbase];
         if (DT == ZX_BF16) {
@@ -495,7 +510,10 @@ __device__ __forceinline__ void load_meta(const DecTensor &T, uint32_t s, bool v
     const uint32_t sbn = T.block_seg[b + 1];
     const uint64_t lo = (uint64_t)b * kBlock;
     const uint32_t nb = (uint32_t)(((lo + kBlock < T.n) ? lo + kBlock : T.n) - lo);
-    if (Gn < G || Gn > T.total_bits || s < sb || s >= sbn || sbn > T.nsegs || Gn - G > (uint64_t)nb * kMaxLen) {
+    // (a segment after a block's first starts inside the block's bits: its rows are
+    // then read within the stream and its padding)
+    if (Gn < G || Gn > T.total_bits || s < sb || s >= sbn || sbn > T.nsegs || Gn - G > (uint64_t)nb * kMaxLen ||
+        (s != sb && (uint64_t)(s - sb) * kSegBits >= Gn - G)) {
         m.b0bad = 0x100u;
         return;
     }
@@ -528,34 +546,45 @@ __device__ __forceinline__ SegMeta meta_at(const SegMeta &m, uint32_t i)
 }
 
 // Loads a segment needs before it can decode: its lanes' stream words and gap bytes
-// (and the next segment's first gap, for lane 63).
+// (and the next segment's first gap, for lane 63), with which of the gaps are real.
+//
+// Every load here is unconditional and its register is written by nothing else:
+// gfx9 counts stores and loads in one counter, so a register write that has to
+// wait for an earlier load into the same register (a default value, say) waits for
+// every store issued since as well.  Values that some lanes do not need are still
+// marked used on all lanes where they are stored, for the same reason.
 struct SegIn {
     u32x4_a4 rv;
     uint32_t rtail;
     uint32_t gap;
     uint32_t gapn;
+    uint32_t real;       // bit 0: `gap` is a chunk's, bit 1: `gapn` is
 };
 
-// Put a segment's requested words into the LDS rows and wait for its gap bytes as
-// well, so that no later wait for them has to drain stores issued in between.
+// Put a segment's requested words and gap bytes into the wavefront's LDS rows.
 __device__ __forceinline__ void rows_store_in(uint32_t *sw, uint32_t lane, const SegIn &in)
 {
+    asm volatile("" ::"v"(in.rtail), "v"(in.gapn));
     rows_store(sw, lane, in.rv, in.rtail);
-    asm volatile("" ::"v"(in.gap), "v"(in.gapn));
+    sw[kGapSlot * kWave + lane] = (in.real & 1u) ? in.gap : (uint32_t)ZX_NO_GAP;
+    if (lane == kWave - 1) sw[kGapSlot * kWave + kWave] = (in.real & 2u) ? in.gapn : (uint32_t)ZX_NO_GAP;
 }
 
-__device__ __forceinline__ void issue_seg(const DecTensor &T, uint32_t s, const SegMeta &m, uint32_t lane, SegIn &in)
+// Request segment s; unless `want` (and a valid descriptor) the loads read the
+// stream's and the gap table's first entries, and no gap counts as real.
+__device__ __forceinline__ void issue_seg(const DecTensor &T, uint32_t s, const SegMeta &m, uint32_t lane, SegIn &in,
+                                          bool want)
 {
-    in.rv = u32x4_a4{0u, 0u, 0u, 0u};
-    in.rtail = 0;
-    in.gap = ZX_NO_GAP;
-    in.gapn = ZX_NO_GAP;
-    if ((m.b0bad & 0x100u) != 0 || m.bits == 0) return;
-    rows_load(T.stream, T.stream_words, ((uint64_t)m.whi << 32) | m.wlo, lane, in.rv, in.rtail);
-    const uint32_t nch = (m.bits + kChunkBits - 1) / kChunkBits;
+    const bool ok = want && (m.b0bad & 0x100u) == 0 && m.bits != 0;
+    const uint64_t W0 = ok ? (((uint64_t)m.whi << 32) | m.wlo) : 0ull;
+    rows_load(T.stream, W0, lane, in.rv, in.rtail);
+    const uint32_t sv = ok ? s : 0u;
+    const uint32_t svn = sv + 1 < T.nsegs ? sv + 1 : sv;
+    in.gap = T.gaps[(uint64_t)sv * kSegChunks + lane];
+    in.gapn = T.gaps[(uint64_t)svn * kSegChunks];
+    const uint32_t nch = ok ? (m.bits + kChunkBits - 1) / kChunkBits : 0u;
     const uint32_t ch = m.j * kSegChunks + lane;
-    if (ch < nch) in.gap = T.gaps[(uint64_t)s * kSegChunks + lane];
-    if (lane == kWave - 1 && ch + 1 < nch) in.gapn = T.gaps[(uint64_t)(s + 1) * kSegChunks];
+    in.real = (ch < nch ? 1u : 0u) | (ch + 1 < nch ? 2u : 0u);
 }
 
 // ---- one segment per wavefront ------------------------------------------------
@@ -573,13 +602,14 @@ __device__ __forceinline__ void issue_seg(const DecTensor &T, uint32_t s, const 
         ent[slot] = hi_ | (extra);                                                       \
     } while (0)
 
-// Decode segment s, whose stream words are already in this wavefront's LDS rows.
-// `in` holds its gap bytes; the next segment's loads are issued into `in` and, once
-// this segment no longer reads its rows, stored to them (`next_pending` cleared).
+// Decode segment s, whose stream words and gap bytes are already in this
+// wavefront's LDS rows.  The next segment's loads are issued into `in` (when
+// has_next) and, once this segment no longer reads its rows, stored to them;
+// returns whether that store was made.
 template <int DT>
-__device__ __forceinline__ void decode_segment_body(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *sw,
+__device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *sw,
                                                     uint32_t s, const SegMeta &m, SegIn &in, bool has_next, uint32_t sn,
-                                                    const SegMeta &mn, uint32_t *err, bool &next_pending)
+                                                    const SegMeta &mn, uint32_t *err)
 {
     constexpr uint32_t A = alphabet_of(DT);
     const uint32_t lane = lane_now();
@@ -595,31 +625,33 @@ __device__ __forceinline__ void decode_segment_body(const DecTensor &T, const DT
     void *out_block = reinterpret_cast<uint8_t *>(T.out) + lo * (DT == ZX_BF16 ? 2 : 1);
     const uint32_t sbase = e0 & ~15u;   // 16-aligned element that stage byte 0 stands for
 
-    // the sign/mantissa bytes of this segment's first write batch and the next
-    // segment's words and gaps are requested first; they arrive while this segment
-    // decodes
-    const uint32_t gap = in.gap;
-    uint32_t gap_next = in.gapn;
+    // the next segment's words and gaps, and this segment's sign/mantissa bytes for
+    // its first write batch, are requested first; they arrive while this segment
+    // decodes.  The bytes are requested only on the path that uses them, so that no
+    // path from their request to the next segment skips their use.
+    wave_sync();
+    const uint32_t gap = sw[kGapSlot * kWave + lane];
+    const uint32_t gap_next = sw[kGapSlot * kWave + lane + 1];
+    issue_seg(T, sn, mn, lane, in, has_next);
+    if (bad) { report(err, ZX_E_CORRUPT); return false; }
+    // any 16 readable bytes for loads whose result is not used: the stream always
+    // has at least kStreamPadWords words
+    const uint8_t *dummy = reinterpret_cast<const uint8_t *>(T.stream);
     uint2 smv[kWriteBatch];
     uint32_t smcut;
-    prefetch_sm<DT>(sm_block, bad ? 0 : e0, bad ? 0 : e_end, smv, smcut);
-    if (has_next) issue_seg(T, sn, mn, lane, in);
-    if (bad) { report(err, ZX_E_CORRUPT); return; }
-
     if (bits == 0) {
         const uint32_t d = T.degenerate[T.per_block ? b : 0];
-        if (d >= A || e0 != 0 || e_end != nb) { report(err, ZX_E_CORRUPT); return; }
+        if (d >= A || e0 != 0 || e_end != nb) { report(err, ZX_E_CORRUPT); return false; }
+        prefetch_sm<DT>(sm_block, e0, e_end, dummy, smv, smcut);
+        settle_sm(smv, smcut);
         write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, true, stage_form(A, d), smv, smcut);
-        return;
+        return false;
     }
-    if (!tab.ok) { report(err, ZX_E_CORRUPT); return; }
+    if (!tab.ok) { report(err, ZX_E_CORRUPT); return false; }
+    prefetch_sm<DT>(sm_block, e0, e_end, dummy, smv, smcut);
 
     const uint32_t nch = (bits + kChunkBits - 1) / kChunkBits;
     const uint32_t ch = j * kSegChunks + lane;
-    {
-        const uint32_t gn = __shfl_down(gap, 1, kWave);
-        if (lane != kWave - 1) gap_next = gn;
-    }
     bool work = gap != ZX_NO_GAP;
     bool lane_bad = false;
     if (work && gap >= kMaxLen) { work = false; lane_bad = true; }
@@ -709,7 +741,8 @@ __device__ __forceinline__ void decode_segment_body(const DecTensor &T, const DT
     }
     uint32_t total;
     const uint32_t off = wave_excl_scan(cnt, total);
-    if (any_lane(lane_bad) || e0 + total != e_end) { report(err, ZX_E_CORRUPT); return; }
+    settle_sm(smv, smcut);
+    if (any_lane(lane_bad) || e0 + total != e_end) { report(err, ZX_E_CORRUPT); return false; }
 
     const uint32_t t0 = e0 - sbase;   // stage position of the segment's first element
     if (t0 + total + 3 <= kStageBytes) {
@@ -717,10 +750,7 @@ __device__ __forceinline__ void decode_segment_body(const DecTensor &T, const DT
             // the rows are read no more: the next segment's words go in now, before
             // this segment's stores are in flight (a later wait for them would have
             // to drain those stores too)
-            if (next_pending) {
-                rows_store_in(sw, lane, in);
-                next_pending = false;
-            }
+            rows_store_in(sw, lane, in);
             // ---- replay the entries into the stage: each entry stores its three symbol
             //      bytes and advances by its symbol count (byte stores: unaligned dword
             //      stores to LDS were measured slower).  A lane's last entry may store up
@@ -763,24 +793,29 @@ __device__ __forceinline__ void decode_segment_body(const DecTensor &T, const DT
             } else if (cnt == 1) {
                 a0[0] = (uint8_t)f3;
             }
-        } else {
-            store_generic(tab, col, stage, start, cnt, t0 + off);
+            wave_sync();
+            write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, false, 0, smv, smcut);
+            return true;
         }
+        store_generic(tab, col, stage, start, cnt, t0 + off);
         wave_sync();
         write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, false, 0, smv, smcut);
-        return;
+        return false;
     }
     write_rounds<DT>(tab, col, stage, start, cnt, off, t0, total, out_block, sm_block, sbase, smv);
+    return false;
 }
 #undef ZX_LOOKUP
 
 template <int DT>
 __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *sw, uint32_t s,
-                               const SegMeta &m, SegIn &in, bool has_next, uint32_t sn, const SegMeta &mn, uint32_t *err)
+                               const SegMeta &m, bool has_next, uint32_t sn, const SegMeta &mn, uint32_t *err)
 {
-    bool next_pending = has_next;
-    decode_segment_body<DT>(T, tab, stage, sw, s, m, in, has_next, sn, mn, err, next_pending);
-    if (next_pending) rows_store_in(sw, lane_now(), in);
+    SegIn in;
+    if (!decode_segment_body<DT>(T, tab, stage, sw, s, m, in, has_next, sn, mn, err)) {
+        wave_sync();
+        rows_store_in(sw, lane_now(), in);
+    }
 }
 
 template <int DT>
@@ -801,7 +836,7 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
     const DecTensor &T = batch.t[t];
     const uint32_t lg = g - T.wg_begin;
     const uint32_t tid = threadIdx.x;
-    const uint32_t wave = tid / kWave;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const uint32_t lane = lane_now();
     uint32_t s_begin, s_end;
     if (T.per_block) {
@@ -816,12 +851,12 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
     // the wavefront's segments are s_begin + wave + kDecWaves k, k < nk; lane k holds
     // the descriptor of the k-th (in groups of 64)
     const uint32_t s0 = s_begin + wave;
-    const uint32_t nk = s0 < s_end ? (s_end - s0 + kDecWaves - 1) / kDecWaves : 0;
+    const uint32_t nk = __builtin_amdgcn_readfirstlane(s0 < s_end ? (s_end - s0 + kDecWaves - 1) / kDecWaves : 0);
     SegMeta mine;
     SegIn in;
     if (T.per_block) {
         load_meta(T, s0 + kDecWaves * lane, lane < nk, mine);
-        if (nk) issue_seg(T, s0, meta_at(mine, 0), lane, in);
+        issue_seg(T, s0, meta_at(mine, 0), lane, in, nk != 0);
         Canon &c = *reinterpret_cast<Canon *>(stage_all);
         canon_build(T.lengths + (uint64_t)lg * A, A, c);
         dtab_fill(c, A, tab);
@@ -839,7 +874,7 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
             pc[k] = i < kTabPieces ? src[i] : make_uint4(0, 0, 0, 0);
         }
         load_meta(T, s0 + kDecWaves * lane, lane < nk, mine);
-        if (nk) issue_seg(T, s0, meta_at(mine, 0), lane, in);
+        issue_seg(T, s0, meta_at(mine, 0), lane, in, nk != 0);
 #pragma unroll
         for (uint32_t k = 0; k < kPer; ++k) {
             const uint32_t i = tid + k * kDecThreads;
@@ -848,7 +883,7 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
     }
     uint8_t *stage = stage_all + wave * kStageBytes;
     uint32_t *swords = words_all + wave * kSegWords;
-    if (nk) rows_store_in(swords, lane, in);
+    rows_store_in(swords, lane, in);
     __syncthreads();
     for (uint32_t k = 0; k < nk; ++k) {
         const uint32_t i = k & (kWave - 1);
@@ -856,12 +891,14 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
         const bool has_next = k + 1 < nk && i + 1 < kWave;
         const SegMeta mu = meta_at(mine, i);
         const SegMeta mn = meta_at(mine, has_next ? i + 1 : i);
-        decode_segment<DT>(T, tab, stage, swords, s, mu, in, has_next, s + kDecWaves, mn, err);
+        decode_segment<DT>(T, tab, stage, swords, s, mu, has_next, s + kDecWaves, mn, err);
         if (i == kWave - 1 && k + 1 < nk) {
             // next group of 64 descriptors
             load_meta(T, s + kDecWaves + kDecWaves * lane, k + 1 + lane < nk, mine);
-            issue_seg(T, s + kDecWaves, meta_at(mine, 0), lane, in);
-            rows_store_in(swords, lane, in);
+            SegIn in2;
+            issue_seg(T, s + kDecWaves, meta_at(mine, 0), lane, in2, true);
+            wave_sync();
+            rows_store_in(swords, lane, in2);
         }
     }
 }

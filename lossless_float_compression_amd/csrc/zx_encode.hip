@@ -544,11 +544,14 @@ using namespace zxk;
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Whole 16-byte groups of code words, then kStreamPadWords zero words: a decoder
+// may read one segment's rows (256 words and two more) from any segment start
+// without a bounds check.
 extern "C" uint64_t zx_stream_words(uint64_t total_bits)
 {
     uint64_t w = (total_bits + 31) / 32;
     w = (w + 3) / 4 * 4;
-    return w + 4;
+    return w + kStreamPadWords;
 }
 
 extern "C" zx_status zx_encode_size(zx_dtype dtype, const void *in, uint64_t n, int per_block,

@@ -332,7 +332,7 @@ uint64_t zxo_stream_words(uint64_t total_bits)
 {
     uint64_t w = (total_bits + 31) / 32;
     w = (w + 3) / 4 * 4;
-    return w + 4; /* at least 16 zero bytes after the last code */
+    return w + 260; /* container layout: 260 zero words after the last code word */
 }
 
 void zxo_free(zxo_container *c)

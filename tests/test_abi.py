@@ -37,8 +37,9 @@ def test_library_exports_every_declared_symbol(zx):
 
 
 def test_stream_words_rule(zx):
-    # round_up(ceil(bits/32), 4) + 4
-    for bits, want in [(0, 4), (1, 8), (32, 8), (128, 8), (129, 12), (1000, 36)]:
+    # round_up(ceil(bits/32), 4) + 260 (one segment's rows, 256 + 2 words, and a
+    # multiple of four: a decoder reads a segment's rows from any start unchecked)
+    for bits, want in [(0, 260), (1, 264), (32, 264), (128, 264), (129, 268), (1000, 292)]:
         assert zx.zx_stream_words(bits) == want
 
 
@@ -70,7 +71,7 @@ def test_argument_errors_return_before_any_launch(zx):
     assert lib.zx_decode_block_batch(arr, outs, 17, None, None) == 1
     # per-tensor container without its decode table
     c = zx.zx.zx_container()
-    c.dtype, c.per_block, c.n, c.nsegs, c.total_bits, c.stream_words = 0, 0, 10, 1, 20, 8
+    c.dtype, c.per_block, c.n, c.nsegs, c.total_bits, c.stream_words = 0, 0, 10, 1, 20, 264
     for f in ("lengths", "degenerate", "signmant", "stream", "block_bitoff", "block_seg", "seg_desc", "gaps"):
         setattr(c, f, 0x10000)
     c.dtab = None

@@ -265,7 +265,7 @@ def numpy_container_parts(dtype, x, lengths, per_block):
             sel = L > t
             shift = (L[sel] - 1 - t).astype(np.uint64)
             bits[start[sel] + t] = ((Cd[sel] >> shift) & np.uint64(1)).astype(np.uint8)
-    words_n = ((total + 31) // 32 + 3) // 4 * 4 + 4
+    words_n = ((total + 31) // 32 + 3) // 4 * 4 + 260
     padded = np.zeros(words_n * 32, np.uint8)
     padded[:total] = bits
     by = np.packbits(padded)  # MSB-first bytes
@@ -340,7 +340,7 @@ def test_all_fp8_patterns(orc):
 @pytest.mark.parametrize("dtype", [0, 1])
 def test_empty_and_constant(orc, dtype):
     c = orc.encode(dtype, np.zeros(0, np.uint16 if dtype == 0 else np.uint8))
-    assert c.n == 0 and c.nsegs == 0 and c.stream.size == 4 and not c.stream.any()
+    assert c.n == 0 and c.nsegs == 0 and c.stream.size == 260 and not c.stream.any()
     assert orc.decode(c).size == 0
     for n in (1, 65536, 65537, 300_000):
         x = np.full(n, 0x3F80 if dtype == 0 else 0x38, np.uint16 if dtype == 0 else np.uint8)
