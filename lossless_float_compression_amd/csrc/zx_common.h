@@ -24,8 +24,8 @@ static_assert(kStreamPadWords % 4 == 0 && kStreamPadWords >= kSegBits / 32 + 2 +
 constexpr int kWave = 64;
 
 // Decode lookup table index width: the primary table maps the next kLutBits
-// stream bits to up to three symbols.
-constexpr int kLutBits = 10;
+// stream bits to up to four symbols.
+constexpr int kLutBits = 11;
 constexpr uint32_t kLutSize = 1u << kLutBits;
 
 __host__ __device__ constexpr uint32_t alphabet_of(int dtype) { return dtype == ZX_BF16 ? 256u : 16u; }
@@ -167,20 +167,22 @@ __host__ __device__ constexpr uint32_t stage_form(uint32_t A, uint32_t e)
 
 // Decoder tables kept in LDS.  For every value x of the next kLutBits stream bits:
 //   lo[x]  bits  0..3   bits taken by the whole codes that fit in the window (adv)
-//          bits 16..23  number of those codes, at most three (ns)
+//          bits  8..11  length of the first three codes together (0 if fewer)
+//          bits 16..23  number of those codes, at most four (ns)
 //          bits 24..27  length of the first code
 //          bits 28..31  length of the first two codes together
 //          lo[x] == 0   the first code is longer than the window
-//   hi[x]  bytes 0..2   stage forms of the decoded symbols, in stream order
-//          byte  3      ns again
+//   hi[x]  bytes 0..3   stage forms of the decoded symbols, in stream order
 // The fields of lo are placed so that a lane can keep its bit position in the low
 // byte and its code count in bits 16..23 of one register and subtract whole entries
-// from it, and so that the low five bits of lo are exactly the shift that consumes
-// the entry from a 32-bit window.  Entry kLutSize is all zero.
+// from it (bits 8..15 of that register start at 255 and absorb the third-code
+// field of up to 23 entries without a borrow), and so that the low five bits of lo
+// are exactly the shift that consumes the entry from a 32-bit window.  Entry
+// kLutSize is all zero.
 //   lim/base/sym: canonical description for codes longer than the window.
 //   lim_short: the largest left-justified 32-bit window that starts with a code of at
 //   most kLutBits bits (canonical codes of length <= L fill [0, lim[L]) in order).
-constexpr uint32_t kLutSymMax = 3;
+constexpr uint32_t kLutSymMax = 4;
 
 struct __align__(16) DTab {
     uint32_t lo[kLutSize + 4];
@@ -215,7 +217,7 @@ __device__ inline void dtab_fill(const Canon &c, uint32_t A, DTab &t)
         uint32_t lo = 0, hi = 0;
         if (c.ok) {
             uint32_t v = x << (32 - kLutBits);   // window, left-justified, zero filled
-            uint32_t used = 0, ns = 0, syms = 0, l1 = 0, l12 = 0;
+            uint32_t used = 0, ns = 0, syms = 0, l1 = 0, l12 = 0, l123 = 0;
             while (ns < kLutSymMax) {
                 // a code is fully inside the window if its length fits in the bits left
                 const uint32_t L = canon_len(c.lim, v, 1);
@@ -226,11 +228,12 @@ __device__ inline void dtab_fill(const Canon &c, uint32_t A, DTab &t)
                 ++ns;
                 if (ns == 1) l1 = used;
                 if (ns == 2) l12 = used;
+                if (ns == 3) l123 = used;
                 v <<= L;
             }
             if (ns) {
-                lo = used | (ns << 16) | (l1 << 24) | (l12 << 28);
-                hi = syms | (ns << 24);
+                lo = used | (l123 << 8) | (ns << 16) | (l1 << 24) | (l12 << 28);
+                hi = syms;
             }
         }
         t.lo[x] = lo;

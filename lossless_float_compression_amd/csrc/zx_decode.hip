@@ -42,9 +42,11 @@ constexpr uint32_t kStageBytes = 3616;         // one byte per output position, 
 // A segment whose exponents do not fit the stage at once (mean code length under
 // about 2.3 bits) is written in rounds of kRoundElems output positions.
 constexpr uint32_t kRoundElems = 3584;
-// Register path: up to kRounds rounds of three lookups per lane.
-constexpr int kRounds = 8;
+// Register path: up to kRounds rounds of three lookups per lane; the symbol counts
+// of the lookups are kept one byte each, four to a register.
+constexpr int kRounds = 7;
 constexpr int kEnt = 3 * kRounds;
+constexpr int kNsRegs = (kEnt + 3) / 4;
 constexpr int kWriteBatch = 7;                 // write-pass pieces per lane whose loads go out together
 // Bit positions within a lane's rows: row r holds bits [32 r, 32 r + 32); row 1 is
 // the word holding the chunk's first bit, so the chunk starts at kPosBase + b0.
@@ -237,7 +239,8 @@ __device__ __forceinline__ uint32_t load_cut_sm(const uint8_t *sm_block, uint32_
 // Sign/mantissa bytes of the first batch of whole pieces of [i_begin, i_end)
 // (piece q = first + lane + 64 k) and of this lane's cut-piece element.  Every load
 // is issued, and nothing else writes its register: a piece (or cut element) the
-// lane does not have reads `dummy` instead, any 16 readable bytes.  (A default
+// lane does not have reads `dummy` instead, any 16 readable bytes (the stream, which
+// has at least kStreamPadWords words).  (A default
 // value written to the register would first wait for the previous segment's load
 // into it, and so, with one counter for loads and stores, for all its stores.)
 template <int DT>
@@ -460,8 +463,9 @@ __device__ void store_generic(const DTab &tab, lds_cu32 *col, uint8_t *stage, ui
 template <int DT>
 __device__ void write_rounds(const DTab &tab, lds_cu32 *col, uint8_t *stage, uint32_t start, uint32_t cnt,
                              uint32_t off, uint32_t t0, uint32_t total, void *out_block, const uint8_t *sm_block,
-                             uint32_t sbase, const uint2 (&none)[kWriteBatch])
+                             uint32_t sbase)
 {
+    const uint2 none[kWriteBatch] = {};
     for (uint32_t r0 = 0; r0 < t0 + total; r0 += kRoundElems) {
         const uint32_t r1 = r0 + kRoundElems;
         uint32_t p = start;
@@ -483,9 +487,10 @@ __device__ void write_rounds(const DTab &tab, lds_cu32 *col, uint8_t *stage, uin
 
 // A segment's descriptor, validated.  Each lane of a wavefront loads the descriptor
 // of one of the wavefront's segments (lane k: its k-th segment), so the dependent
-// loads (segment -> block -> bit offset) are paid once per 64 segments; the values
-// of the segment at hand are then read from that lane.
-struct SegMeta {
+// loads (segment -> block -> bit offset) are paid once per 64 segments.  The
+// descriptors are then kept in LDS (not in registers, which the decode needs) and
+// read back one segment at a time as wavefront-uniform values.
+struct __align__(16) SegMeta {
     uint32_t b;          // block
     uint32_t e0;         // first element, within the block
     uint32_t e_end;      // end element, within the block
@@ -503,6 +508,9 @@ __device__ __forceinline__ void load_meta(const DecTensor &T, uint32_t s, bool v
     if (!valid) return;
     const uint32_t b = T.seg_desc[2 * (uint64_t)s];
     const uint32_t e0 = T.seg_desc[2 * (uint64_t)s + 1];
+    // the next descriptor's first element is requested with this one, before it is
+    // known to be needed (it is when segment s + 1 is in the same block)
+    const uint32_t e0n = T.seg_desc[2 * (uint64_t)(s + 1 < T.nsegs ? s + 1 : s) + 1];
     if (b >= T.nblocks) { m.b0bad = 0x100u; return; }
     const uint64_t G = T.block_bitoff[b];
     const uint64_t Gn = T.block_bitoff[b + 1];
@@ -517,7 +525,7 @@ __device__ __forceinline__ void load_meta(const DecTensor &T, uint32_t s, bool v
         m.b0bad = 0x100u;
         return;
     }
-    const uint32_t e_end = (s + 1 < sbn) ? T.seg_desc[2 * (uint64_t)(s + 1) + 1] : nb;
+    const uint32_t e_end = (s + 1 < sbn) ? e0n : nb;
     if (e0 > e_end || e_end > nb) { m.b0bad = 0x100u; return; }
     const uint64_t W0 = (G >> 5) + (uint64_t)(s - sb) * (kSegBits / 32);
     m.b = b;
@@ -528,6 +536,22 @@ __device__ __forceinline__ void load_meta(const DecTensor &T, uint32_t s, bool v
     m.wlo = (uint32_t)W0;
     m.whi = (uint32_t)(W0 >> 32);
     m.b0bad = (uint32_t)(G & 31);
+}
+
+// Descriptor i of a wavefront's LDS copy, as wavefront-uniform values.
+__device__ __forceinline__ SegMeta meta_get(const SegMeta *ms, uint32_t i)
+{
+    const SegMeta v = ms[i];   // one address for the whole wavefront
+    SegMeta u;
+    u.b = __builtin_amdgcn_readfirstlane(v.b);
+    u.e0 = __builtin_amdgcn_readfirstlane(v.e0);
+    u.e_end = __builtin_amdgcn_readfirstlane(v.e_end);
+    u.bits = __builtin_amdgcn_readfirstlane(v.bits);
+    u.j = __builtin_amdgcn_readfirstlane(v.j);
+    u.wlo = __builtin_amdgcn_readfirstlane(v.wlo);
+    u.whi = __builtin_amdgcn_readfirstlane(v.whi);
+    u.b0bad = __builtin_amdgcn_readfirstlane(v.b0bad);
+    return u;
 }
 
 // Descriptor held by lane i, as wavefront-uniform values.
@@ -558,7 +582,8 @@ struct SegIn {
     uint32_t rtail;
     uint32_t gap;
     uint32_t gapn;
-    uint32_t real;       // bit 0: `gap` is a chunk's, bit 1: `gapn` is
+    uint32_t nch;        // the segment's block has nch chunks and the segment's
+    uint32_t ch0;        // first is chunk ch0 (wavefront-uniform values)
 };
 
 // Put a segment's requested words and gap bytes into the wavefront's LDS rows.
@@ -566,8 +591,9 @@ __device__ __forceinline__ void rows_store_in(uint32_t *sw, uint32_t lane, const
 {
     asm volatile("" ::"v"(in.rtail), "v"(in.gapn));
     rows_store(sw, lane, in.rv, in.rtail);
-    sw[kGapSlot * kWave + lane] = (in.real & 1u) ? in.gap : (uint32_t)ZX_NO_GAP;
-    if (lane == kWave - 1) sw[kGapSlot * kWave + kWave] = (in.real & 2u) ? in.gapn : (uint32_t)ZX_NO_GAP;
+    const uint32_t ch = in.ch0 + lane;
+    sw[kGapSlot * kWave + lane] = ch < in.nch ? in.gap : (uint32_t)ZX_NO_GAP;
+    if (lane == kWave - 1) sw[kGapSlot * kWave + kWave] = ch + 1 < in.nch ? in.gapn : (uint32_t)ZX_NO_GAP;
 }
 
 // Request segment s; unless `want` (and a valid descriptor) the loads read the
@@ -582,24 +608,35 @@ __device__ __forceinline__ void issue_seg(const DecTensor &T, uint32_t s, const 
     const uint32_t svn = sv + 1 < T.nsegs ? sv + 1 : sv;
     in.gap = T.gaps[(uint64_t)sv * kSegChunks + lane];
     in.gapn = T.gaps[(uint64_t)svn * kSegChunks];
-    const uint32_t nch = ok ? (m.bits + kChunkBits - 1) / kChunkBits : 0u;
-    const uint32_t ch = m.j * kSegChunks + lane;
-    in.real = (ch < nch ? 1u : 0u) | (ch + 1 < nch ? 2u : 0u);
+    in.nch = ok ? (m.bits + kChunkBits - 1) / kChunkBits : 0u;
+    in.ch0 = m.j * kSegChunks;
 }
 
 // ---- one segment per wavefront ------------------------------------------------
 
+// Byte selector that puts byte 2 of the first v_perm operand into byte j and keeps
+// the second operand's other bytes.
+__host__ __device__ constexpr uint32_t ns_sel(int j)
+{
+    return j == 0 ? 0x03020106u : j == 1 ? 0x03020600u : j == 2 ? 0x03060100u : 0x06020100u;
+}
+// Symbol count of lookup k, from the packed count bytes.
+#define ZX_NS(k) ((nsb[(k) >> 2] >> (8 * ((k) & 3))) & 0xFFu)
+
 // One table lookup at the front of `win` for the lanes in `a`; the others read the
-// zero entry and keep their state.
-#define ZX_LOOKUP(a, slot, extra)                                                        \
+// zero entry and keep their state.  `xsym` and `xns` add a symbol decoded before
+// the lookup (a long code in slot 0) to the entry and to its count.
+#define ZX_LOOKUP(a, slot, xsym, xns)                                                    \
     do {                                                                                 \
-        const uint32_t x_ = (a) ? ((win >> 20) & 0xFFCu) : (kLutSize * 4u);              \
+        const uint32_t x_ = (a) ? ((win >> (30 - kLutBits)) & ((kLutSize - 1u) << 2))    \
+                                : (kLutSize * 4u);                                       \
         const uint32_t lo_ = lds_word(tab.lo, x_);                                       \
         const uint32_t hi_ = lds_word(tab.hi, x_);                                       \
         win <<= (lo_ & 31u);                                                             \
         Bprev = (a) ? B : Bprev;                                                         \
         B -= lo_;                                                                        \
-        ent[slot] = hi_ | (extra);                                                       \
+        ent[slot] = hi_ | (xsym);                                                        \
+        nsb[(slot) >> 2] = __builtin_amdgcn_perm(lo_ | (xns), nsb[(slot) >> 2], ns_sel((slot) & 3)); \
     } while (0)
 
 // Decode segment s, whose stream words and gap bytes are already in this
@@ -634,21 +671,17 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     const uint32_t gap_next = sw[kGapSlot * kWave + lane + 1];
     issue_seg(T, sn, mn, lane, in, has_next);
     if (bad) { report(err, ZX_E_CORRUPT); return false; }
-    // any 16 readable bytes for loads whose result is not used: the stream always
-    // has at least kStreamPadWords words
-    const uint8_t *dummy = reinterpret_cast<const uint8_t *>(T.stream);
-    uint2 smv[kWriteBatch];
-    uint32_t smcut;
     if (bits == 0) {
         const uint32_t d = T.degenerate[T.per_block ? b : 0];
         if (d >= A || e0 != 0 || e_end != nb) { report(err, ZX_E_CORRUPT); return false; }
-        prefetch_sm<DT>(sm_block, e0, e_end, dummy, smv, smcut);
+        uint2 smv[kWriteBatch];
+        uint32_t smcut;
+        prefetch_sm<DT>(sm_block, e0, e_end, reinterpret_cast<const uint8_t *>(T.stream), smv, smcut);
         settle_sm(smv, smcut);
         write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, true, stage_form(A, d), smv, smcut);
         return false;
     }
     if (!tab.ok) { report(err, ZX_E_CORRUPT); return false; }
-    prefetch_sm<DT>(sm_block, e0, e_end, dummy, smv, smcut);
 
     const uint32_t nch = (bits + kChunkBits - 1) / kChunkBits;
     const uint32_t ch = j * kSegChunks + lane;
@@ -666,12 +699,13 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     lds_cu32 *col = window_col(sw, lane);
     const uint32_t start = kPosBase + b0 + gap;
     const uint32_t lim = kPosBase + b0 + cend;
-    // B: low byte 256 - position, bits 16..23 minus the code count; a lane is active
-    // while its position is below lim, i.e. while B's low byte exceeds thr
-    // (a lane without a chunk, or one found damaged, gets thr = 255: never active)
+    // B: low byte 256 - position, bits 8..15 absorb the entries' third-code field,
+    // bits 16..23 minus the code count; a lane is active while its position is below
+    // lim, i.e. while B's low byte exceeds thr (a lane without a chunk, or one found
+    // damaged, gets thr = 255: never active)
     uint32_t thr = work ? 256u - lim : 255u;
     constexpr uint32_t kIdleQ = 256u - kPosBase;   // a harmless window for idle lanes
-    uint32_t B = work ? 256u - start : kIdleQ;
+    uint32_t B = 0xFF00u | (work ? 256u - start : kIdleQ);
     uint32_t Bprev = B;
     const uint32_t lim_short = tab.lim_short;
 
@@ -679,16 +713,20 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     // entries of rounds that do not run are never read: the replay stops once no lane
     // has symbols left
     uint32_t ent[kEnt];
+    uint32_t nsb[kNsRegs];
 #pragma unroll
     for (int k = 0; k < kEnt; ++k) ent[k] = __builtin_nondeterministic_value(0u);
+#pragma unroll
+    for (int k = 0; k < kNsRegs; ++k) nsb[k] = __builtin_nondeterministic_value(0u);
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
         bool act = (B & 0xFFu) > thr;
         const uint64_t am = __builtin_amdgcn_ballot_w64(act);
         if (am == 0) break;
         uint32_t win = window(col, B);
+        uint32_t Bw = B;                           // B when win was read
         const bool lng = act && win > lim_short;   // the next code is longer than the table window
-        uint32_t eslow = 0;
+        uint32_t eslow = 0, nslow = 0;
         if ((__builtin_amdgcn_ballot_w64(win > lim_short) & am) != 0) {
             if (lng) {
                 const uint32_t L = slow_len(tab, win);
@@ -697,20 +735,24 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
                     lane_bad = true;
                     act = false;
                 } else {
-                    eslow = slow_sym(tab, win, L) | (1u << 24);
+                    eslow = slow_sym(tab, win, L);
+                    nslow = 1u << 16;
                     Bprev = B;
                     B -= L | (1u << 16);
                     act = (B & 0xFFu) > thr;
                     win = window(col, B);
+                    Bw = B;
                 }
             }
         }
         const bool a0 = act && !lng;   // a long code took slot 0
-        ZX_LOOKUP(a0, 3 * r, eslow);
+        ZX_LOOKUP(a0, 3 * r, eslow, nslow);
         act = act && (B & 0xFFu) > thr;
-        ZX_LOOKUP(act, 3 * r + 1, 0u);
-        act = act && (B & 0xFFu) > thr;
-        ZX_LOOKUP(act, 3 * r + 2, 0u);
+        ZX_LOOKUP(act, 3 * r + 1, 0u, 0u);
+        // the third lookup needs kLutBits valid window bits: two lookups may have
+        // taken up to 2 kLutBits of the 32 (a lane that lacks them waits a round)
+        act = act && (B & 0xFFu) > thr && ((Bw - B) & 0xFFu) + kLutBits <= 32u;
+        ZX_LOOKUP(act, 3 * r + 2, 0u, 0u);
     }
     const bool more = __builtin_amdgcn_ballot_w64((B & 0xFFu) > thr) != 0;
 
@@ -726,9 +768,12 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
             if (ns >= 2 && pl + ((el >> 24) & 0xFu) >= lim) {
                 drop = ns - 1;
                 endp = pl + ((el >> 24) & 0xFu);
-            } else if (ns == 3 && pl + (el >> 28) >= lim) {
-                drop = 1;
+            } else if (ns >= 3 && pl + (el >> 28) >= lim) {
+                drop = ns - 2;
                 endp = pl + (el >> 28);
+            } else if ((el & (4u << 16)) != 0 && pl + ((el >> 8) & 0xFu) >= lim) {   // ns == 4
+                drop = 1;
+                endp = pl + ((el >> 8) & 0xFu);
             }
             cnt = ((0u - (B >> 16)) & 0xFFu) - drop;
             if (endp != expect) lane_bad = true;
@@ -741,71 +786,84 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     }
     uint32_t total;
     const uint32_t off = wave_excl_scan(cnt, total);
-    settle_sm(smv, smcut);
     if (any_lane(lane_bad) || e0 + total != e_end) { report(err, ZX_E_CORRUPT); return false; }
 
     const uint32_t t0 = e0 - sbase;   // stage position of the segment's first element
-    if (t0 + total + 3 <= kStageBytes) {
-        if (!more) {
-            // the rows are read no more: the next segment's words go in now, before
-            // this segment's stores are in flight (a later wait for them would have
-            // to drain those stores too)
-            rows_store_in(sw, lane, in);
-            // ---- replay the entries into the stage: each entry stores its three symbol
-            //      bytes and advances by its symbol count (byte stores: unaligned dword
-            //      stores to LDS were measured slower).  A lane's last entry may store up
-            //      to two bytes past its end, onto the first positions of the lanes after
-            //      it, so after a barrier every lane rewrites its first three positions.
-            // first three symbols: the first entry's, topped up from the entries after it
-            // (a stalled lookup leaves an empty entry; a long code fills one slot)
-            uint32_t f3 = ent[0];
-            uint32_t nf = ent[0] >> 24;
-            const uint32_t need = cnt < 3u ? cnt : 3u;
-#pragma unroll
-            for (int k = 1; k < 7; ++k) {
-                if (__builtin_amdgcn_ballot_w64(nf < need) == 0) break;
-                if (nf < need) {
-                    f3 = (f3 & ((1u << (8 * nf)) - 1u)) | (ent[k] << (8 * nf));
-                    nf += ent[k] >> 24;
-                }
-            }
-            uint8_t *a = stage + t0 + off;
-            uint8_t *const aend = a + cnt;
-#pragma unroll
-            for (int k = 0; k < kEnt; ++k) {
-                if (__builtin_amdgcn_ballot_w64(a < aend) == 0) break;
-                if (a < aend) {
-                    a[0] = (uint8_t)ent[k];
-                    a[1] = (uint8_t)(ent[k] >> 8);
-                    a[2] = (uint8_t)(ent[k] >> 16);
-                    a += ent[k] >> 24;
-                }
-            }
-            wave_sync();
-            uint8_t *const a0 = stage + t0 + off;
-            if (cnt >= 3) {
-                a0[0] = (uint8_t)f3;
-                a0[1] = (uint8_t)(f3 >> 8);
-                a0[2] = (uint8_t)(f3 >> 16);
-            } else if (cnt == 2) {
-                a0[0] = (uint8_t)f3;
-                a0[1] = (uint8_t)(f3 >> 8);
-            } else if (cnt == 1) {
-                a0[0] = (uint8_t)f3;
-            }
-            wave_sync();
-            write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, false, 0, smv, smcut);
-            return true;
-        }
-        store_generic(tab, col, stage, start, cnt, t0 + off);
-        wave_sync();
-        write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, false, 0, smv, smcut);
+    if (t0 + total + 3 > kStageBytes) {
+        write_rounds<DT>(tab, col, stage, start, cnt, off, t0, total, out_block, sm_block, sbase);
         return false;
     }
-    write_rounds<DT>(tab, col, stage, start, cnt, off, t0, total, out_block, sm_block, sbase, smv);
-    return false;
+    // some lane needed more lookups than the registers hold: its symbols go to the
+    // stage one code at a time, and no entry is replayed
+    if (more) store_generic(tab, col, stage, start, cnt, t0 + off);
+    const uint32_t rcnt = more ? 0u : cnt;
+
+    // the rows are read no more: the next segment's words go in now, before this
+    // segment's stores are in flight (a later wait for them would have to drain
+    // those stores too)
+    rows_store_in(sw, lane, in);
+    // the sign/mantissa bytes of the first write batch are requested now: they arrive
+    // during the replay, and their registers are free during the count pass.  From
+    // here to their use below there is no exit, so every path uses them before any
+    // store goes out.
+    uint2 smv[kWriteBatch];
+    uint32_t smcut;
+    prefetch_sm<DT>(sm_block, e0, e_end, reinterpret_cast<const uint8_t *>(T.stream), smv, smcut);
+
+    // ---- replay the entries into the stage: each entry stores its four symbol bytes
+    //      and advances by its symbol count (byte stores: unaligned dword stores to LDS
+    //      stall).  A lane's last entry may store up to three bytes past its end, onto
+    //      the first positions of the lanes after it, so after a barrier every lane
+    //      rewrites its first three positions.
+    // first three symbols: the first entry's, topped up from the entries after it (a
+    // stalled lookup leaves an empty entry; a long code fills one slot; three rounds
+    // hold at least three symbols)
+    uint32_t f3 = ent[0];
+    uint32_t nf = ZX_NS(0);
+    const uint32_t need = rcnt < 3u ? rcnt : 3u;
+#pragma unroll
+    for (int k = 1; k < 7; ++k) {
+        if (__builtin_amdgcn_ballot_w64(nf < need) == 0) break;
+        if (nf < need) {
+            f3 = (f3 & ((1u << (8 * nf)) - 1u)) | (ent[k] << (8 * nf));
+            nf += ZX_NS(k);
+        }
+    }
+    uint8_t *a = stage + t0 + off;
+    uint8_t *const aend = a + rcnt;
+#pragma unroll
+    for (int k = 0; k < kEnt; ++k) {
+        if (__builtin_amdgcn_ballot_w64(a < aend) == 0) break;
+        if (a < aend) {
+            // two pairs of non-adjacent bytes, kept apart: four adjacent byte stores
+            // would be merged into one unaligned dword store
+            a[0] = (uint8_t)ent[k];
+            a[2] = (uint8_t)(ent[k] >> 16);
+            asm volatile("" ::: "memory");
+            a[1] = (uint8_t)(ent[k] >> 8);
+            a[3] = (uint8_t)(ent[k] >> 24);
+            a += ZX_NS(k);
+        }
+    }
+    wave_sync();
+    uint8_t *const a0 = stage + t0 + off;
+    if (rcnt >= 3) {
+        a0[0] = (uint8_t)f3;
+        a0[1] = (uint8_t)(f3 >> 8);
+        a0[2] = (uint8_t)(f3 >> 16);
+    } else if (rcnt == 2) {
+        a0[0] = (uint8_t)f3;
+        a0[1] = (uint8_t)(f3 >> 8);
+    } else if (rcnt == 1) {
+        a0[0] = (uint8_t)f3;
+    }
+    wave_sync();
+    settle_sm(smv, smcut);
+    write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, false, 0, smv, smcut);
+    return true;
 }
 #undef ZX_LOOKUP
+#undef ZX_NS
 
 template <int DT>
 __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *sw, uint32_t s,
@@ -825,8 +883,10 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
     __shared__ DTab tab;
     __shared__ __align__(16) uint8_t stage_all[kDecWaves * kStageBytes];
     __shared__ __align__(16) uint32_t words_all[kDecWaves * kSegWords];
+    __shared__ SegMeta meta_all[kDecWaves * kWave];
     // kDecWgPerCu workgroups share the CU's 160 KB of LDS
-    static_assert(sizeof(DTab) + sizeof(stage_all) + sizeof(words_all) <= 160u * 1024u / kDecWgPerCu - 512u,
+    static_assert(sizeof(DTab) + sizeof(stage_all) + sizeof(words_all) + sizeof(meta_all) <=
+                      160u * 1024u / kDecWgPerCu - 512u,
                   "decode workgroup LDS budget");
     static_assert(sizeof(Canon) <= sizeof(stage_all), "Canon is built inside the stage area");
 
@@ -883,22 +943,27 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
     }
     uint8_t *stage = stage_all + wave * kStageBytes;
     uint32_t *swords = words_all + wave * kSegWords;
+    SegMeta *metas = meta_all + wave * kWave;
     rows_store_in(swords, lane, in);
+    metas[lane] = mine;
     __syncthreads();
     for (uint32_t k = 0; k < nk; ++k) {
         const uint32_t i = k & (kWave - 1);
         const uint32_t s = s0 + kDecWaves * k;
         const bool has_next = k + 1 < nk && i + 1 < kWave;
-        const SegMeta mu = meta_at(mine, i);
-        const SegMeta mn = meta_at(mine, has_next ? i + 1 : i);
+        const SegMeta mu = meta_get(metas, i);
+        const SegMeta mn = meta_get(metas, has_next ? i + 1 : i);
         decode_segment<DT>(T, tab, stage, swords, s, mu, has_next, s + kDecWaves, mn, err);
         if (i == kWave - 1 && k + 1 < nk) {
             // next group of 64 descriptors
-            load_meta(T, s + kDecWaves + kDecWaves * lane, k + 1 + lane < nk, mine);
+            SegMeta m2;
+            load_meta(T, s + kDecWaves + kDecWaves * lane, k + 1 + lane < nk, m2);
             SegIn in2;
-            issue_seg(T, s + kDecWaves, meta_at(mine, 0), lane, in2, true);
+            issue_seg(T, s + kDecWaves, meta_at(m2, 0), lane, in2, true);
             wave_sync();
             rows_store_in(swords, lane, in2);
+            metas[lane] = m2;
+            wave_sync();
         }
     }
 }
