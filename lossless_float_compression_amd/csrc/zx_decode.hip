@@ -298,6 +298,16 @@ __device__ __forceinline__ uint32_t fuse_bf16_pair(uint32_t S, uint32_t E, uint3
 constexpr uint32_t kSelA01 = 0x01050004u, kSelB01 = 0x05010400u;   // elements 0, 1
 constexpr uint32_t kSelA23 = 0x03070206u, kSelB23 = 0x07030602u;   // elements 2, 3
 
+// BF16, four elements at once: bit-select every low byte (exponent bit 0 | mantissa)
+// and every high byte (sign | exponent bits 7..1), then interleave them into the
+// two output words.  Four operations for four elements.
+__device__ __forceinline__ uint2 fuse_bf16_quad(uint32_t S, uint32_t E)
+{
+    const uint32_t lo = (E & 0x80808080u) | (S & 0x7F7F7F7Fu);
+    const uint32_t hi = (S & 0x80808080u) | (E & 0x7F7F7F7Fu);
+    return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
+}
+
 // FP8: four sign|mantissa nibbles N (element k at bits 4k..4k+3) and four staged
 // exponents E3 (already at bits 3..6).  Each output byte is sign << 7 | exp << 3 | mant.
 __device__ __forceinline__ uint32_t fuse_fp8_quad(uint32_t N, uint32_t E3)
@@ -313,10 +323,9 @@ __device__ __forceinline__ uint4 fuse_piece(uint2 smv, uint4 e)
 {
     uint4 r;
     if (DT == ZX_BF16) {
-        r.x = fuse_bf16_pair(smv.x, e.x, kSelA01, kSelB01);
-        r.y = fuse_bf16_pair(smv.x, e.x, kSelA23, kSelB23);
-        r.z = fuse_bf16_pair(smv.y, e.y, kSelA01, kSelB01);
-        r.w = fuse_bf16_pair(smv.y, e.y, kSelA23, kSelB23);
+        const uint2 w01 = fuse_bf16_quad(smv.x, e.x);
+        const uint2 w23 = fuse_bf16_quad(smv.y, e.y);
+        r = make_uint4(w01.x, w01.y, w23.x, w23.y);
     } else {
         r.x = fuse_fp8_quad(smv.x & 0xFFFFu, e.x);
         r.y = fuse_fp8_quad(smv.x >> 16, e.y);
