@@ -44,6 +44,13 @@ def parse():
     p.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--copies", type=int, default=0, help="rotation depth (0 = enough for 1 GiB)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--overlap", action="store_true",
+                   help="c3 only: measure how much per-layer decode hides behind the layer's GEMMs")
+    p.add_argument("--overlap-layers", type=int, default=8)
+    p.add_argument("--overlap-reps", type=int, default=5)
+    p.add_argument("--overlap-batches", type=int, nargs="+", default=[1, 16, 128, 1024, 4096])
+    p.add_argument("--overlap-wgs", type=int, nargs="+", default=[0, 256, 128, 64],
+                   help="caps on the decode's resident workgroups to try (0 = default)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain device copies of 256 MiB (reference for HBM byte counters)")
@@ -262,6 +269,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.overlap and args.config != "c3":
+        print("--overlap applies to --config c3", file=sys.stderr)
+        sys.exit(2)
     if args.config in ("c1", "c2", "c4"):
         res = bench_single(args)
     else:

@@ -165,7 +165,111 @@ def run_c5(args):
     }
 
 
+def run_overlap(args):
+    """Per-layer decode hidden behind the consumer: layer l+1 is decoded on a side
+    stream into the other of two scratch buffer sets while the 7 GEMMs of layer l
+    (y = x W^T, x of `batch` tokens, BF16) run on the main stream.  For each batch
+    size: decode alone, GEMMs alone (on decoded weights) and the pipelined loop,
+    per layer, averaged over the layers after the first."""
+    from lossless_float_compression_amd.pipeline import LayerPipeline
+    n_layers = args.overlap_layers
+    per_layer = len(workloads.C3_SHAPES)
+    comps, raw_layer = [], 0
+    for i in range(n_layers * per_layer):
+        x = workloads.c3_tensor(i)
+        if i < per_layer:
+            raw_layer += x.numel() * 2
+        comps.append(zx.compress(x))
+        del x
+    layers = [comps[l * per_layer:(l + 1) * per_layer] for l in range(n_layers)]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pipe = LayerPipeline(layers, depth=2, err=err)
+    main = torch.cuda.current_stream()
+    shapes = list(workloads.C3_SHAPES.values())
+    results = []
+    for batch in args.overlap_batches:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(7_000_000 + batch)
+        xs = [torch.randn((batch, shp[1]), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+              for shp in shapes]
+        ys = [torch.empty((batch, shp[0]), device="cuda", dtype=torch.bfloat16) for shp in shapes]
+
+        def consumer(l, w):
+            for j in range(per_layer):
+                torch.matmul(xs[j], w[j].view(torch.bfloat16).t(), out=ys[j])
+
+        def timed(fn):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = _events(2)
+            e0.record(main)
+            for _ in range(args.overlap_reps):
+                fn()
+            e1.record(main)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.overlap_reps / n_layers
+
+        def decode_only():
+            for l in range(n_layers):
+                pipe.start(l)
+                pipe.acquire(l, main)
+                pipe.release(l, main)
+
+        dec = [pipe.bufs[0]]
+        pipe.start(0)
+        dec_w = pipe.acquire(0, main)
+        pipe.release(0, main)
+
+        def gemm_only():
+            for l in range(n_layers):
+                consumer(l, dec_w)
+
+        def pipelined():
+            pipe.run(consumer, main)
+
+        pipe.max_workgroups = 0
+        t_dec = timed(decode_only)
+        t_mm = timed(gemm_only)
+        flops = 2.0 * batch * sum(o * i for o, i in shapes)
+        row = {"batch": batch, "decode_ms": round(t_dec, 4), "gemm_ms": round(t_mm, 4),
+               "gemm_TFLOPs": round(flops / (t_mm * 1e-3) / 1e12, 1), "pipelined": []}
+        for wgs in args.overlap_wgs:
+            pipe.max_workgroups = wgs
+            t_pipe = timed(pipelined)
+            # the share of the (uncapped) decode time that no longer adds to the layer time
+            hidden = (t_dec + t_mm - t_pipe) / t_dec if t_dec > 0 else 0.0
+            row["pipelined"].append({"decode_workgroups": wgs or "default (2 per CU)", "ms": round(t_pipe, 4),
+                                     "hidden_frac": round(hidden, 3)})
+        pipe.max_workgroups = 0
+        row["hidden_frac"] = max(p["hidden_frac"] for p in row["pipelined"])
+        results.append(row)
+        del xs, ys, dec
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    # the pipeline's buffers after a run hold the last two layers: compare them
+    for l in (n_layers - 2, n_layers - 1):
+        pipe.start(l)
+        w = pipe.acquire(l, main)
+        for j in range(per_layer):
+            assert torch.equal(w[j].view(torch.int16), workloads.c3_tensor(l * per_layer + j)), "pipeline decode mismatch"
+        pipe.release(l, main)
+    torch.cuda.synchronize()
+    return {
+        "metric": "per-layer decode hidden behind the consumer GEMMs (decode of layer l+1 on a second stream "
+                  "into double-buffered scratch while layer l multiplies)",
+        "value": results[-1]["hidden_frac"], "unit": "fraction of decode time hidden", "n_gpus": 1,
+        "steps": args.overlap_reps, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"c3 layers 0..{n_layers - 1}: 7 GEMMs per layer, y = x W^T",
+                   "layer_raw_bytes": int(raw_layer), "batches": list(args.overlap_batches)},
+        "results": results,
+    }
+
+
 def run(args):
+    if getattr(args, "overlap", False):
+        return run_overlap(args)
     if args.config == "c3":
         return run_c3(args)
     return run_c5(args)

@@ -176,6 +176,15 @@ zx_status zx_decode(const zx_container *c, void *out, uint32_t *err, hipStream_t
 zx_status zx_decode_block_batch(const zx_container *cs, void *const *outs, uint32_t count,
                                 uint32_t *err, hipStream_t stream);
 
+/* zx_decode_block_batch with the per-tensor-codebook decode spread over at most
+ * max_workgroups resident workgroups (0: two per CU, as zx_decode_block_batch).  For
+ * decoding the next layer while the current layer's GEMMs run on another stream
+ * (DFloat11 article, 方法介绍: block-level decode into a temporary buffer): fewer
+ * decode workgroups leave CUs, and their LDS, to the GEMM.  Containers with
+ * per-block codebooks still take one workgroup per block. */
+zx_status zx_decode_block_batch_wg(const zx_container *cs, void *const *outs, uint32_t count,
+                                   uint32_t max_workgroups, uint32_t *err, hipStream_t stream);
+
 /* Stream length in u32 words for a given number of code bits. */
 uint64_t zx_stream_words(uint64_t total_bits);
 const char *zx_status_string(zx_status s);

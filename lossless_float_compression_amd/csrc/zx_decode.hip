@@ -1018,8 +1018,8 @@ static zx_status check_container(const zx_container *c, const void *out)
     return ZX_OK;
 }
 
-extern "C" zx_status zx_decode_block_batch(const zx_container *cs, void *const *outs, uint32_t count, uint32_t *err,
-                                           hipStream_t stream)
+extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *const *outs, uint32_t count,
+                                              uint32_t max_workgroups, uint32_t *err, hipStream_t stream)
 {
     if (count == 0) return ZX_OK;
     if (!cs || !outs || count > (uint32_t)kMaxBatch) return ZX_E_INVAL;
@@ -1032,7 +1032,8 @@ extern "C" zx_status zx_decode_block_batch(const zx_container *cs, void *const *
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    const uint64_t slots = (uint64_t)cus * kDecWgPerCu;   // resident 512-thread workgroups per CU
+    uint64_t slots = (uint64_t)cus * kDecWgPerCu;   // resident 512-thread workgroups per CU
+    if (max_workgroups != 0 && max_workgroups < slots) slots = max_workgroups;
     uint64_t seg_total = 0;
     for (uint32_t i = 0; i < count; ++i)
         if (!cs[i].per_block) seg_total += cs[i].nsegs;
@@ -1085,9 +1086,15 @@ extern "C" zx_status zx_decode_block_batch(const zx_container *cs, void *const *
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
 }
 
+extern "C" zx_status zx_decode_block_batch(const zx_container *cs, void *const *outs, uint32_t count, uint32_t *err,
+                                           hipStream_t stream)
+{
+    return zx_decode_block_batch_wg(cs, outs, count, 0, err, stream);
+}
+
 extern "C" zx_status zx_decode(const zx_container *c, void *out, uint32_t *err, hipStream_t stream)
 {
-    return zx_decode_block_batch(c, &out, 1, err, stream);
+    return zx_decode_block_batch_wg(c, &out, 1, 0, err, stream);
 }
 
 extern "C" const char *zx_status_string(zx_status s)

@@ -48,7 +48,7 @@ class zx_container(C.Structure):
 
 
 EXPORTS = ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
-           "zx_decode_table_bytes", "zx_decode", "zx_decode_block_batch", "zx_stream_words",
+           "zx_decode_table_bytes", "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_stream_words",
            "zx_status_string", "zx_version")
 
 
@@ -70,13 +70,14 @@ def lib():
         L.zx_decode_table_bytes.restype = C.c_size_t
         L.zx_decode.argtypes = [C.POINTER(zx_container), P, P, P]
         L.zx_decode_block_batch.argtypes = [C.POINTER(zx_container), C.POINTER(C.c_void_p), U32, P, P]
+        L.zx_decode_block_batch_wg.argtypes = [C.POINTER(zx_container), C.POINTER(C.c_void_p), U32, U32, P, P]
         L.zx_stream_words.argtypes = [U64]
         L.zx_stream_words.restype = U64
         L.zx_status_string.argtypes = [I]
         L.zx_status_string.restype = C.c_char_p
         L.zx_version.restype = C.c_char_p
         for f in ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
-                  "zx_decode", "zx_decode_block_batch"):
+                  "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -143,11 +144,16 @@ def zx_decode(container: zx_container, out, err=None, stream=None):
     _check("zx_decode", lib().zx_decode(C.byref(container), _ptr(out), _ptr(err), _stream(stream)))
 
 
-def zx_decode_block_batch(containers: Sequence[zx_container], outs: Sequence[torch.Tensor], err=None, stream=None):
+def zx_decode_block_batch(containers: Sequence[zx_container], outs: Sequence[torch.Tensor], err=None, stream=None,
+                          max_workgroups: int = 0):
     k = len(containers)
     arr = (zx_container * k)(*containers)
     optrs = (C.c_void_p * k)(*[o.data_ptr() for o in outs])
-    _check("zx_decode_block_batch", lib().zx_decode_block_batch(arr, optrs, k, _ptr(err), _stream(stream)))
+    if max_workgroups:
+        _check("zx_decode_block_batch_wg",
+               lib().zx_decode_block_batch_wg(arr, optrs, k, int(max_workgroups), _ptr(err), _stream(stream)))
+    else:
+        _check("zx_decode_block_batch", lib().zx_decode_block_batch(arr, optrs, k, _ptr(err), _stream(stream)))
 
 
 # ----------------------------------------------------------------- compressed tensor

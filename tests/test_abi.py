@@ -25,7 +25,8 @@ def zx():
 def test_header_lists_the_api():
     names = declared_functions()
     for f in ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
-              "zx_decode", "zx_decode_block_batch", "zx_stream_words", "zx_status_string", "zx_version"):
+              "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_stream_words", "zx_status_string",
+              "zx_version"):
         assert f in names
 
 
