@@ -7,14 +7,25 @@
 // length-limited code by package-merge (coin-collector form), leaves before
 // packages on weight ties.
 //
-// The wavefront sorts the present symbols in parallel; the merges themselves are a
-// chain of dependent steps and run on one lane.  Per-block scope launches one
+// The wavefront sorts the present symbols in parallel.  The Huffman merge is a chain
+// of dependent steps: with up to 64 present symbols it runs in registers (lane i
+// holds leaf i and internal node i, queue heads are read across lanes) and the
+// depths come from pointer jumping; larger alphabets and package-merge run on one
+// lane over LDS.  Per-block scope launches one
 // workgroup per block, so thousands of codebooks are built at once.
 #include "zx_common.h"
 
 namespace zxk {
 
 constexpr uint32_t kPmWords = 16;  // 512 bits: one flag per merged-list item
+
+// 64-bit value held by lane i (i wavefront-uniform).
+__device__ __forceinline__ uint64_t read_u64(uint64_t v, uint32_t i)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, i);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), i);
+    return ((uint64_t)hi << 32) | lo;
+}
 
 template <int DT>
 __global__ __launch_bounds__(64) void k_codebook(const uint32_t *__restrict__ hist, uint32_t max_len,
@@ -56,21 +67,70 @@ __global__ __launch_bounds__(64) void k_codebook(const uint32_t *__restrict__ hi
         if (lane == 0) degenerate[cb] = (k == 1) ? present[0] : (uint16_t)ZX_NO_DEGENERATE;
         return;
     }
-    // leaves ordered by (count, symbol): each present symbol's rank
+    // leaves ordered by (count, symbol): each present symbol's rank, comparing packed
+    // keys count << 16 | symbol (distinct, so the ranks are a permutation)
+    uint64_t *key = pm_a;    // free until package-merge
     for (uint32_t i = lane; i < k; i += kWave) {
         const uint32_t s = present[i];
-        const uint32_t c = cnt[s];
-        uint32_t r = 0;
-        for (uint32_t j = 0; j < k; ++j) {
-            const uint32_t t = present[j];
-            const uint32_t ct = cnt[t];
-            r += (ct < c || (ct == c && t < s)) ? 1u : 0u;
-        }
-        leaf_sym[r] = (uint16_t)s;
-        w[r] = c;
+        key[i] = ((uint64_t)cnt[s] << 16) | s;
     }
     __syncthreads();
-    if (lane == 0) {
+    for (uint32_t i = lane; i < k; i += kWave) {
+        const uint64_t mine = key[i];
+        uint32_t r = 0;
+        for (uint32_t j = 0; j < k; ++j) r += key[j] < mine ? 1u : 0u;
+        leaf_sym[r] = (uint16_t)(mine & 0xFFFFu);
+        w[r] = mine >> 16;
+    }
+    __syncthreads();
+    if (k <= kWave) {
+        // ---- register path (up to 64 leaves, e.g. every FP8 code and most BF16 ones):
+        // lane i holds leaf i's weight and, once it is made, internal node i's; the
+        // queue heads are read with readlane, so a merge step touches no memory
+        const uint64_t lw = lane < k ? w[lane] : ~0ull;
+        uint64_t nw = ~0ull;               // weight of internal node `lane`
+        uint32_t lpar = 0, npar = 0;       // parent (internal node index) of leaf / node `lane`
+        uint32_t q1 = 0, q2 = 0, made = 0;
+        for (uint32_t step = 0; step + 1 < k; ++step) {
+            uint64_t val[2];
+            for (int t = 0; t < 2; ++t) {
+                const uint64_t a = q1 < k ? read_u64(lw, q1) : ~0ull;
+                const uint64_t b = q2 < made ? read_u64(nw, q2) : ~0ull;
+                // the leaf queue wins weight ties
+                const bool take_leaf = q1 < k && (q2 >= made || a <= b);
+                if (take_leaf) {
+                    if (lane == q1) lpar = made;
+                    val[t] = a;
+                    ++q1;
+                } else {
+                    if (lane == q2) npar = made;
+                    val[t] = b;
+                    ++q2;
+                }
+            }
+            if (lane == made) nw = val[0] + val[1];
+            ++made;
+        }
+        // depths by pointer jumping: each internal node's distance to the root (the
+        // last node made, its own parent at distance 0), then one more hop for leaves
+        const uint32_t root = made - 1;
+        uint32_t dn = lane < root ? 1u : 0u;
+        uint32_t pn = lane < root ? npar : root;
+        for (int it = 0; it < 6; ++it) {
+            const uint32_t dpn = (uint32_t)__shfl((int)dn, (int)pn, kWave);
+            const uint32_t ppn = (uint32_t)__shfl((int)pn, (int)pn, kWave);
+            dn += dpn;
+            pn = ppn;
+        }
+        const uint32_t dleaf = (uint32_t)__shfl((int)dn, (int)lpar, kWave) + 1u;
+        uint32_t maxd = lane < k ? dleaf : 0u;
+        for (int o = 32; o >= 1; o >>= 1) {
+            const uint32_t y = (uint32_t)__shfl_xor((int)maxd, o, kWave);
+            maxd = y > maxd ? y : maxd;
+        }
+        if (lane < k) depth[lane] = (uint8_t)dleaf;
+        if (lane == 0) s_maxd = maxd;
+    } else if (lane == 0) {
         // two queues: leaves [q1, k), merged nodes [q2, made)
         uint32_t q1 = 0, q2 = k, made = k;
         for (uint32_t step = 0; step + 1 < k; ++step) {

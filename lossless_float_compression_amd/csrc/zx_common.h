@@ -73,23 +73,34 @@ struct Canon {
     uint32_t ok;                        // 1 if the lengths form a complete prefix code
 };
 
-// Build `c` from lengths_g[0..A).  Every thread of the workgroup must call it;
-// blockDim.x must be a multiple of 64, >= A and <= 1024.
-__device__ inline void canon_build(const uint8_t *__restrict__ lengths_g, uint32_t A, Canon &c)
+// Build `c` from the code lengths of symbols 0..A-1, thread t holding symbol t's
+// length in `l` (threads t >= A pass anything).  Every thread of the workgroup must
+// call it; blockDim.x must be a multiple of 64, >= A and <= 1024.
+__device__ inline void canon_build_from(uint32_t l, uint32_t A, Canon &c)
 {
     const uint32_t tid = threadIdx.x;
     const uint32_t wave = tid / kWave;
-    const uint32_t nwaves = blockDim.x / kWave;
-    uint32_t l = 0;
-    if (tid < A) l = lengths_g[tid];
+    const uint32_t nsw = (A + kWave - 1) / kWave;   // waves that hold symbols
+    if (tid >= A) l = 0;
     if (tid < A) c.len[tid] = (uint8_t)l;
-    // per-wave count and in-wave rank of each symbol among symbols of its length
+    // per-wave count and in-wave rank of each symbol among symbols of its length,
+    // for the lengths up to the wave's longest (the counts above it are zero)
     uint32_t rank = 0;
-    const uint64_t lt = lanemask_lt();
-    for (uint32_t L = 1; L <= kMaxLen; ++L) {
-        uint64_t m = __ballot(tid < A && l == L);
-        if (l == L) rank = (uint32_t)__popcll(m & lt);
-        if (lane_id() == 0) c.wcnt[wave][L] = (uint32_t)__popcll(m);
+    if (wave < nsw) {
+        uint32_t mx = l;
+        for (int o = kWave / 2; o >= 1; o >>= 1) {
+            const uint32_t y = (uint32_t)__shfl_xor((int)mx, o, kWave);
+            mx = y > mx ? y : mx;
+        }
+        mx = __builtin_amdgcn_readfirstlane(mx);
+        const uint64_t lt = lanemask_lt();
+        for (uint32_t L = 1; L <= mx; ++L) {
+            const uint64_t m = __ballot(l == L);
+            if (l == L) rank = (uint32_t)__popcll(m & lt);
+            if (lane_id() == 0) c.wcnt[wave][L] = (uint32_t)__popcll(m);
+        }
+        const uint32_t L = lane_id();
+        if (L > mx && L <= kMaxLen) c.wcnt[wave][L] = 0;
     }
     __syncthreads();
     if (wave == 0) {
@@ -101,7 +112,7 @@ __device__ inline void canon_build(const uint8_t *__restrict__ lengths_g, uint32
         const bool isl = L >= 1 && L <= kMaxLen;
         uint32_t cnt = 0;
         if (isl)
-            for (uint32_t w = 0; w < nwaves; ++w) cnt += c.wcnt[w][L];
+            for (uint32_t w = 0; w < nsw; ++w) cnt += c.wcnt[w][L];
         uint32_t nsym;
         const uint32_t idx = wave_excl_scan(cnt, nsym);
         const uint64_t t = isl ? (uint64_t)cnt << (kMaxLen - L) : 0ull;
@@ -143,6 +154,12 @@ __device__ inline void canon_build(const uint8_t *__restrict__ lengths_g, uint32
         c.code[tid] = code;
     }
     __syncthreads();
+}
+
+__device__ inline void canon_build(const uint8_t *__restrict__ lengths_g, uint32_t A, Canon &c)
+{
+    const uint32_t tid = threadIdx.x;
+    canon_build_from(tid < A ? lengths_g[tid] : 0u, A, c);
 }
 
 // Length of the code at the front of a left-justified 32-bit window, searching
@@ -198,8 +215,15 @@ struct __align__(16) DTab {
 };
 static_assert(sizeof(DTab) % 16 == 0, "DTab must copy in 16-byte pieces");
 
-// Fill a DTab for alphabet size A from a built Canon; every thread of the workgroup calls it.
-__device__ inline void dtab_fill(const Canon &c, uint32_t A, DTab &t)
+// Fill a DTab for alphabet size A from a built Canon; every thread of the workgroup
+// calls it.  `t1` is LDS scratch of kLutSize entries: first the code at the front of
+// every kLutBits-bit window (its length, and its symbol's stage form in the high
+// byte; 0 when that code is longer than the window), then each entry of the table
+// chains up to four lookups of it.  Shifting a window left by the bits already used
+// fills it with zeros, and a code no longer than the bits left is decided by real
+// bits alone (codes are prefix-free), so the chained lookups read the same codes as
+// a search of the shifted window would.
+__device__ inline void dtab_fill(const Canon &c, uint32_t A, DTab &t, uint16_t *t1)
 {
     const uint32_t tid = threadIdx.x;
     for (uint32_t i = tid; i < kMaxLen + 2; i += blockDim.x) t.lim[i] = (i == 0) ? 0ull : c.lim[i];
@@ -214,22 +238,31 @@ __device__ inline void dtab_fill(const Canon &c, uint32_t A, DTab &t)
         t.pad_[0] = t.pad_[1] = t.pad_[2] = 0;
     }
     for (uint32_t x = tid; x < kLutSize; x += blockDim.x) {
+        uint32_t e = 0;
+        if (c.ok) {
+            const uint32_t v = x << (32 - kLutBits);   // window, left-justified, zero filled
+            const uint32_t L = canon_len(c.lim, v, 1);
+            if (L <= (uint32_t)kLutBits)
+                e = L | (stage_form(A, c.sym[c.offset[L] + ((v >> (32 - L)) - c.first[L])]) << 8);
+        }
+        t1[x] = (uint16_t)e;
+    }
+    __syncthreads();
+    for (uint32_t x = tid; x < kLutSize; x += blockDim.x) {
         uint32_t lo = 0, hi = 0;
         if (c.ok) {
-            uint32_t v = x << (32 - kLutBits);   // window, left-justified, zero filled
             uint32_t used = 0, ns = 0, syms = 0, l1 = 0, l12 = 0, l123 = 0;
             while (ns < kLutSymMax) {
                 // a code is fully inside the window if its length fits in the bits left
-                const uint32_t L = canon_len(c.lim, v, 1);
-                if (L > kLutBits - used) break;
-                const uint32_t sy = c.sym[c.offset[L] + ((v >> (32 - L)) - c.first[L])];
-                syms |= stage_form(A, sy) << (8 * ns);
+                const uint32_t e = t1[(x << used) & (kLutSize - 1)];
+                const uint32_t L = e & 0xFFu;
+                if (L == 0 || L > kLutBits - used) break;
+                syms |= (e >> 8) << (8 * ns);
                 used += L;
                 ++ns;
                 if (ns == 1) l1 = used;
                 if (ns == 2) l12 = used;
                 if (ns == 3) l123 = used;
-                v <<= L;
             }
             if (ns) {
                 lo = used | (l123 << 8) | (ns << 16) | (l1 << 24) | (l12 << 28);

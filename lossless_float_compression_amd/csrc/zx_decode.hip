@@ -296,7 +296,6 @@ __device__ __forceinline__ uint32_t fuse_bf16_pair(uint32_t S, uint32_t E, uint3
     return (a & 0x80808080u) | (b & 0x7F7F7F7Fu);
 }
 constexpr uint32_t kSelA01 = 0x01050004u, kSelB01 = 0x05010400u;   // elements 0, 1
-constexpr uint32_t kSelA23 = 0x03070206u, kSelB23 = 0x07030602u;   // elements 2, 3
 
 // BF16, four elements at once: bit-select every low byte (exponent bit 0 | mantissa)
 // and every high byte (sign | exponent bits 7..1), then interleave them into the
@@ -927,8 +926,9 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
         load_meta(T, s0 + kDecWaves * lane, lane < nk, mine);
         issue_seg(T, s0, meta_at(mine, 0), lane, in, nk != 0);
         Canon &c = *reinterpret_cast<Canon *>(stage_all);
+        static_assert(sizeof(Canon) % 4 == 0 && sizeof(Canon) + kLutSize * 2 <= kDecWaves * kStageBytes, "table scratch");
         canon_build(T.lengths + (uint64_t)lg * A, A, c);
-        dtab_fill(c, A, tab);
+        dtab_fill(c, A, tab, reinterpret_cast<uint16_t *>(stage_all + sizeof(Canon)));
     } else {
         // the prepared table is requested first, the descriptors next; the table is
         // stored to LDS once it arrives
@@ -980,8 +980,9 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
 __global__ __launch_bounds__(1024) void k_build_dtab(const uint8_t *__restrict__ lengths, uint32_t A, DTab *__restrict__ out)
 {
     __shared__ Canon c;
+    __shared__ uint16_t t1[kLutSize];
     canon_build(lengths, A, c);
-    dtab_fill(c, A, *out);
+    dtab_fill(c, A, *out, t1);
 }
 
 }  // namespace zxk

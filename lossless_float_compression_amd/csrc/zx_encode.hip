@@ -70,52 +70,89 @@ __global__ __launch_bounds__(kSizeThreads) void k_block_bits(const void *__restr
     }
 }
 
-// In-place inclusive scan over [1..nblocks] of both arrays; one workgroup.
+// In-place inclusive scan over [1..nblocks] of both arrays; one workgroup.  The
+// arrays pass through LDS in tiles of 8192 entries: loaded and stored with
+// consecutive threads on consecutive entries, scanned with each thread owning eight
+// consecutive entries (the LDS index is padded by one slot per eight, so those
+// eight-entry runs start on different banks), and a running carry links the tiles.
+constexpr uint32_t kScanPer = 8;
+constexpr uint32_t kScanTile = 1024 * kScanPer;
+__device__ __forceinline__ uint32_t scan_pad(uint32_t i) { return i + (i >> 3); }
+
 __global__ __launch_bounds__(1024) void k_scan_blocks(uint64_t nblocks, uint64_t *__restrict__ block_bitoff,
                                                       uint32_t *__restrict__ block_seg, uint64_t *__restrict__ totals)
 {
+    __shared__ uint64_t tb[kScanTile + kScanTile / 8];
+    __shared__ uint32_t tsg[kScanTile + kScanTile / 8];
     __shared__ uint64_t wb[16];
     __shared__ uint32_t ws[16];
     const uint32_t tid = threadIdx.x;
-    const uint64_t per = (nblocks + 1023) / 1024;
-    const uint64_t lo = 1 + tid * per;
-    const uint64_t hi = (lo + per <= nblocks + 1) ? lo + per : nblocks + 1;
-    uint64_t sb = 0;
-    uint32_t ss = 0;
-    for (uint64_t i = lo; i < hi; ++i) {
-        sb += block_bitoff[i];
-        ss += block_seg[i];
-    }
-    // exclusive scan of (sb, ss) over the workgroup
-    uint64_t xb = sb;
-    uint32_t xs = ss;
     const uint32_t lane = lane_id();
-    for (int d = 1; d < kWave; d <<= 1) {
-        uint64_t yb = __shfl_up(xb, d, kWave);
-        uint32_t ys = __shfl_up(xs, d, kWave);
-        if (lane >= (uint32_t)d) { xb += yb; xs += ys; }
+    const uint32_t wave = tid / kWave;
+    uint64_t carry_b = 0;
+    uint32_t carry_s = 0;
+    for (uint64_t base = 1; base <= nblocks; base += kScanTile) {
+        const uint32_t cnt = (uint32_t)(nblocks + 1 - base < kScanTile ? nblocks + 1 - base : kScanTile);
+#pragma unroll
+        for (uint32_t j = 0; j < kScanPer; ++j) {
+            const uint32_t i = tid + 1024 * j;
+            tb[scan_pad(i)] = i < cnt ? block_bitoff[base + i] : 0ull;
+            tsg[scan_pad(i)] = i < cnt ? block_seg[base + i] : 0u;
+        }
+        __syncthreads();
+        uint64_t vb[kScanPer];
+        uint32_t vs[kScanPer];
+        uint64_t sb = 0;
+        uint32_t ss = 0;
+#pragma unroll
+        for (uint32_t j = 0; j < kScanPer; ++j) {
+            vb[j] = tb[scan_pad(kScanPer * tid + j)];
+            vs[j] = tsg[scan_pad(kScanPer * tid + j)];
+            sb += vb[j];
+            ss += vs[j];
+        }
+        // exclusive scan of (sb, ss) over the workgroup
+        uint64_t xb = sb;
+        uint32_t xs = ss;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const uint64_t yb = __shfl_up(xb, d, kWave);
+            const uint32_t ys = __shfl_up(xs, d, kWave);
+            if (lane >= (uint32_t)d) { xb += yb; xs += ys; }
+        }
+        if (lane == kWave - 1) { wb[wave] = xb; ws[wave] = xs; }
+        __syncthreads();
+        uint64_t ob = carry_b + (xb - sb), tile_b = 0;
+        uint32_t os = carry_s + (xs - ss), tile_s = 0;
+        for (uint32_t w = 0; w < 16; ++w) {
+            if (w < wave) { ob += wb[w]; os += ws[w]; }
+            tile_b += wb[w];
+            tile_s += ws[w];
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < kScanPer; ++j) {
+            ob += vb[j];
+            os += vs[j];
+            tb[scan_pad(kScanPer * tid + j)] = ob;
+            tsg[scan_pad(kScanPer * tid + j)] = os;
+        }
+        __syncthreads();
+#pragma unroll
+        for (uint32_t j = 0; j < kScanPer; ++j) {
+            const uint32_t i = tid + 1024 * j;
+            if (i < cnt) {
+                block_bitoff[base + i] = tb[scan_pad(i)];
+                block_seg[base + i] = tsg[scan_pad(i)];
+            }
+        }
+        carry_b += tile_b;
+        carry_s += tile_s;
+        __syncthreads();   // LDS and the wave totals are reused by the next tile
     }
-    if (lane == kWave - 1) { wb[tid / kWave] = xb; ws[tid / kWave] = xs; }
-    __syncthreads();
-    uint64_t ob = 0;
-    uint32_t os = 0;
-    for (uint32_t w = 0; w < tid / kWave; ++w) { ob += wb[w]; os += ws[w]; }
-    ob += xb - sb;
-    os += xs - ss;
-    for (uint64_t i = lo; i < hi; ++i) {
-        ob += block_bitoff[i];
-        os += block_seg[i];
-        block_bitoff[i] = ob;
-        block_seg[i] = os;
-    }
-    if (tid == 0) { block_bitoff[0] = 0; block_seg[0] = 0; }
-    __syncthreads();
-    if (tid == 1023) {
-        uint64_t tb = 0;
-        uint32_t ts = 0;
-        for (uint32_t w = 0; w < 16; ++w) { tb += wb[w]; ts += ws[w]; }
-        totals[0] = tb;
-        totals[1] = ts;
+    if (tid == 0) {
+        block_bitoff[0] = 0;
+        block_seg[0] = 0;
+        totals[0] = carry_b;
+        totals[1] = carry_s;
     }
 }
 
@@ -137,116 +174,157 @@ __global__ void k_clear_shared_words(uint64_t nblocks, const uint64_t *__restric
 
 // -------------------------------------------------------------------- bit packing
 // A full block whose bits fit the LDS stage (at most 8192 words: any mean code length
-// up to about 4 bits) is packed in one pass: all of the block's input is requested
-// first; every round stores its sign/mantissa bytes (one unconditional store per
-// thread) and places its codes, gap bytes and segment entries in LDS; the stream
-// words, gaps and segment entries are stored at the end.  Stores count among the
-// outstanding vector-memory accesses, so waiting for a load issued before a store
-// is only cheap when the number of accesses issued after the load is known
-// statically; with every store before the last wait unconditional it is.  Other
+// up to about 4 bits) is packed in one pass.  The whole block's input (8 loads per
+// thread) is requested at the kernel's start together with the code lengths, so it
+// arrives while the code table is built; it is then split at once: sign/mantissa
+// bytes (nibbles) go straight to memory and the exponent symbols to LDS, one byte
+// per element.  The rounds that follow read only LDS: each looks up its threads'
+// codes in a table of (code, length) pairs, scans their bit counts over the
+// workgroup and places the codes, gap bytes and segment entries in LDS; the stream
+// words, gaps and segment entries are stored at the end.  The rounds are bound by
+// vector-ALU issue (about 20 instructions per element), not by memory.  Other
 // blocks (the last, partial block of a tensor, or very long codes) take the
 // round-by-round path in k_encode.
 constexpr uint32_t kOnePassBits = (kStageWords - 2) * 32;
 constexpr uint32_t kOnePassChunks = kOnePassBits / kChunkBits;
 constexpr uint32_t kOnePassSegs = kOnePassChunks / kSegChunks;
 constexpr uint32_t kRoundsPerBlock = kBlock / kRound;
+constexpr uint32_t kEncBadFlag = 0x100;   // code table: symbol not allowed in this block
+
+// A full block's input, one thread's share: 16 bytes (BF16) or 8 bytes (FP8) per
+// round, i.e. 8 elements at block element r * kRound + tid * kEncPerThread.
+template <int DT>
+struct BlockIn {
+    static constexpr uint32_t RW = DT == ZX_BF16 ? 4 : 2;
+    uint32_t w[kRoundsPerBlock][RW];
+};
+
+// Request a full block's input for this thread.  A block that is not full requests
+// the same 16 bytes of `dummy` eight times instead, so the number of loads in
+// flight is the same on every path.
+template <int DT>
+__device__ __forceinline__ void load_block_in(const void *__restrict__ in, uint64_t lo, bool full, const void *dummy,
+                                              BlockIn<DT> &x)
+{
+    const uint32_t tid = threadIdx.x;
+#pragma unroll
+    for (uint32_t r = 0; r < kRoundsPerBlock; ++r) {
+        const uint64_t e = lo + (uint64_t)r * kRound + tid * kEncPerThread;
+        if (DT == ZX_BF16) {
+            const uint4 *a = full ? reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(in) + e)
+                                  : reinterpret_cast<const uint4 *>(dummy);
+            const uint4 q = *a;
+            x.w[r][0] = q.x; x.w[r][1] = q.y; x.w[r][2 % BlockIn<DT>::RW] = q.z; x.w[r][3 % BlockIn<DT>::RW] = q.w;
+        } else {
+            const uint2 *a = full ? reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(in) + e)
+                                  : reinterpret_cast<const uint2 *>(dummy);
+            const uint2 q = *a;
+            x.w[r][0] = q.x; x.w[r][1] = q.y;
+        }
+    }
+}
 
 template <int DT>
-__device__ __forceinline__ void encode_onepass(const void *__restrict__ in, uint64_t lo, uint32_t nb, uint64_t b, const Canon &c,
+__device__ __forceinline__ void encode_onepass(const BlockIn<DT> &x, uint64_t lo, uint64_t b, const Canon &c,
                                                uint32_t degen, uint64_t G, uint32_t bits, uint32_t s0, uint32_t nsb, uint32_t nch,
                                                uint64_t w_first, uint64_t w_last, uint8_t *__restrict__ signmant,
                                                uint32_t *__restrict__ stream, uint32_t *__restrict__ seg_desc,
                                                uint8_t *__restrict__ gaps, uint32_t *__restrict__ err, uint32_t *stage,
-                                               uint8_t *gapbuf, uint32_t *segbuf, uint32_t (*part2)[kEncThreads / kWave],
-                                               uint32_t &s_bad)
+                                               uint8_t *symbuf, uint2 *ctab, uint8_t *gapbuf, uint32_t *segbuf,
+                                               uint32_t (*part2)[kEncThreads / kWave], uint32_t &s_bad)
 {
-    constexpr uint32_t RW = DT == ZX_BF16 ? 4 : 2;   // input words per thread per round
     const uint32_t tid = threadIdx.x;
-    // ---- input requested two rounds ahead
-    const uint8_t *src = reinterpret_cast<const uint8_t *>(in) + (lo + tid * kEncPerThread) * (DT == ZX_BF16 ? 2 : 1);
-    auto load_round = [&](uint32_t r, uint32_t (&w)[RW]) {
-        const uint8_t *a = src + (uint64_t)r * kRound * (DT == ZX_BF16 ? 2 : 1);
-        if (DT == ZX_BF16) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(a);
-            w[0] = q.x; w[1] = q.y; w[2 % RW] = q.z; w[3 % RW] = q.w;
-        } else {
-            const uint2 q = *reinterpret_cast<const uint2 *>(a);
-            w[0] = q.x; w[1] = q.y;
-        }
-    };
-    uint32_t nx1[RW], nx2[RW];
-    load_round(0, nx1);
-    load_round(1, nx2);
-    for (uint32_t i = tid; i < kStageWords; i += kEncThreads) stage[i] = 0;
-    if (tid == 0) s_bad = 0;
-    __syncthreads();
-
-    const uint32_t a0 = (uint32_t)(G & 31);
-    uint32_t P = 0;    // block-relative bit of the round's first code
-    bool bad = false;
-#pragma unroll 1
-    for (uint32_t r = 0; r < kRoundsPerBlock; ++r) {
-        uint32_t raw[RW];
+    // ---- split every round: sign/mantissa bytes (nibbles) stored at once, exponent
+    //      symbols into LDS, one byte per element in block order
 #pragma unroll
-        for (uint32_t k = 0; k < RW; ++k) {
-            raw[k] = nx1[k];
-            nx1[k] = nx2[k];
-        }
-        if (r + 2 < kRoundsPerBlock) load_round(r + 2, nx2);
+    for (uint32_t r = 0; r < kRoundsPerBlock; ++r) {
         const uint32_t i0 = r * kRound + tid * kEncPerThread;
-        // ---- split: sign/mantissa bytes (nibbles) stored right away
-        uint32_t sym[kEncPerThread];
         if (DT == ZX_BF16) {
             uint32_t t[4];
 #pragma unroll
             for (uint32_t w = 0; w < 4; ++w) {
-                const uint32_t x = raw[w];
-                t[w] = (x & 0x007F007Fu) | ((x >> 8) & 0x00800080u);   // [sm, 0, sm, 0]
-                sym[2 * w] = (x >> 7) & 0xFFu;
-                sym[2 * w + 1] = (x >> 23) & 0xFFu;
+                const uint32_t v = x.w[r][w];
+                t[w] = (v & 0x007F007Fu) | ((v >> 8) & 0x00800080u);   // [sm, 0, sm, 0]
             }
-            *reinterpret_cast<uint2 *>(signmant + lo + tid * kEncPerThread + (uint64_t)r * kRound) =
+            *reinterpret_cast<uint2 *>(signmant + lo + i0) =
                 make_uint2(__builtin_amdgcn_perm(t[1], t[0], 0x06040200u), __builtin_amdgcn_perm(t[3], t[2], 0x06040200u));
+            // x >> 7 holds the first element's exponent in byte 0 and the second's in byte 2
+            const uint32_t e01 = __builtin_amdgcn_perm(x.w[r][1] >> 7, x.w[r][0] >> 7, 0x06040200u);
+            const uint32_t e23 = __builtin_amdgcn_perm(x.w[r][3 % BlockIn<DT>::RW] >> 7, x.w[r][2 % BlockIn<DT>::RW] >> 7, 0x06040200u);
+            *reinterpret_cast<uint2 *>(symbuf + i0) = make_uint2(e01, e23);
         } else {
             uint32_t t[2];
 #pragma unroll
             for (uint32_t w = 0; w < 2; ++w) {
-                const uint32_t x = raw[w];
-                const uint32_t nb4 = (x & 0x07070707u) | ((x >> 4) & 0x08080808u);   // one nibble per byte
-                t[w] = (nb4 | (nb4 >> 4)) & 0x00FF00FFu;                               // two nibbles per half
-#pragma unroll
-                for (uint32_t k = 0; k < 4; ++k) sym[4 * w + k] = (x >> (8 * k + 3)) & 0xFu;
+                const uint32_t v = x.w[r][w];
+                const uint32_t nb4 = (v & 0x07070707u) | ((v >> 4) & 0x08080808u);   // one nibble per byte
+                t[w] = (nb4 | (nb4 >> 4)) & 0x00FF00FFu;                              // two nibbles per half
             }
-            *reinterpret_cast<uint32_t *>(signmant + (lo + tid * kEncPerThread) / 2 + (uint64_t)r * (kRound / 2)) =
-                __builtin_amdgcn_perm(t[1], t[0], 0x06040200u);
+            *reinterpret_cast<uint32_t *>(signmant + (lo + i0) / 2) = __builtin_amdgcn_perm(t[1], t[0], 0x06040200u);
+            *reinterpret_cast<uint2 *>(symbuf + i0) = make_uint2((x.w[r][0] >> 3) & 0x0F0F0F0Fu, (x.w[r][1] >> 3) & 0x0F0F0F0Fu);
         }
-        // ---- code lengths; codes concatenated; code starts as a bit mask
-        uint32_t lmin = 255;
-        uint32_t tb = 0;
-        uint64_t acc = 0;
-        uint64_t starts = 0;   // bit j: a code starts j bits into this thread's codes (j < 64)
+    }
+    for (uint32_t i = tid; i < kStageWords; i += kEncThreads) stage[i] = 0;
+    if (tid == 0) s_bad = 0;
+    // code table: the code, and its length with a flag for a symbol the block may not
+    // hold (no code, or in a block of zero bits any symbol but the degenerate one)
+    if (tid < alphabet_of(DT)) {
+        const uint32_t l = c.len[tid];
+        const bool flag = bits ? l == 0 : tid != degen;
+        ctab[tid] = make_uint2(c.code[tid], l | (flag ? kEncBadFlag : 0u));
+    }
+    __syncthreads();
+
+    const uint32_t a0 = (uint32_t)(G & 31);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    bool bad = false;
+    // A round is split at its barrier: `pre` looks up the codes of the thread's 8
+    // elements and publishes the wave's bit count; after the barrier `xscan` turns
+    // the wave counts into this thread's offset; `post` places the codes and the
+    // auxiliary entries.  Round r's `pre` and round r-1's `post` share one barrier
+    // interval, so the table lookups of one overlap the stage writes of the other.
+    struct Rd {
+        uint64_t acc;      // the thread's codes, concatenated (exact while tb <= 64)
+        uint64_t starts;   // bit j: a code starts j bits into them (exact while j < 64)
+        uint32_t tb;       // their total length
+        uint32_t o;        // bits before them in the round
+        uint32_t R;        // bits in the round
+    };
+    auto pre = [&](uint32_t r, Rd &d) {
+        const uint32_t i0 = r * kRound + tid * kEncPerThread;
+        const uint2 sv = *reinterpret_cast<const uint2 *>(symbuf + i0);
+        uint32_t flags = 0;
+        d.tb = 0;
+        d.acc = 0;
+        d.starts = 0;
 #pragma unroll
         for (uint32_t k = 0; k < kEncPerThread; ++k) {
-            const uint32_t lk = c.len[sym[k]];
-            lmin = lk < lmin ? lk : lmin;
-            if (!bits && sym[k] != degen) bad = true;
-            acc = (acc << lk) | c.code[sym[k]];
-            starts |= (tb < 64 ? 1ull : 0ull) << (tb & 63);
-            tb += lk;
+            const uint32_t sy = ((k < 4 ? sv.x : sv.y) >> (8 * (k & 3))) & 0xFFu;
+            const uint2 e = ctab[sy];
+            flags |= e.y;
+            d.acc = (d.acc << (e.y & 63u)) | e.x;
+            d.starts |= 1ull << (d.tb & 63u);
+            d.tb += e.y & 0xFFu;
         }
-        if (bits && lmin == 0) bad = true;
-        // ---- workgroup exclusive scan of code bits (partials double-buffered by round)
+        if (flags & kEncBadFlag) bad = true;
         uint32_t wtot;
-        uint32_t o = wave_excl_scan(tb, wtot);
-        if (lane_id() == 0) part2[r & 1][tid / kWave] = wtot;
-        __syncthreads();
-        uint32_t R = 0;
-        for (uint32_t w = 0; w < kEncThreads / kWave; ++w) {
-            const uint32_t pw = part2[r & 1][w];
-            if (w < tid / kWave) o += pw;
-            R += pw;
-        }
-        const uint32_t p0 = P + o;       // block-relative bit of this thread's first code
+        d.o = wave_excl_scan(d.tb, wtot);
+        if (lane_id() == 0) part2[r & 1][wave] = wtot;   // double-buffered by round
+    };
+    auto xscan = [&](uint32_t r, Rd &d) {
+        // lanes 0..15 of every wave scan the 16 wave totals
+        int pv = (int)part2[r & 1][lane_id() & 15u];
+        pv += __builtin_amdgcn_update_dpp(0, pv, 0x111, 0xF, 0xF, true);   // row_shr:1
+        pv += __builtin_amdgcn_update_dpp(0, pv, 0x112, 0xF, 0xF, true);   // row_shr:2
+        pv += __builtin_amdgcn_update_dpp(0, pv, 0x114, 0xF, 0xF, true);   // row_shr:4
+        pv += __builtin_amdgcn_update_dpp(0, pv, 0x118, 0xF, 0xF, true);   // row_shr:8
+        d.R = (uint32_t)__builtin_amdgcn_readlane(pv, kEncThreads / kWave - 1);
+        if (wave) d.o += (uint32_t)__builtin_amdgcn_readlane(pv, wave - 1);
+    };
+    auto post = [&](uint32_t r, const Rd &d, uint32_t P) {
+        const uint32_t i0 = r * kRound + tid * kEncPerThread;
+        const uint32_t tb = d.tb;
+        const uint32_t p0 = P + d.o;     // block-relative bit of this thread's first code
         const uint32_t q0 = a0 + p0;     // its stage bit
         const uint32_t bnd = (p0 + kChunkBits - 1) & ~(kChunkBits - 1);   // first chunk boundary >= p0
         if (tb <= 64) {
@@ -254,7 +332,7 @@ __device__ __forceinline__ void encode_onepass(const void *__restrict__ in, uint
             //      neighbouring threads only at the ends
             if (tb) {
                 const uint32_t sh = q0 & 31;
-                const uint64_t X = acc << (64 - tb);
+                const uint64_t X = d.acc << (64 - tb);
                 uint32_t *w = &stage[q0 >> 5];
                 atomicOr(&w[0], (uint32_t)(X >> (32 + sh)));
                 if (sh + tb > 32) atomicOr(&w[1], (uint32_t)(X >> sh));
@@ -265,22 +343,24 @@ __device__ __forceinline__ void encode_onepass(const void *__restrict__ in, uint
             //      code starts at tb)
             if (bnd < p0 + tb) {
                 const uint32_t rel = bnd - p0;
-                const uint64_t after = starts >> rel;
+                const uint64_t after = d.starts >> rel;
                 const uint32_t m = after ? (uint32_t)__builtin_ctzll(after) : tb - rel;
                 gapbuf[bnd / kChunkBits] = (uint8_t)(bnd + m < bits ? m : ZX_NO_GAP);
                 if (bnd % (kChunkBits * kSegChunks) == 0 && bnd > 0)   // first element of a segment
-                    segbuf[bnd / (kChunkBits * kSegChunks)] = i0 + (uint32_t)__builtin_popcountll(starts & ((1ull << rel) - 1));
+                    segbuf[bnd / (kChunkBits * kSegChunks)] = i0 + (uint32_t)__builtin_popcountll(d.starts & ((1ull << rel) - 1));
             }
         } else {
-            // ---- long codes: code by code, recomputed from the input
+            // ---- long codes: code by code, the symbols read again
+            const uint2 sv = *reinterpret_cast<const uint2 *>(symbuf + i0);
             uint32_t pk = p0;
 #pragma unroll
             for (uint32_t k = 0; k < kEncPerThread; ++k) {
-                const uint32_t lk = c.len[sym[k]];
+                const uint32_t sy = ((k < 4 ? sv.x : sv.y) >> (8 * (k & 3))) & 0xFFu;
+                const uint32_t lk = c.len[sy];
                 if (lk == 0) continue;
                 const uint32_t q = a0 + pk;
                 const uint32_t sh = q & 31;
-                const uint64_t x = (uint64_t)c.code[sym[k]] << (64 - lk - sh);
+                const uint64_t x = (uint64_t)c.code[sy] << (64 - lk - sh);
                 atomicOr(&stage[q >> 5], (uint32_t)(x >> 32));
                 if (sh + lk > 32) atomicOr(&stage[(q >> 5) + 1], (uint32_t)x);
                 const uint32_t cd = (pk + kChunkBits - 1) / kChunkBits;
@@ -296,8 +376,22 @@ __device__ __forceinline__ void encode_onepass(const void *__restrict__ in, uint
                 pk += lk;
             }
         }
-        P += R;
+    };
+    Rd cur, prev;
+    uint32_t P = 0;    // block-relative bit of round r-1's first code
+    pre(0, cur);
+    __syncthreads();
+    xscan(0, cur);
+#pragma unroll 1
+    for (uint32_t r = 1; r < kRoundsPerBlock; ++r) {
+        prev = cur;
+        pre(r, cur);
+        post(r - 1, prev, P);
+        P += prev.R;
+        __syncthreads();
+        xscan(r, cur);
     }
+    post(kRoundsPerBlock - 1, cur, P);
     if (bad) s_bad = 1;
     __syncthreads();
     // ---- all stores
@@ -337,11 +431,18 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
     __shared__ uint8_t gapbuf[kOnePassChunks];
     __shared__ uint32_t segbuf[kOnePassSegs];
     __shared__ uint32_t part2[2][kEncThreads / kWave];
+    __shared__ __align__(16) uint8_t symbuf[kBlock];
+    __shared__ uint2 ctab[256];
 
     const uint32_t tid = threadIdx.x;
     const uint64_t b = blockIdx.x;
     const uint64_t cb = per_block ? b : 0;
-    canon_build(lengths + cb * A, A, c);
+    // the code lengths and, for a full block, its first two rounds of input are
+    // requested together, so the input arrives while the code table is built
+    const uint32_t lsym = lengths[cb * A + (tid < A ? tid : A - 1)];
+    BlockIn<DT> x;
+    load_block_in<DT>(in, b * kBlock, (b + 1) * (uint64_t)kBlock <= n, block_bitoff, x);
+    canon_build_from(lsym, A, c);
     const uint32_t degen = degenerate[cb];
     const uint64_t G = block_bitoff[b];
     const uint64_t bits = block_bitoff[b + 1] - G;
@@ -359,8 +460,8 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
     const uint64_t w_first = G >> 5;
     const uint64_t w_last = bits ? (G + bits - 1) >> 5 : w_first;
     if (nb == kBlock && (G & 31) + bits <= kOnePassBits) {
-        encode_onepass<DT>(in, lo, nb, b, c, degen, G, (uint32_t)bits, s0, nsb, nch, w_first, w_last, signmant, stream, seg_desc,
-                           gaps, err, stage, gapbuf, segbuf, part2, s_bad);
+        encode_onepass<DT>(x, lo, b, c, degen, G, (uint32_t)bits, s0, nsb, nch, w_first, w_last, signmant, stream, seg_desc,
+                           gaps, err, stage, symbuf, ctab, gapbuf, segbuf, part2, s_bad);
         return;
     }
 
@@ -380,7 +481,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
     bool bad = false;
     const uint32_t nrounds = (nb + kRound - 1) / kRound;
     // raw 16 (BF16) or 8 (FP8) input bytes of this thread, loaded one round ahead
-    constexpr uint32_t RW = DT == ZX_BF16 ? 4 : 2;
+    constexpr uint32_t RW = BlockIn<DT>::RW;
     auto load_raw = [&](uint32_t r, uint32_t (&w)[RW]) {
         const uint32_t i0 = r * kRound + tid * kEncPerThread;
         if (i0 + kEncPerThread <= nb) {

@@ -104,7 +104,9 @@ def test_c5_kv_cache_round_trip_and_sampled_blocks():
     bitoff = np_u(c.block_bitoff, np.uint64)
     bseg = np_u(c.block_seg, np.uint32)
     rng = np.random.default_rng(5)
-    sample = sorted(set([0, 1, nb // 2, nb - 1] + list(rng.integers(0, nb, 8))))
+    # the block scan runs in tiles of 8192 blocks: include the blocks around the tile seams
+    seams = [8191, 8192, 8193, 16383, 16384, 24575, 24576]
+    sample = sorted(set([0, 1, nb // 2, nb - 1] + seams + list(rng.integers(0, nb, 8))))
     stream = np_u(c.stream, np.uint32)
     for b in sample:
         say("c5 block", b)
