@@ -80,7 +80,8 @@ typedef enum {
     ZX_E_UNSUPPORTED = 2,  /* unknown dtype                                        */
     ZX_E_CODEBOOK = 3,     /* max_len infeasible, or data/codebook mismatch        */
     ZX_E_CORRUPT = 4,      /* container inconsistent (device-detected)             */
-    ZX_E_HIP = 5           /* a HIP launch failed                                  */
+    ZX_E_HIP = 5,          /* a HIP launch failed                                  */
+    ZX_E_NOSPACE = 6       /* K/V slots: a block's code bits exceed its slot         */
 } zx_status;
 
 typedef enum {
@@ -184,6 +185,77 @@ zx_status zx_decode_block_batch(const zx_container *cs, void *const *outs, uint3
  * per-block codebooks still take one workgroup per block. */
 zx_status zx_decode_block_batch_wg(const zx_container *cs, void *const *outs, uint32_t count,
                                    uint32_t max_workgroups, uint32_t *err, hipStream_t stream);
+
+/* ---- K/V slot pool --------------------------------------------------------------
+ * A K/V cache kept in preallocated fixed-size slots, one 65536-element block per
+ * slot: new blocks are compressed into their slots as they fill, and reused blocks
+ * are decompressed on demand (ZipFloat page, section 4.2: slot-based K/V layout with
+ * incremental compressed writes; section 3.3: K/V blocks written to fixed per-block
+ * slots, without locks or a shared allocation counter).
+ *
+ * Every slot holds one block as a complete container with its own codebook
+ * (per_block = 1, n = 65536) at fixed offsets in the pool's arrays; its code stream
+ * has a fixed capacity of cap_words words, chosen by the caller (cap_words * 32 /
+ * 65536 bits per element).  A block whose code bits exceed the capacity is not
+ * stored (status ZX_E_NOSPACE for that block); the caller keeps it another way.
+ * Slot s of each array starts at s times the stride that zx_kv_slot_sizes gives.
+ * All pointers are caller-allocated device memory. */
+typedef struct zx_kv_pool {
+    int32_t dtype;             /* zx_dtype                                              */
+    uint32_t n_slots;
+    uint32_t cap_words;        /* stream capacity per slot: a multiple of 256, 256..8192 */
+    uint32_t reserved_;        /* 0                                                     */
+    uint8_t *signmant;         /* [n_slots][sm_bytes]                                   */
+    uint32_t *stream;          /* [n_slots][stream_words]                               */
+    uint8_t *gaps;             /* [n_slots][seg_stride][64]                             */
+    uint32_t *seg_desc;        /* [n_slots][seg_stride][2]                              */
+    uint8_t *lengths;          /* [n_slots][A]                                          */
+    uint16_t *degenerate;      /* [n_slots]                                             */
+    uint64_t *block_bitoff;    /* [n_slots][2]: {0, code bits of the slot's block}      */
+    uint32_t *block_seg;       /* [n_slots][2]: {0, segments of the slot's block}       */
+} zx_kv_pool;
+
+typedef struct zx_kv_sizes {
+    uint64_t sm_bytes;         /* 65536 (BF16) or 32768 (FP8)                           */
+    uint64_t stream_words;     /* zx_stream_words(cap_words * 32): capacity + padding   */
+    uint32_t max_segs;         /* segments a full slot uses: cap_words / 256            */
+    uint32_t seg_stride;       /* max_segs rounded up to even (16-byte slot alignment)  */
+    uint32_t alphabet;         /* 256 or 16                                             */
+    uint32_t reserved_;
+} zx_kv_sizes;
+
+/* Per-slot strides for a pool of the given dtype and capacity (ZX_E_INVAL if
+ * cap_words is not a multiple of 256 in 256..8192). */
+zx_status zx_kv_slot_sizes(zx_dtype dtype, uint32_t cap_words, zx_kv_sizes *out);
+
+/* Workspace bytes that zx_kv_encode_slots needs for nblk blocks. */
+size_t zx_kv_workspace_bytes(zx_dtype dtype, uint32_t nblk);
+
+/* Compress nblk full blocks into their slots with no host synchronisation: per-block
+ * histograms, codebooks and sizes are computed on the device, and each block is
+ * written into slot slot_ids[j] (ZipFloat page, 4.2: new K/V entries compressed
+ * into preallocated slots as they are produced).
+ *   src        nblk * 65536 elements (BF16 as u16 bits, FP8 as u8 bits), 16-byte aligned
+ *   slot_ids   device u32[nblk], distinct slots < n_slots
+ *   max_len    code length limit, as zx_build_codebook
+ *   workspace  device, zx_kv_workspace_bytes(dtype, nblk) bytes, 16-byte aligned
+ *   status     device u32[nblk] out: ZX_OK, ZX_E_NOSPACE (block left out, its slot
+ *              marked empty), ZX_E_INVAL (slot id out of range) or ZX_E_CODEBOOK
+ *   err        optional device word: the first non-zero block status
+ * The slot contents equal what zx_encode writes for that block alone with
+ * per_block = 1 (stream bits after the block's last code and up to the end of the
+ * slot's stream are zero).  Blocks written by one call must go to distinct slots;
+ * calls that write the same slot race. */
+zx_status zx_kv_encode_slots(const zx_kv_pool *pool, const void *src, uint32_t nblk,
+                             const uint32_t *slot_ids, uint32_t max_len, void *workspace,
+                             size_t ws_bytes, uint32_t *status, uint32_t *err, hipStream_t stream);
+
+/* The container of slot `slot` (host struct of device pointers into the pool), for
+ * zx_decode / zx_decode_block_batch: decoding reused K/V blocks on demand (ZipFloat
+ * page, 4.2).  Its nsegs and total_bits are the slot's capacities; the block's own
+ * segment count and bit length are read on the device from block_seg and
+ * block_bitoff, so no host copy of them is needed. */
+zx_status zx_kv_slot_container(const zx_kv_pool *pool, uint32_t slot, zx_container *out);
 
 /* Stream length in u32 words for a given number of code bits. */
 uint64_t zx_stream_words(uint64_t total_bits);

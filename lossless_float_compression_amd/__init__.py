@@ -8,3 +8,4 @@ from .zx import (  # noqa: F401
     empty_output, lib, zx_build_codebook, zx_build_decode_table, zx_decode, zx_decode_block_batch,
     zx_decode_table_bytes, zx_encode, zx_encode_size, zx_histogram, zx_stream_words,
 )
+from .kvslots import KVSlotPool  # noqa: F401,E402

@@ -1107,6 +1107,7 @@ extern "C" const char *zx_status_string(zx_status s)
     case ZX_E_CODEBOOK: return "codebook error (length limit infeasible or data without a code)";
     case ZX_E_CORRUPT: return "corrupt container";
     case ZX_E_HIP: return "HIP launch failure";
+    case ZX_E_NOSPACE: return "block does not fit its slot";
     }
     return "unknown status";
 }

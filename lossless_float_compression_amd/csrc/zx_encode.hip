@@ -639,6 +639,98 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
     if (tid == 0 && s_bad) report(err, ZX_E_CODEBOOK);
 }
 
+// -------------------------------------------------------------------- K/V slots
+// One workgroup per block: the block (always full) is encoded exactly as in
+// k_encode's one-pass path, as a container of its own (block 0, stream bit 0,
+// segment 0) inside slot slot_ids[j]; its codebook, sizes and descriptors go to the
+// slot's entries of the pool arrays.  The code lengths, code table and block sizes
+// come from the workspace filled by the histogram, codebook and block-size kernels.
+struct KvSlots {
+    uint8_t *signmant;
+    uint32_t *stream;
+    uint8_t *gaps;
+    uint32_t *seg_desc;
+    uint8_t *lengths;
+    uint16_t *degenerate;
+    uint64_t *block_bitoff;
+    uint32_t *block_seg;
+    uint32_t n_slots;
+    uint32_t cap_bits;
+    uint32_t max_segs;
+    uint32_t seg_stride;
+    uint64_t stream_words;
+};
+
+template <int DT>
+__global__ __launch_bounds__(kEncThreads) void k_encode_slots(KvSlots P, const void *__restrict__ src,
+                                                              const uint32_t *__restrict__ slot_ids,
+                                                              const uint8_t *__restrict__ wlen,
+                                                              const uint16_t *__restrict__ wdeg,
+                                                              const uint64_t *__restrict__ wbits,
+                                                              const uint32_t *__restrict__ wnseg,
+                                                              uint32_t *__restrict__ status, uint32_t *__restrict__ err)
+{
+    constexpr uint32_t A = alphabet_of(DT);
+    constexpr uint32_t kSmBytes = DT == ZX_BF16 ? kBlock : kBlock / 2;
+    __shared__ Canon c;
+    __shared__ uint32_t stage[kStageWords];
+    __shared__ uint32_t s_bad;
+    __shared__ uint8_t gapbuf[kOnePassChunks];
+    __shared__ uint32_t segbuf[kOnePassSegs];
+    __shared__ uint32_t part2[2][kEncThreads / kWave];
+    __shared__ __align__(16) uint8_t symbuf[kBlock];
+    __shared__ uint2 ctab[256];
+
+    const uint32_t tid = threadIdx.x;
+    const uint64_t j = blockIdx.x;
+    const uint32_t lsym = wlen[j * A + (tid < A ? tid : A - 1)];
+    BlockIn<DT> x;
+    load_block_in<DT>(src, j * kBlock, true, nullptr, x);
+    canon_build_from(lsym, A, c);
+    const uint32_t slot = slot_ids[j];
+    const uint32_t degen = wdeg[j];
+    const uint64_t bits = wbits[j + 1];
+    const uint32_t nsb = wnseg[j + 1];
+    if (slot >= P.n_slots) {
+        if (tid == 0) {
+            status[j] = ZX_E_INVAL;
+            report(err, ZX_E_INVAL);
+        }
+        return;
+    }
+    if (bits > P.cap_bits || nsb > P.max_segs) {
+        // the block does not fit: the slot is left holding no segments
+        if (tid == 0) {
+            P.block_bitoff[2 * (uint64_t)slot] = 0;
+            P.block_bitoff[2 * (uint64_t)slot + 1] = 0;
+            P.block_seg[2 * (uint64_t)slot] = 0;
+            P.block_seg[2 * (uint64_t)slot + 1] = 0;
+            status[j] = ZX_E_NOSPACE;
+            report(err, ZX_E_NOSPACE);
+        }
+        return;
+    }
+    uint8_t *sm = P.signmant + (uint64_t)slot * kSmBytes;
+    uint32_t *st = P.stream + (uint64_t)slot * P.stream_words;
+    uint8_t *gp = P.gaps + (uint64_t)slot * P.seg_stride * kSegChunks;
+    uint32_t *sd = P.seg_desc + (uint64_t)slot * P.seg_stride * 2;
+    if (tid < A) P.lengths[(uint64_t)slot * A + tid] = (uint8_t)lsym;
+    if (tid == 0) {
+        P.degenerate[slot] = (uint16_t)degen;
+        P.block_bitoff[2 * (uint64_t)slot] = 0;
+        P.block_bitoff[2 * (uint64_t)slot + 1] = bits;
+        P.block_seg[2 * (uint64_t)slot] = 0;
+        P.block_seg[2 * (uint64_t)slot + 1] = nsb;
+    }
+    const uint32_t nch = (uint32_t)((bits + kChunkBits - 1) / kChunkBits);
+    encode_onepass<DT>(x, 0, 0, c, degen, 0, (uint32_t)bits, 0, nsb, nch, ~0ull, ~0ull, sm, st, sd, gp, err, stage, symbuf,
+                       ctab, gapbuf, segbuf, part2, s_bad);
+    // the rest of the slot's stream, padding included, is zero
+    const uint32_t nw = (uint32_t)((bits + 31) / 32);
+    for (uint64_t w = nw + tid; w < P.stream_words; w += kEncThreads) st[w] = 0;
+    if (tid == 0) status[j] = s_bad ? ZX_E_CODEBOOK : ZX_OK;
+}
+
 }  // namespace zxk
 
 using namespace zxk;
@@ -711,4 +803,127 @@ extern "C" zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int p
         hipLaunchKernelGGL(k_encode<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream_, in, n, per_block, lengths,
                            degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, err);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}
+
+// ---- K/V slot pool
+static uint32_t kv_alphabet(zx_dtype d) { return d == ZX_BF16 ? 256u : 16u; }
+
+extern "C" zx_status zx_kv_slot_sizes(zx_dtype dtype, uint32_t cap_words, zx_kv_sizes *out)
+{
+    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    if (!out || cap_words < 256 || cap_words > kStageWords - 2 || cap_words % 256 != 0) return ZX_E_INVAL;
+    out->sm_bytes = dtype == ZX_BF16 ? kBlock : kBlock / 2;
+    out->stream_words = zx_stream_words((uint64_t)cap_words * 32);
+    out->max_segs = cap_words / (kSegBits / 32);
+    out->seg_stride = (out->max_segs + 1) & ~1u;
+    out->alphabet = kv_alphabet(dtype);
+    out->reserved_ = 0;
+    return ZX_OK;
+}
+
+// workspace: hist u32[nblk][A], lengths u8[nblk][A], degenerate u16[nblk],
+// bits u64[nblk+1], segments u32[nblk+1]; each part 16-byte aligned
+static size_t kv_round16(size_t x) { return (x + 15) & ~(size_t)15; }
+struct KvWs {
+    size_t hist, len, deg, bits, nseg, total;
+};
+static KvWs kv_ws(zx_dtype dtype, uint32_t nblk)
+{
+    const size_t A = kv_alphabet(dtype);
+    KvWs w;
+    w.hist = 0;
+    w.len = w.hist + kv_round16((size_t)nblk * A * 4);
+    w.deg = w.len + kv_round16((size_t)nblk * A);
+    w.bits = w.deg + kv_round16((size_t)nblk * 2);
+    w.nseg = w.bits + kv_round16(((size_t)nblk + 1) * 8);
+    w.total = w.nseg + kv_round16(((size_t)nblk + 1) * 4);
+    return w;
+}
+
+extern "C" size_t zx_kv_workspace_bytes(zx_dtype dtype, uint32_t nblk) { return kv_ws(dtype, nblk).total; }
+
+static bool kv_pool_ok(const zx_kv_pool *p, zx_kv_sizes *sz)
+{
+    if (!p || zx_kv_slot_sizes((zx_dtype)p->dtype, p->cap_words, sz) != ZX_OK) return false;
+    if (!p->signmant || !p->stream || !p->gaps || !p->seg_desc || !p->lengths || !p->degenerate || !p->block_bitoff ||
+        !p->block_seg)
+        return false;
+    return aligned16(p->signmant) && aligned16(p->stream) && aligned16(p->seg_desc) && aligned16(p->block_bitoff) &&
+           ((uintptr_t)p->block_seg & 7u) == 0;
+}
+
+extern "C" zx_status zx_kv_encode_slots(const zx_kv_pool *pool, const void *src, uint32_t nblk, const uint32_t *slot_ids,
+                                        uint32_t max_len, void *workspace, size_t ws_bytes, uint32_t *status, uint32_t *err,
+                                        hipStream_t stream)
+{
+    if (pool && pool->dtype != ZX_BF16 && pool->dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    zx_kv_sizes sz;
+    if (!kv_pool_ok(pool, &sz)) return ZX_E_INVAL;
+    if (nblk == 0) return ZX_OK;
+    const zx_dtype dtype = (zx_dtype)pool->dtype;
+    const KvWs w = kv_ws(dtype, nblk);
+    if (!src || !slot_ids || !status || !workspace || !aligned16(src) || !aligned16(workspace) || ws_bytes < w.total ||
+        nblk > 0x7FFFFFFFu)
+        return ZX_E_INVAL;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + w.hist);
+    uint8_t *len = ws + w.len;
+    uint16_t *deg = reinterpret_cast<uint16_t *>(ws + w.deg);
+    uint64_t *bits = reinterpret_cast<uint64_t *>(ws + w.bits);
+    uint32_t *nseg = reinterpret_cast<uint32_t *>(ws + w.nseg);
+    const uint64_t n = (uint64_t)nblk * kBlock;
+    zx_status st = zx_histogram(dtype, src, n, nullptr, hist, stream);
+    if (st != ZX_OK) return st;
+    st = zx_build_codebook(dtype, hist, nblk, max_len, len, deg, stream);
+    if (st != ZX_OK) return st;
+    if (dtype == ZX_BF16)
+        hipLaunchKernelGGL(k_block_bits<ZX_BF16>, dim3(nblk), dim3(kSizeThreads), 0, stream, src, n, 1, len, hist, bits, nseg);
+    else
+        hipLaunchKernelGGL(k_block_bits<ZX_FP8_E4M3FN>, dim3(nblk), dim3(kSizeThreads), 0, stream, src, n, 1, len, hist, bits,
+                           nseg);
+    if (hipGetLastError() != hipSuccess) return ZX_E_HIP;
+    KvSlots P;
+    P.signmant = pool->signmant;
+    P.stream = pool->stream;
+    P.gaps = pool->gaps;
+    P.seg_desc = pool->seg_desc;
+    P.lengths = pool->lengths;
+    P.degenerate = pool->degenerate;
+    P.block_bitoff = pool->block_bitoff;
+    P.block_seg = pool->block_seg;
+    P.n_slots = pool->n_slots;
+    P.cap_bits = pool->cap_words * 32;
+    P.max_segs = sz.max_segs;
+    P.seg_stride = sz.seg_stride;
+    P.stream_words = sz.stream_words;
+    if (dtype == ZX_BF16)
+        hipLaunchKernelGGL(k_encode_slots<ZX_BF16>, dim3(nblk), dim3(kEncThreads), 0, stream, P, src, slot_ids, len, deg, bits,
+                           nseg, status, err);
+    else
+        hipLaunchKernelGGL(k_encode_slots<ZX_FP8_E4M3FN>, dim3(nblk), dim3(kEncThreads), 0, stream, P, src, slot_ids, len, deg,
+                           bits, nseg, status, err);
+    return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}
+
+extern "C" zx_status zx_kv_slot_container(const zx_kv_pool *pool, uint32_t slot, zx_container *out)
+{
+    zx_kv_sizes sz;
+    if (!kv_pool_ok(pool, &sz) || !out || slot >= pool->n_slots) return ZX_E_INVAL;
+    const uint64_t A = sz.alphabet;
+    out->dtype = pool->dtype;
+    out->per_block = 1;
+    out->n = kBlock;
+    out->nsegs = sz.max_segs;
+    out->total_bits = (uint64_t)pool->cap_words * 32;
+    out->stream_words = sz.stream_words;
+    out->lengths = pool->lengths + slot * A;
+    out->degenerate = pool->degenerate + slot;
+    out->signmant = pool->signmant + slot * sz.sm_bytes;
+    out->stream = pool->stream + slot * sz.stream_words;
+    out->block_bitoff = pool->block_bitoff + 2 * (uint64_t)slot;
+    out->block_seg = pool->block_seg + 2 * (uint64_t)slot;
+    out->seg_desc = pool->seg_desc + 2 * (uint64_t)slot * sz.seg_stride;
+    out->gaps = pool->gaps + (uint64_t)slot * sz.seg_stride * kSegChunks;
+    out->dtab = nullptr;
+    return ZX_OK;
 }

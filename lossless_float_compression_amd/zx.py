@@ -28,7 +28,8 @@ LIB_PATH = os.path.join(_HERE, "libzx.so")
 _lib = None
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype", 3: "codebook error",
-           4: "corrupt container", 5: "HIP launch failure"}
+           4: "corrupt container", 5: "HIP launch failure", 6: "block does not fit its slot"}
+ZX_E_NOSPACE = 6
 
 
 class ZxError(RuntimeError):
@@ -47,9 +48,25 @@ class zx_container(C.Structure):
     ]
 
 
+class zx_kv_pool(C.Structure):
+    _fields_ = [
+        ("dtype", C.c_int32), ("n_slots", C.c_uint32), ("cap_words", C.c_uint32), ("reserved_", C.c_uint32),
+        ("signmant", C.c_void_p), ("stream", C.c_void_p), ("gaps", C.c_void_p), ("seg_desc", C.c_void_p),
+        ("lengths", C.c_void_p), ("degenerate", C.c_void_p), ("block_bitoff", C.c_void_p), ("block_seg", C.c_void_p),
+    ]
+
+
+class zx_kv_sizes(C.Structure):
+    _fields_ = [
+        ("sm_bytes", C.c_uint64), ("stream_words", C.c_uint64), ("max_segs", C.c_uint32), ("seg_stride", C.c_uint32),
+        ("alphabet", C.c_uint32), ("reserved_", C.c_uint32),
+    ]
+
+
 EXPORTS = ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
            "zx_decode_table_bytes", "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_stream_words",
-           "zx_status_string", "zx_version")
+           "zx_status_string", "zx_version", "zx_kv_slot_sizes", "zx_kv_workspace_bytes", "zx_kv_encode_slots",
+           "zx_kv_slot_container")
 
 
 def lib():
@@ -76,8 +93,14 @@ def lib():
         L.zx_status_string.argtypes = [I]
         L.zx_status_string.restype = C.c_char_p
         L.zx_version.restype = C.c_char_p
+        L.zx_kv_slot_sizes.argtypes = [I, U32, C.POINTER(zx_kv_sizes)]
+        L.zx_kv_workspace_bytes.argtypes = [I, U32]
+        L.zx_kv_workspace_bytes.restype = C.c_size_t
+        L.zx_kv_encode_slots.argtypes = [C.POINTER(zx_kv_pool), P, U32, P, U32, P, C.c_size_t, P, P, P]
+        L.zx_kv_slot_container.argtypes = [C.POINTER(zx_kv_pool), U32, C.POINTER(zx_container)]
         for f in ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
-                  "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg"):
+                  "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_kv_slot_sizes",
+                  "zx_kv_encode_slots", "zx_kv_slot_container"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -213,8 +236,8 @@ def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_sc
              stream=None) -> Compressed:
     """Encode a device tensor (bf16 or int16 bits -> BF16; float8_e4m3fn or uint8 bits -> FP8).
 
-    Runs histogram -> codebook -> block sizes, reads back the two totals (the single
-    host synchronisation) to size the outputs, then encodes."""
+    Runs histogram -> codebook -> block sizes (and the decode table), reads back the
+    two totals (the single host synchronisation) to size the outputs, then encodes."""
     dtype, flat = _as_bits(x)
     if not flat.is_cuda:
         raise ValueError("compress expects a device tensor")
@@ -239,18 +262,20 @@ def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_sc
         lengths = lengths[:0]
         degenerate = degenerate[:0]
     zx_encode_size(dtype, flat, n, per_block, lengths, block_hist, block_bitoff, block_seg, totals, stream)
-    total_bits, nsegs = (int(v) for v in totals.cpu().tolist())
-    signmant = torch.empty(n if dtype == BF16 else (n + 1) // 2, **u8)
-    words = torch.empty(zx_stream_words(total_bits), **i32)
-    seg_desc = torch.empty((nsegs, 2), **i32)
-    gaps = torch.empty((nsegs, SEG_CHUNKS), **u8)
-    err = torch.zeros(1, **i32)
-    zx_encode(dtype, flat, n, per_block, lengths, degenerate, block_bitoff, block_seg, total_bits, nsegs,
-              signmant, words, seg_desc, gaps, err, stream)
+    # work that does not depend on the sizes goes before the readback: the decode
+    # table (it needs only the code lengths) and the outputs of known size
     dtab = None
     if not per_block:
         dtab = torch.empty(zx_decode_table_bytes(), **u8)
         zx_build_decode_table(dtype, lengths, dtab, stream)
+    signmant = torch.empty(n if dtype == BF16 else (n + 1) // 2, **u8)
+    err = torch.zeros(1, **i32)
+    total_bits, nsegs = (int(v) for v in totals.cpu().tolist())
+    words = torch.empty(zx_stream_words(total_bits), **i32)
+    seg_desc = torch.empty((nsegs, 2), **i32)
+    gaps = torch.empty((nsegs, SEG_CHUNKS), **u8)
+    zx_encode(dtype, flat, n, per_block, lengths, degenerate, block_bitoff, block_seg, total_bits, nsegs,
+              signmant, words, seg_desc, gaps, err, stream)
     c = Compressed(dtype=dtype, per_block=int(per_block), n=n, shape=tuple(x.shape), total_bits=total_bits,
                    nsegs=nsegs, lengths=lengths, degenerate=degenerate, signmant=signmant, stream=words,
                    block_bitoff=block_bitoff, block_seg=block_seg, seg_desc=seg_desc, gaps=gaps, dtab=dtab,

@@ -46,7 +46,7 @@ def test_stream_words_rule(zx):
 
 def test_status_strings(zx):
     lib = zx.lib()
-    for s in range(6):
+    for s in range(7):
         assert lib.zx_status_string(s)
 
 
