@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--overlap-batches", type=int, nargs="+", default=[1, 16, 128, 1024, 4096])
     p.add_argument("--overlap-wgs", type=int, nargs="+", default=[0, 256, 128, 64],
                    help="caps on the decode's resident workgroups to try (0 = default)")
+    p.add_argument("--kv-slots", action="store_true",
+                   help="c5 only: fill the K/V cache online into fixed compressed slots, then decode slots on demand")
+    p.add_argument("--kv-bits", type=float, default=3.5, help="slot stream capacity in bits per element")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain device copies of 256 MiB (reference for HBM byte counters)")
@@ -271,6 +274,9 @@ def main():
         sys.exit(1)
     if args.overlap and args.config != "c3":
         print("--overlap applies to --config c3", file=sys.stderr)
+        sys.exit(2)
+    if args.kv_slots and args.config != "c5":
+        print("--kv-slots applies to --config c5", file=sys.stderr)
         sys.exit(2)
     if args.config in ("c1", "c2", "c4"):
         res = bench_single(args)

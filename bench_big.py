@@ -274,7 +274,102 @@ def run_overlap(args):
     }
 
 
+def run_kv_slots(args):
+    """K/V cache [2, 32, 8, 32768, 128] filled online into fixed compressed slots.
+
+    The cache grows by 512 tokens at a time; each such step completes one 65536-
+    element block in every (kv, layer, head) slab, 512 blocks in all, which one
+    zx_kv_encode_slots call compresses into their slots (no host synchronisation).
+    The 512 new blocks are first gathered into a contiguous staging buffer (where a
+    serving loop would have written the new tokens), outside the timed region.
+    Then reused blocks are decoded on demand: all 64 blocks of every slab of one
+    layer (2 x 8 x 64 = 1024 slots) in one zx_kv_decode_slots launch."""
+    from lossless_float_compression_amd.kvslots import KVSlotPool
+    t0 = time.time()
+    x = workloads.c5()                                   # int16 [2, 32, 8, 32768, 128]
+    raw = x.numel() * 2
+    nb_tok = 32768 // 512
+    xv = x.view(2, 32, 8, nb_tok, 512 * 128)             # block (kv, layer, head, t)
+    n_slabs = 2 * 32 * 8
+    pool = KVSlotPool(n_slabs * nb_tok, bits_per_elem=args.kv_bits)
+    stage = torch.empty((n_slabs, 512 * 128), dtype=torch.int16, device="cuda")
+    slab_ids = torch.arange(n_slabs, dtype=torch.int32, device="cuda")
+    status = torch.empty((nb_tok, n_slabs), dtype=torch.int32, device="cuda")
+    # slot of block (slab, t) = slab * nb_tok + t
+    ev = [_events(2) for _ in range(nb_tok)]
+    pool.append(xv[:, :, :, 0].reshape(n_slabs, -1).contiguous(), slab_ids * nb_tok, status=status[0])   # warm-up
+    torch.cuda.synchronize()
+    for t in range(nb_tok):
+        stage.copy_(xv[:, :, :, t].reshape(n_slabs, -1))
+        sid = slab_ids * nb_tok + t
+        ev[t][0].record()
+        pool.append(stage, sid, status=status[t])
+        ev[t][1].record()
+    torch.cuda.synchronize()
+    app_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    st = status.cpu().numpy()
+    overflow = int((st == 6).sum())
+    assert ((st == 0) | (st == 6)).all(), "append reported an error"
+    setup_s = time.time() - t0
+    blk_raw = n_slabs * 65536 * 2
+    # decode on demand: every block of layer 5 (both kv, 8 heads, 64 blocks each)
+    layer = 5
+    slots = [((kv * 32 + layer) * 8 + h) * nb_tok + t for kv in range(2) for h in range(8) for t in range(nb_tok)]
+    fits = [s for s in slots if st[s % nb_tok, s // nb_tok] == 0]
+    out = torch.empty((len(fits), 65536), dtype=torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fits_t = torch.tensor(fits, dtype=torch.int32, device="cuda")
+    for _ in range(args.warmup):
+        pool.decode(fits_t, out=out, err=err)
+    torch.cuda.synchronize()
+    dev = []
+    for _ in range(args.steps):
+        e = _events(2)
+        e[0].record()
+        pool.decode(fits_t, out=out, err=err)
+        e[1].record()
+        torch.cuda.synchronize()
+        dev.append(e[0].elapsed_time(e[1]))
+    assert int(err.item()) == 0
+    ref = x.view(2, 32, 8, nb_tok, 65536)
+    for i, s in enumerate(fits):
+        slab, t = divmod(s, nb_tok)
+        kv, rest = divmod(slab, 256)
+        l, h = divmod(rest, 8)
+        assert torch.equal(out[i].view(torch.int16), ref[kv, l, h, t]), f"slot {s} did not round-trip"
+    dec_ms = float(np.mean(dev))
+    app = float(app_ms[1:].mean()) if nb_tok > 1 else float(app_ms.mean())
+    used_bits = pool.block_bitoff[:, 1].sum().item()
+    # bytes the stored blocks occupy in their slots (the rest of each slot is reserve)
+    nseg_sum = pool.block_seg[:, 1].sum().item()
+    words = ((pool.block_bitoff[:, 1] + 31) // 32).sum().item()
+    stored = pool.n_slots * (pool.sizes.sm_bytes + pool.sizes.alphabet + 2 + 16 + 8) + words * 4 + nseg_sum * (64 + 8)
+    # algorithmic bytes of an append: raw blocks read, sign/mantissa bytes, code bits and
+    # gap bytes written (one gap byte per 128 code bits)
+    app_alg = blk_raw + n_slabs * 65536 + (used_bits / 8 + used_bits / 128) * n_slabs / pool.n_slots
+    return {
+        "metric": "K/V append: raw GB/s compressed into fixed slots per 512-token step; on-demand slot decode GB/s",
+        "value": round(blk_raw / (app * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u32", "data": "synthetic",
+        "config": {"workload": "c5 K/V cache [2,32,8,32768,128] filled 512 tokens at a time into one slot per "
+                               "65536-element block", "slots": pool.n_slots, "cap_words": pool.cap_words,
+                   "blocks_per_append": n_slabs},
+        "append_ms": round(app, 4), "append_blocks": n_slabs,
+        "append_roofline": {"bound": "hbm", "achieved": round(app_alg / (app * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": round(app_alg / (app * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "overflow_blocks": overflow,
+        "decode_slots": len(fits), "decode_ms": round(dec_ms, 4),
+        "decode_GBps": round(len(fits) * 65536 * 2 / (dec_ms * 1e-3) / 1e9, 2),
+        "pool_bytes": pool.nbytes(), "pool_ratio": round(pool.nbytes() / pool.raw_bytes(), 5),
+        "stored_ratio": round(stored / pool.raw_bytes(), 5),
+        "setup_s": round(setup_s, 1),
+    }
+
+
 def run(args):
+    if getattr(args, "kv_slots", False):
+        return run_kv_slots(args)
     if getattr(args, "overlap", False):
         return run_overlap(args)
     if args.config == "c3":

@@ -257,6 +257,15 @@ zx_status zx_kv_encode_slots(const zx_kv_pool *pool, const void *src, uint32_t n
  * block_bitoff, so no host copy of them is needed. */
 zx_status zx_kv_slot_container(const zx_kv_pool *pool, uint32_t slot, zx_container *out);
 
+/* Decode the blocks in slots slot_ids[0..count) (device u32 array) into rows of
+ * `out` (count * 65536 elements: row j holds slot slot_ids[j]) with one kernel
+ * launch, one workgroup per slot: reused K/V blocks decompressed on demand (ZipFloat
+ * page, 4.2).  A slot whose block did not fit holds no segments and leaves its row
+ * unwritten; a slot id >= n_slots sets err to ZX_E_CORRUPT and leaves its row
+ * unwritten. */
+zx_status zx_kv_decode_slots(const zx_kv_pool *pool, const uint32_t *slot_ids, uint32_t count,
+                             void *out, uint32_t *err, hipStream_t stream);
+
 /* Stream length in u32 words for a given number of code bits. */
 uint64_t zx_stream_words(uint64_t total_bits);
 const char *zx_status_string(zx_status s);

@@ -74,9 +74,23 @@ struct DecTensor {
     uint32_t segs_per_wg;
 };
 
+// Slot-list decode: workgroup g decodes the one-block container in slot
+// slot_ids[g] of a K/V slot pool.  t[0] then describes slot 0's container and the
+// strides below give every other slot's arrays; workgroup g's output is row g.
+struct DecSlots {
+    const uint32_t *slot_ids;   // null: no slot list
+    uint64_t sm_bytes;          // sign/mantissa bytes per slot
+    uint64_t stream_words;      // stream words per slot
+    uint64_t seg_stride;        // segment entries per slot
+    uint64_t out_bytes;         // output bytes per row
+    uint32_t alphabet;
+    uint32_t n_slots;
+};
+
 struct DecBatch {
     DecTensor t[kMaxBatch];
     uint32_t count;
+    DecSlots slots;
 };
 
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
@@ -884,7 +898,9 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
     }
 }
 
-template <int DT>
+// SLOTS: the batch is a slot list (DecSlots); a separate instantiation, so that the
+// tensor-batch decode keeps reading its descriptor straight from the kernel arguments.
+template <int DT, bool SLOTS>
 __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(const DecBatch batch, uint32_t *err)
 {
     constexpr uint32_t A = alphabet_of(DT);
@@ -899,10 +915,7 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
     static_assert(sizeof(Canon) <= sizeof(stage_all), "Canon is built inside the stage area");
 
     const uint32_t g = blockIdx.x;
-    uint32_t t = 0;
-    while (t + 1 < batch.count && g >= batch.t[t + 1].wg_begin) ++t;
-    const DecTensor &T = batch.t[t];
-    const uint32_t lg = g - T.wg_begin;
+    auto body = [&](const DecTensor &T, const uint32_t lg) {
     const uint32_t tid = threadIdx.x;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const uint32_t lane = lane_now();
@@ -974,6 +987,30 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
             metas[lane] = m2;
             wave_sync();
         }
+    }
+    };
+    if constexpr (SLOTS) {
+        const DecSlots &S = batch.slots;
+        const uint64_t slot = S.slot_ids[g];
+        if (slot >= S.n_slots) {
+            if (threadIdx.x == 0) report(err, ZX_E_CORRUPT);
+            return;
+        }
+        DecTensor T = batch.t[0];
+        T.signmant += slot * S.sm_bytes;
+        T.stream += slot * S.stream_words;
+        T.block_bitoff += 2 * slot;
+        T.block_seg += 2 * slot;
+        T.seg_desc += 2 * slot * S.seg_stride;
+        T.gaps += slot * S.seg_stride * kSegChunks;
+        T.lengths += slot * S.alphabet;
+        T.degenerate += slot;
+        T.out = static_cast<uint8_t *>(T.out) + (uint64_t)g * S.out_bytes;
+        body(T, 0);
+    } else {
+        uint32_t t = 0;
+        while (t + 1 < batch.count && g >= batch.t[t + 1].wg_begin) ++t;
+        body(batch.t[t], g - batch.t[t].wg_begin);
     }
 }
 
@@ -1081,9 +1118,55 @@ extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *cons
     batch.count = used;
     if (used == 0) return ZX_OK;
     if (dt == ZX_BF16)
-        hipLaunchKernelGGL(k_decode<ZX_BF16>, dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
+        hipLaunchKernelGGL((k_decode<ZX_BF16, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
     else
-        hipLaunchKernelGGL(k_decode<ZX_FP8_E4M3FN>, dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
+        hipLaunchKernelGGL((k_decode<ZX_FP8_E4M3FN, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
+    return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}
+
+extern "C" zx_status zx_kv_decode_slots(const zx_kv_pool *pool, const uint32_t *slot_ids, uint32_t count, void *out,
+                                        uint32_t *err, hipStream_t stream)
+{
+    zx_container c;
+    zx_kv_sizes sz;
+    if (!pool || zx_kv_slot_container(pool, 0, &c) != ZX_OK || zx_kv_slot_sizes((zx_dtype)pool->dtype, pool->cap_words, &sz) != ZX_OK)
+        return ZX_E_INVAL;
+    if (count == 0) return ZX_OK;
+    if (!slot_ids || !out || !aligned16(out) || count > 0x7FFFFFFFu) return ZX_E_INVAL;
+    DecBatch batch;
+    memset(&batch, 0, sizeof(batch));
+    DecTensor &T = batch.t[0];
+    T.signmant = c.signmant;
+    T.stream = c.stream;
+    T.block_bitoff = c.block_bitoff;
+    T.block_seg = c.block_seg;
+    T.seg_desc = c.seg_desc;
+    T.gaps = c.gaps;
+    T.lengths = c.lengths;
+    T.degenerate = c.degenerate;
+    T.dtab = nullptr;
+    T.out = out;
+    T.n = c.n;
+    T.total_bits = c.total_bits;
+    T.stream_words = c.stream_words;
+    T.nsegs = (uint32_t)c.nsegs;
+    T.nblocks = 1;
+    T.per_block = 1;
+    T.wg_begin = 0;
+    T.wg_count = count;
+    T.segs_per_wg = 0;
+    batch.count = 1;
+    batch.slots.slot_ids = slot_ids;
+    batch.slots.sm_bytes = sz.sm_bytes;
+    batch.slots.stream_words = sz.stream_words;
+    batch.slots.seg_stride = sz.seg_stride;
+    batch.slots.out_bytes = pool->dtype == ZX_BF16 ? 2ull * kBlock : (uint64_t)kBlock;
+    batch.slots.alphabet = sz.alphabet;
+    batch.slots.n_slots = pool->n_slots;
+    if (pool->dtype == ZX_BF16)
+        hipLaunchKernelGGL((k_decode<ZX_BF16, true>), dim3(count), dim3(kDecThreads), 0, stream, batch, err);
+    else
+        hipLaunchKernelGGL((k_decode<ZX_FP8_E4M3FN, true>), dim3(count), dim3(kDecThreads), 0, stream, batch, err);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
 }
 

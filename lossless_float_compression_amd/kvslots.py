@@ -125,17 +125,38 @@ class KVSlotPool:
             self._conts[slot] = c
         return c
 
-    def decode(self, slots: Sequence[int], out: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None,
-               stream=None) -> torch.Tensor:
-        """Decompress the blocks in `slots` (host ints) into out[j] (shape [k, 65536],
-        bf16 or float8_e4m3fn), up to 16 slots per kernel launch.  A slot whose block
-        did not fit holds no segments and leaves its row unwritten."""
-        k = len(slots)
+    def _out(self, k: int, out: Optional[torch.Tensor]) -> torch.Tensor:
         if out is None:
             tdt = torch.bfloat16 if self.dtype == _zx.BF16 else torch.float8_e4m3fn
             out = torch.empty((k, BLOCK), dtype=tdt, device=self.signmant.device)
         if out.shape[0] != k or out[0].numel() != BLOCK or not out.is_contiguous():
             raise ValueError("out must be contiguous [len(slots), 65536]")
+        return out
+
+    def decode(self, slots, out: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+        """Decompress the blocks in `slots` (a device int32 tensor, or host ints) into
+        out[j] (shape [k, 65536], bf16 or float8_e4m3fn) with one launch, one
+        workgroup per slot (zx_kv_decode_slots).  A slot whose block did not fit holds
+        no segments and leaves its row unwritten."""
+        if not torch.is_tensor(slots):
+            slots = torch.tensor(list(slots), dtype=torch.int32).to(self.signmant.device, non_blocking=True)
+        if slots.dtype != torch.int32 or not slots.is_cuda:
+            raise ValueError("slots must be a device int32 tensor or a sequence of ints")
+        k = slots.numel()
+        out = self._out(k, out)
+        st = _zx.lib().zx_kv_decode_slots(C.byref(self.pool), _zx._ptr(slots), k, _zx._ptr(out), _zx._ptr(err),
+                                          _zx._stream(stream))
+        if st != 0:
+            raise _zx.ZxError("zx_kv_decode_slots", st)
+        return out
+
+    def decode_containers(self, slots: Sequence[int], out: Optional[torch.Tensor] = None,
+                          err: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """As `decode`, through the per-slot containers and the tensor-batch decode
+        (up to 16 slots per launch)."""
+        k = len(slots)
+        out = self._out(k, out)
         rows = list(out.view(k, BLOCK))
         for i in range(0, k, _zx.MAX_BATCH):
             _zx.zx_decode_block_batch([self.container(s) for s in slots[i:i + _zx.MAX_BATCH]],

@@ -66,7 +66,7 @@ class zx_kv_sizes(C.Structure):
 EXPORTS = ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
            "zx_decode_table_bytes", "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_stream_words",
            "zx_status_string", "zx_version", "zx_kv_slot_sizes", "zx_kv_workspace_bytes", "zx_kv_encode_slots",
-           "zx_kv_slot_container")
+           "zx_kv_slot_container", "zx_kv_decode_slots")
 
 
 def lib():
@@ -98,9 +98,10 @@ def lib():
         L.zx_kv_workspace_bytes.restype = C.c_size_t
         L.zx_kv_encode_slots.argtypes = [C.POINTER(zx_kv_pool), P, U32, P, U32, P, C.c_size_t, P, P, P]
         L.zx_kv_slot_container.argtypes = [C.POINTER(zx_kv_pool), U32, C.POINTER(zx_container)]
+        L.zx_kv_decode_slots.argtypes = [C.POINTER(zx_kv_pool), P, U32, P, P, P]
         for f in ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
                   "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_kv_slot_sizes",
-                  "zx_kv_encode_slots", "zx_kv_slot_container"):
+                  "zx_kv_encode_slots", "zx_kv_slot_container", "zx_kv_decode_slots"):
             getattr(L, f).restype = I
         _lib = L
     return _lib

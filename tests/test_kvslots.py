@@ -148,14 +148,17 @@ def test_append_matches_oracle_and_decodes_on_demand():
     xb = np_u(x, np.uint16)
     for j, s in enumerate(slots):
         slot_matches_oracle(pool, s, xb[j], 0)
-    order = [3, 14, 5, 2, 0, 9, 11, 7]
-    say("kv decode 8 slots")
+    order = [3, 14, 5, 2, 0, 9, 11, 7, 3]               # any order, repeats allowed
     derr = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("kv decode 9 slots, slot list")
     y = pool.decode(order, err=derr)
+    say("kv decode 9 slots, containers")
+    y2 = pool.decode_containers(order, err=derr)
     torch.cuda.synchronize()
     assert int(derr.item()) == 0
     for i, s in enumerate(order):
         assert torch.equal(y[i].view(torch.int16), x[slots.index(s)]), s
+    assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
 
 
 @pytest.mark.gpu
@@ -169,6 +172,7 @@ def test_append_more_than_a_batch_and_rewrite_a_slot():
     assert status.tolist() == [0] * 24
     y = pool.decode(slots)
     assert torch.equal(y.view(torch.int16), x)
+    assert torch.equal(pool.decode_containers(slots).view(torch.int16), x)   # 16 per launch, then 8
     # overwrite slot 20 with another block: the slot holds that block only
     z = kv_blocks(0, 7)[5:6].contiguous()
     say("kv rewrite slot 20")
@@ -192,6 +196,13 @@ def test_block_that_does_not_fit_leaves_its_slot_empty():
     assert int(err.item()) == 6
     assert pool.block_seg[0].tolist() == [0, 0] and pool.block_seg[1].tolist() == [0, 0]
     assert torch.equal(pool.decode([2]).view(torch.int16), c)
+    # a slot id past the pool is reported and its row left alone
+    derr = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y = torch.zeros((2, BLOCK), dtype=torch.bfloat16, device="cuda")
+    pool.decode([2, 4], out=y, err=derr)
+    torch.cuda.synchronize()
+    assert int(derr.item()) == 4
+    assert torch.equal(y[0].view(torch.int16), c[0]) and not y[1].view(torch.int16).any()
 
 
 @pytest.mark.gpu
@@ -211,3 +222,4 @@ def test_fp8_slots():
         slot_matches_oracle(pool, s, xb[j], 1)
     y = pool.decode(slots)
     assert torch.equal(y.view(torch.uint8), x)
+    assert torch.equal(pool.decode_containers(slots).view(torch.uint8), x)
