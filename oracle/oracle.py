@@ -1,6 +1,7 @@
-"""ctypes marshalling for the C oracle in zx_oracle.c (test infrastructure only).
+"""ctypes marshalling for the C oracle in zx_oracle.c and zf_oracle.c (test
+infrastructure only).
 
-Every computation happens in the C file.  This module only converts between numpy
+Every computation happens in the C files.  This module only converts between numpy
 arrays and the C structures.
 """
 from __future__ import annotations
@@ -20,16 +21,18 @@ SEG_CHUNKS = 64
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "zx_oracle.c")
+_SRC_ZF = os.path.join(_HERE, "zf_oracle.c")
+ZF_BLOCK = 2048
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile zx_oracle.c with gcc into oracle/liboracle.so."""
+    """Compile zx_oracle.c and zf_oracle.c with gcc into oracle/liboracle.so."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-shared", "-fPIC",
-                               "-o", tmp, _SRC])
+                               "-o", tmp, _SRC, _SRC_ZF])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -43,6 +46,15 @@ class _CContainer(C.Structure):
         ("signmant", C.POINTER(C.c_uint8)), ("stream", C.POINTER(C.c_uint32)),
         ("block_bitoff", C.POINTER(C.c_uint64)), ("block_seg", C.POINTER(C.c_uint32)),
         ("seg_desc", C.POINTER(C.c_uint32)), ("gaps", C.POINTER(C.c_uint8)),
+    ]
+
+
+class _ZfContainer(C.Structure):
+    _fields_ = [
+        ("dtype", C.c_int32), ("reserved_", C.c_int32),
+        ("n", C.c_uint64), ("nblocks", C.c_uint64), ("nrecords", C.c_uint64), ("signmant_bytes", C.c_uint64),
+        ("lb", C.POINTER(C.c_uint8)), ("planes", C.POINTER(C.c_uint8)), ("rec_off", C.POINTER(C.c_uint64)),
+        ("records", C.POINTER(C.c_uint16)), ("signmant", C.POINTER(C.c_uint8)),
     ]
 
 
@@ -66,6 +78,13 @@ def load():
         lib.zxo_encode.argtypes = [C.c_int, P, C.c_uint64, C.c_int, C.c_int, C.POINTER(_CContainer)]
         lib.zxo_decode.argtypes = [C.POINTER(_CContainer), P]
         lib.zxo_free.argtypes = [C.POINTER(_CContainer)]
+        if lib.zfo_sizeof_container() != C.sizeof(_ZfContainer):
+            raise RuntimeError("oracle struct layout mismatch; rebuild oracle")
+        lib.zfo_mode.argtypes = [P, C.c_uint64, C.c_uint32]
+        lib.zfo_mode.restype = C.c_uint32
+        lib.zfo_encode.argtypes = [C.c_int, P, C.c_uint64, C.POINTER(_ZfContainer)]
+        lib.zfo_decode.argtypes = [C.POINTER(_ZfContainer), P]
+        lib.zfo_free.argtypes = [C.POINTER(_ZfContainer)]
         _lib = lib
     return _lib
 
@@ -249,3 +268,73 @@ def decode(c: Container) -> np.ndarray:
     if rc != 0:
         raise ValueError(f"oracle decode rejected the container rc={rc}")
     return out[: c.n]
+
+
+# ---------------------------------------------------------------- dominant-range codec
+
+@dataclass
+class ZfContainer:
+    """One tensor in the dominant-range layout (2048-element blocks; numpy arrays)."""
+    dtype: int
+    n: int
+    lb: np.ndarray          # uint8 [nblocks]
+    planes: np.ndarray      # uint8 [nblocks, 3, 256]
+    rec_off: np.ndarray     # uint64 [nblocks + 1]
+    records: np.ndarray     # uint16 [nrecords]
+    signmant: np.ndarray    # uint8 [n] or [ceil(n/2)]
+
+    @property
+    def nblocks(self) -> int:
+        return (self.n + ZF_BLOCK - 1) // ZF_BLOCK
+
+    def nbytes(self) -> int:
+        """All container bytes: every array plus a 64-byte header."""
+        return int(64 + self.lb.nbytes + self.planes.nbytes + self.rec_off.nbytes + self.records.nbytes
+                   + self.signmant.nbytes)
+
+
+def zf_mode(exps: np.ndarray, alphabet: int) -> int:
+    e = np.ascontiguousarray(exps, dtype=np.uint8)
+    return int(load().zfo_mode(_p(e), e.size, alphabet))
+
+
+def zf_encode(dtype: int, x: np.ndarray) -> ZfContainer:
+    """Encode raw bits (uint16 for BF16, uint8 for FP8) with the dominant-range codec."""
+    lib = load()
+    x = np.ascontiguousarray(x).reshape(-1)
+    want = np.uint16 if dtype == BF16 else np.uint8
+    if x.dtype != want:
+        x = x.view(want)
+    cc = _ZfContainer()
+    rc = lib.zfo_encode(dtype, _p(x) if x.size else None, x.size, C.byref(cc))
+    if rc != 0:
+        raise ValueError(f"oracle zf encode failed rc={rc}")
+    try:
+        nb = int(cc.nblocks)
+        c = ZfContainer(dtype=dtype, n=int(cc.n), lb=_arr(cc.lb, nb, np.uint8),
+                        planes=_arr(cc.planes, nb * 3 * 256, np.uint8).reshape(nb, 3, 256),
+                        rec_off=_arr(cc.rec_off, nb + 1, np.uint64), records=_arr(cc.records, cc.nrecords, np.uint16),
+                        signmant=_arr(cc.signmant, cc.signmant_bytes, np.uint8))
+    finally:
+        lib.zfo_free(C.byref(cc))
+    return c
+
+
+def zf_decode(c: ZfContainer) -> np.ndarray:
+    lib = load()
+    keep = [np.ascontiguousarray(a) for a in (c.lb, c.planes, c.rec_off, c.records, c.signmant)]
+    cc = _ZfContainer()
+    cc.dtype, cc.n, cc.nblocks, cc.nrecords = c.dtype, c.n, c.nblocks, keep[3].size
+    cc.signmant_bytes = keep[4].size
+    cc.lb = keep[0].ctypes.data_as(C.POINTER(C.c_uint8))
+    cc.planes = keep[1].ctypes.data_as(C.POINTER(C.c_uint8))
+    cc.rec_off = keep[2].astype(np.uint64).ctypes.data_as(C.POINTER(C.c_uint64)) if keep[2].dtype != np.uint64 \
+        else keep[2].ctypes.data_as(C.POINTER(C.c_uint64))
+    cc.records = keep[3].astype(np.uint16).ctypes.data_as(C.POINTER(C.c_uint16)) if keep[3].dtype != np.uint16 \
+        else keep[3].ctypes.data_as(C.POINTER(C.c_uint16))
+    cc.signmant = keep[4].ctypes.data_as(C.POINTER(C.c_uint8))
+    out = np.empty(max(c.n, 1), np.uint16 if c.dtype == BF16 else np.uint8)
+    rc = lib.zfo_decode(C.byref(cc), _p(out))
+    if rc != 0:
+        raise ValueError(f"oracle zf decode failed rc={rc}")
+    return out[:c.n]
