@@ -266,6 +266,49 @@ zx_status zx_kv_slot_container(const zx_kv_pool *pool, uint32_t slot, zx_contain
 zx_status zx_kv_decode_slots(const zx_kv_pool *pool, const uint32_t *slot_ids, uint32_t count,
                              void *out, uint32_t *err, hipStream_t stream);
 
+/* ---- dominant-range codec ---------------------------------------------------------
+ * A second codec behind the same conventions (ZipFloat page, sections 3.1-3.3): blocks
+ * of 2048 elements; per block, MD is the most frequent exponent (ties to the smallest)
+ * and l_b = MD - 6; every exponent is remapped to v = e - l_b modulo the exponent
+ * field; the low 3 bits of every v go into three 256-byte bit planes (plane p, byte k,
+ * bit i = bit p of element 8k+i's v), and each element with v >= 8 gets a 2-byte record
+ * (index << 5) | (v >> 3), in element order.  Sign and mantissa are stored as in
+ * zx_container (n bytes BF16, ceil(n/2) nibble bytes FP8).  No entropy coding: every
+ * element encodes and decodes on its own. */
+typedef struct zx_zf_container {
+    int32_t dtype;             /* zx_dtype                                            */
+    int32_t reserved_;
+    uint64_t n;                /* elements                                            */
+    uint64_t nrecords;         /* rec_off[nblocks]                                    */
+    const uint8_t *lb;         /* [nblocks], nblocks = ceil(n / 2048)                 */
+    const uint8_t *planes;     /* [nblocks][3][256]                                   */
+    const uint64_t *rec_off;   /* [nblocks + 1] exclusive prefix of records per block */
+    const uint16_t *records;   /* [nrecords]                                          */
+    const uint8_t *signmant;   /* as zx_container                                     */
+} zx_zf_container;
+
+/* Workspace bytes zx_zf_encode_size and zx_zf_encode need for n elements. */
+size_t zx_zf_scan_workspace_bytes(uint64_t n);
+
+/* Per-block l_b and record offsets, and the record total the caller reads back to size
+ * the record array (ZipFloat page, 3.2: MD and l_b = MD - 6; 3.3: the records).
+ *   in        n elements (BF16 u16 bits / FP8 u8 bits), 16-byte aligned
+ *   lb        out u8[nblocks];  rec_off  out u64[nblocks+1] (finished by zx_zf_encode)
+ *   workspace device, zx_zf_scan_workspace_bytes(n) bytes, kept for zx_zf_encode
+ *   total     out u64[1] (device): the number of records */
+zx_status zx_zf_encode_size(zx_dtype dtype, const void *in, uint64_t n, uint8_t *lb, uint64_t *rec_off,
+                            void *workspace, size_t ws_bytes, uint64_t *total, hipStream_t stream);
+
+/* Planes, records and sign/mantissa bytes; turns rec_off into the exclusive offsets.
+ *   planes  out u8[nblocks][3][256];  records  out u16[total_records];  signmant out */
+zx_status zx_zf_encode(zx_dtype dtype, const void *in, uint64_t n, const uint8_t *lb, uint64_t *rec_off,
+                       const void *workspace, uint64_t total_records, uint8_t *planes, uint16_t *records,
+                       uint8_t *signmant, hipStream_t stream);
+
+/* Decode (ZipFloat page, 3.3: reverse bit-matrix unpacking, every block on its own).
+ * err: optional device word, ZX_E_CORRUPT if a block's records run past nrecords. */
+zx_status zx_zf_decode(const zx_zf_container *c, void *out, uint32_t *err, hipStream_t stream);
+
 /* Stream length in u32 words for a given number of code bits. */
 uint64_t zx_stream_words(uint64_t total_bits);
 const char *zx_status_string(zx_status s);

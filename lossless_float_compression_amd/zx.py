@@ -63,10 +63,19 @@ class zx_kv_sizes(C.Structure):
     ]
 
 
+class zx_zf_container(C.Structure):
+    _fields_ = [
+        ("dtype", C.c_int32), ("reserved_", C.c_int32), ("n", C.c_uint64), ("nrecords", C.c_uint64),
+        ("lb", C.c_void_p), ("planes", C.c_void_p), ("rec_off", C.c_void_p), ("records", C.c_void_p),
+        ("signmant", C.c_void_p),
+    ]
+
+
 EXPORTS = ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
            "zx_decode_table_bytes", "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_stream_words",
            "zx_status_string", "zx_version", "zx_kv_slot_sizes", "zx_kv_workspace_bytes", "zx_kv_encode_slots",
-           "zx_kv_slot_container", "zx_kv_decode_slots")
+           "zx_kv_slot_container", "zx_kv_decode_slots", "zx_zf_scan_workspace_bytes", "zx_zf_encode_size",
+           "zx_zf_encode", "zx_zf_decode")
 
 
 def lib():
@@ -99,9 +108,15 @@ def lib():
         L.zx_kv_encode_slots.argtypes = [C.POINTER(zx_kv_pool), P, U32, P, U32, P, C.c_size_t, P, P, P]
         L.zx_kv_slot_container.argtypes = [C.POINTER(zx_kv_pool), U32, C.POINTER(zx_container)]
         L.zx_kv_decode_slots.argtypes = [C.POINTER(zx_kv_pool), P, U32, P, P, P]
+        L.zx_zf_scan_workspace_bytes.argtypes = [U64]
+        L.zx_zf_scan_workspace_bytes.restype = C.c_size_t
+        L.zx_zf_encode_size.argtypes = [I, P, U64, P, P, P, C.c_size_t, P, P]
+        L.zx_zf_encode.argtypes = [I, P, U64, P, P, P, U64, P, P, P, P]
+        L.zx_zf_decode.argtypes = [C.POINTER(zx_zf_container), P, P, P]
         for f in ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
                   "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_kv_slot_sizes",
-                  "zx_kv_encode_slots", "zx_kv_slot_container", "zx_kv_decode_slots"):
+                  "zx_kv_encode_slots", "zx_kv_slot_container", "zx_kv_decode_slots", "zx_zf_encode_size",
+                  "zx_zf_encode", "zx_zf_decode"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -308,3 +323,74 @@ def decompress_batch(cs: Sequence[Compressed], outs: Optional[List[torch.Tensor]
         outs = [empty_output(c) for c in cs]
     zx_decode_block_batch([c.container() for c in cs], outs, err, stream)
     return outs
+
+
+# ----------------------------------------------------------------- dominant-range codec
+
+ZF_BLOCK = 2048
+
+
+@dataclass
+class ZfCompressed:
+    """A tensor in the dominant-range layout (device tensors)."""
+    dtype: int
+    n: int
+    shape: tuple
+    nrecords: int
+    lb: torch.Tensor         # uint8 [nblocks]
+    planes: torch.Tensor     # uint8 [nblocks, 3, 256]
+    rec_off: torch.Tensor    # int64 [nblocks + 1]
+    records: torch.Tensor    # int16 [max(nrecords, 1)]
+    signmant: torch.Tensor   # uint8
+    fp8_scale: Optional[float] = None
+
+    def container(self) -> zx_zf_container:
+        return zx_zf_container(self.dtype, 0, self.n, self.nrecords, self.lb.data_ptr(), self.planes.data_ptr(),
+                               self.rec_off.data_ptr(), self.records.data_ptr(), self.signmant.data_ptr())
+
+    def nbytes(self) -> int:
+        """All container bytes: the arrays (records counted as stored) plus a 64-byte header."""
+        return int(64 + self.lb.numel() + self.planes.numel() + self.rec_off.numel() * 8 + 2 * self.nrecords
+                   + self.signmant.numel())
+
+    def raw_bytes(self) -> int:
+        return self.n * (2 if self.dtype == BF16 else 1)
+
+
+def compress_zf(x: torch.Tensor, fp8_scale: Optional[float] = None, stream=None) -> ZfCompressed:
+    """Encode a device tensor with the dominant-range codec: block parameters and
+    record offsets, one 8-byte read of the record total, then planes and records."""
+    dtype, flat = _as_bits(x)
+    if not flat.is_cuda:
+        raise ValueError("compress_zf expects a device tensor")
+    flat = flat.contiguous()
+    dev = flat.device
+    n = flat.numel()
+    nb = (n + ZF_BLOCK - 1) // ZF_BLOCK
+    L = lib()
+    ws = torch.empty(max(int(L.zx_zf_scan_workspace_bytes(n)), 16), dtype=torch.uint8, device=dev)
+    lb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    rec_off = torch.empty(nb + 1, dtype=torch.int64, device=dev)
+    total = torch.empty(1, dtype=torch.int64, device=dev)
+    s = _stream(stream)
+    _check("zx_zf_encode_size", L.zx_zf_encode_size(dtype, _ptr(flat), n, _ptr(lb), _ptr(rec_off), _ptr(ws), ws.numel(),
+                                                    _ptr(total), s))
+    planes = torch.empty((max(nb, 1), 3, 256), dtype=torch.uint8, device=dev)
+    signmant = torch.empty(max(n if dtype == BF16 else (n + 1) // 2, 1), dtype=torch.uint8, device=dev)
+    nrec = int(total.item())
+    records = torch.empty(max(nrec, 1), dtype=torch.int16, device=dev)
+    _check("zx_zf_encode", L.zx_zf_encode(dtype, _ptr(flat), n, _ptr(lb), _ptr(rec_off), _ptr(ws), nrec, _ptr(planes),
+                                          _ptr(records), _ptr(signmant), s))
+    return ZfCompressed(dtype=dtype, n=n, shape=tuple(x.shape), nrecords=nrec, lb=lb[:nb], planes=planes[:nb],
+                        rec_off=rec_off, records=records, signmant=signmant[:n if dtype == BF16 else (n + 1) // 2],
+                        fp8_scale=fp8_scale)
+
+
+def decompress_zf(c: ZfCompressed, out: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    if out is None:
+        tdt = torch.bfloat16 if c.dtype == BF16 else torch.float8_e4m3fn
+        out = torch.empty(c.shape, dtype=tdt, device=c.signmant.device)
+    cont = c.container()
+    _check("zx_zf_decode", lib().zx_zf_decode(C.byref(cont), _ptr(out), _ptr(err), _stream(stream)))
+    return out
