@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--overlap-batches", type=int, nargs="+", default=[1, 16, 128, 1024, 4096])
     p.add_argument("--overlap-wgs", type=int, nargs="+", default=[0, 256, 128, 64],
                    help="caps on the decode's resident workgroups to try (0 = default)")
+    p.add_argument("--codec", default="huffman", choices=["huffman", "zf"],
+                   help="zf: the dominant-range codec (2048-element blocks, 3 dense bit planes, outlier records)")
     p.add_argument("--kv-slots", action="store_true",
                    help="c5 only: fill the K/V cache online into fixed compressed slots, then decode slots on demand")
     p.add_argument("--kv-bits", type=float, default=3.5, help="slot stream capacity in bits per element")
@@ -278,7 +280,7 @@ def main():
     if args.kv_slots and args.config != "c5":
         print("--kv-slots applies to --config c5", file=sys.stderr)
         sys.exit(2)
-    if args.config in ("c1", "c2", "c4"):
+    if args.codec == "huffman" and args.config in ("c1", "c2", "c4"):
         res = bench_single(args)
     else:
         import bench_big

@@ -367,7 +367,106 @@ def run_kv_slots(args):
     }
 
 
+def _zf_alg_bytes(c) -> int:
+    """Algorithmic bytes of one dominant-range decode: the container read, the output written."""
+    nb = c.lb.numel()
+    return int(c.signmant.numel() + c.planes.numel() + 2 * c.nrecords + nb + 8 * (nb + 1) + c.raw_bytes())
+
+
+def _zf_inputs(cfg):
+    """(list of device tensors decoded per step, description) for the dominant-range bench."""
+    import bench
+    if cfg in ("c1", "c2", "c4"):
+        x, desc, _ = bench.make_input(cfg)
+        return [x], desc
+    if cfg == "c5":
+        return [workloads.c5()], "c5: BF16 K/V [2,32,8,32768,128], 0.5*t(5) with 4/128 channels x20"
+    # c3: layer 0's seven tensors (the per-layer decode unit)
+    per_layer = len(workloads.C3_SHAPES)
+    return [workloads.c3_tensor(i) for i in range(per_layer)], "c3: Llama-3-8B-shaped BF16, layer 0 (7 tensors)"
+
+
+def run_zf(args):
+    """Dominant-range codec (ZipFloat page, 3.1-3.3) on the same workloads as the
+    Huffman codec: decode launches back to back over copies rotating through >= 1 GiB
+    (one launch per tensor; a c3 step is layer 0's seven tensors), encode timed after
+    one untimed call, ratio of all container bytes to the raw tensor."""
+    t0 = time.time()
+    xs0, desc = _zf_inputs(args.config)
+    raw = sum(x.numel() * x.element_size() for x in xs0)
+    cs0 = [zx.compress_zf(x) for x in xs0]
+    alg = sum(_zf_alg_bytes(c) for c in cs0)
+    R = max(2, -(-(1 << 30) // (alg + raw)))
+    if raw * R > (24 << 30):
+        R = 1
+    copies = [xs0] + [[x.clone() for x in xs0] for _ in range(R - 1)]
+    cs = [cs0] + [[zx.compress_zf(x) for x in xs] for xs in copies[1:]]
+    outs = [[torch.empty_like(x) for x in xs] for xs in copies]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    # encode: one untimed call per tensor, then the timed ones
+    torch.cuda.synchronize()
+    enc = []
+    for _ in range(3):
+        e = _events(2)
+        e[0].record()
+        for x in xs0:
+            zx.compress_zf(x)
+        e[1].record()
+        torch.cuda.synchronize()
+        enc.append(e[0].elapsed_time(e[1]))
+    enc_ms = float(np.mean(enc[1:]))
+    import ctypes
+    L = zx.lib()
+    conts = [[c.container() for c in cc] for cc in cs]
+    optrs = [[ctypes.c_void_p(o.data_ptr()) for o in oo] for oo in outs]
+    eptr = ctypes.c_void_p(err.data_ptr())
+    sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step(k):
+        bad = 0
+        for c, o in zip(conts[k % R], optrs[k % R]):
+            bad |= L.zx_zf_decode(ctypes.byref(c), o, eptr, sptr)
+        return bad
+
+    for k in range(max(args.warmup, R)):
+        step(k)
+    torch.cuda.synchronize()
+    n_launch = max(args.steps, 100)
+    d0, d1 = _events(2)
+    d0.record()
+    bad = 0
+    for k in range(n_launch):
+        bad |= step(k)
+    d1.record()
+    torch.cuda.synchronize()
+    assert bad == 0 and int(err.item()) == 0
+    dec_ms = d0.elapsed_time(d1) / n_launch
+    for xs, oo in zip(copies, outs):
+        for x, o in zip(xs, oo):
+            assert torch.equal(o.view(x.dtype), x), "dominant-range decode did not round-trip"
+    comp = sum(c.nbytes() for c in cs0)
+    recs = sum(c.nrecords for c in cs0)
+    n_el = sum(c.n for c in cs0)
+    achieved = alg / (dec_ms * 1e-3) / 1e9
+    return {
+        "metric": "dominant-range codec: decode GB/s (output) and % HBM roofline; encode GB/s; compression ratio",
+        "value": round(raw / (dec_ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": n_launch,
+        "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+        "data": "synthetic", "config": {"workload": desc, "codec": "dominant-range (2048-element blocks, l_b = MD - 6)",
+                                        "elements": int(n_el), "raw_bytes": int(raw), "rotation_copies": R},
+        "decode_ms": round(dec_ms, 5), "encode_ms": round(enc_ms, 5),
+        "encode_GBps": round(raw / (enc_ms * 1e-3) / 1e9, 2),
+        "ratio": round(comp / raw, 5), "outlier_fraction": round(recs / n_el, 6),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_zf_decode",
+                     "alg_bytes_per_launch": int(alg // len(cs0))},
+        "setup_s": round(time.time() - t0, 1),
+    }
+
+
 def run(args):
+    if getattr(args, "codec", "huffman") == "zf":
+        return run_zf(args)
     if getattr(args, "kv_slots", False):
         return run_kv_slots(args)
     if getattr(args, "overlap", False):

@@ -15,7 +15,10 @@
 // Every step is element-parallel: a thread owns 8 consecutive elements, which are
 // exactly one byte of each plane.  Decode scatters a block's records into an LDS
 // array of high bits and then fuses each thread's 8 elements with one 16-byte (BF16)
-// or 8-byte (FP8) store, so it is bound by memory traffic alone.
+// or 8-byte (FP8) store, so it is bound by memory traffic alone.  The analysis and
+// decode passes take four blocks per workgroup step and issue all of a step's loads
+// first: one block's few bytes per thread would leave too little in flight to keep
+// HBM busy.
 #include "zx_common.h"
 
 namespace zxk {
@@ -76,53 +79,75 @@ __device__ __forceinline__ ZfIn<DT> zf_load(const void *__restrict__ in, uint64_
 
 __device__ __forceinline__ uint32_t zf_byte(const uint32_t (&v)[2], uint32_t k) { return (v[k / 4] >> (8 * (k % 4))) & 0xFFu; }
 
-// ---- analyze: l_b and the outlier count of every block
+// ---- analyze: l_b and the outlier count of every block.  A workgroup takes kZfUnroll
+// consecutive blocks per step, with every input load of the step issued first; wave
+// u then finds block u's most frequent exponent.
+constexpr uint32_t kZfUnroll = 4;
+static_assert(kZfUnroll == kZfThreads / kWave, "one wave per block of a step finds its mode");
+
 template <int DT>
-__global__ __launch_bounds__(kZfThreads) void k_zf_analyze(const void *__restrict__ in, uint64_t n, uint8_t *__restrict__ lb_out,
-                                                           uint64_t *__restrict__ counts)
+__global__ __launch_bounds__(kZfThreads) void k_zf_analyze(const void *__restrict__ in, uint64_t n, uint64_t nb,
+                                                           uint8_t *__restrict__ lb_out, uint64_t *__restrict__ counts)
 {
     constexpr uint32_t A = alphabet_of(DT);
-    __shared__ uint32_t hist[kZfThreads / kWave][256];
-    __shared__ uint32_t part[kZfThreads / kWave];
-    __shared__ uint32_t s_lb;
+    __shared__ uint32_t hist[kZfUnroll][kZfThreads / kWave][256];
+    __shared__ uint32_t part[kZfUnroll][kZfThreads / kWave];
+    __shared__ uint32_t s_lb[kZfUnroll];
     const uint32_t tid = threadIdx.x;
     const uint32_t wave = tid / kWave;
-    const uint64_t b = blockIdx.x;
-    const uint64_t e0 = b * kZfBlock + (uint64_t)tid * 8;
-    const uint32_t cnt = e0 >= n ? 0u : (n - e0 < 8 ? (uint32_t)(n - e0) : 8u);
-    const ZfIn<DT> x = zf_load<DT>(in, e0, cnt);
-    for (uint32_t i = tid; i < (kZfThreads / kWave) * 256; i += kZfThreads) (&hist[0][0])[i] = 0;
-    __syncthreads();
-    for (uint32_t k = 0; k < cnt; ++k) atomicAdd(&hist[wave][zf_byte(x.e, k)], 1u);
-    __syncthreads();
-    if (wave == 0) {
-        // most frequent exponent, ties to the smallest: maximise count << 8 | (255 - symbol)
-        uint32_t best = 0;
-        for (uint32_t s = lane_id(); s < A; s += kWave) {
-            uint32_t c = 0;
-            for (uint32_t w = 0; w < kZfThreads / kWave; ++w) c += hist[w][s];
-            const uint32_t key = (c << 8) | (255u - s);
-            best = key > best ? key : best;
+    for (uint64_t b0 = (uint64_t)blockIdx.x * kZfUnroll; b0 < nb; b0 += (uint64_t)gridDim.x * kZfUnroll) {
+        ZfIn<DT> x[kZfUnroll];
+        uint32_t cnt[kZfUnroll];
+#pragma unroll
+        for (uint32_t u = 0; u < kZfUnroll; ++u) {
+            const uint64_t e0 = (b0 + u) * kZfBlock + (uint64_t)tid * 8;
+            cnt[u] = e0 >= n ? 0u : (n - e0 < 8 ? (uint32_t)(n - e0) : 8u);
+            x[u] = zf_load<DT>(in, e0, cnt[u]);
         }
-        for (int o = kWave / 2; o >= 1; o >>= 1) {
-            const uint32_t y = (uint32_t)__shfl_xor((int)best, o, kWave);
-            best = y > best ? y : best;
+        for (uint32_t i = tid; i < kZfUnroll * (kZfThreads / kWave) * 256; i += kZfThreads) (&hist[0][0][0])[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (uint32_t u = 0; u < kZfUnroll; ++u)
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k)
+                if (k < cnt[u]) atomicAdd(&hist[u][wave][zf_byte(x[u].e, k)], 1u);
+        __syncthreads();
+        {
+            // wave u: block u's most frequent exponent, ties to the smallest (maximise
+            // count << 8 | (255 - symbol))
+            const uint32_t u = wave;
+            uint32_t best = 0;
+            for (uint32_t sy = lane_id(); sy < A; sy += kWave) {
+                uint32_t c = 0;
+                for (uint32_t w = 0; w < kZfThreads / kWave; ++w) c += hist[u][w][sy];
+                const uint32_t key = (c << 8) | (255u - sy);
+                best = key > best ? key : best;
+            }
+            for (int o = kWave / 2; o >= 1; o >>= 1) {
+                const uint32_t y = (uint32_t)__shfl_xor((int)best, o, kWave);
+                best = y > best ? y : best;
+            }
+            if (lane_id() == 0) s_lb[u] = ((255u - (best & 0xFFu)) + A - 6u) % A;
         }
-        if (lane_id() == 0) s_lb = ((255u - (best & 0xFFu)) + A - 6u) % A;
-    }
-    __syncthreads();
-    const uint32_t lb = s_lb;
-    uint32_t outl = 0;
-    for (uint32_t k = 0; k < cnt; ++k) outl += ((zf_byte(x.e, k) + A - lb) % A) >= 8u ? 1u : 0u;
-    uint32_t tot;
-    wave_excl_scan(outl, tot);
-    if (lane_id() == 0) part[wave] = tot;
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t s = 0;
-        for (uint32_t w = 0; w < kZfThreads / kWave; ++w) s += part[w];
-        lb_out[b] = (uint8_t)lb;
-        counts[b + 1] = s;   // scanned into offsets afterwards
+        __syncthreads();
+#pragma unroll
+        for (uint32_t u = 0; u < kZfUnroll; ++u) {
+            const uint32_t lb = s_lb[u];
+            uint32_t outl = 0;
+#pragma unroll
+            for (uint32_t k = 0; k < 8; ++k) outl += (k < cnt[u] && ((zf_byte(x[u].e, k) + A - lb) % A) >= 8u) ? 1u : 0u;
+            uint32_t tot;
+            wave_excl_scan(outl, tot);
+            if (lane_id() == 0) part[u][wave] = tot;
+        }
+        __syncthreads();
+        if (tid < kZfUnroll && b0 + tid < nb) {
+            uint32_t sum = 0;
+            for (uint32_t w = 0; w < kZfThreads / kWave; ++w) sum += part[tid][w];
+            lb_out[b0 + tid] = (uint8_t)s_lb[tid];
+            counts[b0 + tid + 1] = sum;   // scanned into offsets afterwards
+        }
+        __syncthreads();   // hist, part and s_lb are reused by the next step
     }
 }
 
@@ -257,7 +282,13 @@ __global__ __launch_bounds__(kZfThreads) void k_zf_encode(const void *__restrict
     }
 }
 
-// ---- decode: grid-stride over blocks
+// ---- decode: one block per 256-thread workgroup step, grid-stride; thread t owns
+// elements 8t..8t+7 (one byte of each plane, 8 sign/mantissa bytes or 4 nibble bytes,
+// one 16- or 8-byte store), so every load and store instruction of a wavefront covers
+// one contiguous range.  A step requests everything it reads at once, including one
+// record per thread (blocks with more than 256 records loop for the rest), scatters
+// the records into an LDS array of high bits (two arrays used in turn, so a step
+// needs two barriers), then fuses and stores.
 template <int DT>
 __global__ __launch_bounds__(kZfThreads) void k_zf_decode(uint64_t n, uint64_t nb, uint64_t nrec, const uint8_t *__restrict__ lbs,
                                                           const uint8_t *__restrict__ planes, const uint64_t *__restrict__ off,
@@ -266,13 +297,17 @@ __global__ __launch_bounds__(kZfThreads) void k_zf_decode(uint64_t n, uint64_t n
                                                           uint32_t *__restrict__ err)
 {
     constexpr uint32_t A = alphabet_of(DT);
-    __shared__ __align__(16) uint8_t high[kZfBlock];
+    __shared__ __align__(16) uint8_t high_all[2][kZfBlock];
     const uint32_t tid = threadIdx.x;
-    for (uint64_t b = blockIdx.x; b < nb; b += gridDim.x) {
+    uint32_t par = 0;
+    for (uint64_t b = blockIdx.x; b < nb; b += gridDim.x, par ^= 1u) {
+        uint8_t *high = high_all[par];
         const uint64_t e0 = b * kZfBlock + (uint64_t)tid * 8;
         const uint32_t cnt = e0 >= n ? 0u : (n - e0 < 8 ? (uint32_t)(n - e0) : 8u);
         const uint32_t lb = lbs[b];
         const uint64_t r0 = off[b], r1 = off[b + 1];
+        const bool rec_ok = r1 > r0 && r1 <= nrec;   // uniform
+        const uint32_t rv = (rec_ok && r0 + tid < r1) ? records[r0 + tid] : 0xFFFFFFFFu;
         const uint8_t *pb = planes + b * 3 * kZfPlaneBytes;
         const uint32_t p0 = pb[tid], p1 = pb[kZfPlaneBytes + tid], p2 = pb[2 * kZfPlaneBytes + tid];
         uint32_t smw[2] = {0, 0};
@@ -283,28 +318,23 @@ __global__ __launch_bounds__(kZfThreads) void k_zf_decode(uint64_t n, uint64_t n
             } else {
                 for (uint32_t k = 0; k < cnt; ++k) smw[k / 4] |= (uint32_t)signmant[e0 + k] << (8 * (k % 4));
             }
-        } else if (cnt) {
+        } else {
             if (cnt == 8)
                 smw[0] = *reinterpret_cast<const uint32_t *>(signmant + e0 / 2);
             else
                 for (uint32_t k = 0; k < cnt; k += 2) smw[0] |= (uint32_t)signmant[(e0 + k) / 2] << (4 * k);
         }
-        const bool has_rec = r1 > r0;   // uniform
-        if (has_rec) {
-            if (r1 < r0 || r1 > nrec) {
-                if (tid == 0) report(err, ZX_E_CORRUPT);
-                continue;
-            }
-            reinterpret_cast<uint64_t *>(high)[tid] = 0;
+        if (r1 > r0 && r1 > nrec && tid == 0) report(err, ZX_E_CORRUPT);
+        uint32_t hw[2] = {0, 0};
+        if (rec_ok) {
+            reinterpret_cast<uint2 *>(high)[tid] = make_uint2(0, 0);
             __syncthreads();
-            for (uint64_t k = r0 + tid; k < r1; k += kZfThreads) {
+            if (rv != 0xFFFFFFFFu) high[rv >> 5] = (uint8_t)(rv & 31u);
+            for (uint64_t k = r0 + kZfThreads + tid; k < r1; k += kZfThreads) {
                 const uint32_t r = records[k];
                 high[r >> 5] = (uint8_t)(r & 31u);
             }
             __syncthreads();
-        }
-        uint32_t hw[2] = {0, 0};
-        if (has_rec) {
             const uint2 h = reinterpret_cast<const uint2 *>(high)[tid];
             hw[0] = h.x; hw[1] = h.y;
         }
@@ -334,7 +364,6 @@ __global__ __launch_bounds__(kZfThreads) void k_zf_decode(uint64_t n, uint64_t n
             else
                 for (uint32_t k = 0; k < cnt; ++k) dst[k] = (uint8_t)(o[k / 4] >> (8 * (k % 4)));
         }
-        if (has_rec) __syncthreads();   // the next block's zeroing waits for these reads
     }
 }
 
@@ -343,6 +372,28 @@ __global__ __launch_bounds__(kZfThreads) void k_zf_decode(uint64_t n, uint64_t n
 using namespace zxk;
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Workgroups for a grid-stride pass over nb blocks, kZfUnroll per step: as many as
+// are resident at once (per_cu 256-thread workgroups per CU, from the kernel's
+// registers), so that no workgroup starts after the others have finished.
+static uint64_t zf_grid_waves(uint64_t nb);
+static uint64_t zf_grid(uint64_t nb, uint32_t per_cu)
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    const uint64_t steps = (nb + kZfUnroll - 1) / kZfUnroll;
+    return steps < (uint64_t)cus * per_cu ? steps : (uint64_t)cus * per_cu;
+}
+
+// Decode: one block per workgroup step, 8 resident 256-thread workgroups per CU.
+static uint64_t zf_grid_waves(uint64_t nb)
+{
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    return nb < (uint64_t)cus * 8 ? nb : (uint64_t)cus * 8;
+}
 
 extern "C" size_t zx_zf_scan_workspace_bytes(uint64_t n)
 {
@@ -365,10 +416,11 @@ extern "C" zx_status zx_zf_encode_size(zx_dtype dtype, const void *in, uint64_t 
         if (hipGetLastError() != hipSuccess) return ZX_E_HIP;
         return hipMemsetAsync(rec_off, 0, 8, stream) == hipSuccess ? ZX_OK : ZX_E_HIP;
     }
+    const uint64_t agrid = zf_grid(nb, 8);   // 56 VGPRs: 8 waves per SIMD
     if (dtype == ZX_BF16)
-        hipLaunchKernelGGL(k_zf_analyze<ZX_BF16>, dim3((uint32_t)nb), dim3(kZfThreads), 0, stream, in, n, lb, rec_off);
+        hipLaunchKernelGGL(k_zf_analyze<ZX_BF16>, dim3((uint32_t)agrid), dim3(kZfThreads), 0, stream, in, n, nb, lb, rec_off);
     else
-        hipLaunchKernelGGL(k_zf_analyze<ZX_FP8_E4M3FN>, dim3((uint32_t)nb), dim3(kZfThreads), 0, stream, in, n, lb, rec_off);
+        hipLaunchKernelGGL(k_zf_analyze<ZX_FP8_E4M3FN>, dim3((uint32_t)agrid), dim3(kZfThreads), 0, stream, in, n, nb, lb, rec_off);
     hipLaunchKernelGGL(k_zf_scan_tiles, dim3((uint32_t)ntiles), dim3(1024), 0, stream, nb, rec_off, tiles);
     hipLaunchKernelGGL(k_zf_scan_top, dim3(1), dim3(1024), 0, stream, (uint32_t)ntiles, tiles, total);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
@@ -403,10 +455,7 @@ extern "C" zx_status zx_zf_decode(const zx_zf_container *c, void *out, uint32_t 
     if (!out || !c->lb || !c->planes || !c->rec_off || !c->signmant || (c->nrecords && !c->records) || !aligned16(out) ||
         !aligned16(c->signmant) || nb > 0x7FFFFFFFull)
         return ZX_E_INVAL;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    const uint64_t grid = nb < (uint64_t)cus * 8 ? nb : (uint64_t)cus * 8;   // 8 resident 256-thread workgroups per CU
+    const uint64_t grid = zf_grid_waves(nb);
     if (c->dtype == ZX_BF16)
         hipLaunchKernelGGL(k_zf_decode<ZX_BF16>, dim3((uint32_t)grid), dim3(kZfThreads), 0, stream, c->n, nb, c->nrecords, c->lb,
                            c->planes, c->rec_off, c->records, c->signmant, out, err);
