@@ -63,15 +63,16 @@ def parse():
 
 
 DECODE_SOURCES = ("lossless_float_compression_amd/csrc/zx_decode.hip", "lossless_float_compression_amd/csrc/zx_common.h")
+ZF_SOURCES = ("lossless_float_compression_amd/csrc/zx_zf.hip", "lossless_float_compression_amd/csrc/zx_common.h")
 
 
-def decode_source_hash() -> str:
-    """Hash of the decode kernel's sources with comments and blank space removed, so
+def decode_source_hash(sources=DECODE_SOURCES) -> str:
+    """Hash of a decode kernel's sources with comments and blank space removed, so
     that only a change of the code itself invalidates counters taken on it."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
+    for f in sources:
         src = open(os.path.join(ROOT, f), encoding="utf-8").read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
         src = re.sub(r"//[^\n]*", " ", src)
@@ -84,11 +85,11 @@ WORKLOAD_SLUG = {"c1": "bf16_1024x1024", "c2": "bf16_4096x4096", "c3": "llama3_8
                  "c4": "fp8_e4m3_8192x8192", "c5": "bf16_kv_cache"}
 
 
-def profiled_traffic(cfg: str):
+def profiled_traffic(cfg: str, kernel: str = "k_decode", sources=DECODE_SOURCES):
     """HBM bytes per decode launch (FETCH_SIZE and WRITE_SIZE counters scaled by a plain
     copy of known size) from the committed counter summary, or None when there is none
     or the decode kernel's sources changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"k_decode_{WORKLOAD_SLUG[cfg]}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{WORKLOAD_SLUG[cfg]}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -96,7 +97,7 @@ def profiled_traffic(cfg: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256_16") != decode_source_hash():
+    if kv.get("source_sha256_16") != decode_source_hash(sources):
         return None
     try:
         return int(kv["hbm_bytes_per_launch"])

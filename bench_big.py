@@ -367,6 +367,11 @@ def run_kv_slots(args):
     }
 
 
+def _zf_traffic(cfg):
+    from bench import ZF_SOURCES, profiled_traffic
+    return profiled_traffic(cfg, "k_zf_decode", ZF_SOURCES)
+
+
 def _zf_alg_bytes(c) -> int:
     """Algorithmic bytes of one dominant-range decode: the container read, the output written."""
     nb = c.lb.numel()
@@ -458,7 +463,8 @@ def run_zf(args):
         "encode_GBps": round(raw / (enc_ms * 1e-3) / 1e9, 2),
         "ratio": round(comp / raw, 5), "outlier_fraction": round(recs / n_el, 6),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_zf_decode",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": _zf_traffic(args.config),
+                     "kernel": "k_zf_decode",
                      "alg_bytes_per_launch": int(alg // len(cs0))},
         "setup_s": round(time.time() - t0, 1),
     }
