@@ -282,6 +282,38 @@ __global__ __launch_bounds__(kZfThreads) void k_zf_encode(const void *__restrict
     }
 }
 
+// ---- decode arithmetic, four elements per 32-bit word (one per byte)
+
+// Bits 0..3 of q to bits 0, 8, 16, 24: the shifted copies q, q << 7, q << 14, q << 21
+// do not overlap, so the product has no carries.
+__device__ __forceinline__ uint32_t zf_spread4(uint32_t q) { return (q * 0x00204081u) & 0x01010101u; }
+
+// Remapped exponents of 4 elements (byte k = element k) from their plane nibbles and
+// high bits: the three plane bits below, the high bits above.
+__device__ __forceinline__ uint32_t zf_v4(uint32_t q0, uint32_t q1, uint32_t q2, uint32_t hi)
+{
+    return zf_spread4(q0) | (zf_spread4(q1) << 1) | (zf_spread4(q2) << 2) | (hi << 3);
+}
+
+// Byte-wise (a + b) mod 256.
+__device__ __forceinline__ uint32_t zf_add_bytes(uint32_t a, uint32_t b)
+{
+    return ((a & 0x7F7F7F7Fu) + (b & 0x7F7F7F7Fu)) ^ ((a ^ b) & 0x80808080u);
+}
+
+// Four BF16 values (two words) from 4 exponents and 4 sign/mantissa bytes: the
+// exponent rotated right by one bit per byte puts its low bit at bit 7 (next to the
+// mantissa, low byte) and its upper seven bits at 0..6 (next to the sign, high byte);
+// two bit-selects build all low and all high bytes, two byte permutes interleave them.
+__device__ __forceinline__ void zf_fuse_bf16(uint32_t e, uint32_t S, uint32_t &w0, uint32_t &w1)
+{
+    const uint32_t er = ((e >> 1) & 0x7F7F7F7Fu) | ((e << 7) & 0x80808080u);
+    const uint32_t lo = (er & 0x80808080u) | (S & 0x7F7F7F7Fu);
+    const uint32_t hi = (S & 0x80808080u) | (er & 0x7F7F7F7Fu);
+    w0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+    w1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+
 // ---- decode: one block per 256-thread workgroup step, grid-stride; thread t owns
 // elements 8t..8t+7 (one byte of each plane, 8 sign/mantissa bytes or 4 nibble bytes,
 // one 16- or 8-byte store), so every load and store instruction of a wavefront covers
@@ -338,19 +370,23 @@ __global__ __launch_bounds__(kZfThreads) void k_zf_decode(uint64_t n, uint64_t n
             const uint2 h = reinterpret_cast<const uint2 *>(high)[tid];
             hw[0] = h.x; hw[1] = h.y;
         }
-        uint32_t o[4] = {0, 0, 0, 0};
+        uint32_t o[4];
+        const uint32_t lrep = lb * 0x01010101u;
 #pragma unroll
-        for (uint32_t k = 0; k < 8; ++k) {
-            const uint32_t v = ((p0 >> k) & 1u) | (((p1 >> k) & 1u) << 1) | (((p2 >> k) & 1u) << 2) | (zf_byte(hw, k) << 3);
-            const uint32_t e = (v + lb) & (A - 1);
+        for (uint32_t h = 0; h < 2; ++h) {
+            const uint32_t v = zf_v4((p0 >> (4 * h)) & 0xFu, (p1 >> (4 * h)) & 0xFu, (p2 >> (4 * h)) & 0xFu, hw[h]);
             if (DT == ZX_BF16) {
-                const uint32_t sm = zf_byte(smw, k);
-                o[k / 2] |= (((sm & 0x80u) << 8) | (e << 7) | (sm & 0x7Fu)) << (16 * (k % 2));
+                zf_fuse_bf16(zf_add_bytes(v, lrep), smw[h], o[2 * h], o[2 * h + 1]);
             } else {
-                const uint32_t nib = (smw[0] >> (4 * k)) & 0xFu;
-                o[k / 4] |= (((nib & 0x8u) << 4) | (e << 3) | (nib & 0x7u)) << (8 * (k % 4));
+                // 4-bit field: v, l_b <= 15, so a plain add never carries out of a byte
+                const uint32_t e = (v + lrep) & 0x0F0F0F0Fu;
+                // sign/mantissa nibbles of elements 4h..4h+3, one per byte
+                const uint32_t nw = (smw[0] >> (16 * h)) & 0xFFFFu;
+                const uint32_t N = ((nw & 0x000Fu) | ((nw & 0x00F0u) << 4) | ((nw & 0x0F00u) << 8) | ((nw & 0xF000u) << 12));
+                o[h] = ((N & 0x08080808u) << 4) | (e << 3) | (N & 0x07070707u);
             }
         }
+        (void)A;
         if (DT == ZX_BF16) {
             uint16_t *dst = reinterpret_cast<uint16_t *>(out) + e0;
             if (cnt == 8)
