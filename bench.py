@@ -53,6 +53,8 @@ def parse():
                    help="caps on the decode's resident workgroups to try (0 = default)")
     p.add_argument("--codec", default="huffman", choices=["huffman", "zf"],
                    help="zf: the dominant-range codec (2048-element blocks, 3 dense bit planes, outlier records)")
+    p.add_argument("--shared-codebook", action="store_true",
+                   help="c3 only: one model-wide codebook over all 225 tensors instead of one per tensor")
     p.add_argument("--kv-slots", action="store_true",
                    help="c5 only: fill the K/V cache online into fixed compressed slots, then decode slots on demand")
     p.add_argument("--kv-bits", type=float, default=3.5, help="slot stream capacity in bits per element")

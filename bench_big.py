@@ -46,19 +46,21 @@ def run_c3(args):
     t0 = time.time()
     comps, raw_total, enc_ms = [], 0, []
     e = _events(2)
+    shared = getattr(args, "shared_codebook", False)
+    cb = zx.build_shared_codebook(workloads.c3_tensor(i) for i in range(len(names))) if shared else None
     for i, (name, shape) in enumerate(names):
         x = workloads.c3_tensor(i)
         raw_total += x.numel() * 2
         if i < per_layer:  # time the encode of layer 0 (its 7 tensors), after one untimed call
-            zx.compress(x)
+            zx.compress(x, codebook=cb)
             torch.cuda.synchronize()
             e[0].record()
-            c = zx.compress(x)
+            c = zx.compress(x, codebook=cb)
             e[1].record()
             torch.cuda.synchronize()
             enc_ms.append((e[0].elapsed_time(e[1]), x.numel() * 2))
         else:
-            c = zx.compress(x)
+            c = zx.compress(x, codebook=cb)
         comps.append(c)
         del x
     torch.cuda.synchronize()
@@ -106,7 +108,8 @@ def run_c3(args):
         "metric": METRIC, "value": round(raw_total / (dec_ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32", "data": "synthetic",
-        "config": {"workload": "c3: Llama-3-8B-shaped BF16 weights, one codebook per tensor, one batched call per layer",
+        "config": {"workload": "c3: Llama-3-8B-shaped BF16 weights, " + ("one model-wide codebook" if shared else
+                                                                             "one codebook per tensor") + ", one batched call per layer",
                    "elements": int(raw_total // 2), "raw_bytes": int(raw_total), "calls_per_step": len(groups)},
         "decode_ms": round(dec_ms, 4), "layer_decode_ms": round(lay_avg, 5), "lm_head_decode_ms": round(float(head_ms.mean()), 5),
         "layer_decode_GBps": round(layer_raw / (lay_avg * 1e-3) / 1e9, 2),

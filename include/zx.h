@@ -119,6 +119,14 @@ typedef struct zx_container {
 zx_status zx_histogram(zx_dtype dtype, const void *in, uint64_t n,
                        uint32_t *tensor_hist, uint32_t *block_hist, hipStream_t stream);
 
+/* Add the exponent counts of n elements to hist64 (u64[A], device, 8-byte aligned; the
+ * caller clears it before the first tensor).  Summed over all linear weights of a
+ * model it gives one model-wide codebook (DFloat11 article, 方法介绍: a Huffman tree
+ * built from the exponents of the model's weights), which every tensor then uses
+ * through zx_encode_size/zx_encode and one shared decode table. */
+zx_status zx_histogram_accumulate(zx_dtype dtype, const void *in, uint64_t n, uint64_t *hist64,
+                                  hipStream_t stream);
+
 /* Code lengths for n_codebooks histograms (DFloat11, 方法介绍: Huffman tree from the
  * exponent distribution; the length limit and tie rules are container v1).
  *   hist        u32[n_codebooks][A]
@@ -127,6 +135,12 @@ zx_status zx_histogram(zx_dtype dtype, const void *in, uint64_t n,
 zx_status zx_build_codebook(zx_dtype dtype, const uint32_t *hist, uint32_t n_codebooks,
                             uint32_t max_len, uint8_t *lengths, uint16_t *degenerate,
                             hipStream_t stream);
+
+/* zx_build_codebook for u64 counts (histograms summed over many tensors; counts must
+ * stay below 2^48). */
+zx_status zx_build_codebook_u64(zx_dtype dtype, const uint64_t *hist, uint32_t n_codebooks,
+                                uint32_t max_len, uint8_t *lengths, uint16_t *degenerate,
+                                hipStream_t stream);
 
 /* Block geometry for encoding: per-block stream bits and segment counts, scanned.
  * (Auxiliary read/write positions: DFloat11, 方法介绍, second component.)

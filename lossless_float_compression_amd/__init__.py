@@ -7,6 +7,6 @@ from .zx import (  # noqa: F401
     BF16, FP8_E4M3FN, BLOCK_ELEMS, Compressed, ZxError, compress, decompress, decompress_batch,
     empty_output, lib, zx_build_codebook, zx_build_decode_table, zx_decode, zx_decode_block_batch,
     zx_decode_table_bytes, zx_encode, zx_encode_size, zx_histogram, zx_stream_words,
-    ZF_BLOCK, ZfCompressed, compress_zf, decompress_zf,
+    ZF_BLOCK, ZfCompressed, compress_zf, decompress_zf, SharedCodebook, build_shared_codebook,
 )
 from .kvslots import KVSlotPool  # noqa: F401,E402

@@ -27,12 +27,14 @@ __device__ __forceinline__ uint64_t read_u64(uint64_t v, uint32_t i)
     return ((uint64_t)hi << 32) | lo;
 }
 
-template <int DT>
-__global__ __launch_bounds__(64) void k_codebook(const uint32_t *__restrict__ hist, uint32_t max_len,
+// H: the count type of the histograms (u32 per tensor or block, u64 for counts summed
+// over many tensors; the packed sort key needs counts below 2^48).
+template <int DT, typename H>
+__global__ __launch_bounds__(64) void k_codebook(const H *__restrict__ hist, uint32_t max_len,
                                                  uint8_t *__restrict__ lengths, uint16_t *__restrict__ degenerate)
 {
     constexpr uint32_t A = alphabet_of(DT);
-    __shared__ uint32_t cnt[256];
+    __shared__ H cnt[256];
     __shared__ uint16_t present[256];
     __shared__ uint16_t leaf_sym[256];
     __shared__ uint64_t w[512];          // leaves 0..k-1 (sorted), merged nodes k..2k-2
@@ -225,9 +227,9 @@ __global__ __launch_bounds__(64) void k_codebook(const uint32_t *__restrict__ hi
 
 using namespace zxk;
 
-extern "C" zx_status zx_build_codebook(zx_dtype dtype, const uint32_t *hist, uint32_t n_codebooks,
-                                       uint32_t max_len, uint8_t *lengths, uint16_t *degenerate,
-                                       hipStream_t stream)
+template <typename H>
+static zx_status build_codebook(zx_dtype dtype, const H *hist, uint32_t n_codebooks, uint32_t max_len, uint8_t *lengths,
+                                uint16_t *degenerate, hipStream_t stream)
 {
     if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
     const uint32_t minlen = dtype == ZX_BF16 ? 8 : 4;
@@ -236,8 +238,23 @@ extern "C" zx_status zx_build_codebook(zx_dtype dtype, const uint32_t *hist, uin
     if (!hist || !lengths || !degenerate) return ZX_E_INVAL;
     if (n_codebooks > 0x7FFFFFFFu) return ZX_E_INVAL;
     if (dtype == ZX_BF16)
-        hipLaunchKernelGGL(k_codebook<ZX_BF16>, dim3(n_codebooks), dim3(64), 0, stream, hist, max_len, lengths, degenerate);
+        hipLaunchKernelGGL((k_codebook<ZX_BF16, H>), dim3(n_codebooks), dim3(64), 0, stream, hist, max_len, lengths, degenerate);
     else
-        hipLaunchKernelGGL(k_codebook<ZX_FP8_E4M3FN>, dim3(n_codebooks), dim3(64), 0, stream, hist, max_len, lengths, degenerate);
+        hipLaunchKernelGGL((k_codebook<ZX_FP8_E4M3FN, H>), dim3(n_codebooks), dim3(64), 0, stream, hist, max_len, lengths,
+                           degenerate);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}
+
+extern "C" zx_status zx_build_codebook(zx_dtype dtype, const uint32_t *hist, uint32_t n_codebooks,
+                                       uint32_t max_len, uint8_t *lengths, uint16_t *degenerate,
+                                       hipStream_t stream)
+{
+    return build_codebook<uint32_t>(dtype, hist, n_codebooks, max_len, lengths, degenerate, stream);
+}
+
+extern "C" zx_status zx_build_codebook_u64(zx_dtype dtype, const uint64_t *hist, uint32_t n_codebooks,
+                                           uint32_t max_len, uint8_t *lengths, uint16_t *degenerate,
+                                           hipStream_t stream)
+{
+    return build_codebook<uint64_t>(dtype, hist, n_codebooks, max_len, lengths, degenerate, stream);
 }

@@ -19,7 +19,8 @@ constexpr uint32_t kHistUnroll = 4;   // 16-byte loads in flight per lane
 template <int DT>
 __global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restrict__ in, uint64_t n,
                                                             uint32_t *__restrict__ tensor_hist,
-                                                            uint32_t *__restrict__ block_hist)
+                                                            uint32_t *__restrict__ block_hist,
+                                                            unsigned long long *__restrict__ hist64)
 {
     constexpr uint32_t A = alphabet_of(DT);
     constexpr uint32_t S = A + 1;                 // copy stride in words
@@ -95,6 +96,7 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restri
         for (uint32_t g = 0; g < kGroups; ++g) t += h[g * S + tid];
         if (block_hist) block_hist[b * A + tid] = t;
         if (tensor_hist && t) atomicAdd(&tensor_hist[tid], t);
+        if (hist64 && t) atomicAdd(&hist64[tid], (unsigned long long)t);
     }
 }
 
@@ -126,8 +128,25 @@ extern "C" zx_status zx_histogram(zx_dtype dtype, const void *in, uint64_t n, ui
     }
     if (nblocks == 0) return ZX_OK;
     if (dtype == ZX_BF16)
-        hipLaunchKernelGGL(k_histogram<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, tensor_hist, block_hist);
+        hipLaunchKernelGGL(k_histogram<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, tensor_hist, block_hist,
+                           nullptr);
     else
-        hipLaunchKernelGGL(k_histogram<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, tensor_hist, block_hist);
+        hipLaunchKernelGGL(k_histogram<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, tensor_hist,
+                           block_hist, nullptr);
+    return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}
+
+extern "C" zx_status zx_histogram_accumulate(zx_dtype dtype, const void *in, uint64_t n, uint64_t *hist64, hipStream_t stream)
+{
+    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    if (!hist64 || (n && !in) || !aligned16(in) || ((uintptr_t)hist64 & 7u)) return ZX_E_INVAL;
+    const uint64_t nblocks = (n + kBlock - 1) / kBlock;
+    if (nblocks > 0x7FFFFFFFull) return ZX_E_INVAL;
+    if (nblocks == 0) return ZX_OK;
+    unsigned long long *h = reinterpret_cast<unsigned long long *>(hist64);
+    if (dtype == ZX_BF16)
+        hipLaunchKernelGGL(k_histogram<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, nullptr, nullptr, h);
+    else
+        hipLaunchKernelGGL(k_histogram<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, nullptr, nullptr, h);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
 }

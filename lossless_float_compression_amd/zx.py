@@ -75,7 +75,7 @@ EXPORTS = ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "
            "zx_decode_table_bytes", "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_stream_words",
            "zx_status_string", "zx_version", "zx_kv_slot_sizes", "zx_kv_workspace_bytes", "zx_kv_encode_slots",
            "zx_kv_slot_container", "zx_kv_decode_slots", "zx_zf_scan_workspace_bytes", "zx_zf_encode_size",
-           "zx_zf_encode", "zx_zf_decode")
+           "zx_zf_encode", "zx_zf_decode", "zx_histogram_accumulate", "zx_build_codebook_u64")
 
 
 def lib():
@@ -113,10 +113,12 @@ def lib():
         L.zx_zf_encode_size.argtypes = [I, P, U64, P, P, P, C.c_size_t, P, P]
         L.zx_zf_encode.argtypes = [I, P, U64, P, P, P, U64, P, P, P, P]
         L.zx_zf_decode.argtypes = [C.POINTER(zx_zf_container), P, P, P]
+        L.zx_histogram_accumulate.argtypes = [I, P, U64, P, P]
+        L.zx_build_codebook_u64.argtypes = [I, P, U32, U32, P, P, P]
         for f in ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
                   "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_kv_slot_sizes",
                   "zx_kv_encode_slots", "zx_kv_slot_container", "zx_kv_decode_slots", "zx_zf_encode_size",
-                  "zx_zf_encode", "zx_zf_decode"):
+                  "zx_zf_encode", "zx_zf_decode", "zx_histogram_accumulate", "zx_build_codebook_u64"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -248,15 +250,59 @@ def _as_bits(x: torch.Tensor):
     raise TypeError(f"unsupported dtype {x.dtype}")
 
 
+@dataclass
+class SharedCodebook:
+    """One codebook for many tensors (device tensors): lengths u8 [1, A], degenerate
+    int16 [1], and its decode table."""
+    dtype: int
+    lengths: torch.Tensor
+    degenerate: torch.Tensor
+    dtab: torch.Tensor
+
+
+def build_shared_codebook(tensors, max_len: int = 32, stream=None) -> SharedCodebook:
+    """A model-wide codebook: the exponent counts of all `tensors` (any iterable, read
+    once) summed in 64 bits (zx_histogram_accumulate), then one Huffman codebook and
+    one decode table."""
+    L = lib()
+    s = _stream(stream)
+    hist = None
+    dtype = dev = None
+    for t in tensors:
+        dt, flat = _as_bits(t)
+        if hist is None:
+            dtype, dev = dt, t.device
+            hist = torch.zeros(alphabet(dtype), dtype=torch.int64, device=dev)
+        elif dt != dtype:
+            raise TypeError("all tensors of a shared codebook must have one dtype")
+        flat = flat.contiguous()
+        _check("zx_histogram_accumulate", L.zx_histogram_accumulate(dtype, _ptr(flat), flat.numel(), _ptr(hist), s))
+    if hist is None:
+        raise ValueError("no tensors")
+    A = alphabet(dtype)
+    lengths = torch.empty((1, A), dtype=torch.uint8, device=dev)
+    degenerate = torch.empty(1, dtype=torch.int16, device=dev)
+    _check("zx_build_codebook_u64", L.zx_build_codebook_u64(dtype, _ptr(hist), 1, int(max_len), _ptr(lengths),
+                                                            _ptr(degenerate), s))
+    dtab = torch.empty(zx_decode_table_bytes(), dtype=torch.uint8, device=dev)
+    zx_build_decode_table(dtype, lengths, dtab, stream)
+    return SharedCodebook(dtype=dtype, lengths=lengths, degenerate=degenerate, dtab=dtab)
+
+
 def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_scale: Optional[float] = None,
-             stream=None) -> Compressed:
+             stream=None, codebook: Optional[SharedCodebook] = None) -> Compressed:
     """Encode a device tensor (bf16 or int16 bits -> BF16; float8_e4m3fn or uint8 bits -> FP8).
 
     Runs histogram -> codebook -> block sizes (and the decode table), reads back the
-    two totals (the single host synchronisation) to size the outputs, then encodes."""
+    two totals (the single host synchronisation) to size the outputs, then encodes.
+    With `codebook` (from build_shared_codebook), the tensor is coded with that
+    codebook and shares its decode table; an exponent without a code sets the
+    container's error word to ZX_E_CODEBOOK."""
     dtype, flat = _as_bits(x)
     if not flat.is_cuda:
         raise ValueError("compress expects a device tensor")
+    if codebook is not None and (per_block or codebook.dtype != dtype):
+        raise ValueError("a shared codebook needs per-tensor scope and the codebook's dtype")
     flat = flat.contiguous()
     dev = flat.device
     n = flat.numel()
@@ -266,14 +312,18 @@ def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_sc
     u8 = dict(dtype=torch.uint8, device=dev)
     i32 = dict(dtype=torch.int32, device=dev)
     block_hist = torch.empty((max(nb, 1), A), **i32)
-    tensor_hist = None if per_block else torch.empty(A, **i32)
-    lengths = torch.empty((max(ncb, 1), A), **u8)
-    degenerate = torch.empty(max(ncb, 1), dtype=torch.int16, device=dev)
+    tensor_hist = None if (per_block or codebook is not None) else torch.empty(A, **i32)
+    if codebook is None:
+        lengths = torch.empty((max(ncb, 1), A), **u8)
+        degenerate = torch.empty(max(ncb, 1), dtype=torch.int16, device=dev)
+    else:
+        lengths, degenerate = codebook.lengths, codebook.degenerate
     block_bitoff = torch.empty(nb + 1, dtype=torch.int64, device=dev)
     block_seg = torch.empty(nb + 1, **i32)
     totals = torch.empty(2, dtype=torch.int64, device=dev)
     zx_histogram(dtype, flat, n, tensor_hist, block_hist, stream)
-    zx_build_codebook(dtype, block_hist if per_block else tensor_hist, ncb, max_len, lengths, degenerate, stream)
+    if codebook is None:
+        zx_build_codebook(dtype, block_hist if per_block else tensor_hist, ncb, max_len, lengths, degenerate, stream)
     if per_block and nb == 0:
         lengths = lengths[:0]
         degenerate = degenerate[:0]
@@ -281,7 +331,9 @@ def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_sc
     # work that does not depend on the sizes goes before the readback: the decode
     # table (it needs only the code lengths) and the outputs of known size
     dtab = None
-    if not per_block:
+    if codebook is not None:
+        dtab = codebook.dtab
+    elif not per_block:
         dtab = torch.empty(zx_decode_table_bytes(), **u8)
         zx_build_decode_table(dtype, lengths, dtab, stream)
     signmant = torch.empty(n if dtype == BF16 else (n + 1) // 2, **u8)

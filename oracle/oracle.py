@@ -76,6 +76,7 @@ def load():
         lib.zxo_stream_words.argtypes = [C.c_uint64]
         lib.zxo_stream_words.restype = C.c_uint64
         lib.zxo_encode.argtypes = [C.c_int, P, C.c_uint64, C.c_int, C.c_int, C.POINTER(_CContainer)]
+        lib.zxo_encode_with_lengths.argtypes = [C.c_int, P, C.c_uint64, P, C.c_uint16, C.POINTER(_CContainer)]
         lib.zxo_decode.argtypes = [C.POINTER(_CContainer), P]
         lib.zxo_free.argtypes = [C.POINTER(_CContainer)]
         if lib.zfo_sizeof_container() != C.sizeof(_ZfContainer):
@@ -196,15 +197,21 @@ def _arr(ptr, count, dtype):
     return np.ctypeslib.as_array(ptr, shape=(int(count),)).copy().astype(dtype, copy=False)
 
 
-def encode(dtype: int, x: np.ndarray, per_block: bool = False, max_len: int = 32) -> Container:
-    """Encode raw bits (uint16 for BF16, uint8 for FP8) into a container."""
+def encode(dtype: int, x: np.ndarray, per_block: bool = False, max_len: int = 32, lengths=None,
+           degenerate: int = 0xFFFF) -> Container:
+    """Encode raw bits (uint16 for BF16, uint8 for FP8) into a container; with
+    `lengths` (and `degenerate`), use that codebook for the whole tensor."""
     lib = load()
     x = np.ascontiguousarray(x).reshape(-1)
     want = np.uint16 if dtype == BF16 else np.uint8
     if x.dtype != want:
         x = x.view(want)
     cc = _CContainer()
-    rc = lib.zxo_encode(dtype, _p(x) if x.size else None, x.size, int(per_block), int(max_len), C.byref(cc))
+    if lengths is not None:
+        ln = np.ascontiguousarray(lengths, dtype=np.uint8)
+        rc = lib.zxo_encode_with_lengths(dtype, _p(x) if x.size else None, x.size, _p(ln), int(degenerate), C.byref(cc))
+    else:
+        rc = lib.zxo_encode(dtype, _p(x) if x.size else None, x.size, int(per_block), int(max_len), C.byref(cc))
     if rc != 0:
         raise ValueError(f"oracle encode failed rc={rc}")
     try:

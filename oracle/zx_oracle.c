@@ -363,9 +363,15 @@ static int get_bit(const uint32_t *stream, uint64_t j) { return (int)((stream[j 
 /* ---- O6/O7: encode a whole tensor into a container --------------------------
  * per_block = 0: one codebook from the tensor's histogram; 1: one per block.
  * max_len: length limit handed to zxo_code_lengths. */
-int zxo_encode(int dtype, const void *x, uint64_t n, int per_block, int max_len, zxo_container *c)
+/* given_len: NULL, or a codebook (lengths[A] and degenerate symbol) to use for the
+ * whole tensor instead of the tensor's own, e.g. one codebook shared by all linear
+ * weights of a model (DFloat11 article, 方法介绍: a Huffman tree over the model's
+ * exponents); an exponent without a code is then ZXO_E_CODEBOOK. */
+static int encode_impl(int dtype, const void *x, uint64_t n, int per_block, int max_len, const uint8_t *given_len,
+                       uint16_t given_degen, zxo_container *c)
 {
     memset(c, 0, sizeof(*c));
+    if (given_len && per_block) return ZXO_E_INVAL;
     if (dtype != ZXO_BF16 && dtype != ZXO_FP8) return ZXO_E_INVAL;
     const uint32_t A = alphabet_of(dtype);
     if (max_len < (dtype == ZXO_BF16 ? 8 : 4) || max_len > ZXO_MAXLEN) return ZXO_E_CODEBOOK;
@@ -393,9 +399,18 @@ int zxo_encode(int dtype, const void *x, uint64_t n, int per_block, int max_len,
     for (uint64_t cb = 0; cb < c->ncb; cb++) {
         uint64_t lo = per_block ? cb * ZXO_BLOCK : 0;
         uint64_t hi = per_block ? (lo + ZXO_BLOCK < n ? lo + ZXO_BLOCK : n) : n;
-        zxo_histogram(exps + lo, hi - lo, A, hist);
-        int m = zxo_code_lengths(hist, (int)A, max_len, c->lengths + cb * A, c->degenerate + cb);
-        if (m < 0) { free(exps); free(codes); free(hist); zxo_free(c); return ZXO_E_CODEBOOK; }
+        if (given_len) {
+            memcpy(c->lengths + cb * A, given_len, A);
+            c->degenerate[cb] = given_degen;
+            for (uint64_t i = lo; i < hi; i++)
+                if (given_len[exps[i]] == 0 && exps[i] != given_degen) {
+                    free(exps); free(codes); free(hist); zxo_free(c); return ZXO_E_CODEBOOK;
+                }
+        } else {
+            zxo_histogram(exps + lo, hi - lo, A, hist);
+            int m = zxo_code_lengths(hist, (int)A, max_len, c->lengths + cb * A, c->degenerate + cb);
+            if (m < 0) { free(exps); free(codes); free(hist); zxo_free(c); return ZXO_E_CODEBOOK; }
+        }
         zxo_canonical_codes(c->lengths + cb * A, (int)A, codes + cb * A);
     }
     if (c->ncb == 0 && !per_block) {
@@ -459,6 +474,18 @@ int zxo_encode(int dtype, const void *x, uint64_t n, int per_block, int max_len,
     free(codes);
     free(hist);
     return ZXO_OK;
+}
+
+int zxo_encode(int dtype, const void *x, uint64_t n, int per_block, int max_len, zxo_container *c)
+{
+    return encode_impl(dtype, x, n, per_block, max_len, NULL, 0, c);
+}
+
+int zxo_encode_with_lengths(int dtype, const void *x, uint64_t n, const uint8_t *lengths, uint16_t degenerate,
+                            zxo_container *c)
+{
+    if (!lengths) return ZXO_E_INVAL;
+    return encode_impl(dtype, x, n, 0, ZXO_MAXLEN, lengths, degenerate, c);
 }
 
 /* ---- O8: bit-serial canonical decode with full consistency checks -----------
