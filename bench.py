@@ -233,6 +233,21 @@ def bench_single(args):
     c = cs[0]
     alg = decode_alg_bytes(c)
     achieved = alg / (dec_avg * 1e-3) / 1e9
+    # context only: the same tensor kept in pinned host memory and copied to the device
+    # per use, the offloading alternative the pages compare against
+    pinned = torch.empty(raw_bytes, dtype=torch.uint8, pin_memory=True)
+    dev_buf = torch.empty(raw_bytes, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        dev_buf.copy_(pinned, non_blocking=True)
+    h0, h1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    h0.record(stream)
+    for _ in range(20):
+        dev_buf.copy_(pinned, non_blocking=True)
+    h1.record(stream)
+    torch.cuda.synchronize()
+    h2d_gbps = raw_bytes * 20 / (h0.elapsed_time(h1) * 1e-3) / 1e9
+    del pinned, dev_buf
     res = {
         "metric": METRIC,
         "value": round(raw_bytes / (dec_avg * 1e-3) / 1e9, 2),
@@ -253,6 +268,7 @@ def bench_single(args):
         "encode_GBps": round(raw_bytes / (float(enc_ms.mean()) * 1e-3) / 1e9, 2),
         "ratio": round(c.nbytes() / raw_bytes, 5),
         "exponent_bits_per_element": round(c.total_bits / c.n, 5),
+        "context_h2d_copy_GBps": round(h2d_gbps, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(args.config),
                      "kernel": "k_decode", "alg_bytes_per_launch": alg},
