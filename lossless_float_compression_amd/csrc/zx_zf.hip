@@ -16,9 +16,7 @@
 // exactly one byte of each plane.  Decode scatters a block's records into an LDS
 // array of high bits and then fuses each thread's 8 elements with one 16-byte (BF16)
 // or 8-byte (FP8) store, so it is bound by memory traffic alone.  The analysis and
-// decode passes take four blocks per workgroup step and issue all of a step's loads
-// first: one block's few bytes per thread would leave too little in flight to keep
-// HBM busy.
+// decode passes run grid-stride, one block per workgroup step.
 #include "zx_common.h"
 
 namespace zxk {
@@ -79,75 +77,82 @@ __device__ __forceinline__ ZfIn<DT> zf_load(const void *__restrict__ in, uint64_
 
 __device__ __forceinline__ uint32_t zf_byte(const uint32_t (&v)[2], uint32_t k) { return (v[k / 4] >> (8 * (k % 4))) & 0xFFu; }
 
-// ---- analyze: l_b and the outlier count of every block.  A workgroup takes kZfUnroll
-// consecutive blocks per step, with every input load of the step issued first; wave
-// u then finds block u's most frequent exponent.
-constexpr uint32_t kZfUnroll = 4;
-static_assert(kZfUnroll == kZfThreads / kWave, "one wave per block of a step finds its mode");
+// ---- analyze: l_b and the outlier count of every block, one block per 256-thread
+// workgroup step (grid-stride, the next block's input requested before this one is
+// counted).  Exponents cluster on a few values, so one shared histogram would
+// serialise its atomics; lane l adds into copy l % C (C = 16 for BF16, 64 for FP8,
+// copies A + 1 words apart so one instruction's atomics on one value fall in
+// different banks), and thread t then sums bin t over the copies.
 
 template <int DT>
 __global__ __launch_bounds__(kZfThreads) void k_zf_analyze(const void *__restrict__ in, uint64_t n, uint64_t nb,
                                                            uint8_t *__restrict__ lb_out, uint64_t *__restrict__ counts)
 {
     constexpr uint32_t A = alphabet_of(DT);
-    __shared__ uint32_t hist[kZfUnroll][kZfThreads / kWave][256];
-    __shared__ uint32_t part[kZfUnroll][kZfThreads / kWave];
-    __shared__ uint32_t s_lb[kZfUnroll];
+    constexpr uint32_t C = DT == ZX_BF16 ? 16 : 64;   // histogram copies
+    constexpr uint32_t S = A + 1;                     // copy stride in words
+    __shared__ uint32_t hist[C * S];
+    __shared__ uint32_t wbest[kZfThreads / kWave];
+    __shared__ uint32_t part[kZfThreads / kWave];
     const uint32_t tid = threadIdx.x;
+    const uint32_t lane = lane_id();
     const uint32_t wave = tid / kWave;
-    for (uint64_t b0 = (uint64_t)blockIdx.x * kZfUnroll; b0 < nb; b0 += (uint64_t)gridDim.x * kZfUnroll) {
-        ZfIn<DT> x[kZfUnroll];
-        uint32_t cnt[kZfUnroll];
-#pragma unroll
-        for (uint32_t u = 0; u < kZfUnroll; ++u) {
-            const uint64_t e0 = (b0 + u) * kZfBlock + (uint64_t)tid * 8;
-            cnt[u] = e0 >= n ? 0u : (n - e0 < 8 ? (uint32_t)(n - e0) : 8u);
-            x[u] = zf_load<DT>(in, e0, cnt[u]);
-        }
-        for (uint32_t i = tid; i < kZfUnroll * (kZfThreads / kWave) * 256; i += kZfThreads) (&hist[0][0][0])[i] = 0;
+    uint32_t *const mine = hist + (lane % C) * S;
+    uint64_t b = blockIdx.x;
+    ZfIn<DT> x;
+    uint32_t cnt = 0;
+    if (b < nb) {
+        const uint64_t e0 = b * kZfBlock + (uint64_t)tid * 8;
+        cnt = e0 >= n ? 0u : (n - e0 < 8 ? (uint32_t)(n - e0) : 8u);
+        x = zf_load<DT>(in, e0, cnt);
+    }
+    for (; b < nb; b += gridDim.x) {
+        for (uint32_t i = tid; i < C * S; i += kZfThreads) hist[i] = 0;
         __syncthreads();
 #pragma unroll
-        for (uint32_t u = 0; u < kZfUnroll; ++u)
-#pragma unroll
-            for (uint32_t k = 0; k < 8; ++k)
-                if (k < cnt[u]) atomicAdd(&hist[u][wave][zf_byte(x[u].e, k)], 1u);
-        __syncthreads();
-        {
-            // wave u: block u's most frequent exponent, ties to the smallest (maximise
-            // count << 8 | (255 - symbol))
-            const uint32_t u = wave;
-            uint32_t best = 0;
-            for (uint32_t sy = lane_id(); sy < A; sy += kWave) {
-                uint32_t c = 0;
-                for (uint32_t w = 0; w < kZfThreads / kWave; ++w) c += hist[u][w][sy];
-                const uint32_t key = (c << 8) | (255u - sy);
-                best = key > best ? key : best;
-            }
-            for (int o = kWave / 2; o >= 1; o >>= 1) {
-                const uint32_t y = (uint32_t)__shfl_xor((int)best, o, kWave);
-                best = y > best ? y : best;
-            }
-            if (lane_id() == 0) s_lb[u] = ((255u - (best & 0xFFu)) + A - 6u) % A;
+        for (uint32_t k = 0; k < 8; ++k)
+            if (k < cnt) atomicAdd(&mine[zf_byte(x.e, k)], 1u);
+        // request the next block's input while this one is summed
+        const ZfIn<DT> cur = x;
+        const uint32_t ccur = cnt;
+        const uint64_t bn = b + gridDim.x;
+        cnt = 0;
+        if (bn < nb) {
+            const uint64_t e0 = bn * kZfBlock + (uint64_t)tid * 8;
+            cnt = e0 >= n ? 0u : (n - e0 < 8 ? (uint32_t)(n - e0) : 8u);
+            x = zf_load<DT>(in, e0, cnt);
         }
         __syncthreads();
-#pragma unroll
-        for (uint32_t u = 0; u < kZfUnroll; ++u) {
-            const uint32_t lb = s_lb[u];
-            uint32_t outl = 0;
-#pragma unroll
-            for (uint32_t k = 0; k < 8; ++k) outl += (k < cnt[u] && ((zf_byte(x[u].e, k) + A - lb) % A) >= 8u) ? 1u : 0u;
-            uint32_t tot;
-            wave_excl_scan(outl, tot);
-            if (lane_id() == 0) part[u][wave] = tot;
+        // most frequent exponent, ties to the smallest: maximise count << 8 | (255 - symbol)
+        uint32_t best = 0;
+        if (tid < A) {
+            uint32_t c = 0;
+#pragma unroll 8
+            for (uint32_t cp = 0; cp < C; ++cp) c += hist[cp * S + tid];
+            best = (c << 8) | (255u - tid);
         }
+        for (int o = kWave / 2; o >= 1; o >>= 1) {
+            const uint32_t y = (uint32_t)__shfl_xor((int)best, o, kWave);
+            best = y > best ? y : best;
+        }
+        if (lane == 0) wbest[wave] = best;
         __syncthreads();
-        if (tid < kZfUnroll && b0 + tid < nb) {
+        best = wbest[0];
+        for (uint32_t w = 1; w < kZfThreads / kWave; ++w) best = wbest[w] > best ? wbest[w] : best;
+        const uint32_t lb = ((255u - (best & 0xFFu)) + A - 6u) % A;
+        uint32_t outl = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < 8; ++k) outl += (k < ccur && ((zf_byte(cur.e, k) + A - lb) % A) >= 8u) ? 1u : 0u;
+        uint32_t tot;
+        wave_excl_scan(outl, tot);
+        if (lane == 0) part[wave] = tot;
+        __syncthreads();
+        if (tid == 0) {
             uint32_t sum = 0;
-            for (uint32_t w = 0; w < kZfThreads / kWave; ++w) sum += part[tid][w];
-            lb_out[b0 + tid] = (uint8_t)s_lb[tid];
-            counts[b0 + tid + 1] = sum;   // scanned into offsets afterwards
+            for (uint32_t w = 0; w < kZfThreads / kWave; ++w) sum += part[w];
+            lb_out[b] = (uint8_t)lb;
+            counts[b + 1] = sum;   // scanned into offsets afterwards
         }
-        __syncthreads();   // hist, part and s_lb are reused by the next step
     }
 }
 
@@ -409,20 +414,8 @@ using namespace zxk;
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Workgroups for a grid-stride pass over nb blocks, kZfUnroll per step: as many as
-// are resident at once (per_cu 256-thread workgroups per CU, from the kernel's
-// registers), so that no workgroup starts after the others have finished.
-static uint64_t zf_grid_waves(uint64_t nb);
-static uint64_t zf_grid(uint64_t nb, uint32_t per_cu)
-{
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    const uint64_t steps = (nb + kZfUnroll - 1) / kZfUnroll;
-    return steps < (uint64_t)cus * per_cu ? steps : (uint64_t)cus * per_cu;
-}
-
-// Decode: one block per workgroup step, 8 resident 256-thread workgroups per CU.
+// Analysis and decode: one block per workgroup step, 8 resident 256-thread workgroups
+// per CU.
 static uint64_t zf_grid_waves(uint64_t nb)
 {
     int dev = 0, cus = 256;
@@ -452,7 +445,7 @@ extern "C" zx_status zx_zf_encode_size(zx_dtype dtype, const void *in, uint64_t 
         if (hipGetLastError() != hipSuccess) return ZX_E_HIP;
         return hipMemsetAsync(rec_off, 0, 8, stream) == hipSuccess ? ZX_OK : ZX_E_HIP;
     }
-    const uint64_t agrid = zf_grid(nb, 8);   // 56 VGPRs: 8 waves per SIMD
+    const uint64_t agrid = zf_grid_waves(nb);   // one block per workgroup step
     if (dtype == ZX_BF16)
         hipLaunchKernelGGL(k_zf_analyze<ZX_BF16>, dim3((uint32_t)agrid), dim3(kZfThreads), 0, stream, in, n, nb, lb, rec_off);
     else
