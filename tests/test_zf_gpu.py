@@ -3,7 +3,8 @@ oracle (oracle/zf_oracle.c) byte for byte: per-block l_b, the three bit planes, 
 record offsets and records, and the sign/mantissa bytes; then the decode must give
 the input back bit for bit.  Sizes span several blocks and ragged tails, the record
 scan's tile seam (8192 blocks), every BF16 and FP8 bit pattern, and the empty tensor.
-A record offset past the record array is reported, not followed.
+A record offset past the record array is reported, not followed.  The 4096x4096 BF16,
+8192x8192 FP8 and 1 GiB BF16 K/V workloads are compared whole.
 """
 import sys
 
@@ -114,3 +115,18 @@ def test_corrupt_record_offset_is_reported():
     zx.decompress_zf(c2, err=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 4
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c4", "c5"])
+def test_full_size_workloads(cfg):
+    """The 4096x4096 BF16, 8192x8192 FP8 and [2,32,8,32768,128] BF16 K/V workloads
+    whole, as the bench encodes and decodes them."""
+    import workloads
+    say("zf full", cfg)
+    if cfg == "c2":
+        check(workloads.c2().cuda().view(torch.int16).reshape(-1), 0)
+    elif cfg == "c4":
+        q, _ = workloads.c4(device="cuda")
+        check(q.reshape(-1), 1)
+    else:
+        check(workloads.c5().reshape(-1), 0)
