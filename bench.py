@@ -248,6 +248,7 @@ def bench_single(args):
     torch.cuda.synchronize()
     h2d_gbps = raw_bytes * 20 / (h0.elapsed_time(h1) * 1e-3) / 1e9
     del pinned, dev_buf
+    from bench_big import copy_context_GBps
     res = {
         "metric": METRIC,
         "value": round(raw_bytes / (dec_avg * 1e-3) / 1e9, 2),
@@ -269,6 +270,7 @@ def bench_single(args):
         "ratio": round(c.nbytes() / raw_bytes, 5),
         "exponent_bits_per_element": round(c.total_bits / c.n, 5),
         "context_h2d_copy_GBps": round(h2d_gbps, 2),
+        "context_d2d_copy_GBps": copy_context_GBps(alg),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(args.config),
                      "kernel": "k_decode", "alg_bytes_per_launch": alg},

@@ -39,6 +39,32 @@ def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
+def copy_context_GBps(traffic: int) -> float:
+    """Context for a roofline fraction: device-to-device copies (hipMemcpyAsync, the
+    runtime's blit kernel) that each move `traffic` bytes, half read and half written,
+    rotated over at least 1 GiB of buffers and timed back to back like the decode
+    launches: the rate a copy-shaped kernel reaches at this transfer size, in the
+    same bytes-moved unit as roofline.achieved."""
+    half = max(traffic // 2 // 256 * 256, 256)
+    R = max(2, -(-(1 << 30) // (2 * half)))
+    src = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(R)]
+    dst = [torch.empty_like(a) for a in src]
+    for a, b in zip(src, dst):
+        a.fill_(1)
+        b.copy_(a)
+    n = max(100, R)
+    e0, e1 = _events(2)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        dst[i % R].copy_(src[i % R])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    del src, dst
+    return round(2 * half / (ms * 1e-3) / 1e9, 1)
+
+
 def run_c3(args):
     names = workloads.c3_names()
     n_layers = workloads.C3_LAYERS
@@ -118,6 +144,7 @@ def run_c3(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": _traffic("c3"), "kernel": "k_decode (one layer call)",
                      "alg_bytes_per_launch": int(layer_alg)},
+        "context_d2d_copy_GBps": copy_context_GBps(int(layer_alg)),
         "setup_s": round(setup_s, 1),
     }
 
@@ -171,6 +198,7 @@ def run_c5(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": _traffic("c5"), "kernel": "k_decode (per-block codebooks)",
                      "alg_bytes_per_launch": int(alg)},
+        "context_d2d_copy_GBps": copy_context_GBps(int(alg)),
         "setup_s": round(setup_s, 1),
     }
 
@@ -469,6 +497,7 @@ def run_zf(args):
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": _zf_traffic(args.config),
                      "kernel": "k_zf_decode",
                      "alg_bytes_per_launch": int(alg // len(cs0))},
+        "context_d2d_copy_GBps": copy_context_GBps(int(alg // len(cs0))),
         "setup_s": round(time.time() - t0, 1),
     }
 
