@@ -10,3 +10,4 @@ from .zx import (  # noqa: F401
     ZF_BLOCK, ZfCompressed, compress_zf, decompress_zf, SharedCodebook, build_shared_codebook,
 )
 from .kvslots import KVSlotPool  # noqa: F401,E402
+from .pipeline import LayerPipeline  # noqa: F401,E402
