@@ -129,6 +129,8 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _stream(stream=None):
+    if isinstance(stream, C.c_void_p):      # already marshalled
+        return stream
     s = torch.cuda.current_stream() if stream is None else stream
     return C.c_void_p(s.cuda_stream)
 
@@ -263,9 +265,13 @@ class SharedCodebook:
 def build_shared_codebook(tensors, max_len: int = 32, stream=None) -> SharedCodebook:
     """A model-wide codebook: the exponent counts of all `tensors` (any iterable, read
     once) summed in 64 bits (zx_histogram_accumulate), then one Huffman codebook and
-    one decode table."""
+    one decode table.  Everything runs on `stream` (a torch stream; default the
+    current one)."""
+    if stream is not None:
+        with torch.cuda.stream(stream):
+            return build_shared_codebook(tensors, max_len, None)
     L = lib()
-    s = _stream(stream)
+    s = _stream(None)
     hist = None
     dtype = dev = None
     for t in tensors:
@@ -285,7 +291,7 @@ def build_shared_codebook(tensors, max_len: int = 32, stream=None) -> SharedCode
     _check("zx_build_codebook_u64", L.zx_build_codebook_u64(dtype, _ptr(hist), 1, int(max_len), _ptr(lengths),
                                                             _ptr(degenerate), s))
     dtab = torch.empty(zx_decode_table_bytes(), dtype=torch.uint8, device=dev)
-    zx_build_decode_table(dtype, lengths, dtab, stream)
+    zx_build_decode_table(dtype, lengths, dtab, s)
     return SharedCodebook(dtype=dtype, lengths=lengths, degenerate=degenerate, dtab=dtab)
 
 
@@ -297,7 +303,13 @@ def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_sc
     two totals (the single host synchronisation) to size the outputs, then encodes.
     With `codebook` (from build_shared_codebook), the tensor is coded with that
     codebook and shares its decode table; an exponent without a code sets the
-    container's error word to ZX_E_CODEBOOK."""
+    container's error word to ZX_E_CODEBOOK.
+
+    `stream` (a torch stream; default the current one) carries every kernel, torch's
+    own fills and the synchronisation of the readback."""
+    if stream is not None:
+        with torch.cuda.stream(stream):
+            return compress(x, per_block, max_len, fp8_scale, None, codebook)
     dtype, flat = _as_bits(x)
     if not flat.is_cuda:
         raise ValueError("compress expects a device tensor")
@@ -309,24 +321,26 @@ def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_sc
     A = alphabet(dtype)
     nb = nblocks_of(n)
     ncb = nb if per_block else 1
+    stream = _stream(None)
     u8 = dict(dtype=torch.uint8, device=dev)
     i32 = dict(dtype=torch.int32, device=dev)
+    # each kernel is enqueued as soon as its buffers exist, so the GPU starts while
+    # the host allocates the rest
     block_hist = torch.empty((max(nb, 1), A), **i32)
     tensor_hist = None if (per_block or codebook is not None) else torch.empty(A, **i32)
+    zx_histogram(dtype, flat, n, tensor_hist, block_hist, stream)
     if codebook is None:
         lengths = torch.empty((max(ncb, 1), A), **u8)
         degenerate = torch.empty(max(ncb, 1), dtype=torch.int16, device=dev)
+        zx_build_codebook(dtype, block_hist if per_block else tensor_hist, ncb, max_len, lengths, degenerate, stream)
     else:
         lengths, degenerate = codebook.lengths, codebook.degenerate
-    block_bitoff = torch.empty(nb + 1, dtype=torch.int64, device=dev)
-    block_seg = torch.empty(nb + 1, **i32)
-    totals = torch.empty(2, dtype=torch.int64, device=dev)
-    zx_histogram(dtype, flat, n, tensor_hist, block_hist, stream)
-    if codebook is None:
-        zx_build_codebook(dtype, block_hist if per_block else tensor_hist, ncb, max_len, lengths, degenerate, stream)
     if per_block and nb == 0:
         lengths = lengths[:0]
         degenerate = degenerate[:0]
+    block_bitoff = torch.empty(nb + 1, dtype=torch.int64, device=dev)
+    block_seg = torch.empty(nb + 1, **i32)
+    totals = torch.empty(2, dtype=torch.int64, device=dev)
     zx_encode_size(dtype, flat, n, per_block, lengths, block_hist, block_bitoff, block_seg, totals, stream)
     # work that does not depend on the sizes goes before the readback: the decode
     # table (it needs only the code lengths) and the outputs of known size
@@ -411,7 +425,11 @@ class ZfCompressed:
 
 def compress_zf(x: torch.Tensor, fp8_scale: Optional[float] = None, stream=None) -> ZfCompressed:
     """Encode a device tensor with the dominant-range codec: block parameters and
-    record offsets, one 8-byte read of the record total, then planes and records."""
+    record offsets, one 8-byte read of the record total, then planes and records.
+    Everything runs on `stream` (a torch stream; default the current one)."""
+    if stream is not None:
+        with torch.cuda.stream(stream):
+            return compress_zf(x, fp8_scale, None)
     dtype, flat = _as_bits(x)
     if not flat.is_cuda:
         raise ValueError("compress_zf expects a device tensor")
@@ -424,7 +442,7 @@ def compress_zf(x: torch.Tensor, fp8_scale: Optional[float] = None, stream=None)
     lb = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     rec_off = torch.empty(nb + 1, dtype=torch.int64, device=dev)
     total = torch.empty(1, dtype=torch.int64, device=dev)
-    s = _stream(stream)
+    s = _stream(None)
     _check("zx_zf_encode_size", L.zx_zf_encode_size(dtype, _ptr(flat), n, _ptr(lb), _ptr(rec_off), _ptr(ws), ws.numel(),
                                                     _ptr(total), s))
     planes = torch.empty((max(nb, 1), 3, 256), dtype=torch.uint8, device=dev)

@@ -214,6 +214,47 @@ def test_encode_is_deterministic():
         assert_same_container(to_oracle(zx.compress(x)), a)
 
 
+def test_encode_on_a_busy_side_stream():
+    """compress, compress_zf and build_shared_codebook given a stream other than the
+    current one: torch's fills and the size readback run on that stream too, so the
+    sizes are read only after its kernels wrote them.  A long matmul queued first on
+    the side stream delays those kernels while the current stream stays idle."""
+    say("side stream")
+    x = rand_bf16(1 << 20, 8).cuda()
+    ref = to_oracle(zx.compress(x))
+    refz = zx.compress_zf(x)
+    a = torch.randn(4096, 4096, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+
+    def busy():
+        with torch.cuda.stream(s):
+            for _ in range(8):
+                torch.mm(a, a, out=b)
+
+    busy()
+    c = zx.compress(x, stream=s)
+    busy()
+    cz = zx.compress_zf(x, stream=s)
+    busy()
+    cb = zx.build_shared_codebook([x], stream=s)
+    c2 = zx.compress(x, stream=s, codebook=cb)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        y = zx.decompress(c, err=err, stream=s)
+    s.synchronize()
+    assert int(c._err.item()) == 0 and int(c2._err.item()) == 0 and int(err.item()) == 0
+    assert_same_container(to_oracle(c), ref)
+    assert_same_container(to_oracle(c2), ref)      # one tensor's shared codebook is its own
+    assert torch.equal(y.view(torch.int16), x.view(torch.int16))
+    assert cz.nrecords == refz.nrecords
+    for f in ("lb", "planes", "rec_off", "signmant"):
+        assert torch.equal(getattr(cz, f), getattr(refz, f)), f
+    assert torch.equal(cz.records[:cz.nrecords], refz.records[:refz.nrecords])
+
+
 # ------------------------------------------------------------------ batch decode
 
 def test_batch_equals_single():
