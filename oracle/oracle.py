@@ -15,6 +15,7 @@ import numpy as np
 
 BF16 = 0
 FP8 = 1
+E8M0 = 2     # FP4 block scale factors: bare 8-bit exponents, the whole byte is coded
 BLOCK = 65536
 CHUNK_BITS = 128
 SEG_CHUNKS = 64
@@ -91,7 +92,7 @@ def load():
 
 
 def _alphabet(dtype: int) -> int:
-    return 256 if dtype == BF16 else 16
+    return 16 if dtype == FP8 else 256
 
 
 def _p(a: np.ndarray):
@@ -138,9 +139,10 @@ def split(dtype: int, x: np.ndarray):
     x = np.ascontiguousarray(x)
     n = x.size
     exps = np.empty(max(n, 1), np.uint8)
-    sm = np.empty(max(n if dtype == BF16 else (n + 1) // 2, 1), np.uint8)
+    nsm = n if dtype == BF16 else (n + 1) // 2 if dtype == FP8 else 0
+    sm = np.empty(max(nsm, 1), np.uint8)
     lib.zxo_split(dtype, _p(x), n, _p(exps), _p(sm))
-    return exps[:n], sm[: (n if dtype == BF16 else (n + 1) // 2)]
+    return exps[:n], sm[:nsm]
 
 
 def histogram(exps: np.ndarray, alphabet: int) -> np.ndarray:

@@ -38,6 +38,7 @@
 /* ---- container v1 constants (format, not tuning) ---------------------------- */
 #define ZXO_BF16 0
 #define ZXO_FP8 1
+#define ZXO_E8M0 2                /* 8-bit exponent-only scale bytes (MX block scales) */
 #define ZXO_BLOCK 65536u          /* elements per block                          */
 #define ZXO_CHUNK_BITS 128u       /* stream bits per decode chunk                */
 #define ZXO_SEG_CHUNKS 64u        /* chunks per segment                          */
@@ -54,7 +55,7 @@
 #define ZXO_E_CORRUPT 4
 
 typedef struct zxo_container {
-    int32_t dtype;            /* ZXO_BF16 or ZXO_FP8                               */
+    int32_t dtype;            /* ZXO_BF16, ZXO_FP8 or ZXO_E8M0                     */
     int32_t per_block;        /* 0: one codebook for the tensor, 1: one per block  */
     uint64_t n;               /* element count                                     */
     uint64_t nblocks;         /* ceil(n / 65536)                                   */
@@ -73,7 +74,7 @@ typedef struct zxo_container {
     uint8_t *gaps;            /* [nsegs][64] first-codeword offset in each chunk    */
 } zxo_container;
 
-static uint32_t alphabet_of(int dtype) { return dtype == ZXO_BF16 ? 256u : 16u; }
+static uint32_t alphabet_of(int dtype) { return dtype == ZXO_FP8 ? 16u : 256u; }
 
 /* ---- O1: field split -------------------------------------------------------
  * BF16 bit layout s|eeeeeeee|mmmmmmm.  The exponent byte is coded; the sign and
@@ -83,7 +84,13 @@ static uint32_t alphabet_of(int dtype) { return dtype == ZXO_BF16 ? 256u : 16u; 
  * of byte i/2 when i is even and in the high nibble when i is odd. */
 void zxo_split(int dtype, const void *x, uint64_t n, uint8_t *exps, uint8_t *sm)
 {
-    if (dtype == ZXO_BF16) {
+    if (dtype == ZXO_E8M0) {
+        /* a block scale factor of the FP4 formats is a bare biased exponent: the
+         * whole byte is the symbol and there is no sign or mantissa */
+        const uint8_t *u = (const uint8_t *)x;
+        for (uint64_t i = 0; i < n; i++) exps[i] = u[i];
+        (void)sm;
+    } else if (dtype == ZXO_BF16) {
         const uint16_t *u = (const uint16_t *)x;
         for (uint64_t i = 0; i < n; i++) {
             uint16_t v = u[i];
@@ -114,7 +121,11 @@ void zxo_split(int dtype, const void *x, uint64_t n, uint8_t *exps, uint8_t *sm)
 /* ---- O9: reassembly (inverse of O1) ---------------------------------------- */
 static void join_fields(int dtype, const uint8_t *exps, const uint8_t *sm, uint64_t n, void *out)
 {
-    if (dtype == ZXO_BF16) {
+    if (dtype == ZXO_E8M0) {
+        uint8_t *o = (uint8_t *)out;
+        for (uint64_t i = 0; i < n; i++) o[i] = exps[i];
+        (void)sm;
+    } else if (dtype == ZXO_BF16) {
         uint16_t *o = (uint16_t *)out;
         for (uint64_t i = 0; i < n; i++) {
             uint16_t sign = (uint16_t)(sm[i] >> 7);
@@ -372,15 +383,15 @@ static int encode_impl(int dtype, const void *x, uint64_t n, int per_block, int 
 {
     memset(c, 0, sizeof(*c));
     if (given_len && per_block) return ZXO_E_INVAL;
-    if (dtype != ZXO_BF16 && dtype != ZXO_FP8) return ZXO_E_INVAL;
+    if (dtype != ZXO_BF16 && dtype != ZXO_FP8 && dtype != ZXO_E8M0) return ZXO_E_INVAL;
     const uint32_t A = alphabet_of(dtype);
-    if (max_len < (dtype == ZXO_BF16 ? 8 : 4) || max_len > ZXO_MAXLEN) return ZXO_E_CODEBOOK;
+    if (max_len < (A == 256u ? 8 : 4) || max_len > ZXO_MAXLEN) return ZXO_E_CODEBOOK;
     c->dtype = dtype;
     c->per_block = per_block;
     c->n = n;
     c->nblocks = (n + ZXO_BLOCK - 1) / ZXO_BLOCK;
     c->ncb = per_block ? c->nblocks : 1;
-    c->signmant_bytes = dtype == ZXO_BF16 ? n : (n + 1) / 2;
+    c->signmant_bytes = dtype == ZXO_BF16 ? n : dtype == ZXO_FP8 ? (n + 1) / 2 : 0;
 
     uint8_t *exps = (uint8_t *)malloc(n ? n : 1);
     c->signmant = (uint8_t *)malloc(c->signmant_bytes ? c->signmant_bytes : 1);
@@ -542,12 +553,12 @@ static int decode_symbol(const canon_table *t, const uint32_t *stream, uint64_t 
     return -1;
 }
 
-/* Decode c into out (BF16: n u16, FP8: n u8).  Checks, per block: the codes end
+/* Decode c into out (BF16: n u16, FP8 and E8M0: n u8).  Checks, per block: the codes end
  * exactly at the next block offset, every stored chunk gap and segment entry equals
  * the value the codeword boundaries imply, and padding is as specified. */
 int zxo_decode(const zxo_container *c, void *out)
 {
-    if (c->dtype != ZXO_BF16 && c->dtype != ZXO_FP8) return ZXO_E_INVAL;
+    if (c->dtype != ZXO_BF16 && c->dtype != ZXO_FP8 && c->dtype != ZXO_E8M0) return ZXO_E_INVAL;
     const uint32_t A = alphabet_of(c->dtype);
     uint64_t n = c->n;
     if (c->nblocks != (n + ZXO_BLOCK - 1) / ZXO_BLOCK) return ZXO_E_INVAL;

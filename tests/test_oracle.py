@@ -229,6 +229,22 @@ def test_split_fp8_matches_frexp(orc):
     assert np.array_equal(nibs[fin] >> 3, np.signbit(vals[fin]).astype(np.uint8))
 
 
+def test_split_e8m0_is_the_scale_exponent(orc):
+    # an E8M0 byte b stands for the scale 2^(b - 127) (b = 255: NaN); the coded
+    # symbol is the whole byte, i.e. that scale's biased exponent, and nothing else
+    # is stored
+    u = np.arange(256, dtype=np.uint8)
+    exps, sm = orc.split(2, u)
+    assert sm.size == 0
+    vals = torch.from_numpy(u).view(torch.float8_e8m0fnu).float().numpy().astype(np.float64)
+    fin = np.isfinite(vals)
+    assert (~fin).sum() == 1 and np.isnan(vals[255])
+    m, e = np.frexp(vals[fin])
+    assert np.all(m == 0.5)                       # powers of two only
+    assert np.array_equal(exps[fin], (e - 1 + 127).astype(np.uint8))
+    assert exps[255] == 255
+
+
 def test_histogram_is_bincount(orc):
     rng = np.random.default_rng(3)
     e = rng.integers(0, 256, size=100_003).astype(np.uint8)
@@ -244,8 +260,10 @@ def numpy_container_parts(dtype, x, lengths, per_block):
     n = x.size
     if dtype == 0:
         e = ((x.astype(np.uint32) >> 7) & 0xFF).astype(np.int64)
-    else:
+    elif dtype == 1:
         e = ((x.astype(np.uint32) >> 3) & 0xF).astype(np.int64)
+    else:
+        e = x.astype(np.int64)
     nb = (n + B - 1) // B
     codes = np.stack([np.asarray(__import__("oracle").canonical_codes(l), np.uint64) for l in lengths])
     cb = (np.arange(n) // B) if per_block else np.zeros(n, np.int64)
@@ -318,6 +336,15 @@ def test_container_fp8_rebuilt(orc, n, per_block):
     check_container(orc, 1, x.view(torch.uint8).numpy(), per_block)
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 4097, 65536, 131073])
+@pytest.mark.parametrize("per_block", [0, 1])
+def test_container_e8m0_rebuilt(orc, n, per_block):
+    # MX-FP4 block scales: a weight matrix with rows of 4096 inputs gives 128 per row
+    s = workloads.fp4_scales(-(-n // 128), 4096, idx=n).reshape(-1)[:n]
+    c = check_container(orc, 2, s, per_block)
+    assert c.signmant.size == 0
+
+
 # ---------------------------------------------------------------- exhaustive round trips
 
 def test_all_bf16_patterns(orc):
@@ -337,7 +364,15 @@ def test_all_fp8_patterns(orc):
             assert c.n == x.size
 
 
-@pytest.mark.parametrize("dtype", [0, 1])
+def test_all_e8m0_patterns(orc):
+    u = np.arange(256, dtype=np.uint8)
+    for x in (u, np.tile(u, 700), np.random.default_rng(2).permutation(np.tile(u, 300))):
+        for pb in (0, 1):
+            c = check_container(orc, 2, x, pb)
+            assert c.n == x.size
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2])
 def test_empty_and_constant(orc, dtype):
     c = orc.encode(dtype, np.zeros(0, np.uint16 if dtype == 0 else np.uint8))
     assert c.n == 0 and c.nsegs == 0 and c.stream.size == 260 and not c.stream.any()

@@ -16,6 +16,11 @@ for each workload:
       (kv, layer, head) slab, 4 of the 128 channels (drawn without replacement)
       are multiplied by 20; cast RNE
 
+  fp4 scales  E8M0 block scale factors of MX-FP4 weights: per 32 consecutive
+      input features of a N(0, 1/sqrt(fan_in)) weight, the byte
+      floor(log2(amax)) - 2 + 127 (2 = the largest exponent of FP4 E2M1),
+      clamped to [0, 254]; for the whole Llama-3-8B-shaped set of c3
+
 CPU generation uses numpy's PCG64 seeded with SeedSequence(0, spawn_key=(cfg, i)).
 The two big sets (c3: 15 GB, c5: 4.3 GB) are drawn on the GPU with a seeded torch
 generator, one tensor or slab at a time.  The values differ from the CPU draw, but
@@ -30,6 +35,8 @@ import torch
 
 BF16 = 0
 FP8 = 1
+E8M0 = 2
+MX_BLOCK = 32
 
 C3_LAYERS = 32
 C3_SHAPES = {  # name -> (out_features, in_features)
@@ -140,3 +147,34 @@ def c5(device="cuda") -> torch.Tensor:
         for layer in range(32):
             out[kv, layer] = c5_slab(kv, layer, device)
     return out
+
+
+def mx_scale_bytes(w: torch.Tensor) -> torch.Tensor:
+    """E8M0 scale bytes of MX-FP4 blocks of 32 along the last dimension of `w`
+    (float32): floor(log2(amax)) - 2 + 127, clamped to [0, 254]; an all-zero
+    block gets 0."""
+    a = w.abs().reshape(*w.shape[:-1], w.shape[-1] // MX_BLOCK, MX_BLOCK).amax(-1)
+    e = torch.floor(torch.log2(torch.where(a > 0, a, torch.ones_like(a)))) - 2 + 127
+    e = torch.where(a > 0, e, torch.zeros_like(e))
+    return e.clamp(0, 254).to(torch.uint8)
+
+
+def fp4_scales(out_f: int, in_f: int, idx: int = 0) -> np.ndarray:
+    """CPU draw: the scale bytes [out_f, in_f / 32] of one N(0, 1/sqrt(in_f)) weight."""
+    g = _rng(6, idx)
+    w = g.standard_normal(size=(out_f, in_f), dtype=np.float32) * np.float32(1.0 / math.sqrt(in_f))
+    return mx_scale_bytes(torch.from_numpy(w)).numpy()
+
+
+def fp4_scales_c3(device="cuda") -> torch.Tensor:
+    """Scale bytes of every tensor of the c3 set (call order of c3_names), drawn on
+    `device` one tensor at a time and concatenated: one uint8 tensor."""
+    parts = []
+    for index, (name, shape) in enumerate(c3_names()):
+        g = torch.Generator(device=device)
+        g.manual_seed(6_000_000 + index)
+        w = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        w.mul_(1.0 / math.sqrt(shape[1]))
+        parts.append(mx_scale_bytes(w).reshape(-1))
+        del w
+    return torch.cat(parts)
