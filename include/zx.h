@@ -86,7 +86,13 @@ typedef enum {
 
 typedef enum {
     ZX_BF16 = 0,           /* 8-bit exponent, alphabet 256 */
-    ZX_FP8_E4M3FN = 1      /* 4-bit exponent, alphabet 16  */
+    ZX_FP8_E4M3FN = 1,     /* 4-bit exponent, alphabet 16  */
+    ZX_E8M0 = 2            /* FP4 block scale factors (Intel summary, FP4 results; blog,
+                              FP4 section): one byte per element that is a bare biased
+                              exponent (value 2^(b-127)); the whole byte is coded, alphabet
+                              256, and there is no sign/mantissa array (signmant may be
+                              NULL).  Not supported by the K/V slot and dominant-range
+                              entry points. */
 } zx_dtype;
 
 /* One compressed tensor (a host struct holding device pointers). */

@@ -231,13 +231,13 @@ template <typename H>
 static zx_status build_codebook(zx_dtype dtype, const H *hist, uint32_t n_codebooks, uint32_t max_len, uint8_t *lengths,
                                 uint16_t *degenerate, hipStream_t stream)
 {
-    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
-    const uint32_t minlen = dtype == ZX_BF16 ? 8 : 4;
+    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN && dtype != ZX_E8M0) return ZX_E_UNSUPPORTED;
+    const uint32_t minlen = alphabet_of(dtype) == 256 ? 8 : 4;
     if (max_len < minlen || max_len > kMaxLen) return ZX_E_CODEBOOK;
     if (n_codebooks == 0) return ZX_OK;
     if (!hist || !lengths || !degenerate) return ZX_E_INVAL;
     if (n_codebooks > 0x7FFFFFFFu) return ZX_E_INVAL;
-    if (dtype == ZX_BF16)
+    if (alphabet_of(dtype) == 256)   // BF16 and E8M0: the kernel depends on the alphabet only
         hipLaunchKernelGGL((k_codebook<ZX_BF16, H>), dim3(n_codebooks), dim3(64), 0, stream, hist, max_len, lengths, degenerate);
     else
         hipLaunchKernelGGL((k_codebook<ZX_FP8_E4M3FN, H>), dim3(n_codebooks), dim3(64), 0, stream, hist, max_len, lengths,

@@ -28,7 +28,7 @@ constexpr int kWave = 64;
 constexpr int kLutBits = 11;
 constexpr uint32_t kLutSize = 1u << kLutBits;
 
-__host__ __device__ constexpr uint32_t alphabet_of(int dtype) { return dtype == ZX_BF16 ? 256u : 16u; }
+__host__ __device__ constexpr uint32_t alphabet_of(int dtype) { return dtype == ZX_FP8_E4M3FN ? 16u : 256u; }
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }

@@ -222,6 +222,7 @@ struct Piece {
 template <int DT>
 __device__ __forceinline__ uint2 load_sm(const uint8_t *sm_block, uint32_t i)
 {
+    if constexpr (DT == ZX_E8M0) return make_uint2(0, 0);   // no sign/mantissa array
     return *reinterpret_cast<const uint2 *>(sm_block + (DT == ZX_BF16 ? i : i / 2));
 }
 
@@ -247,6 +248,7 @@ __device__ __forceinline__ uint32_t cut_elem(uint32_t i_begin, uint32_t i_end)
 template <int DT>
 __device__ __forceinline__ uint32_t load_cut_sm(const uint8_t *sm_block, uint32_t ii)
 {
+    if constexpr (DT == ZX_E8M0) return 0u;
     return ii != ~0u ? (uint32_t)sm_block[DT == ZX_BF16 ? ii : ii / 2] : 0u;
 }
 
@@ -261,6 +263,12 @@ template <int DT>
 __device__ __forceinline__ void prefetch_sm(const uint8_t *sm_block, uint32_t i_begin, uint32_t i_end,
                                             const uint8_t *dummy, uint2 (&smv)[kWriteBatch], uint32_t &smcut)
 {
+    if constexpr (DT == ZX_E8M0) {   // nothing to read: the symbol is the whole element
+        smcut = 0;
+#pragma unroll
+        for (int k = 0; k < kWriteBatch; ++k) smv[k] = make_uint2(0, 0);
+        return;
+    }
     const uint32_t ii = cut_elem<DT>(i_begin, i_end);
     smcut = *(ii != ~0u ? sm_block + (DT == ZX_BF16 ? ii : ii / 2) : dummy);
     constexpr uint32_t P = Piece<DT>::kElems;
@@ -330,12 +338,22 @@ __device__ __forceinline__ uint32_t fuse_fp8_quad(uint32_t N, uint32_t E3)
     return x + (x & 0x08080808u) * 15u + E3;                             // sign bit 3 -> bit 7
 }
 
+// E8M0: four staged symbols (each rotated right by one bit, the form of a 256-symbol
+// alphabet) back to the bytes themselves.
+__device__ __forceinline__ uint32_t unrotate_quad(uint32_t E)
+{
+    return ((E << 1) & 0xFEFEFEFEu) | ((E >> 7) & 0x01010101u);
+}
+
 // Output words of one piece.
 template <int DT>
 __device__ __forceinline__ uint4 fuse_piece(uint2 smv, uint4 e)
 {
     uint4 r;
-    if (DT == ZX_BF16) {
+    if constexpr (DT == ZX_E8M0) {
+        (void)smv;
+        r = make_uint4(unrotate_quad(e.x), unrotate_quad(e.y), unrotate_quad(e.z), unrotate_quad(e.w));
+    } else if (DT == ZX_BF16) {
         const uint2 w01 = fuse_bf16_quad(smv.x, e.x);
         const uint2 w23 = fuse_bf16_quad(smv.y, e.y);
         r = make_uint4(w01.x, w01.y, w23.x, w23.y);
@@ -393,7 +411,9 @@ __device__ __forceinline__ void write_cut_pieces(void *out_block, uint32_t i_beg
     asm volatile("" ::"v"(smb));
     if (ii != ~0u) {
         const uint32_t ex = degen ? dform : stage[ii - sbase];
-        if (DT == ZX_BF16) {
+        if constexpr (DT == ZX_E8M0) {
+            reinterpret_cast<uint8_t *>(out_block)[ii] = (uint8_t)(unrotate_quad(ex) & 0xFFu);
+        } else if (DT == ZX_BF16) {
             reinterpret_cast<uint16_t *>(out_block)[ii] = (uint16_t)fuse_bf16_pair(smb, ex, kSelA01, kSelB01);
         } else {
             const uint32_t nn = (ii & 1) ? (smb >> 4) : (smb & 0xFu);
@@ -680,7 +700,7 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     const uint32_t j = m.j;
     const uint64_t lo = (uint64_t)b * kBlock;
     const uint32_t nb = (uint32_t)(((lo + kBlock < T.n) ? lo + kBlock : T.n) - lo);
-    const uint8_t *sm_block = T.signmant + (DT == ZX_BF16 ? lo : lo / 2);
+    const uint8_t *sm_block = DT == ZX_E8M0 ? T.signmant : T.signmant + (DT == ZX_BF16 ? lo : lo / 2);
     void *out_block = reinterpret_cast<uint8_t *>(T.out) + lo * (DT == ZX_BF16 ? 2 : 1);
     const uint32_t sbase = e0 & ~15u;   // 16-aligned element that stage byte 0 stands for
 
@@ -1032,7 +1052,7 @@ extern "C" size_t zx_decode_table_bytes(void) { return sizeof(DTab); }
 
 extern "C" zx_status zx_build_decode_table(zx_dtype dtype, const uint8_t *lengths, uint32_t *dtab, hipStream_t stream)
 {
-    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN && dtype != ZX_E8M0) return ZX_E_UNSUPPORTED;
     if (!lengths || !dtab || !aligned16(dtab)) return ZX_E_INVAL;
     // one table entry per thread
     hipLaunchKernelGGL(k_build_dtab, dim3(1), dim3(1024), 0, stream, lengths, alphabet_of(dtype), reinterpret_cast<DTab *>(dtab));
@@ -1042,11 +1062,11 @@ extern "C" zx_status zx_build_decode_table(zx_dtype dtype, const uint8_t *length
 static zx_status check_container(const zx_container *c, const void *out)
 {
     if (!c) return ZX_E_INVAL;
-    if (c->dtype != ZX_BF16 && c->dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    if (c->dtype != ZX_BF16 && c->dtype != ZX_FP8_E4M3FN && c->dtype != ZX_E8M0) return ZX_E_UNSUPPORTED;
     if (c->n == 0) return ZX_OK;
     const uint64_t nblocks = (c->n + kBlock - 1) / kBlock;
     if (nblocks > 0x7FFFFFFFull || c->nsegs > 0xFFFFFFFFull || c->nsegs < nblocks) return ZX_E_INVAL;
-    if (!out || !c->lengths || !c->degenerate || !c->signmant || !c->stream || !c->block_bitoff || !c->block_seg || !c->seg_desc ||
+    if (!out || !c->lengths || !c->degenerate || (!c->signmant && c->dtype != ZX_E8M0) || !c->stream || !c->block_bitoff || !c->block_seg || !c->seg_desc ||
         !c->gaps)
         return ZX_E_INVAL;
     if (!c->per_block && !c->dtab) return ZX_E_INVAL;
@@ -1119,6 +1139,8 @@ extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *cons
     if (used == 0) return ZX_OK;
     if (dt == ZX_BF16)
         hipLaunchKernelGGL((k_decode<ZX_BF16, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
+    else if (dt == ZX_E8M0)
+        hipLaunchKernelGGL((k_decode<ZX_E8M0, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
     else
         hipLaunchKernelGGL((k_decode<ZX_FP8_E4M3FN, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;

@@ -50,6 +50,8 @@ __global__ __launch_bounds__(kSizeThreads) void k_block_bits(const void *__restr
             uint32_t e;
             if (DT == ZX_BF16)
                 e = (reinterpret_cast<const uint16_t *>(in)[i] >> 7) & 0xFFu;
+            else if (DT == ZX_E8M0)
+                e = reinterpret_cast<const uint8_t *>(in)[i];
             else
                 e = (reinterpret_cast<const uint8_t *>(in)[i] >> 3) & 0xFu;
             bits += len[e];
@@ -239,7 +241,9 @@ __device__ __forceinline__ void encode_onepass(const BlockIn<DT> &x, uint64_t lo
 #pragma unroll
     for (uint32_t r = 0; r < kRoundsPerBlock; ++r) {
         const uint32_t i0 = r * kRound + tid * kEncPerThread;
-        if (DT == ZX_BF16) {
+        if (DT == ZX_E8M0) {
+            *reinterpret_cast<uint2 *>(symbuf + i0) = make_uint2(x.w[r][0], x.w[r][1]);
+        } else if (DT == ZX_BF16) {
             uint32_t t[4];
 #pragma unroll
             for (uint32_t w = 0; w < 4; ++w) {
@@ -505,7 +509,16 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
         if (r + 1 < nrounds) load_raw(r + 1, nxt);
         uint32_t u[kEncPerThread];
         // ---- split
-        if (DT == ZX_BF16) {
+        if (DT == ZX_E8M0) {
+            const uint8_t *src = reinterpret_cast<const uint8_t *>(in) + lo + i0;
+            if (have == kEncPerThread) {
+#pragma unroll
+                for (uint32_t k = 0; k < kEncPerThread; ++k) u[k] = (cur[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+            } else {
+#pragma unroll
+                for (uint32_t k = 0; k < kEncPerThread; ++k) u[k] = (k < have) ? src[k] : 0u;
+            }
+        } else if (DT == ZX_BF16) {
             const uint16_t *src = reinterpret_cast<const uint16_t *>(in) + lo + i0;
             if (have == kEncPerThread) {
 #pragma unroll
@@ -548,7 +561,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
         uint32_t tb = 0;
 #pragma unroll
         for (uint32_t k = 0; k < kEncPerThread; ++k) {
-            sym[k] = (DT == ZX_BF16) ? ((u[k] >> 7) & 0xFFu) : ((u[k] >> 3) & 0xFu);
+            sym[k] = (DT == ZX_BF16) ? ((u[k] >> 7) & 0xFFu) : (DT == ZX_E8M0) ? u[k] : ((u[k] >> 3) & 0xFu);
             if (k < have) {
                 const uint32_t l = c.len[sym[k]];
                 if (bits ? (l == 0) : (sym[k] != degen)) bad = true;
@@ -752,7 +765,7 @@ extern "C" zx_status zx_encode_size(zx_dtype dtype, const void *in, uint64_t n, 
                                     uint64_t *block_bitoff, uint32_t *block_seg, uint64_t *totals,
                                     hipStream_t stream)
 {
-    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN && dtype != ZX_E8M0) return ZX_E_UNSUPPORTED;
     if (!block_bitoff || !block_seg || !totals) return ZX_E_INVAL;
     const uint64_t nblocks = (n + kBlock - 1) / kBlock;
     if (nblocks > 0x7FFFFFFFull) return ZX_E_INVAL;
@@ -761,6 +774,9 @@ extern "C" zx_status zx_encode_size(zx_dtype dtype, const void *in, uint64_t n, 
     if (nblocks) {
         if (dtype == ZX_BF16)
             hipLaunchKernelGGL(k_block_bits<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kSizeThreads), 0, stream, in, n, per_block, lengths,
+                               block_hist, block_bitoff, block_seg);
+        else if (dtype == ZX_E8M0)
+            hipLaunchKernelGGL(k_block_bits<ZX_E8M0>, dim3((uint32_t)nblocks), dim3(kSizeThreads), 0, stream, in, n, per_block, lengths,
                                block_hist, block_bitoff, block_seg);
         else
             hipLaunchKernelGGL(k_block_bits<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kSizeThreads), 0, stream, in, n, per_block,
@@ -778,11 +794,12 @@ extern "C" zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int p
                                uint8_t *signmant, uint32_t *stream, uint32_t *seg_desc, uint8_t *gaps,
                                uint32_t *err, hipStream_t stream_)
 {
-    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN && dtype != ZX_E8M0) return ZX_E_UNSUPPORTED;
     const uint64_t nblocks = (n + kBlock - 1) / kBlock;
     if (nblocks > 0x7FFFFFFFull || nsegs > 0xFFFFFFFFull) return ZX_E_INVAL;
     if (!stream || !block_bitoff) return ZX_E_INVAL;
-    if (nblocks && (!in || !lengths || !degenerate || !block_seg || !signmant || !seg_desc || !gaps)) return ZX_E_INVAL;
+    if (nblocks && (!in || !lengths || !degenerate || !block_seg || (!signmant && dtype != ZX_E8M0) || !seg_desc || !gaps))
+        return ZX_E_INVAL;
     if (!aligned16(in) || !aligned16(signmant) || !aligned16(stream)) return ZX_E_INVAL;
     if (nsegs < nblocks) return ZX_E_INVAL;
     const uint64_t words = zx_stream_words(total_bits);
@@ -798,6 +815,9 @@ extern "C" zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int p
     if (nblocks == 0) return ZX_OK;
     if (dtype == ZX_BF16)
         hipLaunchKernelGGL(k_encode<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream_, in, n, per_block, lengths,
+                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, err);
+    else if (dtype == ZX_E8M0)
+        hipLaunchKernelGGL(k_encode<ZX_E8M0>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream_, in, n, per_block, lengths,
                            degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, err);
     else
         hipLaunchKernelGGL(k_encode<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream_, in, n, per_block, lengths,

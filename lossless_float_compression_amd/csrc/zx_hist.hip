@@ -68,6 +68,7 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restri
                 for (uint32_t k = 0; k < EPV; ++k) {
                     uint32_t e;
                     if (DT == ZX_BF16) e = (words[u][k >> 1] >> (16 * (k & 1) + 7)) & 0xFFu;
+                    else if (DT == ZX_E8M0) e = (words[u][k >> 2] >> (8 * (k & 3))) & 0xFFu;
                     else e = (words[u][k >> 2] >> (8 * (k & 3) + 3)) & 0xFu;
                     atomicAdd(&mine[e], 1u);
                 }
@@ -75,6 +76,7 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restri
                 for (uint32_t k = 0; k < have[u]; ++k) {
                     uint32_t e;
                     if (DT == ZX_BF16) e = (words[u][k >> 1] >> (16 * (k & 1) + 7)) & 0xFFu;
+                    else if (DT == ZX_E8M0) e = (words[u][k >> 2] >> (8 * (k & 3))) & 0xFFu;
                     else e = (words[u][k >> 2] >> (8 * (k & 3) + 3)) & 0xFu;
                     atomicAdd(&mine[e], 1u);
                 }
@@ -114,7 +116,7 @@ static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 extern "C" zx_status zx_histogram(zx_dtype dtype, const void *in, uint64_t n, uint32_t *tensor_hist,
                                   uint32_t *block_hist, hipStream_t stream)
 {
-    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN && dtype != ZX_E8M0) return ZX_E_UNSUPPORTED;
     if (!tensor_hist && !block_hist) return ZX_E_INVAL;
     if (n && !in) return ZX_E_INVAL;
     if (!aligned16(in) || !aligned16(tensor_hist) || !aligned16(block_hist)) return ZX_E_INVAL;
@@ -130,6 +132,9 @@ extern "C" zx_status zx_histogram(zx_dtype dtype, const void *in, uint64_t n, ui
     if (dtype == ZX_BF16)
         hipLaunchKernelGGL(k_histogram<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, tensor_hist, block_hist,
                            nullptr);
+    else if (dtype == ZX_E8M0)
+        hipLaunchKernelGGL(k_histogram<ZX_E8M0>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, tensor_hist, block_hist,
+                           nullptr);
     else
         hipLaunchKernelGGL(k_histogram<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, tensor_hist,
                            block_hist, nullptr);
@@ -138,7 +143,7 @@ extern "C" zx_status zx_histogram(zx_dtype dtype, const void *in, uint64_t n, ui
 
 extern "C" zx_status zx_histogram_accumulate(zx_dtype dtype, const void *in, uint64_t n, uint64_t *hist64, hipStream_t stream)
 {
-    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN && dtype != ZX_E8M0) return ZX_E_UNSUPPORTED;
     if (!hist64 || (n && !in) || !aligned16(in) || ((uintptr_t)hist64 & 7u)) return ZX_E_INVAL;
     const uint64_t nblocks = (n + kBlock - 1) / kBlock;
     if (nblocks > 0x7FFFFFFFull) return ZX_E_INVAL;
@@ -146,6 +151,8 @@ extern "C" zx_status zx_histogram_accumulate(zx_dtype dtype, const void *in, uin
     unsigned long long *h = reinterpret_cast<unsigned long long *>(hist64);
     if (dtype == ZX_BF16)
         hipLaunchKernelGGL(k_histogram<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, nullptr, nullptr, h);
+    else if (dtype == ZX_E8M0)
+        hipLaunchKernelGGL(k_histogram<ZX_E8M0>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, nullptr, nullptr, h);
     else
         hipLaunchKernelGGL(k_histogram<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kHistThreads), 0, stream, in, n, nullptr, nullptr, h);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;

@@ -19,6 +19,7 @@ import torch
 
 BF16 = 0
 FP8_E4M3FN = 1
+E8M0 = 2   # FP4 block scale factors: every byte a bare exponent, coded whole
 BLOCK_ELEMS = 65536
 SEG_CHUNKS = 64
 MAX_BATCH = 16
@@ -141,7 +142,7 @@ def _check(fn: str, st: int):
 
 
 def alphabet(dtype: int) -> int:
-    return 256 if dtype == BF16 else 16
+    return 16 if dtype == FP8_E4M3FN else 256
 
 
 def nblocks_of(n: int) -> int:
@@ -244,7 +245,10 @@ class Compressed:
 
 
 def _as_bits(x: torch.Tensor):
-    """(dtype code, flat raw-bit view) of a bf16 / float8_e4m3fn / int16 / uint8 tensor."""
+    """(dtype code, flat raw-bit view) of a bf16 / float8_e4m3fn / float8_e8m0fnu / int16 /
+    uint8 tensor (int16 reads as BF16 bits, uint8 as FP8 E4M3FN bits)."""
+    if x.dtype == torch.float8_e8m0fnu:
+        return E8M0, x.reshape(-1).view(torch.uint8)
     if x.dtype in (torch.bfloat16, torch.int16):
         return BF16, x.reshape(-1).view(torch.int16)
     if x.dtype in (torch.float8_e4m3fn, torch.uint8):
@@ -297,7 +301,8 @@ def build_shared_codebook(tensors, max_len: int = 32, stream=None) -> SharedCode
 
 def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_scale: Optional[float] = None,
              stream=None, codebook: Optional[SharedCodebook] = None) -> Compressed:
-    """Encode a device tensor (bf16 or int16 bits -> BF16; float8_e4m3fn or uint8 bits -> FP8).
+    """Encode a device tensor (bf16 or int16 bits -> BF16; float8_e4m3fn or uint8 bits -> FP8;
+    float8_e8m0fnu -> E8M0, the block scales of FP4 formats, coded whole byte).
 
     Runs histogram -> codebook -> block sizes (and the decode table), reads back the
     two totals (the single host synchronisation) to size the outputs, then encodes.
@@ -350,7 +355,7 @@ def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_sc
     elif not per_block:
         dtab = torch.empty(zx_decode_table_bytes(), **u8)
         zx_build_decode_table(dtype, lengths, dtab, stream)
-    signmant = torch.empty(n if dtype == BF16 else (n + 1) // 2, **u8)
+    signmant = torch.empty(n if dtype == BF16 else (n + 1) // 2 if dtype == FP8_E4M3FN else 0, **u8)
     err = torch.zeros(1, **i32)
     total_bits, nsegs = (int(v) for v in totals.cpu().tolist())
     words = torch.empty(zx_stream_words(total_bits), **i32)
@@ -370,6 +375,8 @@ def empty_output(c: Compressed, device=None) -> torch.Tensor:
     dev = device if device is not None else c.signmant.device
     if c.dtype == BF16:
         return torch.empty(c.shape, dtype=torch.bfloat16, device=dev)
+    if c.dtype == E8M0:
+        return torch.empty(c.shape, dtype=torch.float8_e8m0fnu, device=dev)
     return torch.empty(c.shape, dtype=torch.float8_e4m3fn, device=dev)
 
 
@@ -431,6 +438,8 @@ def compress_zf(x: torch.Tensor, fp8_scale: Optional[float] = None, stream=None)
         with torch.cuda.stream(stream):
             return compress_zf(x, fp8_scale, None)
     dtype, flat = _as_bits(x)
+    if dtype == E8M0:
+        raise TypeError("the dominant-range codec takes BF16 and FP8 E4M3FN tensors")
     if not flat.is_cuda:
         raise ValueError("compress_zf expects a device tensor")
     flat = flat.contiguous()

@@ -7,7 +7,7 @@ codec) hold every step of the methods.
 This module only marshals numpy arrays in and out of it through ctypes.
 """
 from .oracle import (  # noqa: F401
-    BF16, FP8, BLOCK, CHUNK_BITS, SEG_CHUNKS, Container, build, load,
+    BF16, FP8, E8M0, BLOCK, CHUNK_BITS, SEG_CHUNKS, Container, build, load,
     split, histogram, huffman_lengths, package_merge, code_lengths,
     canonical_codes, stream_words, encode, decode,
     ZF_BLOCK, ZfContainer, zf_mode, zf_encode, zf_decode,

@@ -15,7 +15,7 @@ def np_u(t: torch.Tensor, dt) -> np.ndarray:
 def to_oracle(c: zx.Compressed) -> oracle.Container:
     return oracle.Container(
         dtype=c.dtype, per_block=c.per_block, n=c.n,
-        lengths=np_u(c.lengths, np.uint8).reshape(-1, 256 if c.dtype == 0 else 16),
+        lengths=np_u(c.lengths, np.uint8).reshape(-1, 16 if c.dtype == 1 else 256),
         degenerate=np_u(c.degenerate, np.uint16),
         signmant=np_u(c.signmant, np.uint8),
         stream=np_u(c.stream, np.uint32),
@@ -31,7 +31,7 @@ def from_oracle(o: oracle.Container, device="cuda") -> zx.Compressed:
     def up(a, dt):
         return torch.from_numpy(np.ascontiguousarray(a).view(dt).copy()).to(device)
     nb = (o.n + 65535) // 65536
-    lengths = up(o.lengths.reshape(-1, 256 if o.dtype == 0 else 16), np.uint8)
+    lengths = up(o.lengths.reshape(-1, 16 if o.dtype == 1 else 256), np.uint8)
     c = zx.Compressed(
         dtype=o.dtype, per_block=o.per_block, n=o.n, shape=(o.n,), total_bits=o.total_bits, nsegs=o.nsegs,
         lengths=lengths, degenerate=up(o.degenerate, np.int16), signmant=up(o.signmant, np.uint8),
