@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--kv-slots", action="store_true",
                    help="c5 only: fill the K/V cache online into fixed compressed slots, then decode slots on demand")
     p.add_argument("--kv-bits", type=float, default=3.5, help="slot stream capacity in bits per element")
+    p.add_argument("--fp4-scales", action="store_true",
+                   help="E8M0 block scales of MX-FP4 weights for the Llama-3-8B-shaped set, Huffman-coded whole byte")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain device copies of 256 MiB (reference for HBM byte counters)")
@@ -301,7 +303,7 @@ def main():
     if args.kv_slots and args.config != "c5":
         print("--kv-slots applies to --config c5", file=sys.stderr)
         sys.exit(2)
-    if args.codec == "huffman" and args.config in ("c1", "c2", "c4"):
+    if args.codec == "huffman" and args.config in ("c1", "c2", "c4") and not args.fp4_scales:
         res = bench_single(args)
     else:
         import bench_big

@@ -502,7 +502,74 @@ def run_zf(args):
     }
 
 
+def run_fp4_scales(args):
+    """E8M0 block scales of MX-FP4 weights (every tensor of the Llama-3-8B-shaped set,
+    blocks of 32 inputs; 2.3e8 bytes) as one tensor with one codebook: decode launches
+    back to back over copies rotating through >= 1 GiB, encode after one untimed call."""
+    t0 = time.time()
+    x0 = workloads.fp4_scales_c3().view(torch.float8_e8m0fnu)
+    raw = x0.numel()
+    c0 = zx.compress(x0)
+    alg0 = _alg_bytes(c0)
+    R = max(2, -(-(1 << 30) // (alg0 + raw)))
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    cs = [c0] + [zx.compress(x) for x in xs[1:]]
+    outs = [zx.empty_output(c) for c in cs]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    enc = []
+    for _ in range(3):
+        e = _events(2)
+        e[0].record()
+        zx.compress(x0)
+        e[1].record()
+        torch.cuda.synchronize()
+        enc.append(e[0].elapsed_time(e[1]))
+    enc_ms = float(np.mean(enc[1:]))
+    setup_s = time.time() - t0
+    import ctypes
+    L = zx.lib()
+    conts = [c.container() for c in cs]
+    optrs = [ctypes.c_void_p(o.data_ptr()) for o in outs]
+    eptr = ctypes.c_void_p(err.data_ptr())
+    sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for k in range(max(args.warmup, R)):
+        assert L.zx_decode(ctypes.byref(conts[k % R]), optrs[k % R], eptr, sptr) == 0
+    torch.cuda.synchronize()
+    n_launch = max(args.steps, 100)
+    d0, d1 = _events(2)
+    d0.record()
+    bad = 0
+    for k in range(n_launch):
+        bad |= L.zx_decode(ctypes.byref(conts[k % R]), optrs[k % R], eptr, sptr)
+    d1.record()
+    torch.cuda.synchronize()
+    assert bad == 0 and int(err.item()) == 0
+    dec_ms = d0.elapsed_time(d1) / n_launch
+    for x, o in zip(xs, outs):
+        assert torch.equal(o.view(torch.uint8), x.view(torch.uint8)), "scale bytes did not round-trip"
+    achieved = alg0 / (dec_ms * 1e-3) / 1e9
+    return {
+        "metric": "E8M0 block-scale codec: decode GB/s (output) and % HBM roofline; encode GB/s; compression ratio",
+        "value": round(raw / (dec_ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": n_launch,
+        "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": "E8M0 scales of MX-FP4 blocks of 32 for the Llama-3-8B-shaped set (N(0,1/sqrt(fan_in))), "
+                               "one tensor, one codebook", "elements": int(raw), "raw_bytes": int(raw), "rotation_copies": R},
+        "decode_ms": round(dec_ms, 5), "encode_ms": round(enc_ms, 5),
+        "encode_GBps": round(raw / (enc_ms * 1e-3) / 1e9, 2),
+        "ratio": round(c0.nbytes() / raw, 5), "bits_per_element": round(c0.total_bits / c0.n, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_decode<E8M0>",
+                     "alg_bytes_per_launch": int(alg0)},
+        "context_d2d_copy_GBps": copy_context_GBps(int(alg0)),
+        "setup_s": round(setup_s, 1),
+    }
+
+
 def run(args):
+    if getattr(args, "fp4_scales", False):
+        return run_fp4_scales(args)
     if getattr(args, "codec", "huffman") == "zf":
         return run_zf(args)
     if getattr(args, "kv_slots", False):
