@@ -47,6 +47,12 @@ constexpr uint32_t kRoundElems = 3584;
 constexpr int kRounds = 7;
 constexpr int kEnt = 3 * kRounds;
 constexpr int kNsRegs = (kEnt + 3) / 4;
+// E8M0 block scales have mean codes near 1.5 bits: a 128-bit chunk holds up to ~130
+// codes and a segment up to 8192 elements, so that type gets 11 rounds and a stage
+// of a whole segment, and runs one workgroup per CU for the LDS this takes.
+template <int DT> constexpr int dec_rounds() { return DT == ZX_E8M0 ? 11 : kRounds; }
+template <int DT> constexpr uint32_t dec_stage_bytes() { return DT == ZX_E8M0 ? 8224u : kStageBytes; }
+template <int DT> constexpr int dec_wg_per_cu() { return DT == ZX_E8M0 ? 1 : kDecWgPerCu; }
 constexpr int kWriteBatch = 7;                 // write-pass pieces per lane whose loads go out together
 // Bit positions within a lane's rows: row r holds bits [32 r, 32 r + 32); row 1 is
 // the word holding the chunk's first bit, so the chunk starts at kPosBase + b0.
@@ -754,14 +760,15 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     // ---- count pass, register path
     // entries of rounds that do not run are never read: the replay stops once no lane
     // has symbols left
-    uint32_t ent[kEnt];
-    uint32_t nsb[kNsRegs];
+    constexpr int kR = dec_rounds<DT>(), kE = 3 * kR, kNs = (kE + 3) / 4;
+    uint32_t ent[kE];
+    uint32_t nsb[kNs];
 #pragma unroll
-    for (int k = 0; k < kEnt; ++k) ent[k] = __builtin_nondeterministic_value(0u);
+    for (int k = 0; k < kE; ++k) ent[k] = __builtin_nondeterministic_value(0u);
 #pragma unroll
-    for (int k = 0; k < kNsRegs; ++k) nsb[k] = __builtin_nondeterministic_value(0u);
+    for (int k = 0; k < kNs; ++k) nsb[k] = __builtin_nondeterministic_value(0u);
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
+    for (int r = 0; r < kR; ++r) {
         bool act = (B & 0xFFu) > thr;
         const uint64_t am = __builtin_amdgcn_ballot_w64(act);
         if (am == 0) break;
@@ -831,7 +838,7 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     if (any_lane(lane_bad) || e0 + total != e_end) { report(err, ZX_E_CORRUPT); return false; }
 
     const uint32_t t0 = e0 - sbase;   // stage position of the segment's first element
-    if (t0 + total + 3 > kStageBytes) {
+    if (t0 + total + 3 > dec_stage_bytes<DT>()) {
         write_rounds<DT>(tab, col, stage, start, cnt, off, t0, total, out_block, sm_block, sbase);
         return false;
     }
@@ -874,7 +881,7 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     uint8_t *a = stage + t0 + off;
     uint8_t *const aend = a + rcnt;
 #pragma unroll
-    for (int k = 0; k < kEnt; ++k) {
+    for (int k = 0; k < kE; ++k) {
         if (__builtin_amdgcn_ballot_w64(a < aend) == 0) break;
         if (a < aend) {
             // two pairs of non-adjacent bytes, kept apart: four adjacent byte stores
@@ -921,16 +928,17 @@ __device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *sta
 // SLOTS: the batch is a slot list (DecSlots); a separate instantiation, so that the
 // tensor-batch decode keeps reading its descriptor straight from the kernel arguments.
 template <int DT, bool SLOTS>
-__global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(const DecBatch batch, uint32_t *err)
+__global__ __launch_bounds__(kDecThreads, dec_wg_per_cu<DT>() * kDecWaves / 4) void k_decode(const DecBatch batch, uint32_t *err)
 {
     constexpr uint32_t A = alphabet_of(DT);
     __shared__ DTab tab;
-    __shared__ __align__(16) uint8_t stage_all[kDecWaves * kStageBytes];
+    constexpr uint32_t kStage = dec_stage_bytes<DT>();
+    __shared__ __align__(16) uint8_t stage_all[kDecWaves * kStage];
     __shared__ __align__(16) uint32_t words_all[kDecWaves * kSegWords];
     __shared__ SegMeta meta_all[kDecWaves * kWave];
     // kDecWgPerCu workgroups share the CU's 160 KB of LDS
     static_assert(sizeof(DTab) + sizeof(stage_all) + sizeof(words_all) + sizeof(meta_all) <=
-                      160u * 1024u / kDecWgPerCu - 512u,
+                      160u * 1024u / dec_wg_per_cu<DT>() - 512u,
                   "decode workgroup LDS budget");
     static_assert(sizeof(Canon) <= sizeof(stage_all), "Canon is built inside the stage area");
 
@@ -959,7 +967,7 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
         load_meta(T, s0 + kDecWaves * lane, lane < nk, mine);
         issue_seg(T, s0, meta_at(mine, 0), lane, in, nk != 0);
         Canon &c = *reinterpret_cast<Canon *>(stage_all);
-        static_assert(sizeof(Canon) % 4 == 0 && sizeof(Canon) + kLutSize * 2 <= kDecWaves * kStageBytes, "table scratch");
+        static_assert(sizeof(Canon) % 4 == 0 && sizeof(Canon) + kLutSize * 2 <= kDecWaves * kStage, "table scratch");
         canon_build(T.lengths + (uint64_t)lg * A, A, c);
         dtab_fill(c, A, tab, reinterpret_cast<uint16_t *>(stage_all + sizeof(Canon)));
     } else {
@@ -983,7 +991,7 @@ __global__ __launch_bounds__(kDecThreads, kDecMinWavesPerSimd) void k_decode(con
             if (i < kTabPieces) dst[i] = pc[k];
         }
     }
-    uint8_t *stage = stage_all + wave * kStageBytes;
+    uint8_t *stage = stage_all + wave * kStage;
     uint32_t *swords = words_all + wave * kSegWords;
     SegMeta *metas = meta_all + wave * kWave;
     rows_store_in(swords, lane, in);
@@ -1090,7 +1098,8 @@ extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *cons
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    uint64_t slots = (uint64_t)cus * kDecWgPerCu;   // resident 512-thread workgroups per CU
+    // resident 512-thread workgroups
+    uint64_t slots = (uint64_t)cus * (dt == ZX_E8M0 ? dec_wg_per_cu<ZX_E8M0>() : kDecWgPerCu);
     if (max_workgroups != 0 && max_workgroups < slots) slots = max_workgroups;
     uint64_t seg_total = 0;
     for (uint32_t i = 0; i < count; ++i)
