@@ -81,3 +81,18 @@ def test_argument_errors_return_before_any_launch(zx):
     c.dtab = 0x30000
     c.stream_words = 5
     assert lib.zx_decode(C.byref(c), P(0x20000), None, None) == 1
+
+
+def test_element_type_codes_agree():
+    """The element-type enum of include/zx.h, the binding's constants and the oracle's
+    are one numbering (BF16 0, FP8 E4M3FN 1, E8M0 block scales 2)."""
+    import oracle
+    import lossless_float_compression_amd as zx
+    text = open(HEADER).read()
+    enum = dict((k, int(v)) for k, v in re.findall(r"\b(ZX_BF16|ZX_FP8_E4M3FN|ZX_E8M0)\s*=\s*(\d+)", text))
+    assert enum == {"ZX_BF16": 0, "ZX_FP8_E4M3FN": 1, "ZX_E8M0": 2}
+    assert (zx.BF16, zx.FP8_E4M3FN, zx.E8M0) == (0, 1, 2)
+    assert (oracle.BF16, oracle.FP8, oracle.E8M0) == (0, 1, 2)
+    src = open(os.path.join(ROOT, "oracle", "zx_oracle.c")).read()
+    assert re.search(r"#define ZXO_E8M0 2\b", src) and re.search(r"#define ZXO_FP8 1\b", src)
+    assert zx.alphabet(zx.E8M0) == 256 and zx.alphabet(zx.FP8_E4M3FN) == 16
