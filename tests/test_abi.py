@@ -95,4 +95,5 @@ def test_element_type_codes_agree():
     assert (oracle.BF16, oracle.FP8, oracle.E8M0) == (0, 1, 2)
     src = open(os.path.join(ROOT, "oracle", "zx_oracle.c")).read()
     assert re.search(r"#define ZXO_E8M0 2\b", src) and re.search(r"#define ZXO_FP8 1\b", src)
-    assert zx.alphabet(zx.E8M0) == 256 and zx.alphabet(zx.FP8_E4M3FN) == 16
+    from lossless_float_compression_amd.zx import alphabet
+    assert alphabet(zx.E8M0) == 256 and alphabet(zx.BF16) == 256 and alphabet(zx.FP8_E4M3FN) == 16
