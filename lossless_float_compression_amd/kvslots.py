@@ -129,8 +129,10 @@ class KVSlotPool:
         if out is None:
             tdt = torch.bfloat16 if self.dtype == _zx.BF16 else torch.float8_e4m3fn
             out = torch.empty((k, BLOCK), dtype=tdt, device=self.signmant.device)
-        if out.shape[0] != k or out[0].numel() != BLOCK or not out.is_contiguous():
-            raise ValueError("out must be contiguous [len(slots), 65536]")
+        esz = 2 if self.dtype == _zx.BF16 else 1
+        if (out.dim() < 1 or out.shape[0] != k or out.numel() != k * BLOCK or not out.is_contiguous()
+                or not out.is_cuda or out.element_size() != esz):
+            raise ValueError(f"out must be a contiguous device tensor [len(slots), 65536] of {esz}-byte elements")
         return out
 
     def decode(self, slots, out: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None,
@@ -138,7 +140,14 @@ class KVSlotPool:
         """Decompress the blocks in `slots` (a device int32 tensor, or host ints) into
         out[j] (shape [k, 65536], bf16 or float8_e4m3fn) with one launch, one
         workgroup per slot (zx_kv_decode_slots).  A slot whose block did not fit holds
-        no segments and leaves its row unwritten."""
+        no segments and leaves its row unwritten.  With a torch `stream` other than the
+        current one, everything (the slot-id copy, the output, the decode) runs on it
+        after the work already enqueued on the current stream."""
+        side = _zx._side_stream(stream)
+        if side is not None:
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                return self.decode(slots, out, err, None)
         if not torch.is_tensor(slots):
             slots = torch.tensor(list(slots), dtype=torch.int32).to(self.signmant.device, non_blocking=True)
         if slots.dtype != torch.int32 or not slots.is_cuda:
@@ -155,6 +164,11 @@ class KVSlotPool:
                           err: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
         """As `decode`, through the per-slot containers and the tensor-batch decode
         (up to 16 slots per launch)."""
+        side = _zx._side_stream(stream)
+        if side is not None:
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                return self.decode_containers(slots, out, err, None)
         k = len(slots)
         out = self._out(k, out)
         rows = list(out.view(k, BLOCK))

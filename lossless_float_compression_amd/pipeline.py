@@ -49,6 +49,9 @@ class LayerPipeline:
         self.max_workgroups = int(max_workgroups)   # 0: the decode's default (two per CU)
         self.side = torch.cuda.Stream()   # default priority
         self.bufs: List[List[torch.Tensor]] = [[_zx.empty_output(c) for c in layers[0]] for _ in range(depth)]
+        # the containers (and the scratch buffers just allocated) were produced on the
+        # current stream: the side stream's first decodes must come after that work
+        self.side.wait_stream(torch.cuda.current_stream())
         self._ready = [torch.cuda.Event() for _ in range(depth)]
         self._free = [torch.cuda.Event() for _ in range(depth)]
         self._freed = [False] * depth     # a release was recorded for this set

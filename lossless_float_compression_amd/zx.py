@@ -380,20 +380,63 @@ def empty_output(c: Compressed, device=None) -> torch.Tensor:
     return torch.empty(c.shape, dtype=torch.float8_e4m3fn, device=dev)
 
 
+def _elem_bytes(dtype: int) -> int:
+    return 2 if dtype == BF16 else 1
+
+
+def check_out(out: torch.Tensor, n: int, dtype: int, what: str = "out") -> None:
+    """A decode writes n elements of the container's width through out's pointer:
+    reject anything that is not exactly that (another width, size or layout would
+    make the kernel write past or across the buffer)."""
+    if not out.is_cuda or not out.is_contiguous() or out.numel() != n or out.element_size() != _elem_bytes(dtype):
+        raise ValueError(f"{what} must be a contiguous device tensor of {n} elements of "
+                         f"{_elem_bytes(dtype)} bytes (got {tuple(out.shape)}, {out.dtype}, "
+                         f"{'device' if out.is_cuda else 'host'}, contiguous={out.is_contiguous()})")
+
+
+def _side_stream(stream):
+    """A torch stream other than the current one, or None.  Work given such a stream
+    first makes it wait for everything already enqueued on the current stream (the
+    producers of the containers and of caller-supplied outputs), then runs with it as
+    the current stream so that any output is allocated on it."""
+    if stream is None or isinstance(stream, C.c_void_p):   # a raw handle: ordering is the caller's
+        return None
+    cur = torch.cuda.current_stream()
+    return None if stream == cur else stream
+
+
 def decompress(c: Compressed, out: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None, stream=None):
     """Decode into `out` (allocated when None).  `err` is an optional int32 device
-    word that receives 4 (corrupt) if the decoder finds an inconsistency."""
+    word that receives 4 (corrupt) if the decoder finds an inconsistency.  With a
+    torch `stream` other than the current one the decode runs on it after the work
+    already enqueued on the current stream."""
+    side = _side_stream(stream)
+    if side is not None:
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            return decompress(c, out, err, None)
     if out is None:
         out = empty_output(c)
+    check_out(out, c.n, c.dtype)
     zx_decode(c.container(), out, err, stream)
     return out
 
 
 def decompress_batch(cs: Sequence[Compressed], outs: Optional[List[torch.Tensor]] = None,
                      err: Optional[torch.Tensor] = None, stream=None):
-    """Decode up to 16 tensors (e.g. one transformer layer) with one kernel launch."""
+    """Decode up to 16 tensors (e.g. one transformer layer) with one kernel launch
+    (stream ordering as `decompress`)."""
+    side = _side_stream(stream)
+    if side is not None:
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            return decompress_batch(cs, outs, err, None)
     if outs is None:
         outs = [empty_output(c) for c in cs]
+    if len(outs) != len(cs):
+        raise ValueError("one output per container")
+    for i, (c, o) in enumerate(zip(cs, outs)):
+        check_out(o, c.n, c.dtype, f"outs[{i}]")
     zx_decode_block_batch([c.container() for c in cs], outs, err, stream)
     return outs
 
@@ -467,9 +510,16 @@ def compress_zf(x: torch.Tensor, fp8_scale: Optional[float] = None, stream=None)
 
 def decompress_zf(c: ZfCompressed, out: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
+    """Decode a dominant-range container (stream ordering as `decompress`)."""
+    side = _side_stream(stream)
+    if side is not None:
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            return decompress_zf(c, out, err, None)
     if out is None:
         tdt = torch.bfloat16 if c.dtype == BF16 else torch.float8_e4m3fn
         out = torch.empty(c.shape, dtype=tdt, device=c.signmant.device)
+    check_out(out, c.n, c.dtype)
     cont = c.container()
     _check("zx_zf_decode", lib().zx_zf_decode(C.byref(cont), _ptr(out), _ptr(err), _stream(stream)))
     return out

@@ -9,6 +9,6 @@ This module only marshals numpy arrays in and out of it through ctypes.
 from .oracle import (  # noqa: F401
     BF16, FP8, E8M0, BLOCK, CHUNK_BITS, SEG_CHUNKS, Container, build, load,
     split, histogram, huffman_lengths, package_merge, code_lengths,
-    canonical_codes, stream_words, encode, decode,
+    canonical_codes, stream_words, encode, decode, decode_blocks, decode_threaded,
     ZF_BLOCK, ZfContainer, zf_mode, zf_encode, zf_decode,
 )

@@ -79,6 +79,7 @@ def load():
         lib.zxo_encode.argtypes = [C.c_int, P, C.c_uint64, C.c_int, C.c_int, C.POINTER(_CContainer)]
         lib.zxo_encode_with_lengths.argtypes = [C.c_int, P, C.c_uint64, P, C.c_uint16, C.POINTER(_CContainer)]
         lib.zxo_decode.argtypes = [C.POINTER(_CContainer), P]
+        lib.zxo_decode_blocks.argtypes = [C.POINTER(_CContainer), C.c_uint64, C.c_uint64, P]
         lib.zxo_free.argtypes = [C.POINTER(_CContainer)]
         if lib.zfo_sizeof_container() != C.sizeof(_ZfContainer):
             raise RuntimeError("oracle struct layout mismatch; rebuild oracle")
@@ -235,9 +236,8 @@ def encode(dtype: int, x: np.ndarray, per_block: bool = False, max_len: int = 32
     return c
 
 
-def decode(c: Container) -> np.ndarray:
-    """Decode a container (from the oracle or from anywhere else); raises on any
-    inconsistency the oracle's checks find."""
+def _marshal(c: Container):
+    """(C container, arrays kept alive for its pointers, output array) for a decode."""
     lib = load()
     A = _alphabet(c.dtype)
     keep = [np.ascontiguousarray(a) for a in (c.lengths.reshape(-1), c.degenerate, c.signmant, c.stream,
@@ -273,9 +273,50 @@ def decode(c: Container) -> np.ndarray:
     cc.seg_desc = ptr(sd, C.c_uint32)
     cc.gaps = ptr(gp, C.c_uint8)
     out = np.empty(max(c.n, 1), np.uint16 if c.dtype == BF16 else np.uint8)
+    return lib, cc, keep, out
+
+
+def decode(c: Container) -> np.ndarray:
+    """Decode a container (from the oracle or from anywhere else); raises on any
+    inconsistency the oracle's checks find."""
+    lib, cc, keep, out = _marshal(c)
     rc = lib.zxo_decode(C.byref(cc), _p(out))
     if rc != 0:
         raise ValueError(f"oracle decode rejected the container rc={rc}")
+    return out[: c.n]
+
+
+def decode_blocks(c: Container, ranges) -> np.ndarray:
+    """Decode the blocks of each (b0, b1) range in `ranges` into one output array
+    (elements of blocks outside the ranges are left unset); raises on any
+    inconsistency in those blocks."""
+    lib, cc, keep, out = _marshal(c)
+    for b0, b1 in ranges:
+        rc = lib.zxo_decode_blocks(C.byref(cc), int(b0), int(b1), _p(out))
+        if rc != 0:
+            raise ValueError(f"oracle decode rejected blocks [{b0}, {b1}) rc={rc}")
+    return out[: c.n]
+
+
+def decode_threaded(c: Container, threads: int) -> np.ndarray:
+    """The same decode with the blocks split into `threads` contiguous ranges, each
+    decoded on its own host thread (the calls release the interpreter lock)."""
+    import threading
+    lib, cc, keep, out = _marshal(c)
+    nb = c.nblocks
+    bounds = [nb * t // threads for t in range(threads + 1)]
+    rcs = [0] * threads
+
+    def run(t):
+        rcs[t] = lib.zxo_decode_blocks(C.byref(cc), bounds[t], bounds[t + 1], _p(out))
+
+    ths = [threading.Thread(target=run, args=(t,)) for t in range(threads)]
+    for th in ths:
+        th.start()
+    for th in ths:
+        th.join()
+    if any(rcs):
+        raise ValueError(f"oracle decode rejected the container rc={rcs}")
     return out[: c.n]
 
 
@@ -331,16 +372,18 @@ def zf_encode(dtype: int, x: np.ndarray) -> ZfContainer:
 
 def zf_decode(c: ZfContainer) -> np.ndarray:
     lib = load()
-    keep = [np.ascontiguousarray(a) for a in (c.lb, c.planes, c.rec_off, c.records, c.signmant)]
+    # converted arrays are bound here, so that every pointer below stays valid until
+    # the call returns
+    keep = [np.ascontiguousarray(c.lb, dtype=np.uint8), np.ascontiguousarray(c.planes, dtype=np.uint8),
+            np.ascontiguousarray(c.rec_off, dtype=np.uint64), np.ascontiguousarray(c.records, dtype=np.uint16),
+            np.ascontiguousarray(c.signmant, dtype=np.uint8)]
     cc = _ZfContainer()
     cc.dtype, cc.n, cc.nblocks, cc.nrecords = c.dtype, c.n, c.nblocks, keep[3].size
     cc.signmant_bytes = keep[4].size
     cc.lb = keep[0].ctypes.data_as(C.POINTER(C.c_uint8))
     cc.planes = keep[1].ctypes.data_as(C.POINTER(C.c_uint8))
-    cc.rec_off = keep[2].astype(np.uint64).ctypes.data_as(C.POINTER(C.c_uint64)) if keep[2].dtype != np.uint64 \
-        else keep[2].ctypes.data_as(C.POINTER(C.c_uint64))
-    cc.records = keep[3].astype(np.uint16).ctypes.data_as(C.POINTER(C.c_uint16)) if keep[3].dtype != np.uint16 \
-        else keep[3].ctypes.data_as(C.POINTER(C.c_uint16))
+    cc.rec_off = keep[2].ctypes.data_as(C.POINTER(C.c_uint64))
+    cc.records = keep[3].ctypes.data_as(C.POINTER(C.c_uint16))
     cc.signmant = keep[4].ctypes.data_as(C.POINTER(C.c_uint8))
     out = np.empty(max(c.n, 1), np.uint16 if c.dtype == BF16 else np.uint8)
     rc = lib.zfo_decode(C.byref(cc), _p(out))

@@ -553,27 +553,38 @@ static int decode_symbol(const canon_table *t, const uint32_t *stream, uint64_t 
     return -1;
 }
 
-/* Decode c into out (BF16: n u16, FP8 and E8M0: n u8).  Checks, per block: the codes end
- * exactly at the next block offset, every stored chunk gap and segment entry equals
- * the value the codeword boundaries imply, and padding is as specified. */
-int zxo_decode(const zxo_container *c, void *out)
+/* Decode blocks [b0, b1) of c into their elements of out (BF16: u16, FP8 and E8M0:
+ * u8; out holds all n elements, only the range's are written).  Checks, per block:
+ * the codes end exactly at the next block offset, every stored chunk gap and segment
+ * entry of the block equals the value the codeword boundaries imply; and, when the
+ * range reaches the last block, that the padding after the last code is zero.
+ * Blocks are independent given their codebook and offsets, so disjoint ranges can be
+ * decoded separately (the per-thread CPU baseline does). */
+static int decode_range(const zxo_container *c, uint64_t b0, uint64_t b1, void *out)
 {
     if (c->dtype != ZXO_BF16 && c->dtype != ZXO_FP8 && c->dtype != ZXO_E8M0) return ZXO_E_INVAL;
     const uint32_t A = alphabet_of(c->dtype);
     uint64_t n = c->n;
     if (c->nblocks != (n + ZXO_BLOCK - 1) / ZXO_BLOCK) return ZXO_E_INVAL;
+    if (b0 > b1 || b1 > c->nblocks) return ZXO_E_INVAL;
     if (c->ncb != (c->per_block ? c->nblocks : 1)) return ZXO_E_INVAL;
     if (c->block_bitoff[0] != 0 || c->block_seg[0] != 0) return ZXO_E_CORRUPT;
     if (c->block_bitoff[c->nblocks] != c->total_bits || c->block_seg[c->nblocks] != c->nsegs) return ZXO_E_CORRUPT;
     if (c->stream_words != zxo_stream_words(c->total_bits)) return ZXO_E_CORRUPT;
-    uint8_t *exps = (uint8_t *)malloc(n ? n : 1);
-    uint8_t *gap_seen = (uint8_t *)malloc((size_t)ZXO_SEG_CHUNKS * (size_t)(c->nsegs ? c->nsegs : 1));
+    if (b0 == b1 && b1 != c->nblocks) return ZXO_OK;   /* the last block's range also checks the padding */
+    /* elements [e0, e1) and segments [s_lo, s_hi) of the range */
+    const uint64_t e0 = b0 * ZXO_BLOCK, e1 = b1 * ZXO_BLOCK < n ? b1 * ZXO_BLOCK : n;
+    const uint32_t s_lo = c->block_seg[b0], s_hi = c->block_seg[b1];
+    if (s_hi < s_lo || s_hi > c->nsegs) return ZXO_E_CORRUPT;
+    const uint64_t nseg_r = (uint64_t)(s_hi - s_lo);
+    uint8_t *exps = (uint8_t *)malloc(e1 - e0 ? e1 - e0 : 1);
+    uint8_t *gap_seen = (uint8_t *)malloc((size_t)ZXO_SEG_CHUNKS * (size_t)(nseg_r ? nseg_r : 1));
     canon_table *t = (canon_table *)malloc(sizeof(canon_table));
     if (!exps || !gap_seen || !t) { free(exps); free(gap_seen); free(t); return ZXO_E_NOMEM; }
-    memset(gap_seen, ZXO_NO_GAP, (size_t)ZXO_SEG_CHUNKS * (size_t)c->nsegs);
+    memset(gap_seen, ZXO_NO_GAP, (size_t)ZXO_SEG_CHUNKS * (size_t)nseg_r);
     int rc = ZXO_OK;
     int64_t built_for = -1;
-    for (uint64_t b = 0; b < c->nblocks && rc == ZXO_OK; b++) {
+    for (uint64_t b = b0; b < b1 && rc == ZXO_OK; b++) {
         uint64_t lo = b * ZXO_BLOCK, hi = lo + ZXO_BLOCK < n ? lo + ZXO_BLOCK : n;
         uint64_t nb = hi - lo;
         uint64_t cb = c->per_block ? b : 0;
@@ -581,7 +592,8 @@ int zxo_decode(const zxo_container *c, void *out)
         if (c->block_bitoff[b + 1] < base) { rc = ZXO_E_CORRUPT; break; }
         uint64_t bits = c->block_bitoff[b + 1] - base;
         uint32_t s0 = c->block_seg[b];
-        if (c->block_seg[b + 1] < s0 || (uint64_t)(c->block_seg[b + 1] - s0) != segs_of(bits)) { rc = ZXO_E_CORRUPT; break; }
+        if (c->block_seg[b + 1] < s0 || (uint64_t)(c->block_seg[b + 1] - s0) != segs_of(bits) || s0 < s_lo ||
+            c->block_seg[b + 1] > s_hi) { rc = ZXO_E_CORRUPT; break; }
         uint64_t nsb = c->block_seg[b + 1] - s0;
         uint64_t *seg_first = (uint64_t *)malloc(sizeof(uint64_t) * (size_t)nsb);
         if (!seg_first) { rc = ZXO_E_NOMEM; break; }
@@ -589,7 +601,7 @@ int zxo_decode(const zxo_container *c, void *out)
         if (bits == 0) {
             uint16_t d = c->degenerate[cb];
             if (nb > 0 && (d == ZXO_NO_DEGEN || d >= A)) rc = ZXO_E_CORRUPT;
-            for (uint64_t i = 0; i < nb && rc == ZXO_OK; i++) exps[lo + i] = (uint8_t)d;
+            for (uint64_t i = 0; i < nb && rc == ZXO_OK; i++) exps[lo - e0 + i] = (uint8_t)d;
         } else {
             if ((int64_t)cb != built_for) {
                 rc = build_canon(c->lengths + cb * A, (int)A, t);
@@ -603,14 +615,14 @@ int zxo_decode(const zxo_container *c, void *out)
                 if (pos >= bits) { rc = ZXO_E_CORRUPT; break; }
                 if ((int64_t)chunk != last_chunk) {
                     uint64_t seg = chunk / ZXO_SEG_CHUNKS, lane = chunk % ZXO_SEG_CHUNKS;
-                    gap_seen[(size_t)(s0 + seg) * ZXO_SEG_CHUNKS + lane] = (uint8_t)(pos - chunk * ZXO_CHUNK_BITS);
+                    gap_seen[(size_t)(s0 - s_lo + seg) * ZXO_SEG_CHUNKS + lane] = (uint8_t)(pos - chunk * ZXO_CHUNK_BITS);
                     if (lane == 0 && seg > 0) seg_first[seg] = i;
                     last_chunk = (int64_t)chunk;
                 }
                 uint64_t p = base + pos;
                 int s = decode_symbol(t, c->stream, base + bits, &p);
                 if (s < 0) { rc = ZXO_E_CORRUPT; break; }
-                exps[lo + i] = (uint8_t)s;
+                exps[lo - e0 + i] = (uint8_t)s;
                 pos = p - base;
             }
             if (rc == ZXO_OK && pos != bits) rc = ZXO_E_CORRUPT;
@@ -621,17 +633,36 @@ int zxo_decode(const zxo_container *c, void *out)
         }
         free(seg_first);
     }
-    if (rc == ZXO_OK && c->nsegs && memcmp(gap_seen, c->gaps, (size_t)ZXO_SEG_CHUNKS * (size_t)c->nsegs) != 0) rc = ZXO_E_CORRUPT;
+    if (rc == ZXO_OK && nseg_r &&
+        memcmp(gap_seen, c->gaps + (size_t)s_lo * ZXO_SEG_CHUNKS, (size_t)ZXO_SEG_CHUNKS * (size_t)nseg_r) != 0)
+        rc = ZXO_E_CORRUPT;
     /* padding after the last code must be zero */
-    if (rc == ZXO_OK) {
+    if (rc == ZXO_OK && b1 == c->nblocks) {
         for (uint64_t j = c->total_bits; j < c->stream_words * 32u; j++)
             if (get_bit(c->stream, j)) { rc = ZXO_E_CORRUPT; break; }
     }
-    if (rc == ZXO_OK) join_fields(c->dtype, exps, c->signmant, n, out);
+    if (rc == ZXO_OK) {
+        const uint64_t esz = c->dtype == ZXO_BF16 ? 2 : 1;
+        /* FP8 nibbles of element e0 start at byte e0 / 2; e0 is a block start, even */
+        const uint8_t *sm = c->dtype == ZXO_BF16 ? c->signmant + e0 : c->signmant + e0 / 2;
+        join_fields(c->dtype, exps, sm, e1 - e0, (uint8_t *)out + e0 * esz);
+    }
     free(exps);
     free(gap_seen);
     free(t);
     return rc;
+}
+
+/* Decode the whole container c into out (n elements). */
+int zxo_decode(const zxo_container *c, void *out)
+{
+    return decode_range(c, 0, c->nblocks, out);
+}
+
+/* Decode blocks [b0, b1) only (see decode_range). */
+int zxo_decode_blocks(const zxo_container *c, uint64_t b0, uint64_t b1, void *out)
+{
+    return decode_range(c, b0, b1, out);
 }
 
 /* sizes exported for the Python wrapper */

@@ -155,6 +155,37 @@ def test_deep_tree_needs_limit(orc):
     assert cost(hist, ln) >= cost(hist, orc.huffman_lengths(hist))
 
 
+def tie_cases():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "huffman_tie_rules.txt")):
+        if line.strip() and not line.startswith("#"):
+            name, limit, counts, lengths, flipped, total = line.split()
+            rows.append((name, int(limit), [int(v) for v in counts.split(",")],
+                         [int(v) for v in lengths.split(",")], [int(v) for v in flipped.split(",")], int(total)))
+    return rows
+
+
+@pytest.mark.parametrize("case", tie_cases(), ids=lambda c: c[0])
+@pytest.mark.parametrize("offset", [0, 100])
+def test_tie_rules_worked_examples(orc, case, offset):
+    """The hand-derived tie cases of tests/golden/huffman_tie_rules.txt: both the
+    rule's lengths and the flipped rule's are optimal (same cost as brute force), and
+    the oracle must build exactly the rule's."""
+    name, limit, counts, lengths, flipped, total = case
+    hist = np.zeros(256, np.uint64)
+    hist[offset:offset + len(counts)] = counts
+    want = np.zeros(256, np.uint8)
+    want[offset:offset + len(lengths)] = lengths
+    assert cost(counts, lengths) == cost(counts, flipped) == total == brute_min_cost(counts, limit)
+    assert kraft_ok(lengths) and kraft_ok(flipped)
+    got, degen = orc.code_lengths(hist, limit)
+    assert degen == 0xFFFF
+    assert np.array_equal(got, want), (name, got[offset:offset + len(counts)])
+    if limit < 32:
+        assert int(orc.huffman_lengths(hist).max()) > limit   # the limit binds: package-merge ran
+        assert np.array_equal(orc.package_merge(hist, limit), want)
+
+
 # ---------------------------------------------------------------- canonical codes
 
 def test_rfc1951_example(orc):
@@ -469,3 +500,54 @@ def test_generator_fp8_properties():
     assert not np.isin(b, [0x7F, 0xFF]).any()  # no NaN
     assert np.isin(b, [0x7E, 0xFE]).any()      # the amax element maps to +-448
     assert 4.5 / 448 < scale < 7.0 / 448
+
+
+# ---------------------------------------------------------------- block-range decode
+
+def bf16_of(f32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+@pytest.mark.parametrize("per_block", [False, True])
+def test_block_ranges_equal_whole_decode(orc, dtype, per_block):
+    """Blocks decode independently given their codebook and offsets: any partition of
+    the blocks into ranges, decoded range by range or on several threads, gives the
+    input back, as the whole-container decode does."""
+    rng = np.random.default_rng(40 + dtype + 3 * per_block)
+    n = 7 * 65536 + 1234
+    if dtype == 0:
+        x = bf16_of(rng.standard_normal(n).astype(np.float32) * 0.03)
+    else:
+        x = np.minimum(rng.geometric(0.3, n), 255).astype(np.uint8)   # skewed bytes, any pattern is legal
+    c = orc.encode(dtype, x, per_block=per_block)
+    assert np.array_equal(orc.decode(c), x)
+    nb = c.nblocks
+    cuts = sorted(set([0, nb] + list(rng.integers(0, nb + 1, 3))))
+    ranges = list(zip(cuts[:-1], cuts[1:]))
+    assert np.array_equal(orc.decode_blocks(c, ranges), x)
+    assert np.array_equal(orc.decode_blocks(c, ranges[::-1]), x)
+    for t in (1, 3, 8):
+        assert np.array_equal(orc.decode_threaded(c, t), x)
+
+
+def test_block_range_reports_only_its_own_damage(orc):
+    rng = np.random.default_rng(9)
+    n = 5 * 65536
+    x = bf16_of(rng.standard_normal(n).astype(np.float32) * 0.03)
+    c = orc.encode(0, x)
+    s = int(c.block_seg[2]) + 1                  # a segment of block 2
+    c.gaps[s, 5] = (int(c.gaps[s, 5]) + 1) % 32
+    with pytest.raises(ValueError):
+        orc.decode(c)
+    with pytest.raises(ValueError):
+        orc.decode_blocks(c, [(2, 3)])
+    y = orc.decode_blocks(c, [(0, 2), (3, 5)])
+    keep = np.r_[0:2 * 65536, 3 * 65536:5 * 65536]
+    assert np.array_equal(y[keep], x[keep])
+    # padding is checked by the range that holds the last block only
+    c2 = orc.encode(0, x)
+    c2.stream[-1] = 1
+    orc.decode_blocks(c2, [(0, 4)])
+    with pytest.raises(ValueError):
+        orc.decode_blocks(c2, [(4, 5)])

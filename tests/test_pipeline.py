@@ -76,3 +76,76 @@ def test_pipeline_round_trip(depth):
     for l in range(n_layers):
         for j in range(len(shapes)):
             assert torch.equal(copies[l][j].view(torch.int16), inputs[l][j].view(torch.int16)), (l, j)
+
+
+def _late_copy(c, busy_a, busy_b):
+    """A copy of container c whose arrays are written on the current stream behind a
+    queue of long matmuls, so they are finished only well after this call returns."""
+    import dataclasses
+    for _ in range(6):
+        torch.mm(busy_a, busy_a, out=busy_b)
+    kw = {f.name: getattr(c, f.name) for f in dataclasses.fields(c)}
+    for f, v in list(kw.items()):
+        if torch.is_tensor(v):
+            kw[f] = v.clone()
+    return type(c)(**kw)
+
+
+@pytest.mark.gpu
+def test_side_stream_decodes_wait_for_the_producer_stream():
+    """decompress(stream=side), decompress_batch(stream=side), KVSlotPool.decode(stream=
+    side) and LayerPipeline start their side-stream work only after what the current
+    stream has queued: here the containers themselves are still being written there."""
+    import lossless_float_compression_amd as zx
+    from lossless_float_compression_amd.kvslots import KVSlotPool
+    print("side stream waits for the producer", file=sys.stderr, flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    xs = [(torch.randn(s, generator=g, device="cuda") * 0.03).to(torch.bfloat16) for s in [(1000, 700), (300, 4096)]]
+    cs = [zx.compress(x) for x in xs]
+    a = torch.randn(4096, 4096, device="cuda")
+    b = torch.empty_like(a)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    late = _late_copy(cs[0], a, b)
+    y = zx.decompress(late, err=err, stream=side)
+    late2 = [_late_copy(c, a, b) for c in cs]
+    ys = zx.decompress_batch(late2, err=err, stream=side)
+    late3 = [[_late_copy(c, a, b) for c in cs] for _ in range(2)]
+    pipe = LayerPipeline(late3, err=err)
+    got = []
+    pipe.run(lambda l, w: got.append([t.clone() for t in w]))
+
+    pool = KVSlotPool(4, zx.BF16, cap_words=8192)
+    blocks = (torch.randn(2 * 65536, generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    pool.append(blocks, torch.tensor([2, 0], dtype=torch.int32, device="cuda"))
+    for _ in range(6):
+        torch.mm(a, a, out=b)
+    ids = torch.tensor([0, 2], dtype=torch.int32, device="cuda")   # written behind the matmuls
+    rows = pool.decode(ids, err=err, stream=side)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(y.view(torch.int16), xs[0].view(torch.int16))
+    for x, t in zip(xs, ys):
+        assert torch.equal(t.view(torch.int16), x.view(torch.int16))
+    for layer in got:
+        for x, t in zip(xs, layer):
+            assert torch.equal(t.view(torch.int16), x.view(torch.int16))
+    assert torch.equal(rows.view(torch.int16), blocks.view(2, 65536)[[1, 0]].view(torch.int16))
+
+
+@pytest.mark.gpu
+def test_decompress_rejects_wrong_outputs():
+    import lossless_float_compression_amd as zx
+    x = (torch.randn(5000, device="cuda") * 0.1).to(torch.bfloat16)
+    c = zx.compress(x)
+    for bad in (torch.empty(5000, dtype=torch.uint8, device="cuda"),          # FP8-sized
+                torch.empty(4999, dtype=torch.bfloat16, device="cuda"),        # short
+                torch.empty((100, 100), dtype=torch.bfloat16, device="cuda").t()[:50],   # not contiguous
+                torch.empty(5000, dtype=torch.bfloat16)):                      # host
+        with pytest.raises(ValueError):
+            zx.decompress(c, out=bad)
+        with pytest.raises(ValueError):
+            zx.decompress_batch([c], outs=[bad])
