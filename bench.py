@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--overlap", action="store_true",
                    help="c3 only: measure how much per-layer decode hides behind the layer's GEMMs")
+    p.add_argument("--layers", type=int, default=32,
+                   help="c3 only: decode the first N transformer layers (and the lm_head) instead of all 32")
     p.add_argument("--overlap-layers", type=int, default=8)
     p.add_argument("--overlap-reps", type=int, default=5)
     p.add_argument("--overlap-batches", type=int, nargs="+", default=[1, 16, 128, 1024, 4096])
@@ -60,7 +62,10 @@ def parse():
     p.add_argument("--kv-bits", type=float, default=3.5, help="slot stream capacity in bits per element")
     p.add_argument("--fp4-scales", action="store_true",
                    help="E8M0 block scales of MX-FP4 weights for the Llama-3-8B-shaped set, Huffman-coded whole byte")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--reps", type=int, default=25, help="timed repetitions (median reported; at least 20)")
+    p.add_argument("--no-layer-call", action="store_true",
+                   help="c2 only: skip the Llama-3-8B-shaped layer-call sub-record")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain device copies of 256 MiB (reference for HBM byte counters)")
     return p.parse_args()
@@ -142,24 +147,190 @@ def make_input(cfg):
     raise ValueError(cfg)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_threads() -> int:
+    """Host threads for the threaded oracle: the cores this process may use, at most 16
+    (one GPU's share of the host on the GPU machines)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _timed_reps(fn, seconds: float, min_reps: int = 3):
+    """Run fn until `seconds` have passed (at least min_reps times); return (median s, reps, last result)."""
+    ts, out = [], None
+    t_end = time.perf_counter() + seconds
+    while len(ts) < min_reps or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        out = fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)), len(ts), out
+
+
 def cpu_baseline(x_cpu_bits: np.ndarray, dtype: int, seconds: float):
-    """The oracle (single-threaded, as it stands) decoding the same tensor's container."""
+    """The oracle as it stands, on this host, on the same tensor: its bit-serial decode of
+    the tensor's container on T threads over independent 65536-element blocks (the
+    reported value), then on one thread, and its single-threaded encode."""
     import oracle
     oracle.build(force=False)
-    c = oracle.encode(dtype, x_cpu_bits)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        y = oracle.decode(c)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    assert np.array_equal(y, x_cpu_bits)
-    gbps = reps * x_cpu_bits.nbytes / el / 1e9
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"full tensor ({x_cpu_bits.size} elements), bit-serial oracle decode repeated {reps}x "
-                      f"over {el:.1f} s on one host core"}
+    T = host_threads()
+    t_enc, n_enc, c = _timed_reps(lambda: oracle.encode(dtype, x_cpu_bits), seconds / 3)
+    t_dec1, n_dec1, y1 = _timed_reps(lambda: oracle.decode(c), seconds / 3)
+    t_decT, n_decT, yT = _timed_reps(lambda: oracle.decode_threaded(c, T), seconds / 3)
+    assert np.array_equal(y1, x_cpu_bits) and np.array_equal(yT, x_cpu_bits)
+    nb = x_cpu_bits.nbytes
+    return {"value": round(nb / t_decT / 1e9, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "sample": (f"full tensor ({x_cpu_bits.size} elements, {c.nblocks} blocks of 65536): bit-serial oracle "
+                       f"decode on {T} threads over contiguous block ranges, median of {n_decT} runs; single-thread "
+                       f"decode median of {n_dec1}, single-thread encode median of {n_enc}"),
+            "decode_1thread_GBps": round(nb / t_dec1 / 1e9, 4),
+            "encode_1thread_GBps": round(nb / t_enc / 1e9, 4),
+            "cpu_model": cpu_model(), "host_threads_available": os.cpu_count()}
+
+
+def exponent_stats(x_bits: np.ndarray, dtype: int, c) -> dict:
+    """Entropy of the exponent histogram, mean and longest code length, input hash."""
+    import hashlib
+    e = ((x_bits >> 7) & 0xFF) if dtype == 0 else ((x_bits >> 3) & 0xF) if dtype == 1 else x_bits
+    h = np.bincount(e.astype(np.int64), minlength=256 if dtype != 1 else 16).astype(np.float64)
+    p = h[h > 0] / h.sum()
+    return {"exponent_entropy_bits": round(float(-(p * np.log2(p)).sum()), 5),
+            "mean_code_bits": round(c.total_bits / c.n, 5),
+            "max_code_bits": int(c.lengths.max().item()),
+            "input_sha256": hashlib.sha256(x_bits.tobytes()).hexdigest()}
+
+
+def median_launch_ms(launch, n_per_rep: int, reps: int = 25, warmup: int = 5):
+    """hipEvents around `n_per_rep` back-to-back launches (one rotation), `reps` times after
+    `warmup` untimed reps; returns (median, mean) per-launch milliseconds."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for i in range(n_per_rep):
+            launch(i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record(stream)
+        for i in range(n_per_rep):
+            launch(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) / n_per_rep for a, b in ev])
+    return float(np.median(per)), float(per.mean())
+
+
+def encode_chain(cs, xs):
+    """A launcher for the device-side encode chain of copy k: histogram, codebook, block
+    sizes, decode table and encode, through the C ABI into preallocated buffers with
+    the sizes already known (the same work compress() does, without its one host read
+    of the totals and without allocation)."""
+    import ctypes
+    import torch
+    import lossless_float_compression_amd as zx
+    L = zx.lib()
+    P = ctypes.c_void_p
+    sptr = P(torch.cuda.current_stream().cuda_stream)
+    bufs = []
+    for c, x in zip(cs, xs):
+        flat = x.reshape(-1).view(torch.int16 if c.dtype == zx.BF16 else torch.uint8)
+        nb = zx.nblocks_of(c.n)
+        A = zx.alphabet(c.dtype)
+        d = dict(flat=flat, th=torch.empty(A, dtype=torch.int32, device="cuda"),
+                 bh=torch.empty((max(nb, 1), A), dtype=torch.int32, device="cuda"),
+                 ln=torch.empty((1, A), dtype=torch.uint8, device="cuda"),
+                 dg=torch.empty(1, dtype=torch.int16, device="cuda"),
+                 bo=torch.empty(nb + 1, dtype=torch.int64, device="cuda"),
+                 bs=torch.empty(nb + 1, dtype=torch.int32, device="cuda"),
+                 tot=torch.empty(2, dtype=torch.int64, device="cuda"),
+                 dt=torch.empty(zx.zx_decode_table_bytes(), dtype=torch.uint8, device="cuda"),
+                 sm=torch.empty_like(c.signmant), st=torch.empty_like(c.stream), sd=torch.empty_like(c.seg_desc),
+                 gp=torch.empty_like(c.gaps), err=torch.zeros(1, dtype=torch.int32, device="cuda"))
+        bufs.append((c, {k: (v if not torch.is_tensor(v) else P(v.data_ptr())) for k, v in d.items()}, d))
+
+    def launch(k):
+        c, p, _ = bufs[k % len(bufs)]
+        st = 0
+        st |= L.zx_histogram(c.dtype, p["flat"], c.n, p["th"], p["bh"], sptr)
+        st |= L.zx_build_codebook(c.dtype, p["th"], 1, 32, p["ln"], p["dg"], sptr)
+        st |= L.zx_encode_size(c.dtype, p["flat"], c.n, 0, p["ln"], p["bh"], p["bo"], p["bs"], p["tot"], sptr)
+        st |= L.zx_build_decode_table(c.dtype, p["ln"], p["dt"], sptr)
+        st |= L.zx_encode(c.dtype, p["flat"], c.n, 0, p["ln"], p["dg"], p["bo"], p["bs"], c.total_bits, c.nsegs,
+                          p["sm"], p["st"], p["sd"], p["gp"], p["err"], sptr)
+        assert st == 0, "encode chain call failed"
+
+    def check():
+        for c, _, d in bufs:
+            assert int(d["err"].item()) == 0
+            assert torch.equal(d["st"], c.stream) and torch.equal(d["gp"], c.gaps) and torch.equal(d["sm"], c.signmant)
+
+    return launch, check
+
+
+def encode_alg_bytes(c) -> int:
+    """Bytes the encode must move: the input read once, every container array written."""
+    return int(c.raw_bytes() + c.nbytes() - 64)
+
+
+def layer_call_record(n_layers: int = 4, reps: int = 25):
+    """One transformer-layer call of the Llama-3-8B-shaped set (7 tensors, one batched
+    decode), rotating over layers 0..n_layers-1 so the reads come from HBM (4 layers
+    move about 2.9 GB, over 10 times the 256 MB Infinity Cache); median of `reps`."""
+    import ctypes
+    import torch
+    import workloads
+    import lossless_float_compression_amd as zx
+    per = len(workloads.C3_SHAPES)
+    layers = []
+    for l in range(n_layers):
+        grp = []
+        for j in range(per):
+            x = workloads.c3_tensor(l * per + j)
+            grp.append(zx.compress(x))
+            del x
+        layers.append(grp)
+    outs = [zx.empty_output(c) for c in layers[0]]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L = zx.lib()
+    arrs = [(zx.zx_container * per)(*[c.container() for c in grp]) for grp in layers]
+    optrs = (ctypes.c_void_p * per)(*[o.data_ptr() for o in outs])
+    eptr = ctypes.c_void_p(err.data_ptr())
+    sptr = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch(i):
+        assert L.zx_decode_block_batch(arrs[i % n_layers], optrs, per, eptr, sptr) == 0
+
+    med, mean = median_launch_ms(launch, n_layers, reps=reps)
+    assert int(err.item()) == 0
+    for grp_i in (0, n_layers - 1):     # outputs of the last call of each layer equal their inputs
+        launch(grp_i)
+        torch.cuda.synchronize()
+        for j, o in enumerate(outs):
+            assert torch.equal(o.view(torch.int16).reshape(-1), workloads.c3_tensor(grp_i * per + j).reshape(-1))
+    alg = sum(decode_alg_bytes(c) for c in layers[0])
+    raw = sum(c.raw_bytes() for c in layers[0])
+    ach = alg / (med * 1e-3) / 1e9
+    return {"workload": f"Llama-3-8B-shaped BF16 layer call (q,k,v,o,gate,up,down; 218,103,808 elements), "
+                        f"rotating over layers 0-{n_layers - 1}",
+            "layer_decode_ms": round(med, 5), "layer_decode_ms_mean": round(mean, 5),
+            "decode_GBps": round(raw / (med * 1e-3) / 1e9, 2),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBPS, 4), "alg_bytes_per_launch": int(alg),
+                         "traffic": profiled_traffic("c3"), "kernel": "k_decode"},
+            "segments_per_call": int(sum(c.nsegs for c in layers[0])),
+            "reps": reps}
 
 
 def bench_single(args):
@@ -204,29 +375,26 @@ def bench_single(args):
     step_dec_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     enc_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     # decode launches back to back over the rotation (each copy cold in the caches),
-    # two events around all of them: the per-launch average without event overhead.
-    # The containers are marshalled once, so the host enqueues launches faster than
-    # the GPU runs them and the events see no host gaps.
+    # events around each rotation: per-launch figures without event overhead.  The
+    # containers are marshalled once, so the host enqueues launches faster than the
+    # GPU runs them and the events see no host gaps.
     import ctypes
     lib = zx.lib()
     conts = [c.container() for c in cs]
     optrs = [ctypes.c_void_p(o.data_ptr()) for o in outs]
     eptr = ctypes.c_void_p(err.data_ptr())
     sptr = ctypes.c_void_p(stream.cuda_stream)
-    n_launch = max(args.steps, 100)
-    for k in range(R):
-        assert lib.zx_decode(ctypes.byref(conts[k]), optrs[k], eptr, sptr) == 0
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    d0.record(stream)
-    bad = 0
-    for i in range(n_launch):
+
+    def dec_launch(i):
         k = i % R
-        bad |= lib.zx_decode(ctypes.byref(conts[k]), optrs[k], eptr, sptr)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    assert bad == 0, "zx_decode returned an error status"
-    dec_avg = d0.elapsed_time(d1) / n_launch
+        assert lib.zx_decode(ctypes.byref(conts[k]), optrs[k], eptr, sptr) == 0
+
+    reps = max(20, args.reps)
+    dec_med, dec_mean = median_launch_ms(dec_launch, R, reps=reps)
+    # the device-side encode chain alone, back to back over the rotation
+    enc_launch, enc_check = encode_chain(cs, xs)
+    enc_med, _ = median_launch_ms(enc_launch, R, reps=reps)
+    enc_check()
     # correctness at full size, outside the timed region
     assert int(err.item()) == 0, "decoder reported a corrupt container"
     for k in range(R):
@@ -234,7 +402,9 @@ def bench_single(args):
         assert torch.equal(y.reshape(-1).view(x0.dtype), xs[k].reshape(-1)), f"copy {k} did not round-trip"
     c = cs[0]
     alg = decode_alg_bytes(c)
-    achieved = alg / (dec_avg * 1e-3) / 1e9
+    achieved = alg / (dec_med * 1e-3) / 1e9
+    enc_alg = encode_alg_bytes(c)
+    enc_e2e_ms = float(np.median(enc_ms))
     # context only: the same tensor kept in pinned host memory and copied to the device
     # per use, the offloading alternative the pages compare against
     pinned = torch.empty(raw_bytes, dtype=torch.uint8, pin_memory=True)
@@ -251,9 +421,11 @@ def bench_single(args):
     h2d_gbps = raw_bytes * 20 / (h0.elapsed_time(h1) * 1e-3) / 1e9
     del pinned, dev_buf
     from bench_big import copy_context_GBps
+    xb = x0.reshape(-1).cpu().numpy()
+    xb = xb.view(np.uint16) if c.dtype == 0 else xb.view(np.uint8)
     res = {
         "metric": METRIC,
-        "value": round(raw_bytes / (dec_avg * 1e-3) / 1e9, 2),
+        "value": round(raw_bytes / (dec_med * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -264,22 +436,33 @@ def bench_single(args):
         "vs_baseline": None,
         "dtype": "u32",
         "data": "synthetic",
-        "config": {"workload": desc, "elements": c.n, "raw_bytes": raw_bytes, "rotation_copies": R},
-        "decode_ms": round(dec_avg, 5),
+        "config": {"workload": desc, "elements": c.n, "raw_bytes": raw_bytes, "rotation_copies": R,
+                   "segments": c.nsegs, "timing": f"median over {reps} reps of {R} back-to-back launches"},
+        "decode_ms": round(dec_med, 5),
+        "decode_ms_mean": round(dec_mean, 5),
         "decode_ms_in_step": round(float(step_dec_ms.mean()), 5),
-        "encode_ms": round(float(enc_ms.mean()), 5),
-        "encode_GBps": round(raw_bytes / (float(enc_ms.mean()) * 1e-3) / 1e9, 2),
+        "encode_ms": round(enc_e2e_ms, 5),
+        "encode_GBps": round(raw_bytes / (enc_e2e_ms * 1e-3) / 1e9, 2),
+        "encode_chain_ms": round(enc_med, 5),
+        "encode_chain_GBps": round(raw_bytes / (enc_med * 1e-3) / 1e9, 2),
+        "encode_roofline": {"bound": "hbm", "alg_bytes": enc_alg, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "chain_achieved": round(enc_alg / (enc_med * 1e-3) / 1e9, 1),
+                            "chain_frac": round(enc_alg / (enc_med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                            "end_to_end_frac": round(enc_alg / (enc_e2e_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "ratio": round(c.nbytes() / raw_bytes, 5),
         "exponent_bits_per_element": round(c.total_bits / c.n, 5),
+        **exponent_stats(xb, c.dtype, c),
         "context_h2d_copy_GBps": round(h2d_gbps, 2),
         "context_d2d_copy_GBps": copy_context_GBps(alg),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(args.config),
                      "kernel": "k_decode", "alg_bytes_per_launch": alg},
     }
+    if args.config == "c2" and not args.no_layer_call:
+        del xs, cs, outs
+        torch.cuda.empty_cache()
+        res["llama3_8b_layer_call"] = layer_call_record()
     if not args.no_cpu:
-        xb = x0.reshape(-1).cpu().numpy()
-        xb = xb.view(np.uint16) if c.dtype == 0 else xb.view(np.uint8)
         res["cpu_baseline"] = cpu_baseline(xb, c.dtype, args.cpu_seconds)
     return res
 

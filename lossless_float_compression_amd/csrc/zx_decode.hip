@@ -1101,9 +1101,37 @@ extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *cons
     // resident 512-thread workgroups
     uint64_t slots = (uint64_t)cus * (dt == ZX_E8M0 ? dec_wg_per_cu<ZX_E8M0>() : kDecWgPerCu);
     if (max_workgroups != 0 && max_workgroups < slots) slots = max_workgroups;
+    // resident workgroup slots for each per-tensor-codebook container: its share of the
+    // slots by segment count, rounded down, then the slots left over go to the largest
+    // remainders.  The total never exceeds the resident slots, so every workgroup starts
+    // at once: one more workgroup than fits would run its whole share after the others.
     uint64_t seg_total = 0;
+    uint32_t nshare = 0;
     for (uint32_t i = 0; i < count; ++i)
-        if (!cs[i].per_block) seg_total += cs[i].nsegs;
+        if (!cs[i].per_block && cs[i].n) { seg_total += cs[i].nsegs; ++nshare; }
+    uint64_t share[kMaxBatch] = {};
+    if (nshare) {
+        if (slots < nshare) slots = nshare;
+        uint64_t given = 0;
+        uint64_t rem[kMaxBatch] = {};
+        for (uint32_t i = 0; i < count; ++i) {
+            if (cs[i].per_block || cs[i].n == 0) continue;
+            const uint64_t num = slots * cs[i].nsegs;
+            share[i] = num / seg_total;
+            rem[i] = num % seg_total;
+            if (share[i] == 0) { share[i] = 1; rem[i] = 0; }
+            given += share[i];
+        }
+        while (given < slots) {
+            uint32_t best = count;
+            for (uint32_t i = 0; i < count; ++i)
+                if (!cs[i].per_block && cs[i].n && (best == count || rem[i] > rem[best])) best = i;
+            if (best == count || rem[best] == 0) break;
+            share[best] += 1;
+            rem[best] = 0;
+            given += 1;
+        }
+    }
     DecBatch batch;
     memset(&batch, 0, sizeof(batch));
     uint32_t wg = 0;
@@ -1133,9 +1161,8 @@ extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *cons
             T.wg_count = T.nblocks;
             T.segs_per_wg = 0;
         } else {
-            // share the resident workgroup slots in proportion to segment counts,
-            // with at least one wavefront's worth of segments per workgroup
-            uint64_t want = (slots * c.nsegs + seg_total - 1) / (seg_total ? seg_total : 1);
+            // at least one wavefront's worth of segments per workgroup
+            uint64_t want = share[i];
             const uint64_t cap = (c.nsegs + kDecWaves - 1) / kDecWaves;
             if (want > cap) want = cap;
             if (want == 0) want = 1;
