@@ -182,7 +182,8 @@ __host__ __device__ constexpr uint32_t stage_form(uint32_t A, uint32_t e)
     return A == 16u ? (e << 3) : (((e >> 1) | (e << 7)) & 0xFFu);
 }
 
-// Decoder tables kept in LDS.  For every value x of the next kLutBits stream bits:
+// Decoder tables kept in LDS.  For every value x of the next kLutBits stream bits one
+// 8-byte entry e[x] = {lo, hi}, read with one 64-bit LDS load:
 //   lo[x]  bits  0..3   bits taken by the whole codes that fit in the window (adv)
 //          bits  8..11  length of the first three codes together (0 if fewer)
 //          bits 16..23  number of those codes, at most four (ns)
@@ -192,18 +193,19 @@ __host__ __device__ constexpr uint32_t stage_form(uint32_t A, uint32_t e)
 //   hi[x]  bytes 0..3   stage forms of the decoded symbols, in stream order
 // The fields of lo are placed so that a lane can keep its bit position in the low
 // byte and its code count in bits 16..23 of one register and subtract whole entries
-// from it (bits 8..15 of that register start at 255 and absorb the third-code
-// field of up to 23 entries without a borrow), and so that the low five bits of lo
-// are exactly the shift that consumes the entry from a 32-bit window.  Entry
-// kLutSize is all zero.
+// from it, and so that the low five bits of lo are exactly the shift that consumes
+// the entry from a 32-bit window.  Bits 8..15 of that register start at 255 and
+// absorb the first-three-codes field of every entry subtracted: each field is at most
+// the bits its entry consumes, so their sum never exceeds the bits a lane consumes,
+// which is below 256 (a lane stops before position kPosBase + 31 + 128 + 32).
+// Entry kLutSize is all zero.
 //   lim/base/sym: canonical description for codes longer than the window.
 //   lim_short: the largest left-justified 32-bit window that starts with a code of at
 //   most kLutBits bits (canonical codes of length <= L fill [0, lim[L]) in order).
 constexpr uint32_t kLutSymMax = 4;
 
 struct __align__(16) DTab {
-    uint32_t lo[kLutSize + 4];
-    uint32_t hi[kLutSize + 4];
+    uint2 e[kLutSize + 4];              // {lo, hi}
     uint64_t lim[kMaxLen + 2];
     int32_t base[kMaxLen + 1];          // offset[L] - first[L]
     uint8_t sym[256];                   // stage form by canonical index
@@ -269,13 +271,9 @@ __device__ inline void dtab_fill(const Canon &c, uint32_t A, DTab &t, uint16_t *
                 hi = syms;
             }
         }
-        t.lo[x] = lo;
-        t.hi[x] = hi;
+        t.e[x] = make_uint2(lo, hi);
     }
-    if (tid < 4) {
-        t.lo[kLutSize + tid] = 0;
-        t.hi[kLutSize + tid] = 0;
-    }
+    if (tid < 4) t.e[kLutSize + tid] = make_uint2(0u, 0u);
 }
 
 }  // namespace zxk

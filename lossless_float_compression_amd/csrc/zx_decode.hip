@@ -8,9 +8,10 @@
 //     chunk l and starts at the chunk's stored gap (the first code starting in it);
 //   * count pass: a lane refreshes a 32-bit window from its LDS word rows with one
 //     funnel shift, then takes three lookups from it; each lookup indexes a
-//     1024-entry LDS table with the next 10 bits and yields up to three symbols.
-//     The entries stay in registers.  A running "256 - position" value gives the
-//     funnel-shift amount and the word row directly, and accumulates the code count;
+//     2048-entry LDS table with the next 11 bits (one 8-byte entry, one 64-bit LDS
+//     read) and yields up to four symbols.  The entries stay in registers.  A
+//     running "256 - position" value gives the funnel-shift amount and the word row
+//     directly, and accumulates the code count;
 //   * a wavefront prefix scan of the per-lane counts, plus the segment's stored first
 //     element, gives each lane its output offset;
 //   * replay: the register entries are dropped into a wavefront-private LDS stage in
@@ -28,7 +29,6 @@ namespace zxk {
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * kWave;
 constexpr int kDecWgPerCu = 2;
-constexpr int kDecMinWavesPerSimd = kDecWgPerCu * kDecWaves / 4;
 constexpr int kMaxBatch = 16;
 
 // Per-wavefront LDS: the lanes' stream words and the exponent stage.
@@ -53,10 +53,17 @@ constexpr int kNsRegs = (kEnt + 3) / 4;
 template <int DT> constexpr int dec_rounds() { return DT == ZX_E8M0 ? 11 : kRounds; }
 template <int DT> constexpr uint32_t dec_stage_bytes() { return DT == ZX_E8M0 ? 8224u : kStageBytes; }
 template <int DT> constexpr int dec_wg_per_cu() { return DT == ZX_E8M0 ? 1 : kDecWgPerCu; }
-constexpr int kWriteBatch = 7;                 // write-pass pieces per lane whose loads go out together
+constexpr int kWriteBatch = 7;                 // write-pass pieces per lane whose loads go out together (at most)
+// pieces per lane in one batch: 7 x 64 x 8 BF16 elements cover a stage; FP8 pieces hold
+// 16 elements, so 4 x 64 x 16 do (and fewer registers are live in the write pass)
+template <int DT> constexpr int write_batch() { return DT == ZX_FP8_E4M3FN ? 4 : kWriteBatch; }
 // Bit positions within a lane's rows: row r holds bits [32 r, 32 r + 32); row 1 is
 // the word holding the chunk's first bit, so the chunk starts at kPosBase + b0.
 constexpr uint32_t kPosBase = 32;
+// A lane's position stays below kPosBase + 31 (block start within its word) + 128
+// (chunk) + kMaxLen (a code started before the chunk end): the "256 - position" byte
+// and the first-three-codes field summed into the byte above it never borrow.
+static_assert(kPosBase + 31 + kChunkBits + kMaxLen < 256, "lane position must fit one byte");
 
 struct DecTensor {
     const uint8_t *signmant;
@@ -123,9 +130,9 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ uint32_t lds_word(const uint32_t *base, uint32_t byte_off)
+__device__ __forceinline__ uint2 lds_pair(const uint2 *base, uint32_t byte_off)
 {
-    return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(base) + byte_off);
+    return *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(base) + byte_off);
 }
 
 // ---- stream words of the lanes' chunks --------------------------------------
@@ -206,9 +213,9 @@ __device__ __forceinline__ uint32_t slow_sym(const DTab &tab, uint32_t v, uint32
 __device__ __forceinline__ uint32_t one_code(const DTab &tab, uint32_t v, uint32_t &sym)
 {
     const uint32_t x = v >> (32 - kLutBits);
-    const uint32_t lo = tab.lo[x];
+    const uint32_t lo = tab.e[x].x;
     if (lo != 0) {
-        sym = tab.hi[x] & 0xFFu;
+        sym = tab.e[x].y & 0xFFu;
         return (lo >> 24) & 0xFu;
     }
     const uint32_t L = slow_len(tab, v);
@@ -272,7 +279,7 @@ __device__ __forceinline__ void prefetch_sm(const uint8_t *sm_block, uint32_t i_
     if constexpr (DT == ZX_E8M0) {   // nothing to read: the symbol is the whole element
         smcut = 0;
 #pragma unroll
-        for (int k = 0; k < kWriteBatch; ++k) smv[k] = make_uint2(0, 0);
+        for (int k = 0; k < write_batch<DT>(); ++k) smv[k] = make_uint2(0, 0);
         return;
     }
     const uint32_t ii = cut_elem<DT>(i_begin, i_end);
@@ -282,7 +289,7 @@ __device__ __forceinline__ void prefetch_sm(const uint8_t *sm_block, uint32_t i_
     const uint32_t qf_begin = (i_begin + P - 1) / P;
     const uint32_t qf_end = i_end / P;
 #pragma unroll
-    for (int k = 0; k < kWriteBatch; ++k) {
+    for (int k = 0; k < write_batch<DT>(); ++k) {
         const uint32_t q = qf_begin + lane + k * kWave;
         const uint8_t *a = q < qf_end ? sm_block + (DT == ZX_BF16 ? q * P : q * P / 2) : dummy;
         smv[k] = *reinterpret_cast<const uint2 *>(a);
@@ -293,10 +300,11 @@ __device__ __forceinline__ void prefetch_sm(const uint8_t *sm_block, uint32_t i_
 // arrived and no store of the segment is out yet.  A register the loads target
 // that looks still pending on some path would make the next segment's first write
 // to it wait for all memory operations, this segment's stores included.
+template <int DT>
 __device__ __forceinline__ void settle_sm(const uint2 (&smv)[kWriteBatch], uint32_t smcut)
 {
 #pragma unroll
-    for (int k = 0; k < kWriteBatch; ++k) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
+    for (int k = 0; k < write_batch<DT>(); ++k) asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
     asm volatile("" ::"v"(smcut));
 }
 
@@ -395,14 +403,14 @@ __device__ __forceinline__ void store_batch(void *out_block, uint32_t qb, uint32
     const uint32_t lane = lane_now();
     uint4 r[kWriteBatch];
 #pragma unroll
-    for (int k = 0; k < kWriteBatch; ++k) {
+    for (int k = 0; k < write_batch<DT>(); ++k) {
         const uint32_t q = qb + lane + k * kWave;
         r[k] = make_uint4(0, 0, 0, 0);
         asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
         if (q < qf_end) r[k] = fuse_piece<DT>(smv[k], piece_exps<DT>(stage + (q * P - sbase), degen, dsplat));
     }
 #pragma unroll
-    for (int k = 0; k < kWriteBatch; ++k) {
+    for (int k = 0; k < write_batch<DT>(); ++k) {
         const uint32_t q = qb + lane + k * kWave;
         if (q < qf_end) store_piece<DT>(out_block, q * P, r[k]);
     }
@@ -449,12 +457,12 @@ __device__ __forceinline__ void write_range(void *out_block, const uint8_t *sm_b
     uint32_t qb = qf_begin;
     if (kPre && qb < qf_end) {
         store_batch<DT>(out_block, qb, qf_end, smv0, stage, sbase, degen, dsplat);
-        qb += kWave * kWriteBatch;
+        qb += kWave * write_batch<DT>();
     }
-    for (; qb < qf_end; qb += kWave * kWriteBatch) {
+    for (; qb < qf_end; qb += kWave * write_batch<DT>()) {
         uint2 smv[kWriteBatch];
 #pragma unroll
-        for (int k = 0; k < kWriteBatch; ++k) {
+        for (int k = 0; k < write_batch<DT>(); ++k) {
             const uint32_t q = qb + lane + k * kWave;
             smv[k] = make_uint2(0, 0);
             if (q < qf_end) smv[k] = load_sm<DT>(sm_block, q * P);
@@ -476,7 +484,7 @@ __device__ uint32_t count_generic(const DTab &tab, lds_cu32 *col, uint32_t start
     if (work) {
         while (p < lim) {
             const uint32_t v = window(col, 256u - p);
-            const uint32_t lo = tab.lo[v >> (32 - kLutBits)];
+            const uint32_t lo = tab.e[v >> (32 - kLutBits)].x;
             if (lo != 0 && p + kLutBits <= lim) {
                 cnt += (lo >> 16) & 0xFFu;
                 p += lo & 0xFFu;
@@ -660,6 +668,33 @@ __device__ __forceinline__ void issue_seg(const DecTensor &T, uint32_t s, const 
     in.ch0 = m.j * kSegChunks;
 }
 
+// ---- the spare stage of the fast decode ---------------------------------------
+//
+// One wavefront at a time may use the workgroup's spare stage, for a segment that
+// needs the code-by-code passes.  The holder waits for no other wavefront while it
+// holds it, so every waiting wavefront gets it in the end; the wait is capped anyway
+// (about a second, far beyond any holder's work), after which the segment is
+// reported corrupt and skipped.
+__device__ __forceinline__ bool spare_acquire(uint32_t *lock)
+{
+    for (uint32_t spin = 0; spin < (1u << 24); ++spin) {
+        uint32_t got = 0;
+        if (lane_now() == 0) got = atomicCAS(lock, 0u, 1u) == 0u ? 1u : 0u;
+        if (__builtin_amdgcn_readfirstlane(got)) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+}
+
+__device__ __forceinline__ void spare_release(uint32_t *lock)
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (lane_now() == 0) atomicExch(lock, 0u);
+}
+
 // ---- one segment per wavefront ------------------------------------------------
 
 // Byte selector that puts byte 2 of the first v_perm operand into byte j and keeps
@@ -676,10 +711,11 @@ __host__ __device__ constexpr uint32_t ns_sel(int j)
 // the lookup (a long code in slot 0) to the entry and to its count.
 #define ZX_LOOKUP(a, slot, xsym, xns)                                                    \
     do {                                                                                 \
-        const uint32_t x_ = (a) ? ((win >> (30 - kLutBits)) & ((kLutSize - 1u) << 2))    \
-                                : (kLutSize * 4u);                                       \
-        const uint32_t lo_ = lds_word(tab.lo, x_);                                       \
-        const uint32_t hi_ = lds_word(tab.hi, x_);                                       \
+        const uint32_t x_ = (a) ? ((win >> (29 - kLutBits)) & ((kLutSize - 1u) << 3))    \
+                                : (kLutSize * 8u);                                       \
+        const uint2 e_ = lds_pair(tab.e, x_);                                            \
+        const uint32_t lo_ = e_.x;                                                       \
+        const uint32_t hi_ = e_.y;                                                       \
         win <<= (lo_ & 31u);                                                             \
         Bprev = (a) ? B : Bprev;                                                         \
         B -= lo_;                                                                        \
@@ -691,10 +727,16 @@ __host__ __device__ constexpr uint32_t ns_sel(int j)
 // wavefront's LDS rows.  The next segment's loads are issued into `in` (when
 // has_next) and, once this segment no longer reads its rows, stored to them;
 // returns whether that store was made.
-template <int DT>
+// FAST: the word rows and the stage share one region (the words of segment k are put
+// in at its start, from `in`, after segment k-1's write pass has read the stage), and a
+// segment that needs the code-by-code passes borrows the workgroup's spare stage under
+// `lock`.  Otherwise the rows have a region of their own and the next segment's words
+// are put in right after the count pass.
+template <int DT, bool FAST = false>
 __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *sw,
                                                     uint32_t s, const SegMeta &m, SegIn &in, bool has_next, uint32_t sn,
-                                                    const SegMeta &mn, uint32_t *err)
+                                                    const SegMeta &mn, uint32_t *err, uint8_t *spare = nullptr,
+                                                    uint32_t *lock = nullptr)
 {
     constexpr uint32_t A = alphabet_of(DT);
     const uint32_t lane = lane_now();
@@ -714,6 +756,7 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     // its first write batch, are requested first; they arrive while this segment
     // decodes.  The bytes are requested only on the path that uses them, so that no
     // path from their request to the next segment skips their use.
+    if constexpr (FAST) rows_store_in(sw, lane, in);
     wave_sync();
     const uint32_t gap = sw[kGapSlot * kWave + lane];
     const uint32_t gap_next = sw[kGapSlot * kWave + lane + 1];
@@ -725,7 +768,7 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
         uint2 smv[kWriteBatch];
         uint32_t smcut;
         prefetch_sm<DT>(sm_block, e0, e_end, reinterpret_cast<const uint8_t *>(T.stream), smv, smcut);
-        settle_sm(smv, smcut);
+        settle_sm<DT>(smv, smcut);
         write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, true, stage_form(A, d), smv, smcut);
         return false;
     }
@@ -839,18 +882,32 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
 
     const uint32_t t0 = e0 - sbase;   // stage position of the segment's first element
     if (t0 + total + 3 > dec_stage_bytes<DT>()) {
-        write_rounds<DT>(tab, col, stage, start, cnt, off, t0, total, out_block, sm_block, sbase);
+        if constexpr (FAST) {
+            if (!spare_acquire(lock)) { report(err, ZX_E_CORRUPT); return false; }
+            write_rounds<DT>(tab, col, spare, start, cnt, off, t0, total, out_block, sm_block, sbase);
+            spare_release(lock);
+        } else {
+            write_rounds<DT>(tab, col, stage, start, cnt, off, t0, total, out_block, sm_block, sbase);
+        }
         return false;
     }
     // some lane needed more lookups than the registers hold: its symbols go to the
-    // stage one code at a time, and no entry is replayed
+    // stage one code at a time, and no entry is replayed.  (FAST: the rows are still
+    // needed for that, so the symbols go to the spare stage.)
+    if constexpr (FAST) {
+        if (more) {
+            if (!spare_acquire(lock)) { report(err, ZX_E_CORRUPT); return false; }
+            stage = spare;
+        }
+    }
     if (more) store_generic(tab, col, stage, start, cnt, t0 + off);
     const uint32_t rcnt = more ? 0u : cnt;
 
     // the rows are read no more: the next segment's words go in now, before this
     // segment's stores are in flight (a later wait for them would have to drain
-    // those stores too)
-    rows_store_in(sw, lane, in);
+    // those stores too).  (FAST: they go in at the next segment's start; the replay
+    // below overwrites the rows.)
+    if constexpr (!FAST) rows_store_in(sw, lane, in);
     // the sign/mantissa bytes of the first write batch are requested now: they arrive
     // during the replay, and their registers are free during the count pass.  From
     // here to their use below there is no exit, so every path uses them before any
@@ -907,8 +964,11 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
         a0[0] = (uint8_t)f3;
     }
     wave_sync();
-    settle_sm(smv, smcut);
+    settle_sm<DT>(smv, smcut);
     write_range<DT, true>(out_block, sm_block, e0, e_end, stage, sbase, false, 0, smv, smcut);
+    if constexpr (FAST) {
+        if (more) spare_release(lock);
+    }
     return true;
 }
 #undef ZX_LOOKUP
@@ -1042,6 +1102,114 @@ __global__ __launch_bounds__(kDecThreads, dec_wg_per_cu<DT>() * kDecWaves / 4) v
     }
 }
 
+// Issue priority of this wavefront from the share of its segments still ahead: 3 at
+// the start, down to 0 for its last quarter.  A SIMD issues from its oldest wavefront
+// first among equal priorities, so without this the workgroups a CU received first run
+// ahead and the last one is left to finish its segments alone with few wavefronts
+// beside it; with it, wavefronts that are behind go first and the CU's wavefronts end
+// close together, at full occupancy until near the end.
+__device__ __forceinline__ void set_priority_by_remaining(uint32_t remaining, uint32_t total)
+{
+    const uint32_t p = __builtin_amdgcn_readfirstlane((4u * remaining - 1u) / total);   // 0..3
+    if (p >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (p == 2) __builtin_amdgcn_s_setprio(2);
+    else if (p == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
+// ---- fast decode of per-tensor-codebook BF16 / FP8 containers ------------------
+//
+// Three 512-thread workgroups per CU (six wavefronts per SIMD) instead of two: each
+// wavefront's stream words and its stage share one region, descriptors are refreshed
+// sixteen at a time, and the code-by-code passes borrow one spare stage per
+// workgroup.  A tensor of 5376 segments (4096 x 4096 BF16) then gets one segment per
+// wavefront instead of two for a third of them, and every wavefront has more company
+// to hide its memory and LDS waits behind.  Segments of mean code length below about
+// 2.3 bits overflow the stage and take the spare one wavefront at a time, so such
+// containers go to k_decode instead (the host picks).
+constexpr int kFastWgPerCu = 3;
+constexpr uint32_t kFastMeta = 16;   // descriptors per wavefront refresh
+static_assert(kSegWords * 4 <= kStageBytes, "the word rows fit the stage region");
+
+struct FastShared {
+    DTab tab;
+    uint8_t region[kDecWaves][kStageBytes];   // rows during the count pass, then the stage
+    SegMeta meta[kDecWaves][kFastMeta];
+    uint8_t spare[kStageBytes];               // the code-by-code passes' stage
+    uint32_t lock;
+};
+static_assert(sizeof(FastShared) <= 160u * 1024u / kFastWgPerCu, "fast decode workgroup LDS budget");
+
+template <int DT>
+__global__ __launch_bounds__(kDecThreads, kFastWgPerCu * kDecWaves / 4) void k_decode_fast(const DecBatch batch, uint32_t *err)
+{
+    static_assert(DT == ZX_BF16 || DT == ZX_FP8_E4M3FN, "fast decode: BF16 and FP8");
+    __shared__ FastShared sh;
+    const uint32_t g = blockIdx.x;
+    uint32_t t = 0;
+    while (t + 1 < batch.count && g >= batch.t[t + 1].wg_begin) ++t;
+    const DecTensor &T = batch.t[t];
+    const uint32_t lg = g - T.wg_begin;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint32_t lane = lane_now();
+    const uint32_t s_begin = lg * T.segs_per_wg;
+    const uint32_t s_end = s_begin + T.segs_per_wg < T.nsegs ? s_begin + T.segs_per_wg : T.nsegs;
+    // the wavefront's segments are s_begin + wave + kDecWaves k, k < nk; lane i < 16
+    // loads the descriptor of the i-th (in groups of 16)
+    const uint32_t s0 = s_begin + wave;
+    const uint32_t nk = __builtin_amdgcn_readfirstlane(s0 < s_end ? (s_end - s0 + kDecWaves - 1) / kDecWaves : 0);
+    // the prepared table is requested first, the descriptors and first words next; the
+    // table is stored to LDS once it arrives
+    const uint4 *src = reinterpret_cast<const uint4 *>(T.dtab);
+    uint4 *dst = reinterpret_cast<uint4 *>(&sh.tab);
+    constexpr uint32_t kTabPieces = sizeof(DTab) / 16;
+    constexpr uint32_t kPer = (kTabPieces + kDecThreads - 1) / kDecThreads;
+    uint4 pc[kPer];
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+        const uint32_t i = tid + k * kDecThreads;
+        pc[k] = i < kTabPieces ? src[i] : make_uint4(0, 0, 0, 0);
+    }
+    SegMeta mine;
+    load_meta(T, s0 + kDecWaves * lane, lane < kFastMeta && lane < nk, mine);
+    SegIn in;
+    issue_seg(T, s0, meta_at(mine, 0), lane, in, nk != 0);
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+        const uint32_t i = tid + k * kDecThreads;
+        if (i < kTabPieces) dst[i] = pc[k];
+    }
+    SegMeta *metas = sh.meta[wave];
+    if (lane < kFastMeta) metas[lane] = mine;
+    if (tid == 0) sh.lock = 0;
+    __syncthreads();
+    uint8_t *reg = sh.region[wave];
+    uint32_t *sw = reinterpret_cast<uint32_t *>(reg);
+    for (uint32_t k = 0; k < nk; ++k) {
+        set_priority_by_remaining(nk - k, nk);
+        const uint32_t i = k & (kFastMeta - 1);
+        const uint32_t s = s0 + kDecWaves * k;
+        const bool has_next = k + 1 < nk && i + 1 < kFastMeta;
+        const SegMeta mu = meta_get(metas, i);
+        const SegMeta mn = meta_get(metas, has_next ? i + 1 : i);
+        decode_segment_body<DT, true>(T, sh.tab, reg, sw, s, mu, in, has_next, s + kDecWaves, mn, err, sh.spare, &sh.lock);
+        if (i == kFastMeta - 1 && k + 1 < nk) {
+            // next group of 16 descriptors, and the words of its first segment (put
+            // in at that segment's start)
+            SegMeta m2;
+            load_meta(T, s + kDecWaves + kDecWaves * lane, lane < kFastMeta && k + 1 + lane < nk, m2);
+            issue_seg(T, s + kDecWaves, meta_at(m2, 0), lane, in, true);
+            wave_sync();
+            if (lane < kFastMeta) metas[lane] = m2;
+            wave_sync();
+        }
+    }
+    // the last request into `in` (a dummy, or the words of a segment this wavefront
+    // does not decode) is used here, so that no load is left unused in flight
+    asm volatile("" ::"v"(in.rv.x), "v"(in.rtail), "v"(in.gap), "v"(in.gapn));
+}
+
 __global__ __launch_bounds__(1024) void k_build_dtab(const uint8_t *__restrict__ lengths, uint32_t A, DTab *__restrict__ out)
 {
     __shared__ Canon c;
@@ -1098,8 +1266,16 @@ extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *cons
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
+    // the fast decode takes BF16 / FP8 batches of per-tensor codebooks whose mean code
+    // length is at least 2.3 bits (a segment then averages under 3562 elements, inside
+    // its stage); anything else goes to k_decode
+    bool fast = dt == ZX_BF16 || dt == ZX_FP8_E4M3FN;
+    for (uint32_t i = 0; i < count && fast; ++i) {
+        if (cs[i].n == 0) continue;
+        if (cs[i].per_block || 10 * cs[i].total_bits < 23 * cs[i].n) fast = false;
+    }
     // resident 512-thread workgroups
-    uint64_t slots = (uint64_t)cus * (dt == ZX_E8M0 ? dec_wg_per_cu<ZX_E8M0>() : kDecWgPerCu);
+    uint64_t slots = (uint64_t)cus * (fast ? kFastWgPerCu : dt == ZX_E8M0 ? dec_wg_per_cu<ZX_E8M0>() : kDecWgPerCu);
     if (max_workgroups != 0 && max_workgroups < slots) slots = max_workgroups;
     // resident workgroup slots for each per-tensor-codebook container: its share of the
     // slots by segment count, rounded down, then the slots left over go to the largest
@@ -1173,7 +1349,11 @@ extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *cons
     }
     batch.count = used;
     if (used == 0) return ZX_OK;
-    if (dt == ZX_BF16)
+    if (fast && dt == ZX_BF16)
+        hipLaunchKernelGGL((k_decode_fast<ZX_BF16>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
+    else if (fast)
+        hipLaunchKernelGGL((k_decode_fast<ZX_FP8_E4M3FN>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
+    else if (dt == ZX_BF16)
         hipLaunchKernelGGL((k_decode<ZX_BF16, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
     else if (dt == ZX_E8M0)
         hipLaunchKernelGGL((k_decode<ZX_E8M0, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);

@@ -251,3 +251,23 @@ def test_dense_runs_in_ordinary_data(dtype):
     assert int(o.lengths[0, top]) == 1
     mx_chunk, mx_seg = regime(o, e)
     assert mx_chunk > 84 and mx_seg < 3600, (mx_chunk, mx_seg)
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_dense_stretch_in_ordinary_data(dtype):
+    """Mean code length above 2.3 bits overall (the decode that shares one LDS region
+    between a wavefront's words and its stage), with a stretch of one short-coded
+    exponent in the middle: those segments hold more elements than the stage, so
+    several wavefronts of one workgroup take the spare stage in turn."""
+    say("dense stretch", dtype)
+    rng = np.random.default_rng(17 + dtype)
+    n = 7 * 65536 + 333
+    top = 120 if dtype == 0 else 12
+    e = (top - rng.geometric(0.3, n).clip(1, 30 if dtype == 0 else 12)).astype(np.uint8)
+    e[150_000:190_000] = top - 1       # the commonest exponent: a code of two bits or less
+    x = bf16_from_exps(e, rng) if dtype == 0 else fp8_from_exps(e, rng)
+    o = parity(dtype, x, per_block=False)
+    assert int(o.lengths[0, top - 1]) <= 2
+    assert o.total_bits * 10 >= 23 * n, o.total_bits / n
+    mx_chunk, mx_seg = regime(o, e)
+    assert mx_seg > 3616, (mx_chunk, mx_seg)
