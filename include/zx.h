@@ -81,7 +81,9 @@ typedef enum {
     ZX_E_CODEBOOK = 3,     /* max_len infeasible, or data/codebook mismatch        */
     ZX_E_CORRUPT = 4,      /* container inconsistent (device-detected)             */
     ZX_E_HIP = 5,          /* a HIP launch failed                                  */
-    ZX_E_NOSPACE = 6       /* K/V slots: a block's code bits exceed its slot         */
+    ZX_E_NOSPACE = 6,      /* K/V slots: a block's code bits exceed its slot         */
+    ZX_E_LIMIT = 7         /* request larger than the fixed scratch of an entry point
+                              that allocates nothing                                 */
 } zx_status;
 
 typedef enum {
@@ -269,6 +271,22 @@ size_t zx_kv_workspace_bytes(zx_dtype dtype, uint32_t nblk);
 zx_status zx_kv_encode_slots(const zx_kv_pool *pool, const void *src, uint32_t nblk,
                              const uint32_t *slot_ids, uint32_t max_len, void *workspace,
                              size_t ws_bytes, uint32_t *status, uint32_t *err, hipStream_t stream);
+
+/* zx_kv_encode_slots for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same work with no
+ * workspace argument.  The workspace is a file-scope device array of the library,
+ * sized for ZX_KV_NOALLOC_MAX_BLOCKS blocks (1,325,088 bytes, held on each device the
+ * library runs on until the process ends); nblk above that returns ZX_E_LIMIT before
+ * anything is enqueued.  The entry point calls no hipMalloc, hipFree or other
+ * allocating routine; on its first call on a device it looks up the array's address
+ * there (hipGetSymbolAddress; ZX_E_HIP if that fails).  Every call on one device uses
+ * the same array: calls that overlap in time on one device (other streams, other host
+ * threads) race, and must be ordered by the caller.  Results equal zx_kv_encode_slots'
+ * for the same arguments. */
+#define ZX_KV_NOALLOC_MAX_BLOCKS 1024u
+zx_status zx_kv_encode_slots_noalloc(const zx_kv_pool *pool, const void *src, uint32_t nblk,
+                                     const uint32_t *slot_ids, uint32_t max_len, uint32_t *status,
+                                     uint32_t *err, hipStream_t stream);
 
 /* The container of slot `slot` (host struct of device pointers into the pool), for
  * zx_decode / zx_decode_block_batch: decoding reused K/V blocks on demand (ZipFloat

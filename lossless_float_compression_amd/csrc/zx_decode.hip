@@ -1429,6 +1429,7 @@ extern "C" const char *zx_status_string(zx_status s)
     case ZX_E_CORRUPT: return "corrupt container";
     case ZX_E_HIP: return "HIP launch failure";
     case ZX_E_NOSPACE: return "block does not fit its slot";
+    case ZX_E_LIMIT: return "request larger than the library's fixed scratch";
     }
     return "unknown status";
 }

@@ -13,6 +13,8 @@
 // global stream words; whole words are then written with plain stores.  The only
 // words two blocks can share are a block's first and last word; those are cleared
 // beforehand and combined with atomicOr, which gives the same bytes in any order.
+#include <mutex>
+
 #include "zx_common.h"
 
 namespace zxk {
@@ -826,7 +828,7 @@ extern "C" zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int p
 }
 
 // ---- K/V slot pool
-static uint32_t kv_alphabet(zx_dtype d) { return d == ZX_BF16 ? 256u : 16u; }
+static constexpr uint32_t kv_alphabet(zx_dtype d) { return d == ZX_BF16 ? 256u : 16u; }
 
 extern "C" zx_status zx_kv_slot_sizes(zx_dtype dtype, uint32_t cap_words, zx_kv_sizes *out)
 {
@@ -843,14 +845,14 @@ extern "C" zx_status zx_kv_slot_sizes(zx_dtype dtype, uint32_t cap_words, zx_kv_
 
 // workspace: hist u32[nblk][A], lengths u8[nblk][A], degenerate u16[nblk],
 // bits u64[nblk+1], segments u32[nblk+1]; each part 16-byte aligned
-static size_t kv_round16(size_t x) { return (x + 15) & ~(size_t)15; }
+static constexpr size_t kv_round16(size_t x) { return (x + 15) & ~(size_t)15; }
 struct KvWs {
     size_t hist, len, deg, bits, nseg, total;
 };
-static KvWs kv_ws(zx_dtype dtype, uint32_t nblk)
+static constexpr KvWs kv_ws(zx_dtype dtype, uint32_t nblk)
 {
     const size_t A = kv_alphabet(dtype);
-    KvWs w;
+    KvWs w{};
     w.hist = 0;
     w.len = w.hist + kv_round16((size_t)nblk * A * 4);
     w.deg = w.len + kv_round16((size_t)nblk * A);
@@ -923,6 +925,58 @@ extern "C" zx_status zx_kv_encode_slots(const zx_kv_pool *pool, const void *src,
         hipLaunchKernelGGL(k_encode_slots<ZX_FP8_E4M3FN>, dim3(nblk), dim3(kEncThreads), 0, stream, P, src, slot_ids, len, deg,
                            bits, nseg, status, err);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}
+
+// ---- K/V append with no allocation ---------------------------------------------
+//
+// For callers that cannot allocate (code under HIP graph capture, serving loops,
+// harnesses that forbid it): the workspace of zx_kv_encode_slots lives in a
+// file-scope device array of fixed size instead of coming from the caller.  Each
+// device holds its own copy at its own address, found once per device with
+// hipGetSymbolAddress; the array's name is only a host-side stand-in and is never
+// handed to a kernel.  Every part of the workspace is written in full by the kernel
+// that produces it before any kernel reads it, so nothing is cleared between calls.
+// Calls on one device share the array: calls that overlap in time on one device race.
+constexpr uint32_t kKvNoAllocMaxBlocks = ZX_KV_NOALLOC_MAX_BLOCKS;
+constexpr size_t kKvScratchBytes = kv_ws(ZX_BF16, kKvNoAllocMaxBlocks).total;
+static_assert(kv_ws(ZX_FP8_E4M3FN, kKvNoAllocMaxBlocks).total <= kKvScratchBytes, "scratch sized for the larger alphabet");
+static __device__ __align__(256) uint8_t scratch[kKvScratchBytes];
+
+constexpr int kScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kScratchDevices];
+
+// Device address of `scratch` on the current device (looked up on the first call per
+// device), or null with *st set.
+static void *scratch_on_current_device(zx_status *st)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+        *st = ZX_E_HIP;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> guard(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            *st = ZX_E_HIP;
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+extern "C" zx_status zx_kv_encode_slots_noalloc(const zx_kv_pool *pool, const void *src, uint32_t nblk,
+                                                const uint32_t *slot_ids, uint32_t max_len, uint32_t *status,
+                                                uint32_t *err, hipStream_t stream)
+{
+    if (nblk > kKvNoAllocMaxBlocks) return ZX_E_LIMIT;
+    if (nblk == 0) return zx_kv_encode_slots(pool, src, 0, slot_ids, max_len, nullptr, 0, status, err, stream);
+    zx_status st = ZX_OK;
+    void *ws = scratch_on_current_device(&st);
+    if (!ws) return st;
+    return zx_kv_encode_slots(pool, src, nblk, slot_ids, max_len, ws, kKvScratchBytes, status, err, stream);
 }
 
 extern "C" zx_status zx_kv_slot_container(const zx_kv_pool *pool, uint32_t slot, zx_container *out)

@@ -91,7 +91,7 @@ class KVSlotPool:
         return self._ws
 
     def append(self, blocks: torch.Tensor, slot_ids: torch.Tensor, status: Optional[torch.Tensor] = None,
-               err: Optional[torch.Tensor] = None, max_len: int = 32, stream=None) -> torch.Tensor:
+               err: Optional[torch.Tensor] = None, max_len: int = 32, stream=None, noalloc: bool = False) -> torch.Tensor:
         """Compress `blocks` (k * 65536 elements, contiguous; bf16/int16 for a BF16
         pool, float8_e4m3fn/uint8 for FP8) into slots `slot_ids` (device int32 [k],
         distinct).  Returns the per-block status (device int32 [k]: 0, or 6 when the
@@ -106,6 +106,15 @@ class KVSlotPool:
             raise ValueError("slot_ids must be a device int32 tensor with one entry per block")
         if status is None:
             status = torch.empty(k, dtype=torch.int32, device=flat.device)
+        if noalloc:
+            # the library's own fixed scratch (zx_kv_encode_slots_noalloc): at most
+            # KV_NOALLOC_MAX_BLOCKS blocks per call, no workspace, and calls on one
+            # device must not overlap
+            st = _zx.lib().zx_kv_encode_slots_noalloc(C.byref(self.pool), _zx._ptr(flat), k, _zx._ptr(slot_ids),
+                                                      int(max_len), _zx._ptr(status), _zx._ptr(err), _zx._stream(stream))
+            if st != 0:
+                raise _zx.ZxError("zx_kv_encode_slots_noalloc", st)
+            return status
         ws = self.workspace(k)
         st = _zx.lib().zx_kv_encode_slots(C.byref(self.pool), _zx._ptr(flat), k, _zx._ptr(slot_ids), int(max_len),
                                           _zx._ptr(ws), ws.numel(), _zx._ptr(status), _zx._ptr(err),

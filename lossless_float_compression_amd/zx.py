@@ -29,8 +29,11 @@ LIB_PATH = os.path.join(_HERE, "libzx.so")
 _lib = None
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported dtype", 3: "codebook error",
-           4: "corrupt container", 5: "HIP launch failure", 6: "block does not fit its slot"}
+           4: "corrupt container", 5: "HIP launch failure", 6: "block does not fit its slot",
+           7: "request larger than the library's fixed scratch"}
 ZX_E_NOSPACE = 6
+ZX_E_LIMIT = 7
+KV_NOALLOC_MAX_BLOCKS = 1024
 
 
 class ZxError(RuntimeError):
@@ -76,7 +79,8 @@ EXPORTS = ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "
            "zx_decode_table_bytes", "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_stream_words",
            "zx_status_string", "zx_version", "zx_kv_slot_sizes", "zx_kv_workspace_bytes", "zx_kv_encode_slots",
            "zx_kv_slot_container", "zx_kv_decode_slots", "zx_zf_scan_workspace_bytes", "zx_zf_encode_size",
-           "zx_zf_encode", "zx_zf_decode", "zx_histogram_accumulate", "zx_build_codebook_u64")
+           "zx_zf_encode", "zx_zf_decode", "zx_histogram_accumulate", "zx_build_codebook_u64",
+           "zx_kv_encode_slots_noalloc")
 
 
 def lib():
@@ -107,6 +111,7 @@ def lib():
         L.zx_kv_workspace_bytes.argtypes = [I, U32]
         L.zx_kv_workspace_bytes.restype = C.c_size_t
         L.zx_kv_encode_slots.argtypes = [C.POINTER(zx_kv_pool), P, U32, P, U32, P, C.c_size_t, P, P, P]
+        L.zx_kv_encode_slots_noalloc.argtypes = [C.POINTER(zx_kv_pool), P, U32, P, U32, P, P, P]
         L.zx_kv_slot_container.argtypes = [C.POINTER(zx_kv_pool), U32, C.POINTER(zx_container)]
         L.zx_kv_decode_slots.argtypes = [C.POINTER(zx_kv_pool), P, U32, P, P, P]
         L.zx_zf_scan_workspace_bytes.argtypes = [U64]
@@ -119,7 +124,8 @@ def lib():
         for f in ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
                   "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_kv_slot_sizes",
                   "zx_kv_encode_slots", "zx_kv_slot_container", "zx_kv_decode_slots", "zx_zf_encode_size",
-                  "zx_zf_encode", "zx_zf_decode", "zx_histogram_accumulate", "zx_build_codebook_u64"):
+                  "zx_zf_encode", "zx_zf_decode", "zx_histogram_accumulate", "zx_build_codebook_u64",
+                  "zx_kv_encode_slots_noalloc"):
             getattr(L, f).restype = I
         _lib = L
     return _lib

@@ -46,8 +46,9 @@ def test_stream_words_rule(zx):
 
 def test_status_strings(zx):
     lib = zx.lib()
-    for s in range(7):
+    for s in range(8):
         assert lib.zx_status_string(s)
+    assert lib.zx_status_string(7) != lib.zx_status_string(99)
 
 
 def test_argument_errors_return_before_any_launch(zx):
@@ -81,6 +82,11 @@ def test_argument_errors_return_before_any_launch(zx):
     c.dtab = 0x30000
     c.stream_words = 5
     assert lib.zx_decode(C.byref(c), P(0x20000), None, None) == 1
+    # the K/V append without allocation takes at most ZX_KV_NOALLOC_MAX_BLOCKS blocks
+    pool = zx.zx.zx_kv_pool()
+    assert zx.zx.KV_NOALLOC_MAX_BLOCKS == 1024
+    assert "#define ZX_KV_NOALLOC_MAX_BLOCKS 1024u" in open(HEADER).read()
+    assert lib.zx_kv_encode_slots_noalloc(C.byref(pool), P(0x1000), 1025, P(0x2000), 32, P(0x3000), None, None) == 7
 
 
 def test_element_type_codes_agree():
