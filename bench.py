@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    p.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "c2-low", "c4-low"])
     p.add_argument("--copies", type=int, default=0, help="rotation depth (0 = enough for 1 GiB)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--overlap", action="store_true",
@@ -91,7 +91,20 @@ def decode_source_hash(sources=DECODE_SOURCES) -> str:
 
 # workload names used in the committed profile summaries
 WORKLOAD_SLUG = {"c1": "bf16_1024x1024", "c2": "bf16_4096x4096", "c3": "llama3_8b_shaped_layer",
-                 "c4": "fp8_e4m3_8192x8192", "c5": "bf16_kv_cache"}
+                 "c4": "fp8_e4m3_8192x8192", "c5": "bf16_kv_cache",
+                 "c2-low": "bf16_4096x4096_low_entropy", "c4-low": "fp8_e4m3_8192x8192_low_entropy"}
+
+
+def decode_kernel_name(cs) -> str:
+    """Which decode kernel the library launches for a batch of containers (the same
+    rule as its host code: per-block codebooks take k_decode; a batch with a container
+    under 2.3 bits per code, or of E8M0 scales, takes the fast decode's low-entropy mode)."""
+    cs = [c for c in cs if c.n]
+    if any(c.per_block for c in cs):
+        return "k_decode (per-block codebooks)"
+    if any(c.dtype == 2 or 10 * c.total_bits < 23 * c.n for c in cs):
+        return "k_decode_fast (low-entropy mode)"
+    return "k_decode_fast"
 
 
 def profiled_traffic(cfg: str, kernel: str = "k_decode", sources=DECODE_SOURCES):
@@ -144,6 +157,12 @@ def make_input(cfg):
     if cfg == "c4":
         q, scale = workloads.c4()
         return (q.cuda(), "c4: FP8 E4M3FN [8192,8192] N(0,1)*448/amax, one codebook, nibble sign+mantissa", scale)
+    if cfg == "c2-low":
+        return (workloads.low_entropy(workloads.BF16).cuda(),
+                "BF16 [4096,4096] low-entropy exponents (one value at p 0.85, geometric tail), one codebook", None)
+    if cfg == "c4-low":
+        return (workloads.low_entropy(workloads.FP8).cuda(),
+                "FP8 E4M3FN [8192,8192] low-entropy exponents (one value at p 0.85, geometric tail), one codebook", 1.0)
     raise ValueError(cfg)
 
 
@@ -328,7 +347,7 @@ def layer_call_record(n_layers: int = 4, reps: int = 25):
             "decode_GBps": round(raw / (med * 1e-3) / 1e9, 2),
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(ach / HBM_PEAK_GBPS, 4), "alg_bytes_per_launch": int(alg),
-                         "traffic": profiled_traffic("c3"), "kernel": "k_decode"},
+                         "traffic": profiled_traffic("c3"), "kernel": decode_kernel_name(layers[0])},
             "segments_per_call": int(sum(c.nsegs for c in layers[0])),
             "reps": reps}
 
@@ -456,7 +475,7 @@ def bench_single(args):
         "context_d2d_copy_GBps": copy_context_GBps(alg),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(args.config),
-                     "kernel": "k_decode", "alg_bytes_per_launch": alg},
+                     "kernel": decode_kernel_name([c]), "alg_bytes_per_launch": alg},
     }
     if args.config == "c2" and not args.no_layer_call:
         del xs, cs, outs
@@ -486,7 +505,7 @@ def main():
     if args.kv_slots and args.config != "c5":
         print("--kv-slots applies to --config c5", file=sys.stderr)
         sys.exit(2)
-    if args.codec == "huffman" and args.config in ("c1", "c2", "c4") and not args.fp4_scales:
+    if args.codec == "huffman" and args.config in ("c1", "c2", "c4", "c2-low", "c4-low") and not args.fp4_scales:
         res = bench_single(args)
     else:
         import bench_big

@@ -35,6 +35,11 @@ def _traffic(cfg):
     return profiled_traffic(cfg)
 
 
+def decode_kernel_name(cs):
+    from bench import decode_kernel_name as name
+    return name(cs)
+
+
 def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
@@ -145,7 +150,7 @@ def run_c3(args):
         "encode_GBps_layer0": round(enc_b / (enc_t * 1e-3) / 1e9, 2),
         "ratio": round(comp_bytes / raw_total, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": _traffic("c3"), "kernel": "k_decode (one layer call)",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": _traffic("c3"), "kernel": decode_kernel_name(groups[0]) + " (one layer call)",
                      "alg_bytes_per_launch": int(layer_alg)},
         "context_d2d_copy_GBps": copy_context_GBps(int(layer_alg)),
         "setup_s": round(setup_s, 1),
@@ -563,7 +568,7 @@ def run_fp4_scales(args):
         "encode_GBps": round(raw / (enc_ms * 1e-3) / 1e9, 2),
         "ratio": round(c0.nbytes() / raw, 5), "bits_per_element": round(c0.total_bits / c0.n, 5),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_decode<E8M0>",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "k_decode_fast<E8M0> (low-entropy mode)",
                      "alg_bytes_per_launch": int(alg0)},
         "context_d2d_copy_GBps": copy_context_GBps(int(alg0)),
         "setup_s": round(setup_s, 1),

@@ -45,8 +45,6 @@ constexpr uint32_t kRoundElems = 3584;
 // Register path: up to kRounds rounds of three lookups per lane; the symbol counts
 // of the lookups are kept one byte each, four to a register.
 constexpr int kRounds = 7;
-constexpr int kEnt = 3 * kRounds;
-constexpr int kNsRegs = (kEnt + 3) / 4;
 // E8M0 block scales have mean codes near 1.5 bits: a 128-bit chunk holds up to ~130
 // codes and a segment up to 8192 elements, so that type gets 11 rounds and a stage
 // of a whole segment, and runs one workgroup per CU for the LDS this takes.
@@ -521,16 +519,17 @@ __device__ void store_generic(const DTab &tab, lds_cu32 *col, uint8_t *stage, ui
     }
 }
 
-// Segments whose exponents do not fit the stage: rounds of kRoundElems stage
-// positions, one code per step, exact writes.
-template <int DT, bool SO>
+// Segments whose exponents do not fit the stage: rounds of WIN stage positions
+// (a multiple of 16), one code per step, exact writes.
+template <int DT, bool SO, uint32_t WIN = kRoundElems>
 __device__ void write_rounds(const DTab &tab, lds_cu32 *col, uint8_t *stage, uint32_t start, uint32_t cnt,
                              uint32_t off, uint32_t t0, uint32_t total, void *out_block, const uint8_t *sm_block,
                              uint32_t sbase)
 {
+    static_assert(WIN % 16 == 0, "stage rounds keep 16-element pieces whole");
     const uint2 none[kWriteBatch] = {};
-    for (uint32_t r0 = 0; r0 < t0 + total; r0 += kRoundElems) {
-        const uint32_t r1 = r0 + kRoundElems;
+    for (uint32_t r0 = 0; r0 < t0 + total; r0 += WIN) {
+        const uint32_t r1 = r0 + WIN;
         uint32_t p = start;
         uint32_t t = t0 + off;
         for (uint32_t i = 0; i < cnt && t < r1; ++i, ++t) {
@@ -704,6 +703,105 @@ __device__ __forceinline__ void spare_release(uint32_t *lock)
 
 // ---- one segment per wavefront ------------------------------------------------
 
+// ---- the low-entropy fast decode's stage geometry ------------------------------
+//
+// Below about 2.3 bits per code a segment holds more elements than the 3616-byte
+// stage and a chunk more codes than seven rounds.  The low-entropy mode runs eleven
+// rounds (33 lookups of up to four codes: a 128-bit chunk holds at most 128 codes,
+// and every lookup but a stalled third one takes four codes or more than 5.5 bits on
+// average) and gives each wavefront a region of kLowRegion bytes.  The rows sit at its
+// start during the count pass; the replay then writes the stage at kLowGuard, in
+// windows of kLowWin positions when a segment holds more elements than that (below
+// about 1.09 bits per code).  The 16 guard bytes before the stage take the up to
+// three bytes an entry that straddles a window's start writes before it, and the 16
+// after it those an entry writes past its end.  The code-by-code passes (a lane
+// that needs more than eleven rounds) keep the rows and use the rest of the region.
+constexpr int kLowRounds = 11;
+constexpr uint32_t kLowRegion = 7584;
+constexpr uint32_t kLowGuard = 16;
+constexpr uint32_t kLowWin = kLowRegion - 2 * kLowGuard;
+constexpr uint32_t kLowGenOff = (kSegWords * 4 + 15) & ~15u;
+constexpr uint32_t kLowGenWin = (kLowRegion - kLowGenOff) & ~15u;
+static_assert(kLowWin % 16 == 0 && kLowGenWin % 16 == 0 && kLowGenWin >= 4096, "low-entropy stage windows");
+
+// Low-entropy mode: replay a lane's `cnt` symbols (register entries `ent`, counts in
+// the bytes of `nsb`), which go to stage positions t0 + off ..., into `st` one window
+// of kLowWin positions at a time, and write each window out.  In a window starting at
+// position w0 an entry at p stores its four bytes at st + p - w0 when any of them can
+// fall inside (p - w0 >= -3), then the lane's first three symbols are stored again
+// over the bytes the lane before it wrote past its end.  Windows start at 16-aligned
+// elements, so the cut pieces are only at the segment's ends; the first window's
+// sign/mantissa bytes come from prefetch_sm over the whole segment.
+template <int DT, bool SO, int kE, int kNs>
+__device__ __forceinline__ void replay_windows(const uint32_t (&ent)[kE], const uint32_t (&nsb)[kNs], uint32_t cnt,
+                                               uint32_t off, uint32_t t0, uint32_t total, uint8_t *st,
+                                               void *out_block, const uint8_t *sm_block, uint32_t e0, uint32_t sbase,
+                                               const uint2 (&smv)[kWriteBatch], uint32_t smcut)
+{
+    const uint2 none[kWriteBatch] = {};
+    // first three symbols: the first entry's, topped up from the entries after it (a
+    // stalled lookup leaves an empty entry; three rounds hold at least three symbols)
+    uint32_t f3 = ent[0];
+    uint32_t nf = nsb[0] & 0xFFu;
+    const uint32_t need = cnt < 3u ? cnt : 3u;
+#pragma unroll
+    for (int k = 1; k < 7; ++k) {
+        if (__builtin_amdgcn_ballot_w64(nf < need) == 0) break;
+        if (nf < need) {
+            f3 = (f3 & ((1u << (8 * nf)) - 1u)) | (ent[k] << (8 * nf));
+            nf += (nsb[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+        }
+    }
+    const uint32_t tend = t0 + total;
+    for (uint32_t w0 = 0;; w0 += kLowWin) {
+        const int32_t base = (int32_t)(t0 + off) - (int32_t)w0;   // the lane's first position in the window
+        const int32_t pend = base + (int32_t)cnt;
+        const int32_t plim = pend < (int32_t)kLowWin ? pend : (int32_t)kLowWin;
+        int32_t pp = base;
+#pragma unroll
+        for (int k = 0; k < kE; ++k) {
+            if (__builtin_amdgcn_ballot_w64(pp < plim) == 0) break;
+            if (pp < plim) {
+                if (pp >= -3) {
+                    uint8_t *a = st + pp;
+                    // two pairs of non-adjacent bytes, kept apart: four adjacent byte
+                    // stores would be merged into one unaligned dword store
+                    a[0] = (uint8_t)ent[k];
+                    a[2] = (uint8_t)(ent[k] >> 16);
+                    asm volatile("" ::: "memory");
+                    a[1] = (uint8_t)(ent[k] >> 8);
+                    a[3] = (uint8_t)(ent[k] >> 24);
+                }
+                pp += (int32_t)((nsb[k >> 2] >> (8 * (k & 3))) & 0xFFu);
+            }
+        }
+        wave_sync();
+        if (base > -3 && base < (int32_t)kLowWin) {
+            uint8_t *const a0 = st + base;
+            if (cnt >= 3) {
+                a0[0] = (uint8_t)f3;
+                a0[1] = (uint8_t)(f3 >> 8);
+                a0[2] = (uint8_t)(f3 >> 16);
+            } else if (cnt == 2) {
+                a0[0] = (uint8_t)f3;
+                a0[1] = (uint8_t)(f3 >> 8);
+            } else if (cnt == 1) {
+                a0[0] = (uint8_t)f3;
+            }
+        }
+        wave_sync();
+        const uint32_t wend = w0 + kLowWin < tend ? w0 + kLowWin : tend;
+        if (w0 == 0) {
+            settle_sm<DT>(smv, smcut);
+            write_range<DT, true, SO>(out_block, sm_block, e0, sbase + wend, st, sbase, false, 0, smv, smcut);
+        } else {
+            write_range<DT, false, SO>(out_block, sm_block, sbase + w0, sbase + wend, st, sbase + w0, false, 0, none, 0u);
+        }
+        if (wend >= tend) break;
+        wave_sync();
+    }
+}
+
 // Byte selector that puts byte 2 of the first v_perm operand into byte j and keeps
 // the second operand's other bytes.
 __host__ __device__ constexpr uint32_t ns_sel(int j)
@@ -739,7 +837,8 @@ __host__ __device__ constexpr uint32_t ns_sel(int j)
 // segment that needs the code-by-code passes borrows the workgroup's spare stage under
 // `lock`.  Otherwise the rows have a region of their own and the next segment's words
 // are put in right after the count pass.
-template <int DT, bool FAST = false, bool SO = false>
+// LOW (with FAST): the low-entropy mode above; no spare stage.
+template <int DT, bool FAST = false, bool SO = false, bool LOW = false>
 __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *sw,
                                                     uint32_t s, const SegMeta &m, SegIn &in, bool has_next, uint32_t sn,
                                                     const SegMeta &mn, uint32_t *err, uint8_t *spare = nullptr,
@@ -810,7 +909,9 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     // ---- count pass, register path
     // entries of rounds that do not run are never read: the replay stops once no lane
     // has symbols left
-    constexpr int kR = dec_rounds<DT>(), kE = 3 * kR, kNs = (kE + 3) / 4;
+    static_assert(!LOW || FAST, "the low-entropy mode is a fast-decode mode");
+    static_assert(!FAST || LOW || DT != ZX_E8M0, "E8M0 takes the fast decode in its low-entropy mode only");
+    constexpr int kR = LOW ? kLowRounds : dec_rounds<DT>(), kE = 3 * kR, kNs = (kE + 3) / 4;
     uint32_t ent[kE];
     uint32_t nsb[kNs];
 #pragma unroll
@@ -887,6 +988,19 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     if (any_lane(lane_bad) || e0 + total != e_end) { report(err, ZX_E_CORRUPT); return false; }
 
     const uint32_t t0 = e0 - sbase;   // stage position of the segment's first element
+    if constexpr (LOW) {
+        if (more) {
+            write_rounds<DT, SO, kLowGenWin>(tab, col, stage + kLowGenOff, start, cnt, off, t0, total, out_block,
+                                             sm_block, sbase);
+            return false;
+        }
+        uint2 smv[kWriteBatch];
+        uint32_t smcut;
+        prefetch_sm<DT>(sm_block, e0, e_end, reinterpret_cast<const uint8_t *>(T.stream), smv, smcut);
+        replay_windows<DT, SO, kE, kNs>(ent, nsb, cnt, off, t0, total, stage + kLowGuard, out_block, sm_block, e0,
+                                        sbase, smv, smcut);
+        return true;
+    }
     if (t0 + total + 3 > dec_stage_bytes<DT>()) {
         if constexpr (FAST) {
             if (!spare_acquire(lock)) { report(err, ZX_E_CORRUPT); return false; }
@@ -1132,25 +1246,31 @@ __device__ __forceinline__ void set_priority_by_remaining(uint32_t remaining, ui
 // wavefront instead of two for a third of them, and every wavefront has more company
 // to hide its memory and LDS waits behind.  Segments of mean code length below about
 // 2.3 bits overflow the stage and take the spare one wavefront at a time, so such
-// containers go to k_decode instead (the host picks).
+// containers take the low-entropy mode (LOW): two workgroups per CU, eleven count
+// rounds and a larger region per wavefront (see kLowRegion), no spare.
 constexpr int kFastWgPerCu = 3;
+constexpr int kLowWgPerCu = 2;
 constexpr uint32_t kFastMeta = 16;   // descriptors per wavefront refresh
 static_assert(kSegWords * 4 <= kStageBytes, "the word rows fit the stage region");
 
+template <bool LOW>
 struct FastShared {
+    static constexpr uint32_t kRegion = LOW ? kLowRegion : kStageBytes;
     DTab tab;
-    uint8_t region[kDecWaves][kStageBytes];   // rows during the count pass, then the stage
+    uint8_t region[kDecWaves][kRegion];       // rows during the count pass, then the stage
     SegMeta meta[kDecWaves][kFastMeta];
-    uint8_t spare[kStageBytes];               // the code-by-code passes' stage
+    uint8_t spare[LOW ? 16u : kStageBytes];   // the code-by-code passes' stage (not LOW)
     uint32_t lock;
 };
-static_assert(sizeof(FastShared) <= 160u * 1024u / kFastWgPerCu, "fast decode workgroup LDS budget");
+static_assert(sizeof(FastShared<false>) <= 160u * 1024u / kFastWgPerCu, "fast decode workgroup LDS budget");
+static_assert(sizeof(FastShared<true>) <= 160u * 1024u / kLowWgPerCu, "low-entropy decode workgroup LDS budget");
 
-template <int DT, bool SO>
-__global__ __launch_bounds__(kDecThreads, kFastWgPerCu * kDecWaves / 4) void k_decode_fast(const DecBatch batch, uint32_t *err)
+template <int DT, bool SO, bool LOW>
+__global__ __launch_bounds__(kDecThreads, (LOW ? kLowWgPerCu : kFastWgPerCu) * kDecWaves / 4) void k_decode_fast(
+    const DecBatch batch, uint32_t *err)
 {
-    static_assert(DT == ZX_BF16 || DT == ZX_FP8_E4M3FN, "fast decode: BF16 and FP8");
-    __shared__ FastShared sh;
+    static_assert(DT == ZX_BF16 || DT == ZX_FP8_E4M3FN || (DT == ZX_E8M0 && LOW), "fast decode: BF16, FP8; E8M0 in LOW");
+    __shared__ FastShared<LOW> sh;
     const uint32_t g = blockIdx.x;
     uint32_t t = 0;
     while (t + 1 < batch.count && g >= batch.t[t + 1].wg_begin) ++t;
@@ -1199,7 +1319,8 @@ __global__ __launch_bounds__(kDecThreads, kFastWgPerCu * kDecWaves / 4) void k_d
         const bool has_next = k + 1 < nk && i + 1 < kFastMeta;
         const SegMeta mu = meta_get(metas, i);
         const SegMeta mn = meta_get(metas, has_next ? i + 1 : i);
-        decode_segment_body<DT, true, SO>(T, sh.tab, reg, sw, s, mu, in, has_next, s + kDecWaves, mn, err, sh.spare, &sh.lock);
+        decode_segment_body<DT, true, SO, LOW>(T, sh.tab, reg, sw, s, mu, in, has_next, s + kDecWaves, mn, err, sh.spare,
+                                               &sh.lock);
         if (i == kFastMeta - 1 && k + 1 < nk) {
             // next group of 16 descriptors, and the words of its first segment (put
             // in at that segment's start)
@@ -1272,16 +1393,22 @@ extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *cons
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    // the fast decode takes BF16 / FP8 batches of per-tensor codebooks whose mean code
-    // length is at least 2.3 bits (a segment then averages under 3562 elements, inside
-    // its stage); anything else goes to k_decode
-    bool fast = dt == ZX_BF16 || dt == ZX_FP8_E4M3FN;
+    // the fast decode takes batches of per-tensor codebooks; in its low-entropy mode
+    // when any container's mean code length is below 2.3 bits (its segments then
+    // average over 3562 elements, beyond the ordinary stage), and always for E8M0
+    // scales (mean codes near 1.5 bits).  Per-block codebooks go to k_decode.
+    bool fast = true;
+    bool low = dt == ZX_E8M0;
     for (uint32_t i = 0; i < count && fast; ++i) {
         if (cs[i].n == 0) continue;
-        if (cs[i].per_block || 10 * cs[i].total_bits < 23 * cs[i].n) fast = false;
+        if (cs[i].per_block) fast = false;
+        if (10 * cs[i].total_bits < 23 * cs[i].n) low = true;
     }
+    low = low && fast;
     // resident 512-thread workgroups
-    uint64_t slots = (uint64_t)cus * (fast ? kFastWgPerCu : dt == ZX_E8M0 ? dec_wg_per_cu<ZX_E8M0>() : kDecWgPerCu);
+    uint64_t slots = (uint64_t)cus * (low    ? kLowWgPerCu
+                                      : fast ? kFastWgPerCu
+                                      : dt == ZX_E8M0 ? dec_wg_per_cu<ZX_E8M0>() : kDecWgPerCu);
     if (max_workgroups != 0 && max_workgroups < slots) slots = max_workgroups;
     // resident workgroup slots for each per-tensor-codebook container: its share of the
     // slots by segment count, rounded down, then the slots left over go to the largest
@@ -1362,15 +1489,19 @@ extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *cons
     uint64_t out_bytes = 0;
     for (uint32_t i = 0; i < count; ++i) out_bytes += cs[i].n * (cs[i].dtype == ZX_BF16 ? 2u : 1u);
     const bool stream_out = out_bytes <= (128ull << 20);
-    if (fast && dt == ZX_BF16 && stream_out)
-        hipLaunchKernelGGL((k_decode_fast<ZX_BF16, true>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
-    else if (fast && dt == ZX_BF16)
-        hipLaunchKernelGGL((k_decode_fast<ZX_BF16, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
-    else if (fast && stream_out)
-        hipLaunchKernelGGL((k_decode_fast<ZX_FP8_E4M3FN, true>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
-    else if (fast)
-        hipLaunchKernelGGL((k_decode_fast<ZX_FP8_E4M3FN, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
-    else if (dt == ZX_BF16)
+    if (fast && dt == ZX_E8M0) {
+        hipLaunchKernelGGL((stream_out ? k_decode_fast<ZX_E8M0, true, true> : k_decode_fast<ZX_E8M0, false, true>),
+                           dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
+    } else if (fast) {
+        const bool bf = dt == ZX_BF16;
+        void (*kern)(const DecBatch, uint32_t *) =
+            low ? (bf ? (stream_out ? k_decode_fast<ZX_BF16, true, true> : k_decode_fast<ZX_BF16, false, true>)
+                      : (stream_out ? k_decode_fast<ZX_FP8_E4M3FN, true, true> : k_decode_fast<ZX_FP8_E4M3FN, false, true>))
+                : (bf ? (stream_out ? k_decode_fast<ZX_BF16, true, false> : k_decode_fast<ZX_BF16, false, false>)
+                      : (stream_out ? k_decode_fast<ZX_FP8_E4M3FN, true, false>
+                                    : k_decode_fast<ZX_FP8_E4M3FN, false, false>));
+        hipLaunchKernelGGL(kern, dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
+    } else if (dt == ZX_BF16)
         hipLaunchKernelGGL((k_decode<ZX_BF16, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
     else if (dt == ZX_E8M0)
         hipLaunchKernelGGL((k_decode<ZX_E8M0, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);

@@ -226,6 +226,22 @@ def test_low_entropy(dtype, per_block, p_top):
 
 
 @pytest.mark.parametrize("dtype", [0, 1])
+@pytest.mark.parametrize("p_top", [0.97, 0.99])
+def test_low_entropy_segments_beyond_one_stage_window(dtype, p_top):
+    """Mean code length about 1.02-1.07 bits: segments of 7700-8100 elements, more than
+    the low-entropy decode's stage window (7552 positions), so their exponents are
+    replayed and written in two windows; chunks of 128 one-bit codes fill every count
+    round."""
+    say("low entropy, two stage windows", dtype, p_top)
+    n = 6 * 65536 + 4_321
+    x, e = low_entropy(dtype, n, p_top, seed=3)
+    o = parity(dtype, x, per_block=False)
+    assert 1.0 < o.total_bits / n < 1.1
+    mx_chunk, mx_seg = regime(o, e)
+    assert mx_chunk == 128 and mx_seg > 7552, (mx_chunk, mx_seg)
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
 def test_dense_runs_in_ordinary_data(dtype):
     """Runs of the one exponent that has a 1-bit code inside otherwise spread data:
     chunks inside a run hold 128 codes (beyond the register rounds) while whole

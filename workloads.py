@@ -16,6 +16,12 @@ for each workload:
       (kv, layer, head) slab, 4 of the 128 channels (drawn without replacement)
       are multiplied by 20; cast RNE
 
+  low entropy  BF16 [4096, 4096] or FP8 E4M3FN [8192, 8192] whose exponent is one
+      value (120 BF16, 7 FP8) with probability 0.85 and otherwise that value minus
+      a geometric(0.45) draw (clipped to 40 BF16, 7 FP8), with uniform sign and
+      mantissa bits: the skew the pages report for K/V caches and scale factors,
+      a mean code length of about 1.3 bits
+
   fp4 scales  E8M0 block scale factors of MX-FP4 weights: per 32 consecutive
       input features of a N(0, 1/sqrt(fan_in)) weight, the byte
       floor(log2(amax)) - 2 + 127 (2 = the largest exponent of FP4 E2M1),
@@ -106,6 +112,23 @@ def c4(device="cpu"):
     scale = (x.abs().max() / 448.0).to(torch.float32)
     q = torch.clamp(x / scale, -448.0, 448.0).to(torch.float8_e4m3fn)
     return q.view(torch.uint8), float(scale.item())
+
+
+def low_entropy(dtype: int, p_top: float = 0.85, seed: int = 0) -> torch.Tensor:
+    """Low-entropy exponents (see the module docstring): BF16 [4096, 4096] as int16
+    bits, or FP8 [8192, 8192] as uint8 bits."""
+    g = _rng(6 + dtype, seed)
+    n = 4096 * 4096 if dtype == BF16 else 8192 * 8192
+    top = 120 if dtype == BF16 else 7
+    tail = np.clip(g.geometric(0.45, n), 1, 40 if dtype == BF16 else 7)
+    e = np.where(g.random(n) < p_top, top, top - tail).astype(np.uint32)
+    if dtype == BF16:
+        r = g.integers(0, 1 << 16, n, dtype=np.uint32)   # sign bit 15, mantissa bits 0..6
+        bits = ((r & 0x807F) | (e << 7)).astype(np.uint16)
+        return torch.from_numpy(bits.view(np.int16)).reshape(4096, 4096)
+    r = g.integers(0, 1 << 8, n, dtype=np.uint32)        # sign bit 7, mantissa bits 0..2
+    bits = ((r & 0x87) | (e << 3)).astype(np.uint8)
+    return torch.from_numpy(bits).reshape(8192, 8192)
 
 
 def c5_outlier_channels() -> np.ndarray:
