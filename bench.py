@@ -101,7 +101,7 @@ def decode_kernel_name(cs) -> str:
     under 2.3 bits per code, or of E8M0 scales, takes the fast decode's low-entropy mode)."""
     cs = [c for c in cs if c.n]
     if any(c.per_block for c in cs):
-        return "k_decode (per-block codebooks)"
+        return "k_decode_fast_blocks (per-block codebooks)"
     if any(c.dtype == 2 or 10 * c.total_bits < 23 * c.n for c in cs):
         return "k_decode_fast (low-entropy mode)"
     return "k_decode_fast"

@@ -1265,6 +1265,80 @@ struct FastShared {
 static_assert(sizeof(FastShared<false>) <= 160u * 1024u / kFastWgPerCu, "fast decode workgroup LDS budget");
 static_assert(sizeof(FastShared<true>) <= 160u * 1024u / kLowWgPerCu, "low-entropy decode workgroup LDS budget");
 
+// The segment loop of a fast-decode wavefront: its segments s0 + kDecWaves k, k < nk,
+// whose first descriptors (up to kFastMeta) are already in the wavefront's LDS copy
+// and whose first words were requested into `in`.  On return `in` holds the last
+// request (a dummy, or the words of a segment this wavefront does not decode).
+template <int DT, bool SO, bool LOW>
+__device__ __forceinline__ void fast_segment_loop(const DecTensor &T, FastShared<LOW> &sh, uint32_t wave, uint32_t s0,
+                                                  uint32_t nk, SegIn &in, uint32_t *err)
+{
+    uint8_t *reg = sh.region[wave];
+    uint32_t *sw = reinterpret_cast<uint32_t *>(reg);
+    SegMeta *metas = sh.meta[wave];
+    for (uint32_t k = 0; k < nk; ++k) {
+        set_priority_by_remaining(nk - k, nk);
+        const uint32_t i = k & (kFastMeta - 1);
+        const uint32_t s = s0 + kDecWaves * k;
+        const bool has_next = k + 1 < nk && i + 1 < kFastMeta;
+        const SegMeta mu = meta_get(metas, i);
+        const SegMeta mn = meta_get(metas, has_next ? i + 1 : i);
+        decode_segment_body<DT, true, SO, LOW>(T, sh.tab, reg, sw, s, mu, in, has_next, s + kDecWaves, mn, err, sh.spare,
+                                               &sh.lock);
+        if (i == kFastMeta - 1 && k + 1 < nk) {
+            // next group of 16 descriptors, and the words of its first segment (put
+            // in at that segment's start)
+            const uint32_t lane = lane_now();
+            SegMeta m2;
+            load_meta(T, s + kDecWaves + kDecWaves * lane, lane < kFastMeta && k + 1 + lane < nk, m2);
+            issue_seg(T, s + kDecWaves, meta_at(m2, 0), lane, in, true);
+            wave_sync();
+            if (lane < kFastMeta) metas[lane] = m2;
+            wave_sync();
+        }
+    }
+}
+
+// Per-block codebooks: one workgroup per block, all eight wavefronts on its segments,
+// the block's table built in LDS first.  The build's scratch (the canonical
+// description and the single-code table) lives in the wavefronts' regions, which no
+// wavefront uses before the table is built.  The block's descriptors and first words
+// are requested before the build, so that they arrive while it runs; the other
+// workgroups resident on the CU (three, or two in the low-entropy mode) keep the
+// memory busy meanwhile.
+constexpr uint32_t kCanonBytes = (sizeof(Canon) + 15u) & ~15u;
+
+template <int DT, bool SO, bool LOW>
+__device__ __forceinline__ void fast_block(const DecTensor &T, uint32_t b, FastShared<LOW> &sh, uint32_t *err)
+{
+    constexpr uint32_t A = alphabet_of(DT);
+    static_assert(kCanonBytes + kLutSize * 2 <= sizeof(sh.region), "table scratch fits the regions");
+    const uint32_t tid = threadIdx.x;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint32_t lane = lane_now();
+    const uint32_t len = tid < A ? T.lengths[(uint64_t)b * A + tid] : 0u;
+    const uint32_t s_begin = T.block_seg[b];
+    uint32_t s_end = T.block_seg[b + 1];
+    if (s_end > T.nsegs || s_begin > s_end) {
+        s_end = s_begin;
+        if (tid == 0) report(err, ZX_E_CORRUPT);
+    }
+    const uint32_t s0 = s_begin + wave;
+    const uint32_t nk = __builtin_amdgcn_readfirstlane(s0 < s_end ? (s_end - s0 + kDecWaves - 1) / kDecWaves : 0);
+    SegMeta mine;
+    load_meta(T, s0 + kDecWaves * lane, lane < kFastMeta && lane < nk, mine);
+    SegIn in;
+    issue_seg(T, s0, meta_at(mine, 0), lane, in, nk != 0);
+    Canon &c = *reinterpret_cast<Canon *>(&sh.region[0][0]);
+    canon_build_from(len, A, c);
+    dtab_fill(c, A, sh.tab, reinterpret_cast<uint16_t *>(&sh.region[0][0] + kCanonBytes));
+    if (lane < kFastMeta) sh.meta[wave][lane] = mine;
+    if (tid == 0) sh.lock = 0;
+    __syncthreads();
+    fast_segment_loop<DT, SO, LOW>(T, sh, wave, s0, nk, in, err);
+    asm volatile("" ::"v"(in.rv.x), "v"(in.rtail), "v"(in.gap), "v"(in.gapn));
+}
+
 template <int DT, bool SO, bool LOW>
 __global__ __launch_bounds__(kDecThreads, (LOW ? kLowWgPerCu : kFastWgPerCu) * kDecWaves / 4) void k_decode_fast(
     const DecBatch batch, uint32_t *err)
@@ -1306,35 +1380,24 @@ __global__ __launch_bounds__(kDecThreads, (LOW ? kLowWgPerCu : kFastWgPerCu) * k
         const uint32_t i = tid + k * kDecThreads;
         if (i < kTabPieces) dst[i] = pc[k];
     }
-    SegMeta *metas = sh.meta[wave];
-    if (lane < kFastMeta) metas[lane] = mine;
+    if (lane < kFastMeta) sh.meta[wave][lane] = mine;
     if (tid == 0) sh.lock = 0;
     __syncthreads();
-    uint8_t *reg = sh.region[wave];
-    uint32_t *sw = reinterpret_cast<uint32_t *>(reg);
-    for (uint32_t k = 0; k < nk; ++k) {
-        set_priority_by_remaining(nk - k, nk);
-        const uint32_t i = k & (kFastMeta - 1);
-        const uint32_t s = s0 + kDecWaves * k;
-        const bool has_next = k + 1 < nk && i + 1 < kFastMeta;
-        const SegMeta mu = meta_get(metas, i);
-        const SegMeta mn = meta_get(metas, has_next ? i + 1 : i);
-        decode_segment_body<DT, true, SO, LOW>(T, sh.tab, reg, sw, s, mu, in, has_next, s + kDecWaves, mn, err, sh.spare,
-                                               &sh.lock);
-        if (i == kFastMeta - 1 && k + 1 < nk) {
-            // next group of 16 descriptors, and the words of its first segment (put
-            // in at that segment's start)
-            SegMeta m2;
-            load_meta(T, s + kDecWaves + kDecWaves * lane, lane < kFastMeta && k + 1 + lane < nk, m2);
-            issue_seg(T, s + kDecWaves, meta_at(m2, 0), lane, in, true);
-            wave_sync();
-            if (lane < kFastMeta) metas[lane] = m2;
-            wave_sync();
-        }
-    }
-    // the last request into `in` (a dummy, or the words of a segment this wavefront
-    // does not decode) is used here, so that no load is left unused in flight
+    fast_segment_loop<DT, SO, LOW>(T, sh, wave, s0, nk, in, err);
+    // the last request into `in` is used here, so that no load is left unused in flight
     asm volatile("" ::"v"(in.rv.x), "v"(in.rtail), "v"(in.gap), "v"(in.gapn));
+}
+
+// The batch of per-block-codebook containers, one workgroup per block (see fast_block).
+template <int DT, bool SO, bool LOW>
+__global__ __launch_bounds__(kDecThreads, (LOW ? kLowWgPerCu : kFastWgPerCu) * kDecWaves / 4) void k_decode_fast_blocks(
+    const DecBatch batch, uint32_t *err)
+{
+    __shared__ FastShared<LOW> sh;
+    const uint32_t g = blockIdx.x;
+    uint32_t t = 0;
+    while (t + 1 < batch.count && g >= batch.t[t + 1].wg_begin) ++t;
+    fast_block<DT, SO, LOW>(batch.t[t], g - batch.t[t].wg_begin, sh, err);
 }
 
 __global__ __launch_bounds__(1024) void k_build_dtab(const uint8_t *__restrict__ lengths, uint32_t A, DTab *__restrict__ out)
@@ -1379,52 +1442,44 @@ static zx_status check_container(const zx_container *c, const void *out)
     return ZX_OK;
 }
 
-extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *const *outs, uint32_t count,
-                                              uint32_t max_workgroups, uint32_t *err, hipStream_t stream)
+// One fast-decode launch over containers idx[0..m) of a batch, all of one codebook
+// scope (per_block) and one dtype.
+static zx_status launch_fast(const zx_container *all, void *const *all_outs, const uint32_t *idx, uint32_t m,
+                             bool per_block, int dt, int cus, uint32_t max_workgroups, uint32_t *err, hipStream_t stream)
 {
-    if (count == 0) return ZX_OK;
-    if (!cs || !outs || count > (uint32_t)kMaxBatch) return ZX_E_INVAL;
-    const int dt = cs[0].dtype;
-    for (uint32_t i = 0; i < count; ++i) {
-        const zx_status st = check_container(&cs[i], outs[i]);
-        if (st != ZX_OK) return st;
-        if (cs[i].dtype != dt) return ZX_E_INVAL;
+    zx_container cs[kMaxBatch];
+    void *outs[kMaxBatch];
+    const uint32_t count = m;
+    for (uint32_t j = 0; j < m; ++j) {
+        cs[j] = all[idx[j]];
+        outs[j] = all_outs[idx[j]];
     }
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    // the fast decode takes batches of per-tensor codebooks; in its low-entropy mode
-    // when any container's mean code length is below 2.3 bits (its segments then
-    // average over 3562 elements, beyond the ordinary stage), and always for E8M0
-    // scales (mean codes near 1.5 bits).  Per-block codebooks go to k_decode.
-    bool fast = true;
+    // the fast decode takes every batch; in its low-entropy mode when any container's
+    // mean code length is below 2.3 bits (its segments then average over 3562
+    // elements, beyond the ordinary stage), and always for E8M0 scales (mean codes near
+    // 1.5 bits).  Per-block codebooks are decoded block by block, each block's table
+    // built in LDS.
     bool low = dt == ZX_E8M0;
-    for (uint32_t i = 0; i < count && fast; ++i) {
-        if (cs[i].n == 0) continue;
-        if (cs[i].per_block) fast = false;
-        if (10 * cs[i].total_bits < 23 * cs[i].n) low = true;
-    }
-    low = low && fast;
+    for (uint32_t i = 0; i < count; ++i)
+        if (cs[i].n && 10 * cs[i].total_bits < 23 * cs[i].n) low = true;
     // resident 512-thread workgroups
-    uint64_t slots = (uint64_t)cus * (low    ? kLowWgPerCu
-                                      : fast ? kFastWgPerCu
-                                      : dt == ZX_E8M0 ? dec_wg_per_cu<ZX_E8M0>() : kDecWgPerCu);
+    uint64_t slots = (uint64_t)cus * (low ? kLowWgPerCu : kFastWgPerCu);
     if (max_workgroups != 0 && max_workgroups < slots) slots = max_workgroups;
-    // resident workgroup slots for each per-tensor-codebook container: its share of the
-    // slots by segment count, rounded down, then the slots left over go to the largest
-    // remainders.  The total never exceeds the resident slots, so every workgroup starts
-    // at once: one more workgroup than fits would run its whole share after the others.
+    // resident workgroup slots for each container: its share of the slots by segment
+    // count, rounded down, then the slots left over go to the largest remainders.  The
+    // total never exceeds the resident slots, so every workgroup starts at once: one
+    // more workgroup than fits would run its whole share after the others.
     uint64_t seg_total = 0;
     uint32_t nshare = 0;
     for (uint32_t i = 0; i < count; ++i)
-        if (!cs[i].per_block && cs[i].n) { seg_total += cs[i].nsegs; ++nshare; }
+        if (cs[i].n) { seg_total += cs[i].nsegs; ++nshare; }
     uint64_t share[kMaxBatch] = {};
     if (nshare) {
         if (slots < nshare) slots = nshare;
         uint64_t given = 0;
         uint64_t rem[kMaxBatch] = {};
         for (uint32_t i = 0; i < count; ++i) {
-            if (cs[i].per_block || cs[i].n == 0) continue;
+            if (cs[i].n == 0) continue;
             const uint64_t num = slots * cs[i].nsegs;
             share[i] = num / seg_total;
             rem[i] = num % seg_total;
@@ -1434,7 +1489,7 @@ extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *cons
         while (given < slots) {
             uint32_t best = count;
             for (uint32_t i = 0; i < count; ++i)
-                if (!cs[i].per_block && cs[i].n && (best == count || rem[i] > rem[best])) best = i;
+                if (cs[i].n && (best == count || rem[i] > rem[best])) best = i;
             if (best == count || rem[best] == 0) break;
             share[best] += 1;
             rem[best] = 0;
@@ -1467,7 +1522,7 @@ extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *cons
         T.per_block = c.per_block ? 1u : 0u;
         T.wg_begin = wg;
         if (c.per_block) {
-            T.wg_count = T.nblocks;
+            T.wg_count = T.nblocks;   // one workgroup per block
             T.segs_per_wg = 0;
         } else {
             // at least one wavefront's worth of segments per workgroup
@@ -1489,25 +1544,62 @@ extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *cons
     uint64_t out_bytes = 0;
     for (uint32_t i = 0; i < count; ++i) out_bytes += cs[i].n * (cs[i].dtype == ZX_BF16 ? 2u : 1u);
     const bool stream_out = out_bytes <= (128ull << 20);
-    if (fast && dt == ZX_E8M0) {
-        hipLaunchKernelGGL((stream_out ? k_decode_fast<ZX_E8M0, true, true> : k_decode_fast<ZX_E8M0, false, true>),
-                           dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
-    } else if (fast) {
-        const bool bf = dt == ZX_BF16;
-        void (*kern)(const DecBatch, uint32_t *) =
-            low ? (bf ? (stream_out ? k_decode_fast<ZX_BF16, true, true> : k_decode_fast<ZX_BF16, false, true>)
-                      : (stream_out ? k_decode_fast<ZX_FP8_E4M3FN, true, true> : k_decode_fast<ZX_FP8_E4M3FN, false, true>))
-                : (bf ? (stream_out ? k_decode_fast<ZX_BF16, true, false> : k_decode_fast<ZX_BF16, false, false>)
-                      : (stream_out ? k_decode_fast<ZX_FP8_E4M3FN, true, false>
-                                    : k_decode_fast<ZX_FP8_E4M3FN, false, false>));
-        hipLaunchKernelGGL(kern, dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
-    } else if (dt == ZX_BF16)
-        hipLaunchKernelGGL((k_decode<ZX_BF16, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
-    else if (dt == ZX_E8M0)
-        hipLaunchKernelGGL((k_decode<ZX_E8M0, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
-    else
-        hipLaunchKernelGGL((k_decode<ZX_FP8_E4M3FN, false>), dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
+    void (*kern)(const DecBatch, uint32_t *);
+    if (per_block) {
+        if (dt == ZX_E8M0)
+            kern = stream_out ? k_decode_fast_blocks<ZX_E8M0, true, true> : k_decode_fast_blocks<ZX_E8M0, false, true>;
+        else if (dt == ZX_BF16)
+            kern = low ? (stream_out ? k_decode_fast_blocks<ZX_BF16, true, true> : k_decode_fast_blocks<ZX_BF16, false, true>)
+                       : (stream_out ? k_decode_fast_blocks<ZX_BF16, true, false>
+                                     : k_decode_fast_blocks<ZX_BF16, false, false>);
+        else
+            kern = low ? (stream_out ? k_decode_fast_blocks<ZX_FP8_E4M3FN, true, true>
+                                     : k_decode_fast_blocks<ZX_FP8_E4M3FN, false, true>)
+                       : (stream_out ? k_decode_fast_blocks<ZX_FP8_E4M3FN, true, false>
+                                     : k_decode_fast_blocks<ZX_FP8_E4M3FN, false, false>);
+    } else {
+        if (dt == ZX_E8M0)
+            kern = stream_out ? k_decode_fast<ZX_E8M0, true, true> : k_decode_fast<ZX_E8M0, false, true>;
+        else if (dt == ZX_BF16)
+            kern = low ? (stream_out ? k_decode_fast<ZX_BF16, true, true> : k_decode_fast<ZX_BF16, false, true>)
+                       : (stream_out ? k_decode_fast<ZX_BF16, true, false> : k_decode_fast<ZX_BF16, false, false>);
+        else
+            kern = low ? (stream_out ? k_decode_fast<ZX_FP8_E4M3FN, true, true> : k_decode_fast<ZX_FP8_E4M3FN, false, true>)
+                       : (stream_out ? k_decode_fast<ZX_FP8_E4M3FN, true, false>
+                                     : k_decode_fast<ZX_FP8_E4M3FN, false, false>);
+    }
+    hipLaunchKernelGGL(kern, dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}
+
+extern "C" zx_status zx_decode_block_batch_wg(const zx_container *cs, void *const *outs, uint32_t count,
+                                              uint32_t max_workgroups, uint32_t *err, hipStream_t stream)
+{
+    if (count == 0) return ZX_OK;
+    if (!cs || !outs || count > (uint32_t)kMaxBatch) return ZX_E_INVAL;
+    const int dt = cs[0].dtype;
+    for (uint32_t i = 0; i < count; ++i) {
+        const zx_status st = check_container(&cs[i], outs[i]);
+        if (st != ZX_OK) return st;
+        if (cs[i].dtype != dt) return ZX_E_INVAL;
+    }
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    // per-tensor and per-block codebooks take separate kernels: a batch that holds both
+    // is two launches on the stream
+    uint32_t pt[kMaxBatch], pb[kMaxBatch];
+    uint32_t npt = 0, npb = 0;
+    for (uint32_t i = 0; i < count; ++i) {
+        if (cs[i].per_block) pb[npb++] = i;
+        else pt[npt++] = i;
+    }
+    if (npt) {
+        const zx_status st = launch_fast(cs, outs, pt, npt, false, dt, cus, max_workgroups, err, stream);
+        if (st != ZX_OK) return st;
+    }
+    if (npb) return launch_fast(cs, outs, pb, npb, true, dt, cus, max_workgroups, err, stream);
+    return ZX_OK;
 }
 
 extern "C" zx_status zx_kv_decode_slots(const zx_kv_pool *pool, const uint32_t *slot_ids, uint32_t count, void *out,
