@@ -252,10 +252,10 @@ def median_launch_ms(launch, n_per_rep: int, reps: int = 25, warmup: int = 5):
 
 
 def encode_chain(cs, xs):
-    """A launcher for the device-side encode chain of copy k: histogram, codebook, block
-    sizes, decode table and encode, through the C ABI into preallocated buffers with
-    the sizes already known (the same work compress() does, without its one host read
-    of the totals and without allocation)."""
+    """A launcher for the device-side encode chain of copy k: zx_encode_plan (histogram,
+    codebook, block sizes, totals, decode table) and zx_encode, through the C ABI into
+    preallocated buffers with the sizes already known (the same work compress() does,
+    without its one host wait for the totals and without allocation)."""
     import ctypes
     import torch
     import lossless_float_compression_amd as zx
@@ -282,10 +282,8 @@ def encode_chain(cs, xs):
     def launch(k):
         c, p, _ = bufs[k % len(bufs)]
         st = 0
-        st |= L.zx_histogram(c.dtype, p["flat"], c.n, p["th"], p["bh"], sptr)
-        st |= L.zx_build_codebook(c.dtype, p["th"], 1, 32, p["ln"], p["dg"], sptr)
-        st |= L.zx_encode_size(c.dtype, p["flat"], c.n, 0, p["ln"], p["bh"], p["bo"], p["bs"], p["tot"], sptr)
-        st |= L.zx_build_decode_table(c.dtype, p["ln"], p["dt"], sptr)
+        st |= L.zx_encode_plan(c.dtype, p["flat"], c.n, 32, p["bh"], p["th"], p["ln"], p["dg"], p["bo"], p["bs"],
+                               p["tot"], None, 0, p["dt"], p["err"], sptr)
         st |= L.zx_encode(c.dtype, p["flat"], c.n, 0, p["ln"], p["dg"], p["bo"], p["bs"], c.total_bits, c.nsegs,
                           p["sm"], p["st"], p["sd"], p["gp"], p["err"], sptr)
         assert st == 0, "encode chain call failed"
@@ -294,6 +292,7 @@ def encode_chain(cs, xs):
         for c, _, d in bufs:
             assert int(d["err"].item()) == 0
             assert torch.equal(d["st"], c.stream) and torch.equal(d["gp"], c.gaps) and torch.equal(d["sm"], c.signmant)
+            assert torch.equal(d["dt"], c.dtab) and torch.equal(d["bo"], c.block_bitoff)
 
     return launch, check
 

@@ -162,6 +162,29 @@ zx_status zx_encode_size(zx_dtype dtype, const void *in, uint64_t n, int per_blo
                          uint64_t *block_bitoff, uint32_t *block_seg, uint64_t *totals,
                          hipStream_t stream);
 
+/* Everything a per-tensor-codebook encode needs before its outputs are sized:
+ * histogram, codebook, block geometry and totals (zx_histogram + zx_build_codebook +
+ * zx_encode_size in as few launches as the tensor allows), then the decode table.
+ * Same tie rules and limits as those calls (DFloat11, 方法介绍: Huffman tree from the
+ * exponent distribution, position data for the two-phase decode).
+ *   block_hist    u32[max(nblocks,1)][A] device workspace
+ *   tensor_hist   u32[A] device workspace
+ *   lengths u8[A], degenerate u16[1], block_bitoff u64[nblocks+1], block_seg
+ *                 u32[nblocks+1], totals u64[2] = {total_bits, nsegs}: device out
+ *   totals_host   NULL, or 3 u64 of pinned host memory: {total_bits, nsegs, tag} are
+ *                 written there, the tag last, as soon as the totals are known (before
+ *                 the decode table), so a host thread may wait for the tag instead of
+ *                 the stream
+ *   dtab          NULL, or zx_decode_table_bytes() device bytes: the decode table
+ *   err           NULL, or a device word set to 0 (the error word zx_encode reports to)
+ * Errors: ZX_E_UNSUPPORTED (dtype), ZX_E_CODEBOOK (max_len out of range), ZX_E_INVAL
+ * (null or misaligned buffers, n >= 2^32), ZX_E_HIP (launch). */
+zx_status zx_encode_plan(zx_dtype dtype, const void *in, uint64_t n, uint32_t max_len,
+                         uint32_t *block_hist, uint32_t *tensor_hist, uint8_t *lengths,
+                         uint16_t *degenerate, uint64_t *block_bitoff, uint32_t *block_seg,
+                         uint64_t *totals, uint64_t *totals_host, uint64_t tag, uint32_t *dtab,
+                         uint32_t *err, hipStream_t stream);
+
 /* Encode: split fields, bit-pack exponent codes, write gaps and segment table
  * (Intel summary, 方法论; DFloat11, 方法介绍 Fig. 2).
  *   in, n, per_block, lengths, degenerate   as above

@@ -59,6 +59,14 @@ __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t &total)
 // Canonical-code description of one codebook, built in LDS by a whole workgroup.
 // Codes of length L are the consecutive integers first[L] .. first[L]+count[L]-1,
 // assigned to symbols in (length, symbol) order (RFC 1951, section 3.2.2).
+// Order the LDS accesses of one wavefront around this point (all its lanes).
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 struct Canon {
     uint32_t count[kMaxLen + 1];
     uint32_t first[kMaxLen + 1];
@@ -230,7 +238,9 @@ __device__ inline void dtab_fill(const Canon &c, uint32_t A, DTab &t, uint16_t *
     const uint32_t tid = threadIdx.x;
     for (uint32_t i = tid; i < kMaxLen + 2; i += blockDim.x) t.lim[i] = (i == 0) ? 0ull : c.lim[i];
     for (uint32_t i = tid; i <= kMaxLen; i += blockDim.x) t.base[i] = (int32_t)c.offset[i] - (int32_t)c.first[i];
-    for (uint32_t i = tid; i < 256; i += blockDim.x) t.sym[i] = (uint8_t)stage_form(A, c.sym[i]);
+    // (entries past the present symbols are never read; zero keeps the table's bytes
+    // a function of the lengths alone)
+    for (uint32_t i = tid; i < 256; i += blockDim.x) t.sym[i] = i < c.nsym ? (uint8_t)stage_form(A, c.sym[i]) : 0u;
     if (tid == 0) {
         t.ok = c.ok;
         t.nsym = c.nsym;

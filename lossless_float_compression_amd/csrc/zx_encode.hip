@@ -15,7 +15,7 @@
 // beforehand and combined with atomicOr, which gives the same bytes in any order.
 #include <mutex>
 
-#include "zx_common.h"
+#include "zx_codebook.h"
 
 namespace zxk {
 
@@ -746,6 +746,213 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_slots(KvSlots P, const v
     if (tid == 0) status[j] = s_bad ? ZX_E_CODEBOOK : ZX_OK;
 }
 
+// -------------------------------------------------------------------- planning
+// Everything a per-tensor-codebook encode needs before its outputs can be sized, in
+// one workgroup after the block histograms: the tensor histogram (the sum of the
+// block ones), the code lengths (one wavefront), each block's bits and segments
+// (sum of count x length over its histogram), their scan, and the two totals.  The
+// totals are then published (to a pinned host word if the caller gave one, with a
+// tag written last, so a host thread can wait on it without waiting for the whole
+// kernel), the error word cleared, and the decode table built while the host sizes
+// the outputs.  For tensors of at most kPlanMaxBlocks blocks (and their histograms
+// at most kPlanMaxHistWords words, read by this one workgroup).
+constexpr uint32_t kPlanThreads = 1024;
+constexpr uint32_t kPlanMaxBlocks = 2048;
+constexpr uint64_t kPlanMaxHistWords = 1u << 17;
+
+__device__ __forceinline__ void publish_totals(uint64_t total_bits, uint64_t nsegs, uint64_t *totals,
+                                               uint64_t *totals_host, uint64_t tag, uint32_t *err)
+{
+    totals[0] = total_bits;
+    totals[1] = nsegs;
+    if (err) *err = 0;
+    if (totals_host) {
+        totals_host[0] = total_bits;
+        totals_host[1] = nsegs;
+        __hip_atomic_store(&totals_host[2], tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kPlanThreads) void k_plan(const uint32_t *__restrict__ block_hist, uint32_t nb,
+                                                       uint32_t max_len, uint8_t *__restrict__ lengths,
+                                                       uint16_t *__restrict__ degenerate, uint64_t *__restrict__ block_bitoff,
+                                                       uint32_t *__restrict__ block_seg, uint64_t *__restrict__ totals,
+                                                       uint64_t *totals_host, uint64_t tag, DTab *__restrict__ dtab,
+                                                       uint32_t *__restrict__ err)
+{
+    constexpr uint32_t A = alphabet_of(DT);
+    struct TableLds {
+        Canon c;
+        uint16_t t1[kLutSize];
+    };
+    __shared__ union {
+        CodebookLds<uint32_t> cb;
+        TableLds tb;
+    } u;
+    __shared__ uint32_t part[kPlanThreads * 4];
+    __shared__ uint32_t bbits[kPlanMaxBlocks];
+    __shared__ uint32_t bsegs[kPlanMaxBlocks];
+    __shared__ uint64_t wsum_b[kPlanThreads / kWave];
+    __shared__ uint32_t wsum_s[kPlanThreads / kWave];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = lane_id();
+    const uint32_t wave = tid / kWave;
+
+    // The block histograms as 16-byte pieces: piece j holds bins 4 (j % (A/4)) .. +3
+    // of block j / (A/4).  Thread t takes pieces t + 1024 k, so it always sees the same
+    // four bins (of blocks t / (A/4) + G4 k), and the pieces go out eight at a time.
+    constexpr uint32_t Q = A / 4;                  // pieces per block
+    static_assert(Q == kWave || Q == 4, "a block's pieces are one wavefront or one quad of lanes");
+    constexpr uint32_t G4 = kPlanThreads / Q;      // blocks per sweep of the workgroup
+    const uint4 *hp = reinterpret_cast<const uint4 *>(block_hist);
+    const uint32_t npieces = nb * Q;
+    const uint32_t q = tid % Q;
+    // Up to kKeep pieces per thread (every tensor of up to 16384 pieces: 256 BF16
+    // blocks, 4096 FP8 ones) stay in registers from the histogram sum to the block
+    // bits; larger plans read them again.
+    constexpr uint32_t kKeep = 16;
+    const bool keep = npieces <= kKeep * kPlanThreads;
+    uint4 kept[kKeep];
+    // tensor histogram: per-thread sums of its four bins, then the G4 groups summed
+    {
+        uint4 acc = make_uint4(0, 0, 0, 0);
+        if (keep) {
+#pragma unroll
+            for (uint32_t k = 0; k < kKeep; ++k) {
+                const uint32_t j = tid + k * kPlanThreads;
+                kept[k] = j < npieces ? hp[j] : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (uint32_t k = 0; k < kKeep; ++k) {
+                acc.x += kept[k].x; acc.y += kept[k].y; acc.z += kept[k].z; acc.w += kept[k].w;
+            }
+        } else {
+            for (uint32_t j0 = 0; j0 < npieces; j0 += 8 * kPlanThreads) {   // (the same trip count on every lane)
+                uint4 v[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t j = j0 + tid + k * kPlanThreads;
+                    v[k] = j < npieces ? hp[j] : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    acc.x += v[k].x; acc.y += v[k].y; acc.z += v[k].z; acc.w += v[k].w;
+                }
+            }
+        }
+        const uint32_t g = tid / Q;
+        part[g * A + 4 * q + 0] = acc.x;
+        part[g * A + 4 * q + 1] = acc.y;
+        part[g * A + 4 * q + 2] = acc.z;
+        part[g * A + 4 * q + 3] = acc.w;
+    }
+    __syncthreads();
+    if constexpr (A == 256) {   // 16 partial sums per bin
+        if (tid < A) {
+            uint32_t t = 0;
+            for (uint32_t g = 0; g < G4; ++g) t += part[g * A + tid];
+            u.cb.cnt[tid] = t;
+        }
+    } else {                    // 256 partial sums per bin: wavefront w sums bin w
+        if (wave < A) {
+            uint32_t t = 0;
+            for (uint32_t g = lane; g < G4; g += kWave) t += part[g * A + wave];
+            uint32_t tot;
+            wave_excl_scan(t, tot);
+            if (lane == 0) u.cb.cnt[wave] = tot;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) codebook_wave<A, uint32_t>(u.cb, max_len, lengths, degenerate);
+    __syncthreads();
+
+    // each block's bits: every piece weighted by its four lengths and summed over the
+    // Q threads (adjacent lanes) that hold one block
+    {
+        const uint32_t l0 = u.cb.out_len[4 * q], l1 = u.cb.out_len[4 * q + 1];
+        const uint32_t l2 = u.cb.out_len[4 * q + 2], l3 = u.cb.out_len[4 * q + 3];
+        auto block_bits = [&](const uint4 v, const uint32_t j) {
+            uint32_t bits = v.x * l0 + v.y * l1 + v.z * l2 + v.w * l3;
+            if constexpr (Q == kWave) {
+                uint32_t tot;
+                wave_excl_scan(bits, tot);
+                bits = tot;
+            } else {                    // a quad of lanes: DPP quad permutes [1,0,3,2], then [2,3,0,1]
+                bits += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits, 0xB1, 0xF, 0xF, false);
+                bits += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)bits, 0x4E, 0xF, 0xF, false);
+            }
+            if (q == 0 && j < npieces) {
+                const uint32_t b = j / Q;
+                const uint32_t nch = (bits + kChunkBits - 1) / kChunkBits;
+                const uint32_t ns = (nch + kSegChunks - 1) / kSegChunks;
+                bbits[b] = bits;
+                bsegs[b] = ns ? ns : 1u;
+            }
+        };
+        if (keep) {
+#pragma unroll
+            for (uint32_t k = 0; k < kKeep; ++k) block_bits(kept[k], tid + k * kPlanThreads);
+        } else {
+            for (uint32_t j0 = 0; j0 < npieces; j0 += 8 * kPlanThreads) {   // (every lane shuffles: same trip count)
+                uint4 v[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t j = j0 + tid + k * kPlanThreads;
+                    v[k] = j < npieces ? hp[j] : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) block_bits(v[k], j0 + tid + k * kPlanThreads);
+            }
+        }
+    }
+    // the table build below reuses the codebook's LDS: each thread keeps its
+    // symbol's length
+    const uint32_t mylen = tid < A ? u.cb.out_len[tid] : 0u;
+    __syncthreads();
+
+    // inclusive scan: thread t owns blocks 2t and 2t + 1
+    uint64_t vb0 = 0, vb1 = 0;
+    uint32_t vs0 = 0, vs1 = 0;
+    if (2 * tid < nb) { vb0 = bbits[2 * tid]; vs0 = bsegs[2 * tid]; }
+    if (2 * tid + 1 < nb) { vb1 = bbits[2 * tid + 1]; vs1 = bsegs[2 * tid + 1]; }
+    uint64_t xb = vb0 + vb1;
+    uint32_t xs = vs0 + vs1;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const uint64_t yb = __shfl_up(xb, d, kWave);
+        const uint32_t ys = __shfl_up(xs, d, kWave);
+        if (lane >= (uint32_t)d) { xb += yb; xs += ys; }
+    }
+    if (lane == kWave - 1) { wsum_b[wave] = xb; wsum_s[wave] = xs; }
+    __syncthreads();
+    uint64_t ob = 0, total_b = 0;
+    uint32_t os = 0, total_s = 0;
+    for (uint32_t w = 0; w < kPlanThreads / kWave; ++w) {
+        if (w < wave) { ob += wsum_b[w]; os += wsum_s[w]; }
+        total_b += wsum_b[w];
+        total_s += wsum_s[w];
+    }
+    ob += xb - (vb0 + vb1);   // exclusive prefix of this thread's pair
+    os += xs - (vs0 + vs1);
+    if (2 * tid < nb) { block_bitoff[2 * tid + 1] = ob + vb0; block_seg[2 * tid + 1] = os + vs0; }
+    if (2 * tid + 1 < nb) { block_bitoff[2 * tid + 2] = ob + vb0 + vb1; block_seg[2 * tid + 2] = os + vs0 + vs1; }
+    if (tid == 0) {
+        block_bitoff[0] = 0;
+        block_seg[0] = 0;
+        publish_totals(total_b, total_s, totals, totals_host, tag, err);
+    }
+    if (!dtab) return;
+    // the decode table, once the totals are out
+    canon_build_from(mylen, A, u.tb.c);
+    dtab_fill(u.tb.c, A, *dtab, u.tb.t1);
+}
+
+// The planning steps' last one for larger tensors (after k_scan_blocks).
+__global__ void k_publish(uint64_t *totals, uint64_t *totals_host, uint64_t tag, uint32_t *err)
+{
+    if (threadIdx.x == 0) publish_totals(totals[0], totals[1], totals, totals_host, tag, err);
+}
+
 }  // namespace zxk
 
 using namespace zxk;
@@ -787,6 +994,45 @@ extern "C" zx_status zx_encode_size(zx_dtype dtype, const void *in, uint64_t n, 
     }
     hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(1024), 0, stream, nblocks, block_bitoff, block_seg, totals);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}
+
+extern "C" zx_status zx_encode_plan(zx_dtype dtype, const void *in, uint64_t n, uint32_t max_len,
+                                    uint32_t *block_hist, uint32_t *tensor_hist, uint8_t *lengths,
+                                    uint16_t *degenerate, uint64_t *block_bitoff, uint32_t *block_seg,
+                                    uint64_t *totals, uint64_t *totals_host, uint64_t tag, uint32_t *dtab,
+                                    uint32_t *err, hipStream_t stream)
+{
+    if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN && dtype != ZX_E8M0) return ZX_E_UNSUPPORTED;
+    const uint32_t A = alphabet_of(dtype);
+    if (max_len < (A == 256 ? 8u : 4u) || max_len > kMaxLen) return ZX_E_CODEBOOK;
+    if (!block_hist || !tensor_hist || !lengths || !degenerate || !block_bitoff || !block_seg || !totals) return ZX_E_INVAL;
+    if ((n && !in) || n >= (1ull << 32)) return ZX_E_INVAL;
+    if (!aligned16(in) || !aligned16(block_hist) || !aligned16(tensor_hist) || !aligned16(dtab) ||
+        ((uintptr_t)totals & 7u) || ((uintptr_t)block_bitoff & 7u) || ((uintptr_t)totals_host & 7u))
+        return ZX_E_INVAL;
+    const uint64_t nblocks = (n + kBlock - 1) / kBlock;
+    zx_status st;
+    if (nblocks <= kPlanMaxBlocks && nblocks * A <= kPlanMaxHistWords) {
+        // block histograms, then the one planning workgroup
+        if (nblocks && (st = zx_histogram(dtype, in, n, nullptr, block_hist, stream)) != ZX_OK) return st;
+        DTab *t = reinterpret_cast<DTab *>(dtab);
+        if (A == 256)
+            hipLaunchKernelGGL(k_plan<ZX_BF16>, dim3(1), dim3(kPlanThreads), 0, stream, block_hist, (uint32_t)nblocks, max_len,
+                               lengths, degenerate, block_bitoff, block_seg, totals, totals_host, tag, t, err);
+        else
+            hipLaunchKernelGGL(k_plan<ZX_FP8_E4M3FN>, dim3(1), dim3(kPlanThreads), 0, stream, block_hist, (uint32_t)nblocks,
+                               max_len, lengths, degenerate, block_bitoff, block_seg, totals, totals_host, tag, t, err);
+        return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+    }
+    // larger tensors: the separate steps, then the totals published and the table built
+    if ((st = zx_histogram(dtype, in, n, tensor_hist, block_hist, stream)) != ZX_OK) return st;
+    if ((st = zx_build_codebook(dtype, tensor_hist, 1, max_len, lengths, degenerate, stream)) != ZX_OK) return st;
+    if ((st = zx_encode_size(dtype, in, n, 0, lengths, block_hist, block_bitoff, block_seg, totals, stream)) != ZX_OK)
+        return st;
+    hipLaunchKernelGGL(k_publish, dim3(1), dim3(64), 0, stream, totals, totals_host, tag, err);
+    if (hipGetLastError() != hipSuccess) return ZX_E_HIP;
+    if (dtab) return zx_build_decode_table(dtype, lengths, dtab, stream);
+    return ZX_OK;
 }
 
 extern "C" zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int per_block,

@@ -14,7 +14,7 @@
 namespace zxk {
 
 constexpr int kHistThreads = 1024;
-constexpr uint32_t kHistUnroll = 4;   // 16-byte loads in flight per lane
+constexpr uint32_t kHistUnroll = 8;   // 16-byte loads in flight per lane (a whole BF16 block in one step)
 
 template <int DT>
 __global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restrict__ in, uint64_t n,

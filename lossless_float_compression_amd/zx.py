@@ -80,7 +80,7 @@ EXPORTS = ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "
            "zx_status_string", "zx_version", "zx_kv_slot_sizes", "zx_kv_workspace_bytes", "zx_kv_encode_slots",
            "zx_kv_slot_container", "zx_kv_decode_slots", "zx_zf_scan_workspace_bytes", "zx_zf_encode_size",
            "zx_zf_encode", "zx_zf_decode", "zx_histogram_accumulate", "zx_build_codebook_u64",
-           "zx_kv_encode_slots_noalloc")
+           "zx_kv_encode_slots_noalloc", "zx_encode_plan")
 
 
 def lib():
@@ -121,11 +121,12 @@ def lib():
         L.zx_zf_decode.argtypes = [C.POINTER(zx_zf_container), P, P, P]
         L.zx_histogram_accumulate.argtypes = [I, P, U64, P, P]
         L.zx_build_codebook_u64.argtypes = [I, P, U32, U32, P, P, P]
+        L.zx_encode_plan.argtypes = [I, P, U64, U32, P, P, P, P, P, P, P, P, U64, P, P, P]
         for f in ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
                   "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_kv_slot_sizes",
                   "zx_kv_encode_slots", "zx_kv_slot_container", "zx_kv_decode_slots", "zx_zf_encode_size",
                   "zx_zf_encode", "zx_zf_decode", "zx_histogram_accumulate", "zx_build_codebook_u64",
-                  "zx_kv_encode_slots_noalloc"):
+                  "zx_kv_encode_slots_noalloc", "zx_encode_plan"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -140,6 +141,13 @@ def _stream(stream=None):
         return stream
     s = torch.cuda.current_stream() if stream is None else stream
     return C.c_void_p(s.cuda_stream)
+
+
+def _raw_stream(dev) -> int:
+    """The current torch stream of `dev` as a raw handle (the cheap accessor when this
+    torch build has it)."""
+    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    return get(dev.index) if get is not None else torch.cuda.current_stream(dev).cuda_stream
 
 
 def _check(fn: str, st: int):
@@ -169,6 +177,15 @@ def zx_build_codebook(dtype, hist, n_codebooks, max_len, lengths, degenerate, st
 def zx_encode_size(dtype, inp, n, per_block, lengths, block_hist, block_bitoff, block_seg, totals, stream=None):
     _check("zx_encode_size", lib().zx_encode_size(dtype, _ptr(inp), n, int(per_block), _ptr(lengths), _ptr(block_hist),
                                                   _ptr(block_bitoff), _ptr(block_seg), _ptr(totals), _stream(stream)))
+
+
+def zx_encode_plan(dtype, inp, n, max_len, block_hist, tensor_hist, lengths, degenerate, block_bitoff, block_seg,
+                   totals, totals_host=None, tag=0, dtab=None, err=None, stream=None):
+    """totals_host: a pinned host int64 tensor of at least 3 entries, or None."""
+    _check("zx_encode_plan", lib().zx_encode_plan(dtype, _ptr(inp), n, max_len, _ptr(block_hist), _ptr(tensor_hist),
+                                                  _ptr(lengths), _ptr(degenerate), _ptr(block_bitoff), _ptr(block_seg),
+                                                  _ptr(totals), _ptr(totals_host), int(tag), _ptr(dtab), _ptr(err),
+                                                  _stream(stream)))
 
 
 def zx_encode(dtype, inp, n, per_block, lengths, degenerate, block_bitoff, block_seg, total_bits, nsegs,
@@ -332,6 +349,8 @@ def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_sc
     A = alphabet(dtype)
     nb = nblocks_of(n)
     ncb = nb if per_block else 1
+    if not per_block and codebook is None and n < (1 << 32):
+        return _compress_planned(x, dtype, flat, n, A, nb, max_len, fp8_scale, _raw_stream(dev))
     stream = _stream(None)
     u8 = dict(dtype=torch.uint8, device=dev)
     i32 = dict(dtype=torch.int32, device=dev)
@@ -374,6 +393,81 @@ def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_sc
                    block_bitoff=block_bitoff, block_seg=block_seg, seg_desc=seg_desc, gaps=gaps, dtab=dtab,
                    fp8_scale=fp8_scale)
     c._err = err  # device word set by the encoder on a data/codebook mismatch
+    return c
+
+
+_plan_tag = [0]
+_plan_ring = {}   # device index -> pinned int64 [_PLAN_SLOTS, 4]: where zx_encode_plan publishes the totals
+_PLAN_SLOTS = 256
+
+
+def _plan_slot(dev):
+    """A pinned 4-word host slot for one compress() call (slots are reused round-robin;
+    each call's unique tag tells its own publication from an older one)."""
+    ring = _plan_ring.get(dev.index)
+    if ring is None:
+        ring = _plan_ring[dev.index] = torch.full((_PLAN_SLOTS, 4), -1, dtype=torch.int64, pin_memory=True)
+    _plan_tag[0] += 1
+    tag = _plan_tag[0]
+    return ring[tag % _PLAN_SLOTS], tag
+
+
+def _layout(sizes):
+    """16-byte-aligned offsets of (bytes, dtype) pieces in one arena, and its size."""
+    offs, off = [], 0
+    for nbytes, _ in sizes:
+        offs.append(off)
+        off += (nbytes + 15) // 16 * 16
+    return offs, off
+
+
+def _compress_planned(x, dtype, flat, n, A, nb, max_len, fp8_scale, stream):
+    """Per-tensor codebook: zx_encode_plan (histogram, codebook, sizes and totals in
+    as few launches as the tensor allows; the decode table after the totals), a wait
+    for the totals on a pinned host word instead of the stream, then zx_encode.  The
+    launches take raw addresses in one arena; the container's tensor views of it are
+    made while the kernels run."""
+    dev = flat.device
+    L = lib()
+    u8 = dict(dtype=torch.uint8, device=dev)
+    nbw = max(nb, 1)
+    sizes = [(zx_decode_table_bytes(), torch.uint8), (8 * (nb + 1), torch.int64), (4 * (nb + 1), torch.int32),
+             (16, torch.int64), (4, torch.int32), (A, torch.uint8), (2, torch.int16)]
+    offs, total = _layout(sizes)
+    ws = torch.empty(nbw * A + A, dtype=torch.int32, device=dev)   # block histograms, tensor histogram
+    arena = torch.empty(total, **u8)
+    base, wsp = arena.data_ptr(), ws.data_ptr()
+    o_dtab, o_bo, o_bs, o_tot, o_err, o_len, o_deg = offs
+    host, tag = _plan_slot(dev)
+    _check("zx_encode_plan", L.zx_encode_plan(dtype, flat.data_ptr(), n, max_len, wsp, wsp + 4 * nbw * A, base + o_len,
+                                              base + o_deg, base + o_bo, base + o_bs, base + o_tot, host.data_ptr(), tag,
+                                              base + o_dtab, base + o_err, stream))
+    signmant = torch.empty(n if dtype == BF16 else (n + 1) // 2 if dtype == FP8_E4M3FN else 0, **u8)
+    dtab, block_bitoff, block_seg, totals, err, lengths, degenerate = (
+        arena[o:o + nbytes].view(dt) for o, (nbytes, dt) in zip(offs, sizes))
+    hv = host.numpy()
+    spins = 0
+    while hv[2] != tag:
+        spins += 1
+        if spins == 20000:          # the stream is busy with earlier work: block on it instead
+            torch.cuda.current_stream().synchronize()
+            if hv[2] != tag:
+                raise RuntimeError("zx_encode_plan did not publish its totals")
+    total_bits, nsegs = int(hv[0]), int(hv[1])
+    nwords = zx_stream_words(total_bits)
+    out_sizes = [(4 * nwords, torch.int32), (8 * nsegs, torch.int32), (SEG_CHUNKS * nsegs, torch.uint8)]
+    ooffs, ototal = _layout(out_sizes)
+    out = torch.empty(ototal, **u8)
+    ob = out.data_ptr()
+    _check("zx_encode", L.zx_encode(dtype, flat.data_ptr(), n, 0, base + o_len, base + o_deg, base + o_bo, base + o_bs,
+                                    total_bits, nsegs, signmant.data_ptr(), ob + ooffs[0], ob + ooffs[1], ob + ooffs[2],
+                                    base + o_err, stream))
+    words, seg_desc, gaps = (out[o:o + nbytes].view(dt) for o, (nbytes, dt) in zip(ooffs, out_sizes))
+    c = Compressed(dtype=dtype, per_block=0, n=n, shape=tuple(x.shape), total_bits=total_bits,
+                   nsegs=nsegs, lengths=lengths.view(1, A), degenerate=degenerate, signmant=signmant, stream=words,
+                   block_bitoff=block_bitoff, block_seg=block_seg, seg_desc=seg_desc.view(nsegs, 2),
+                   gaps=gaps.view(nsegs, SEG_CHUNKS), dtab=dtab, fp8_scale=fp8_scale)
+    c._err = err
     return c
 
 
