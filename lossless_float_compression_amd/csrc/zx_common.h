@@ -249,11 +249,19 @@ __device__ inline void dtab_fill(const Canon &c, uint32_t A, DTab &t, uint16_t *
         t.lim_short = l == 0 ? 0u : (l >= (1ull << 32) ? 0xFFFFFFFFu : (uint32_t)(l - 1));
         t.pad_[0] = t.pad_[1] = t.pad_[2] = 0;
     }
+    // the limits of lengths 1..kLutBits, read once: the length of the code at the front
+    // of a window is one more than the number of those limits the window reaches (they
+    // do not decrease with the length), when that is at most kLutBits
+    uint64_t lim_s[kLutBits];
+#pragma unroll
+    for (int L = 0; L < kLutBits; ++L) lim_s[L] = c.lim[L + 1];
     for (uint32_t x = tid; x < kLutSize; x += blockDim.x) {
         uint32_t e = 0;
         if (c.ok) {
             const uint32_t v = x << (32 - kLutBits);   // window, left-justified, zero filled
-            const uint32_t L = canon_len(c.lim, v, 1);
+            uint32_t L = 1;
+#pragma unroll
+            for (int j = 0; j < kLutBits; ++j) L += (uint64_t)v >= lim_s[j] ? 1u : 0u;
             if (L <= (uint32_t)kLutBits)
                 e = L | (stage_form(A, c.sym[c.offset[L] + ((v >> (32 - L)) - c.first[L])]) << 8);
         }
