@@ -28,7 +28,6 @@ namespace zxk {
 
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * kWave;
-constexpr int kDecWgPerCu = 2;
 constexpr int kMaxBatch = 16;
 
 // Per-wavefront LDS: the lanes' stream words and the exponent stage.
@@ -42,15 +41,10 @@ constexpr uint32_t kStageBytes = 3616;         // one byte per output position, 
 // A segment whose exponents do not fit the stage at once (mean code length under
 // about 2.3 bits) is written in rounds of kRoundElems output positions.
 constexpr uint32_t kRoundElems = 3584;
-// Register path: up to kRounds rounds of three lookups per lane; the symbol counts
-// of the lookups are kept one byte each, four to a register.
+// Register path: up to kRounds rounds of three lookups per lane (kLowRounds in the
+// low-entropy mode); the symbol counts of the lookups are kept one byte each, four to
+// a register.
 constexpr int kRounds = 7;
-// E8M0 block scales have mean codes near 1.5 bits: a 128-bit chunk holds up to ~130
-// codes and a segment up to 8192 elements, so that type gets 11 rounds and a stage
-// of a whole segment, and runs one workgroup per CU for the LDS this takes.
-template <int DT> constexpr int dec_rounds() { return DT == ZX_E8M0 ? 11 : kRounds; }
-template <int DT> constexpr uint32_t dec_stage_bytes() { return DT == ZX_E8M0 ? 8224u : kStageBytes; }
-template <int DT> constexpr int dec_wg_per_cu() { return DT == ZX_E8M0 ? 1 : kDecWgPerCu; }
 constexpr int kWriteBatch = 7;                 // write-pass pieces per lane whose loads go out together (at most)
 // pieces per lane in one batch: 7 x 64 x 8 BF16 elements cover a stage; FP8 pieces hold
 // 16 elements, so 4 x 64 x 16 do (and fewer registers are live in the write pass)
@@ -822,17 +816,13 @@ __host__ __device__ constexpr uint32_t ns_sel(int j)
         nsb[(slot) >> 2] = __builtin_amdgcn_perm(lo_ | (xns), nsb[(slot) >> 2], ns_sel((slot) & 3)); \
     } while (0)
 
-// Decode segment s, whose stream words and gap bytes are already in this
-// wavefront's LDS rows.  The next segment's loads are issued into `in` (when
-// has_next) and, once this segment no longer reads its rows, stored to them;
-// returns whether that store was made.
-// FAST: the word rows and the stage share one region (the words of segment k are put
-// in at its start, from `in`, after segment k-1's write pass has read the stage), and a
-// segment that needs the code-by-code passes borrows the workgroup's spare stage under
-// `lock`.  Otherwise the rows have a region of their own and the next segment's words
-// are put in right after the count pass.
-// LOW (with FAST): the low-entropy mode above; no spare stage.
-template <int DT, bool FAST = false, bool SO = false, bool LOW = false>
+// Decode segment s.  The wavefront's word rows and its stage share one region: the
+// segment's stream words and gap bytes, requested into `in` while the segment before
+// it decoded, are put in at its start (after that segment's write pass has read the
+// stage), and the next segment's are requested into `in` (when has_next).  A segment
+// that needs the code-by-code passes borrows the workgroup's spare stage under `lock`.
+// LOW: the low-entropy mode above; no spare stage.
+template <int DT, bool SO, bool LOW>
 __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *sw,
                                                     uint32_t s, const SegMeta &m, SegIn &in, bool has_next, uint32_t sn,
                                                     const SegMeta &mn, uint32_t *err, uint8_t *spare = nullptr,
@@ -856,7 +846,7 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     // its first write batch, are requested first; they arrive while this segment
     // decodes.  The bytes are requested only on the path that uses them, so that no
     // path from their request to the next segment skips their use.
-    if constexpr (FAST) rows_store_in(sw, lane, in);
+    rows_store_in(sw, lane, in);
     wave_sync();
     const uint32_t gap = sw[kGapSlot * kWave + lane];
     const uint32_t gap_next = sw[kGapSlot * kWave + lane + 1];
@@ -903,9 +893,8 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     // ---- count pass, register path
     // entries of rounds that do not run are never read: the replay stops once no lane
     // has symbols left
-    static_assert(!LOW || FAST, "the low-entropy mode is a fast-decode mode");
-    static_assert(!FAST || LOW || DT != ZX_E8M0, "E8M0 takes the fast decode in its low-entropy mode only");
-    constexpr int kR = LOW ? kLowRounds : dec_rounds<DT>(), kE = 3 * kR, kNs = (kE + 3) / 4;
+    static_assert(LOW || DT != ZX_E8M0, "E8M0 takes the low-entropy mode only");
+    constexpr int kR = LOW ? kLowRounds : kRounds, kE = 3 * kR, kNs = (kE + 3) / 4;
     uint32_t ent[kE];
     uint32_t nsb[kNs];
 #pragma unroll
@@ -995,33 +984,22 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
                                         sbase, smv, smcut);
         return true;
     }
-    if (t0 + total + 3 > dec_stage_bytes<DT>()) {
-        if constexpr (FAST) {
-            if (!spare_acquire(lock)) { report(err, ZX_E_CORRUPT); return false; }
-            write_rounds<DT, SO>(tab, col, spare, start, cnt, off, t0, total, out_block, sm_block, sbase);
-            spare_release(lock);
-        } else {
-            write_rounds<DT, SO>(tab, col, stage, start, cnt, off, t0, total, out_block, sm_block, sbase);
-        }
+    if (t0 + total + 3 > kStageBytes) {
+        if (!spare_acquire(lock)) { report(err, ZX_E_CORRUPT); return false; }
+        write_rounds<DT, SO>(tab, col, spare, start, cnt, off, t0, total, out_block, sm_block, sbase);
+        spare_release(lock);
         return false;
     }
     // some lane needed more lookups than the registers hold: its symbols go to the
-    // stage one code at a time, and no entry is replayed.  (FAST: the rows are still
-    // needed for that, so the symbols go to the spare stage.)
-    if constexpr (FAST) {
-        if (more) {
-            if (!spare_acquire(lock)) { report(err, ZX_E_CORRUPT); return false; }
-            stage = spare;
-        }
+    // stage one code at a time, and no entry is replayed.  The rows are still needed
+    // for that, so the symbols go to the spare stage.
+    if (more) {
+        if (!spare_acquire(lock)) { report(err, ZX_E_CORRUPT); return false; }
+        stage = spare;
+        store_generic(tab, col, stage, start, cnt, t0 + off);
     }
-    if (more) store_generic(tab, col, stage, start, cnt, t0 + off);
     const uint32_t rcnt = more ? 0u : cnt;
 
-    // the rows are read no more: the next segment's words go in now, before this
-    // segment's stores are in flight (a later wait for them would have to drain
-    // those stores too).  (FAST: they go in at the next segment's start; the replay
-    // below overwrites the rows.)
-    if constexpr (!FAST) rows_store_in(sw, lane, in);
     // the sign/mantissa bytes of the first write batch are requested now: they arrive
     // during the replay, and their registers are free during the count pass.  From
     // here to their use below there is no exit, so every path uses them before any
@@ -1080,141 +1058,11 @@ __device__ __forceinline__ bool decode_segment_body(const DecTensor &T, const DT
     wave_sync();
     settle_sm<DT>(smv, smcut);
     write_range<DT, true, SO>(out_block, sm_block, e0, e_end, stage, sbase, false, 0, smv, smcut);
-    if constexpr (FAST) {
-        if (more) spare_release(lock);
-    }
+    if (more) spare_release(lock);
     return true;
 }
 #undef ZX_LOOKUP
 #undef ZX_NS
-
-template <int DT>
-__device__ void decode_segment(const DecTensor &T, const DTab &tab, uint8_t *stage, uint32_t *sw, uint32_t s,
-                               const SegMeta &m, bool has_next, uint32_t sn, const SegMeta &mn, uint32_t *err)
-{
-    SegIn in;
-    if (!decode_segment_body<DT>(T, tab, stage, sw, s, m, in, has_next, sn, mn, err)) {
-        wave_sync();
-        rows_store_in(sw, lane_now(), in);
-    }
-}
-
-// SLOTS: the batch is a slot list (DecSlots); a separate instantiation, so that the
-// tensor-batch decode keeps reading its descriptor straight from the kernel arguments.
-template <int DT, bool SLOTS>
-__global__ __launch_bounds__(kDecThreads, dec_wg_per_cu<DT>() * kDecWaves / 4) void k_decode(const DecBatch batch, uint32_t *err)
-{
-    constexpr uint32_t A = alphabet_of(DT);
-    __shared__ DTab tab;
-    constexpr uint32_t kStage = dec_stage_bytes<DT>();
-    __shared__ __align__(16) uint8_t stage_all[kDecWaves * kStage];
-    __shared__ __align__(16) uint32_t words_all[kDecWaves * kSegWords];
-    __shared__ SegMeta meta_all[kDecWaves * kWave];
-    // kDecWgPerCu workgroups share the CU's 160 KB of LDS
-    static_assert(sizeof(DTab) + sizeof(stage_all) + sizeof(words_all) + sizeof(meta_all) <=
-                      160u * 1024u / dec_wg_per_cu<DT>() - 512u,
-                  "decode workgroup LDS budget");
-    static_assert(sizeof(Canon) <= sizeof(stage_all), "Canon is built inside the stage area");
-
-    const uint32_t g = blockIdx.x;
-    auto body = [&](const DecTensor &T, const uint32_t lg) {
-    const uint32_t tid = threadIdx.x;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const uint32_t lane = lane_now();
-    uint32_t s_begin, s_end;
-    if (T.per_block) {
-        s_begin = T.block_seg[lg];
-        s_end = T.block_seg[lg + 1];
-        if (s_end > T.nsegs || s_begin > s_end) { s_end = s_begin; if (tid == 0) report(err, ZX_E_CORRUPT); }
-    } else {
-        s_begin = lg * T.segs_per_wg;
-        s_end = s_begin + T.segs_per_wg;
-        if (s_end > T.nsegs) s_end = T.nsegs;
-    }
-    // the wavefront's segments are s_begin + wave + kDecWaves k, k < nk; lane k holds
-    // the descriptor of the k-th (in groups of 64)
-    const uint32_t s0 = s_begin + wave;
-    const uint32_t nk = __builtin_amdgcn_readfirstlane(s0 < s_end ? (s_end - s0 + kDecWaves - 1) / kDecWaves : 0);
-    SegMeta mine;
-    SegIn in;
-    if (T.per_block) {
-        load_meta(T, s0 + kDecWaves * lane, lane < nk, mine);
-        issue_seg(T, s0, meta_at(mine, 0), lane, in, nk != 0);
-        Canon &c = *reinterpret_cast<Canon *>(stage_all);
-        static_assert(sizeof(Canon) % 4 == 0 && sizeof(Canon) + kLutSize * 2 <= kDecWaves * kStage, "table scratch");
-        canon_build(T.lengths + (uint64_t)lg * A, A, c);
-        dtab_fill(c, A, tab, reinterpret_cast<uint16_t *>(stage_all + sizeof(Canon)));
-    } else {
-        // the prepared table is requested first, the descriptors next; the table is
-        // stored to LDS once it arrives
-        const uint4 *src = reinterpret_cast<const uint4 *>(T.dtab);
-        uint4 *dst = reinterpret_cast<uint4 *>(&tab);
-        constexpr uint32_t kTabPieces = sizeof(DTab) / 16;
-        constexpr uint32_t kPer = (kTabPieces + kDecThreads - 1) / kDecThreads;
-        uint4 pc[kPer];
-#pragma unroll
-        for (uint32_t k = 0; k < kPer; ++k) {
-            const uint32_t i = tid + k * kDecThreads;
-            pc[k] = i < kTabPieces ? src[i] : make_uint4(0, 0, 0, 0);
-        }
-        load_meta(T, s0 + kDecWaves * lane, lane < nk, mine);
-        issue_seg(T, s0, meta_at(mine, 0), lane, in, nk != 0);
-#pragma unroll
-        for (uint32_t k = 0; k < kPer; ++k) {
-            const uint32_t i = tid + k * kDecThreads;
-            if (i < kTabPieces) dst[i] = pc[k];
-        }
-    }
-    uint8_t *stage = stage_all + wave * kStage;
-    uint32_t *swords = words_all + wave * kSegWords;
-    SegMeta *metas = meta_all + wave * kWave;
-    rows_store_in(swords, lane, in);
-    metas[lane] = mine;
-    __syncthreads();
-    for (uint32_t k = 0; k < nk; ++k) {
-        const uint32_t i = k & (kWave - 1);
-        const uint32_t s = s0 + kDecWaves * k;
-        const bool has_next = k + 1 < nk && i + 1 < kWave;
-        const SegMeta mu = meta_get(metas, i);
-        const SegMeta mn = meta_get(metas, has_next ? i + 1 : i);
-        decode_segment<DT>(T, tab, stage, swords, s, mu, has_next, s + kDecWaves, mn, err);
-        if (i == kWave - 1 && k + 1 < nk) {
-            // next group of 64 descriptors
-            SegMeta m2;
-            load_meta(T, s + kDecWaves + kDecWaves * lane, k + 1 + lane < nk, m2);
-            SegIn in2;
-            issue_seg(T, s + kDecWaves, meta_at(m2, 0), lane, in2, true);
-            wave_sync();
-            rows_store_in(swords, lane, in2);
-            metas[lane] = m2;
-            wave_sync();
-        }
-    }
-    };
-    if constexpr (SLOTS) {
-        const DecSlots &S = batch.slots;
-        const uint64_t slot = S.slot_ids[g];
-        if (slot >= S.n_slots) {
-            if (threadIdx.x == 0) report(err, ZX_E_CORRUPT);
-            return;
-        }
-        DecTensor T = batch.t[0];
-        T.signmant += slot * S.sm_bytes;
-        T.stream += slot * S.stream_words;
-        T.block_bitoff += 2 * slot;
-        T.block_seg += 2 * slot;
-        T.seg_desc += 2 * slot * S.seg_stride;
-        T.gaps += slot * S.seg_stride * kSegChunks;
-        T.lengths += slot * S.alphabet;
-        T.degenerate += slot;
-        T.out = static_cast<uint8_t *>(T.out) + (uint64_t)g * S.out_bytes;
-        body(T, 0);
-    } else {
-        uint32_t t = 0;
-        while (t + 1 < batch.count && g >= batch.t[t + 1].wg_begin) ++t;
-        body(batch.t[t], g - batch.t[t].wg_begin);
-    }
-}
 
 // Issue priority of this wavefront from the share of its segments still ahead: 3 at
 // the start, down to 0 for its last quarter.  A SIMD issues from its oldest wavefront
@@ -1231,17 +1079,19 @@ __device__ __forceinline__ void set_priority_by_remaining(uint32_t remaining, ui
     else __builtin_amdgcn_s_setprio(0);
 }
 
-// ---- fast decode of per-tensor-codebook BF16 / FP8 containers ------------------
+// ---- the decode kernels ---------------------------------------------------------
 //
-// Three 512-thread workgroups per CU (six wavefronts per SIMD) instead of two: each
-// wavefront's stream words and its stage share one region, descriptors are refreshed
-// sixteen at a time, and the code-by-code passes borrow one spare stage per
-// workgroup.  A tensor of 5376 segments (4096 x 4096 BF16) then gets one segment per
-// wavefront instead of two for a third of them, and every wavefront has more company
-// to hide its memory and LDS waits behind.  Segments of mean code length below about
-// 2.3 bits overflow the stage and take the spare one wavefront at a time, so such
-// containers take the low-entropy mode (LOW): two workgroups per CU, eleven count
+// Three 512-thread workgroups per CU (six wavefronts per SIMD): each wavefront's
+// stream words and its stage share one region (3616 bytes), descriptors are
+// refreshed sixteen at a time, and the code-by-code passes borrow one spare stage
+// per workgroup.  A tensor of 5376 segments (4096 x 4096 BF16) gets one segment per
+// wavefront, and every wavefront has five others on its SIMD to hide its memory and
+// LDS waits behind.  Segments of mean code length below about 2.3 bits overflow the
+// stage and would take the spare one wavefront at a time, so such containers (and
+// all E8M0 ones) take the low-entropy mode (LOW): two workgroups per CU, eleven count
 // rounds and a larger region per wavefront (see kLowRegion), no spare.
+// k_decode_fast takes per-tensor codebooks, persistent over a share of the segments;
+// k_decode_fast_blocks per-block ones (and K/V slot lists), one workgroup per block.
 constexpr int kFastWgPerCu = 3;
 constexpr int kLowWgPerCu = 2;
 constexpr uint32_t kFastMeta = 16;   // descriptors per wavefront refresh
@@ -1277,7 +1127,7 @@ __device__ __forceinline__ void fast_segment_loop(const DecTensor &T, FastShared
         const bool has_next = k + 1 < nk && i + 1 < kFastMeta;
         const SegMeta mu = meta_get(metas, i);
         const SegMeta mn = meta_get(metas, has_next ? i + 1 : i);
-        decode_segment_body<DT, true, SO, LOW>(T, sh.tab, reg, sw, s, mu, in, has_next, s + kDecWaves, mn, err, sh.spare,
+        decode_segment_body<DT, SO, LOW>(T, sh.tab, reg, sw, s, mu, in, has_next, s + kDecWaves, mn, err, sh.spare,
                                                &sh.lock);
         if (i == kFastMeta - 1 && k + 1 < nk) {
             // next group of 16 descriptors, and the words of its first segment (put
@@ -1383,15 +1233,38 @@ __global__ __launch_bounds__(kDecThreads, (LOW ? kLowWgPerCu : kFastWgPerCu) * k
 }
 
 // The batch of per-block-codebook containers, one workgroup per block (see fast_block).
-template <int DT, bool SO, bool LOW>
+// SLOTS: the batch is a slot list (DecSlots): workgroup g decodes the one-block
+// container in slot slot_ids[g] of a K/V slot pool into row g of the output; t[0]
+// describes slot 0's container and the strides give every other slot's arrays.
+template <int DT, bool SO, bool LOW, bool SLOTS>
 __global__ __launch_bounds__(kDecThreads, (LOW ? kLowWgPerCu : kFastWgPerCu) * kDecWaves / 4) void k_decode_fast_blocks(
     const DecBatch batch, uint32_t *err)
 {
     __shared__ FastShared<LOW> sh;
     const uint32_t g = blockIdx.x;
-    uint32_t t = 0;
-    while (t + 1 < batch.count && g >= batch.t[t + 1].wg_begin) ++t;
-    fast_block<DT, SO, LOW>(batch.t[t], g - batch.t[t].wg_begin, sh, err);
+    if constexpr (SLOTS) {
+        const DecSlots &S = batch.slots;
+        const uint64_t slot = S.slot_ids[g];
+        if (slot >= S.n_slots) {
+            if (threadIdx.x == 0) report(err, ZX_E_CORRUPT);
+            return;
+        }
+        DecTensor T = batch.t[0];
+        T.signmant += slot * S.sm_bytes;
+        T.stream += slot * S.stream_words;
+        T.block_bitoff += 2 * slot;
+        T.block_seg += 2 * slot;
+        T.seg_desc += 2 * slot * S.seg_stride;
+        T.gaps += slot * S.seg_stride * kSegChunks;
+        T.lengths += slot * S.alphabet;
+        T.degenerate += slot;
+        T.out = static_cast<uint8_t *>(T.out) + (uint64_t)g * S.out_bytes;
+        fast_block<DT, SO, LOW>(T, 0, sh, err);
+    } else {
+        uint32_t t = 0;
+        while (t + 1 < batch.count && g >= batch.t[t + 1].wg_begin) ++t;
+        fast_block<DT, SO, LOW>(batch.t[t], g - batch.t[t].wg_begin, sh, err);
+    }
 }
 
 __global__ __launch_bounds__(1024) void k_build_dtab(const uint8_t *__restrict__ lengths, uint32_t A, DTab *__restrict__ out)
@@ -1541,16 +1414,16 @@ static zx_status launch_fast(const zx_container *all, void *const *all_outs, con
     void (*kern)(const DecBatch, uint32_t *);
     if (per_block) {
         if (dt == ZX_E8M0)
-            kern = stream_out ? k_decode_fast_blocks<ZX_E8M0, true, true> : k_decode_fast_blocks<ZX_E8M0, false, true>;
+            kern = stream_out ? k_decode_fast_blocks<ZX_E8M0, true, true, false> : k_decode_fast_blocks<ZX_E8M0, false, true, false>;
         else if (dt == ZX_BF16)
-            kern = low ? (stream_out ? k_decode_fast_blocks<ZX_BF16, true, true> : k_decode_fast_blocks<ZX_BF16, false, true>)
-                       : (stream_out ? k_decode_fast_blocks<ZX_BF16, true, false>
-                                     : k_decode_fast_blocks<ZX_BF16, false, false>);
+            kern = low ? (stream_out ? k_decode_fast_blocks<ZX_BF16, true, true, false> : k_decode_fast_blocks<ZX_BF16, false, true, false>)
+                       : (stream_out ? k_decode_fast_blocks<ZX_BF16, true, false, false>
+                                     : k_decode_fast_blocks<ZX_BF16, false, false, false>);
         else
-            kern = low ? (stream_out ? k_decode_fast_blocks<ZX_FP8_E4M3FN, true, true>
-                                     : k_decode_fast_blocks<ZX_FP8_E4M3FN, false, true>)
-                       : (stream_out ? k_decode_fast_blocks<ZX_FP8_E4M3FN, true, false>
-                                     : k_decode_fast_blocks<ZX_FP8_E4M3FN, false, false>);
+            kern = low ? (stream_out ? k_decode_fast_blocks<ZX_FP8_E4M3FN, true, true, false>
+                                     : k_decode_fast_blocks<ZX_FP8_E4M3FN, false, true, false>)
+                       : (stream_out ? k_decode_fast_blocks<ZX_FP8_E4M3FN, true, false, false>
+                                     : k_decode_fast_blocks<ZX_FP8_E4M3FN, false, false, false>);
     } else {
         if (dt == ZX_E8M0)
             kern = stream_out ? k_decode_fast<ZX_E8M0, true, true> : k_decode_fast<ZX_E8M0, false, true>;
@@ -1635,10 +1508,16 @@ extern "C" zx_status zx_kv_decode_slots(const zx_kv_pool *pool, const uint32_t *
     batch.slots.out_bytes = pool->dtype == ZX_BF16 ? 2ull * kBlock : (uint64_t)kBlock;
     batch.slots.alphabet = sz.alphabet;
     batch.slots.n_slots = pool->n_slots;
-    if (pool->dtype == ZX_BF16)
-        hipLaunchKernelGGL((k_decode<ZX_BF16, true>), dim3(count), dim3(kDecThreads), 0, stream, batch, err);
-    else
-        hipLaunchKernelGGL((k_decode<ZX_FP8_E4M3FN, true>), dim3(count), dim3(kDecThreads), 0, stream, batch, err);
+    // a pool whose slots hold under 2.3 bits per element only has low-entropy blocks:
+    // the low-entropy mode; otherwise the ordinary one (whose spare stage takes any
+    // low-entropy segment)
+    const bool low = 10ull * 32ull * pool->cap_words < 23ull * kBlock;
+    void (*kern)(const DecBatch, uint32_t *) =
+        pool->dtype == ZX_BF16 ? (low ? k_decode_fast_blocks<ZX_BF16, false, true, true>
+                                      : k_decode_fast_blocks<ZX_BF16, false, false, true>)
+                               : (low ? k_decode_fast_blocks<ZX_FP8_E4M3FN, false, true, true>
+                                      : k_decode_fast_blocks<ZX_FP8_E4M3FN, false, false, true>);
+    hipLaunchKernelGGL(kern, dim3(count), dim3(kDecThreads), 0, stream, batch, err);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
 }
 
