@@ -26,8 +26,9 @@
 
 namespace zxk {
 
-constexpr int kDecWaves = 8;
+constexpr int kDecWaves = 8;                  // wavefronts per decode workgroup (at most)
 constexpr int kDecThreads = kDecWaves * kWave;
+constexpr int kMinDecWaves = 6;               // a per-tensor launch may use 6..8 (see the host)
 constexpr int kMaxBatch = 16;
 
 // Per-wavefront LDS: the lanes' stream words and the exponent stage.
@@ -1109,13 +1110,14 @@ struct FastShared {
 static_assert(sizeof(FastShared<false>) <= 160u * 1024u / kFastWgPerCu, "fast decode workgroup LDS budget");
 static_assert(sizeof(FastShared<true>) <= 160u * 1024u / kLowWgPerCu, "low-entropy decode workgroup LDS budget");
 
-// The segment loop of a fast-decode wavefront: its segments s0 + kDecWaves k, k < nk,
-// whose first descriptors (up to kFastMeta) are already in the wavefront's LDS copy
+// The segment loop of a fast-decode wavefront: its segments s0 + nw k, k < nk (nw:
+// the workgroup's wavefronts), whose first descriptors (up to kFastMeta) are already
+// in the wavefront's LDS copy
 // and whose first words were requested into `in`.  On return `in` holds the last
 // request (a dummy, or the words of a segment this wavefront does not decode).
 template <int DT, bool SO, bool LOW>
-__device__ __forceinline__ void fast_segment_loop(const DecTensor &T, FastShared<LOW> &sh, uint32_t wave, uint32_t s0,
-                                                  uint32_t nk, SegIn &in, uint32_t *err)
+__device__ __forceinline__ void fast_segment_loop(const DecTensor &T, FastShared<LOW> &sh, uint32_t wave, uint32_t nw,
+                                                  uint32_t s0, uint32_t nk, SegIn &in, uint32_t *err)
 {
     uint8_t *reg = sh.region[wave];
     uint32_t *sw = reinterpret_cast<uint32_t *>(reg);
@@ -1123,19 +1125,19 @@ __device__ __forceinline__ void fast_segment_loop(const DecTensor &T, FastShared
     for (uint32_t k = 0; k < nk; ++k) {
         set_priority_by_remaining(nk - k, nk);
         const uint32_t i = k & (kFastMeta - 1);
-        const uint32_t s = s0 + kDecWaves * k;
+        const uint32_t s = s0 + nw * k;
         const bool has_next = k + 1 < nk && i + 1 < kFastMeta;
         const SegMeta mu = meta_get(metas, i);
         const SegMeta mn = meta_get(metas, has_next ? i + 1 : i);
-        decode_segment_body<DT, SO, LOW>(T, sh.tab, reg, sw, s, mu, in, has_next, s + kDecWaves, mn, err, sh.spare,
+        decode_segment_body<DT, SO, LOW>(T, sh.tab, reg, sw, s, mu, in, has_next, s + nw, mn, err, sh.spare,
                                                &sh.lock);
         if (i == kFastMeta - 1 && k + 1 < nk) {
             // next group of 16 descriptors, and the words of its first segment (put
             // in at that segment's start)
             const uint32_t lane = lane_now();
             SegMeta m2;
-            load_meta(T, s + kDecWaves + kDecWaves * lane, lane < kFastMeta && k + 1 + lane < nk, m2);
-            issue_seg(T, s + kDecWaves, meta_at(m2, 0), lane, in, true);
+            load_meta(T, s + nw + nw * lane, lane < kFastMeta && k + 1 + lane < nk, m2);
+            issue_seg(T, s + nw, meta_at(m2, 0), lane, in, true);
             wave_sync();
             if (lane < kFastMeta) metas[lane] = m2;
             wave_sync();
@@ -1179,7 +1181,7 @@ __device__ __forceinline__ void fast_block(const DecTensor &T, uint32_t b, FastS
     if (lane < kFastMeta) sh.meta[wave][lane] = mine;
     if (tid == 0) sh.lock = 0;
     __syncthreads();
-    fast_segment_loop<DT, SO, LOW>(T, sh, wave, s0, nk, in, err);
+    fast_segment_loop<DT, SO, LOW>(T, sh, wave, kDecWaves, s0, nk, in, err);
     asm volatile("" ::"v"(in.rv.x), "v"(in.rtail), "v"(in.gap), "v"(in.gapn));
 }
 
@@ -1196,38 +1198,39 @@ __global__ __launch_bounds__(kDecThreads, (LOW ? kLowWgPerCu : kFastWgPerCu) * k
     const uint32_t lg = g - T.wg_begin;
     const uint32_t tid = threadIdx.x;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint32_t nw = __builtin_amdgcn_readfirstlane(blockDim.x / kWave);   // kMinDecWaves..kDecWaves
     const uint32_t lane = lane_now();
     const uint32_t s_begin = lg * T.segs_per_wg;
     const uint32_t s_end = s_begin + T.segs_per_wg < T.nsegs ? s_begin + T.segs_per_wg : T.nsegs;
-    // the wavefront's segments are s_begin + wave + kDecWaves k, k < nk; lane i < 16
-    // loads the descriptor of the i-th (in groups of 16)
+    // the wavefront's segments are s_begin + wave + nw k, k < nk; lane i < 16 loads
+    // the descriptor of the i-th (in groups of 16)
     const uint32_t s0 = s_begin + wave;
-    const uint32_t nk = __builtin_amdgcn_readfirstlane(s0 < s_end ? (s_end - s0 + kDecWaves - 1) / kDecWaves : 0);
+    const uint32_t nk = __builtin_amdgcn_readfirstlane(s0 < s_end ? (s_end - s0 + nw - 1) / nw : 0);
     // the prepared table is requested first, the descriptors and first words next; the
     // table is stored to LDS once it arrives
     const uint4 *src = reinterpret_cast<const uint4 *>(T.dtab);
     uint4 *dst = reinterpret_cast<uint4 *>(&sh.tab);
     constexpr uint32_t kTabPieces = sizeof(DTab) / 16;
-    constexpr uint32_t kPer = (kTabPieces + kDecThreads - 1) / kDecThreads;
+    constexpr uint32_t kPer = (kTabPieces + kMinDecWaves * kWave - 1) / (kMinDecWaves * kWave);
     uint4 pc[kPer];
 #pragma unroll
     for (uint32_t k = 0; k < kPer; ++k) {
-        const uint32_t i = tid + k * kDecThreads;
+        const uint32_t i = tid + k * blockDim.x;
         pc[k] = i < kTabPieces ? src[i] : make_uint4(0, 0, 0, 0);
     }
     SegMeta mine;
-    load_meta(T, s0 + kDecWaves * lane, lane < kFastMeta && lane < nk, mine);
+    load_meta(T, s0 + nw * lane, lane < kFastMeta && lane < nk, mine);
     SegIn in;
     issue_seg(T, s0, meta_at(mine, 0), lane, in, nk != 0);
 #pragma unroll
     for (uint32_t k = 0; k < kPer; ++k) {
-        const uint32_t i = tid + k * kDecThreads;
+        const uint32_t i = tid + k * blockDim.x;
         if (i < kTabPieces) dst[i] = pc[k];
     }
     if (lane < kFastMeta) sh.meta[wave][lane] = mine;
     if (tid == 0) sh.lock = 0;
     __syncthreads();
-    fast_segment_loop<DT, SO, LOW>(T, sh, wave, s0, nk, in, err);
+    fast_segment_loop<DT, SO, LOW>(T, sh, wave, nw, s0, nk, in, err);
     // the last request into `in` is used here, so that no load is left unused in flight
     asm volatile("" ::"v"(in.rv.x), "v"(in.rtail), "v"(in.gap), "v"(in.gapn));
 }
@@ -1363,6 +1366,21 @@ static zx_status launch_fast(const zx_container *all, void *const *all_outs, con
             given += 1;
         }
     }
+    // Per-tensor codebooks whose shares hold at most 8 segments per slot: workgroups of
+    // nw = 6..8 wavefronts, the fewest that give every wavefront one segment, so that
+    // the resident slots fill evenly (BF16 4096 x 4096: 768 workgroups of 7 instead of
+    // 672 of 8, which left 160 CUs with three workgroups and 96 with two).  Larger
+    // shares take 8 and loop.
+    uint32_t nw = kDecWaves;
+    if (!per_block) {
+        uint64_t need = kMinDecWaves;
+        for (uint32_t i = 0; i < count; ++i) {
+            if (cs[i].n == 0) continue;
+            const uint64_t q = (cs[i].nsegs + share[i] - 1) / share[i];
+            if (q > need) need = q;
+        }
+        if (need <= kDecWaves) nw = (uint32_t)need;
+    }
     DecBatch batch;
     memset(&batch, 0, sizeof(batch));
     uint32_t wg = 0;
@@ -1392,9 +1410,9 @@ static zx_status launch_fast(const zx_container *all, void *const *all_outs, con
             T.wg_count = T.nblocks;   // one workgroup per block
             T.segs_per_wg = 0;
         } else {
-            // at least one wavefront's worth of segments per workgroup
+            // at least one segment per wavefront of the workgroup
             uint64_t want = share[i];
-            const uint64_t cap = (c.nsegs + kDecWaves - 1) / kDecWaves;
+            const uint64_t cap = (c.nsegs + nw - 1) / nw;
             if (want > cap) want = cap;
             if (want == 0) want = 1;
             T.segs_per_wg = (uint32_t)((c.nsegs + want - 1) / want);
@@ -1435,7 +1453,7 @@ static zx_status launch_fast(const zx_container *all, void *const *all_outs, con
                        : (stream_out ? k_decode_fast<ZX_FP8_E4M3FN, true, false>
                                      : k_decode_fast<ZX_FP8_E4M3FN, false, false>);
     }
-    hipLaunchKernelGGL(kern, dim3(wg), dim3(kDecThreads), 0, stream, batch, err);
+    hipLaunchKernelGGL(kern, dim3(wg), dim3(nw * kWave), 0, stream, batch, err);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
 }
 
