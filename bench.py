@@ -97,7 +97,7 @@ WORKLOAD_SLUG = {"c1": "bf16_1024x1024", "c2": "bf16_4096x4096", "c3": "llama3_8
 
 def decode_kernel_name(cs) -> str:
     """Which decode kernel the library launches for a batch of containers (the same
-    rule as its host code: per-block codebooks take k_decode; a batch with a container
+    rule as its host code: per-block codebooks take k_decode_fast_blocks; a batch with a container
     under 2.3 bits per code, or of E8M0 scales, takes the fast decode's low-entropy mode)."""
     cs = [c for c in cs if c.n]
     if any(c.per_block for c in cs):

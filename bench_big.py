@@ -293,7 +293,7 @@ def run_overlap(args):
             t_pipe = timed(pipelined)
             # the share of the (uncapped) decode time that no longer adds to the layer time
             hidden = (t_dec + t_mm - t_pipe) / t_dec if t_dec > 0 else 0.0
-            row["pipelined"].append({"decode_workgroups": wgs or "default (2 per CU)", "ms": round(t_pipe, 4),
+            row["pipelined"].append({"decode_workgroups": wgs or "default (all resident slots)", "ms": round(t_pipe, 4),
                                      "hidden_frac": round(hidden, 3)})
         pipe.max_workgroups = 0
         row["hidden_frac"] = max(p["hidden_frac"] for p in row["pipelined"])

@@ -223,7 +223,7 @@ zx_status zx_decode_block_batch(const zx_container *cs, void *const *outs, uint3
                                 uint32_t *err, hipStream_t stream);
 
 /* zx_decode_block_batch with the per-tensor-codebook decode spread over at most
- * max_workgroups resident workgroups (0: two per CU, as zx_decode_block_batch).  For
+ * max_workgroups resident workgroups (0: all resident slots, as zx_decode_block_batch).  For
  * decoding the next layer while the current layer's GEMMs run on another stream
  * (DFloat11 article, 方法介绍: block-level decode into a temporary buffer): fewer
  * decode workgroups leave CUs, and their LDS, to the GEMM.  Containers with

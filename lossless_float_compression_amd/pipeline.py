@@ -46,7 +46,7 @@ class LayerPipeline:
         self.layers = [list(layer) for layer in layers]
         self.depth = depth
         self.err = err
-        self.max_workgroups = int(max_workgroups)   # 0: the decode's default (two per CU)
+        self.max_workgroups = int(max_workgroups)   # 0: the decode's default (all resident slots)
         self.side = torch.cuda.Stream()   # default priority
         self.bufs: List[List[torch.Tensor]] = [[_zx.empty_output(c) for c in layers[0]] for _ in range(depth)]
         # the containers (and the scratch buffers just allocated) were produced on the
