@@ -295,6 +295,16 @@ zx_status zx_kv_encode_slots(const zx_kv_pool *pool, const void *src, uint32_t n
                              const uint32_t *slot_ids, uint32_t max_len, void *workspace,
                              size_t ws_bytes, uint32_t *status, uint32_t *err, hipStream_t stream);
 
+/* zx_kv_encode_slots in one launch and without a workspace: each block's workgroup
+ * builds its histogram, its code lengths (same tie rules and limits) and its size
+ * from the block it holds, then encodes it into its slot (ZipFloat page, 4.2: online
+ * compression of new entries into preallocated slots; DFloat11, 方法介绍: the tree from
+ * the exponent distribution).  Same arguments, statuses and bytes as
+ * zx_kv_encode_slots, with no workspace; ZX_E_CODEBOOK for max_len out of range. */
+zx_status zx_kv_encode_slots_fused(const zx_kv_pool *pool, const void *src, uint32_t nblk,
+                                   const uint32_t *slot_ids, uint32_t max_len, uint32_t *status,
+                                   uint32_t *err, hipStream_t stream);
+
 /* zx_kv_encode_slots for callers that cannot allocate (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the same work with no
  * workspace argument.  The workspace is a file-scope device array of the library,

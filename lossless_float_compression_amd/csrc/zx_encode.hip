@@ -746,6 +746,122 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_slots(KvSlots P, const v
     if (tid == 0) status[j] = s_bad ? ZX_E_CODEBOOK : ZX_OK;
 }
 
+// The same append in one launch, with no workspace: each workgroup builds its block's
+// histogram from the input it holds in registers (32 lane copies in the symbol buffer,
+// which the split overwrites later), its code lengths in one wavefront (the codebook's
+// LDS in the stage, which the rounds overwrite later), and its bits and segment count,
+// then encodes exactly as k_encode_slots.
+constexpr uint32_t kFusedHistCopies = 32;
+
+template <int DT>
+__device__ __forceinline__ uint32_t block_exp(const BlockIn<DT> &x, uint32_t r, uint32_t e)
+{
+    if constexpr (DT == ZX_BF16) return (x.w[r][e >> 1] >> (16 * (e & 1) + 7)) & 0xFFu;
+    return (x.w[r][e >> 2] >> (8 * (e & 3) + 3)) & 0xFu;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kEncThreads) void k_encode_slots_fused(KvSlots P, const void *__restrict__ src,
+                                                                    const uint32_t *__restrict__ slot_ids, uint32_t max_len,
+                                                                    uint32_t *__restrict__ status, uint32_t *__restrict__ err)
+{
+    constexpr uint32_t A = alphabet_of(DT);
+    constexpr uint32_t kSmBytes = DT == ZX_BF16 ? kBlock : kBlock / 2;
+    __shared__ Canon c;
+    __shared__ __align__(16) uint32_t stage[kStageWords];
+    __shared__ uint32_t s_bad;
+    __shared__ uint8_t gapbuf[kOnePassChunks];
+    __shared__ uint32_t segbuf[kOnePassSegs];
+    __shared__ uint32_t part2[2][kEncThreads / kWave];
+    __shared__ __align__(16) uint8_t symbuf[kBlock];
+    __shared__ uint2 ctab[256];
+    __shared__ uint8_t lenbuf[256];
+    __shared__ uint16_t degbuf;
+    static_assert(sizeof(CodebookLds<uint32_t>) <= sizeof(stage), "the codebook's LDS fits the stage");
+    static_assert(kFusedHistCopies * (A + 1) * 4 <= kBlock, "the histogram copies fit the symbol buffer");
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid % kWave;
+    const uint32_t wave = tid / kWave;
+    const uint64_t j = blockIdx.x;
+    BlockIn<DT> x;
+    load_block_in<DT>(src, j * kBlock, true, nullptr, x);
+    const uint32_t slot = slot_ids[j];
+    // histogram: lane l counts into copy l % 32 (stride A + 1: lanes l and l + 32 share
+    // a copy, and the banks of one instruction's atomics differ but for those pairs)
+    uint32_t *h = reinterpret_cast<uint32_t *>(symbuf);
+    for (uint32_t i = tid; i < kFusedHistCopies * (A + 1); i += kEncThreads) h[i] = 0;
+    __syncthreads();
+    uint32_t *mine = h + (lane % kFusedHistCopies) * (A + 1);
+#pragma unroll
+    for (uint32_t r = 0; r < kRoundsPerBlock; ++r) {
+#pragma unroll
+        for (uint32_t e = 0; e < kEncPerThread; ++e) atomicAdd(&mine[block_exp<DT>(x, r, e)], 1u);
+    }
+    __syncthreads();
+    CodebookLds<uint32_t> &L = *reinterpret_cast<CodebookLds<uint32_t> *>(stage);
+    if (tid < A) {
+        uint32_t t = 0;
+        for (uint32_t k = 0; k < kFusedHistCopies; ++k) t += h[k * (A + 1) + tid];
+        L.cnt[tid] = t;
+    }
+    __syncthreads();
+    if (wave == 0) codebook_wave<A, uint32_t>(L, max_len, lenbuf, &degbuf);
+    __syncthreads();
+    const uint32_t lsym = tid < A ? lenbuf[tid] : 0u;
+    // the block's bits: count x length summed over the workgroup
+    {
+        uint32_t tot;
+        wave_excl_scan(tid < A ? L.cnt[tid] * lsym : 0u, tot);
+        if (lane == 0) part2[0][wave] = tot;
+    }
+    __syncthreads();
+    uint32_t bits32 = 0;
+    for (uint32_t w = 0; w < kEncThreads / kWave; ++w) bits32 += part2[0][w];
+    const uint64_t bits = bits32;
+    const uint32_t nch = (uint32_t)((bits + kChunkBits - 1) / kChunkBits);
+    const uint32_t nsb = nch ? (nch + kSegChunks - 1) / kSegChunks : 1u;
+    const uint32_t degen = degbuf;
+    canon_build_from(lsym, A, c);   // (its barriers also end every read of the codebook's LDS)
+    if (slot >= P.n_slots) {
+        if (tid == 0) {
+            status[j] = ZX_E_INVAL;
+            report(err, ZX_E_INVAL);
+        }
+        return;
+    }
+    if (bits > P.cap_bits || nsb > P.max_segs) {
+        // the block does not fit: the slot is left holding no segments
+        if (tid == 0) {
+            P.block_bitoff[2 * (uint64_t)slot] = 0;
+            P.block_bitoff[2 * (uint64_t)slot + 1] = 0;
+            P.block_seg[2 * (uint64_t)slot] = 0;
+            P.block_seg[2 * (uint64_t)slot + 1] = 0;
+            status[j] = ZX_E_NOSPACE;
+            report(err, ZX_E_NOSPACE);
+        }
+        return;
+    }
+    uint8_t *sm = P.signmant + (uint64_t)slot * kSmBytes;
+    uint32_t *st = P.stream + (uint64_t)slot * P.stream_words;
+    uint8_t *gp = P.gaps + (uint64_t)slot * P.seg_stride * kSegChunks;
+    uint32_t *sd = P.seg_desc + (uint64_t)slot * P.seg_stride * 2;
+    if (tid < A) P.lengths[(uint64_t)slot * A + tid] = (uint8_t)lsym;
+    if (tid == 0) {
+        P.degenerate[slot] = (uint16_t)degen;
+        P.block_bitoff[2 * (uint64_t)slot] = 0;
+        P.block_bitoff[2 * (uint64_t)slot + 1] = bits;
+        P.block_seg[2 * (uint64_t)slot] = 0;
+        P.block_seg[2 * (uint64_t)slot + 1] = nsb;
+    }
+    encode_onepass<DT>(x, 0, 0, c, degen, 0, (uint32_t)bits, 0, nsb, nch, ~0ull, ~0ull, sm, st, sd, gp, err, stage, symbuf,
+                       ctab, gapbuf, segbuf, part2, s_bad);
+    // the rest of the slot's stream, padding included, is zero
+    const uint32_t nw = (uint32_t)((bits + 31) / 32);
+    for (uint64_t w = nw + tid; w < P.stream_words; w += kEncThreads) st[w] = 0;
+    if (tid == 0) status[j] = s_bad ? ZX_E_CODEBOOK : ZX_OK;
+}
+
 // -------------------------------------------------------------------- planning
 // Everything a per-tensor-codebook encode needs before its outputs can be sized, in
 // one workgroup after the block histograms: the tensor histogram (the sum of the
@@ -1170,6 +1286,40 @@ extern "C" zx_status zx_kv_encode_slots(const zx_kv_pool *pool, const void *src,
     else
         hipLaunchKernelGGL(k_encode_slots<ZX_FP8_E4M3FN>, dim3(nblk), dim3(kEncThreads), 0, stream, P, src, slot_ids, len, deg,
                            bits, nseg, status, err);
+    return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}
+
+extern "C" zx_status zx_kv_encode_slots_fused(const zx_kv_pool *pool, const void *src, uint32_t nblk,
+                                              const uint32_t *slot_ids, uint32_t max_len, uint32_t *status, uint32_t *err,
+                                              hipStream_t stream)
+{
+    if (pool && pool->dtype != ZX_BF16 && pool->dtype != ZX_FP8_E4M3FN) return ZX_E_UNSUPPORTED;
+    zx_kv_sizes sz;
+    if (!kv_pool_ok(pool, &sz)) return ZX_E_INVAL;
+    const uint32_t A = alphabet_of(pool->dtype);
+    if (max_len < (A == 256 ? 8u : 4u) || max_len > kMaxLen) return ZX_E_CODEBOOK;
+    if (nblk == 0) return ZX_OK;
+    if (!src || !slot_ids || !status || !aligned16(src) || nblk > 0x7FFFFFFFu) return ZX_E_INVAL;
+    KvSlots P;
+    P.signmant = pool->signmant;
+    P.stream = pool->stream;
+    P.gaps = pool->gaps;
+    P.seg_desc = pool->seg_desc;
+    P.lengths = pool->lengths;
+    P.degenerate = pool->degenerate;
+    P.block_bitoff = pool->block_bitoff;
+    P.block_seg = pool->block_seg;
+    P.n_slots = pool->n_slots;
+    P.cap_bits = pool->cap_words * 32;
+    P.max_segs = sz.max_segs;
+    P.seg_stride = sz.seg_stride;
+    P.stream_words = sz.stream_words;
+    if (pool->dtype == ZX_BF16)
+        hipLaunchKernelGGL(k_encode_slots_fused<ZX_BF16>, dim3(nblk), dim3(kEncThreads), 0, stream, P, src, slot_ids, max_len,
+                           status, err);
+    else
+        hipLaunchKernelGGL(k_encode_slots_fused<ZX_FP8_E4M3FN>, dim3(nblk), dim3(kEncThreads), 0, stream, P, src, slot_ids,
+                           max_len, status, err);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
 }
 

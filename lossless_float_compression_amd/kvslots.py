@@ -91,11 +91,16 @@ class KVSlotPool:
         return self._ws
 
     def append(self, blocks: torch.Tensor, slot_ids: torch.Tensor, status: Optional[torch.Tensor] = None,
-               err: Optional[torch.Tensor] = None, max_len: int = 32, stream=None, noalloc: bool = False) -> torch.Tensor:
+               err: Optional[torch.Tensor] = None, max_len: int = 32, stream=None, noalloc: bool = False,
+               fused: bool = True) -> torch.Tensor:
         """Compress `blocks` (k * 65536 elements, contiguous; bf16/int16 for a BF16
         pool, float8_e4m3fn/uint8 for FP8) into slots `slot_ids` (device int32 [k],
         distinct).  Returns the per-block status (device int32 [k]: 0, or 6 when the
-        block did not fit and its slot was left empty).  Nothing waits for the GPU."""
+        block did not fit and its slot was left empty).  Nothing waits for the GPU.
+        By default one launch builds each block's histogram, codebook and stream
+        (zx_kv_encode_slots_fused); fused=False takes the separate histogram, codebook
+        and size launches with a workspace (zx_kv_encode_slots), noalloc=True those
+        launches with the library's fixed scratch.  All three write the same bytes."""
         dt, flat = _zx._as_bits(blocks)
         if dt != self.dtype:
             raise TypeError("blocks have another dtype than the pool")
@@ -114,6 +119,12 @@ class KVSlotPool:
                                                       int(max_len), _zx._ptr(status), _zx._ptr(err), _zx._stream(stream))
             if st != 0:
                 raise _zx.ZxError("zx_kv_encode_slots_noalloc", st)
+            return status
+        if fused:
+            st = _zx.lib().zx_kv_encode_slots_fused(C.byref(self.pool), _zx._ptr(flat), k, _zx._ptr(slot_ids),
+                                                    int(max_len), _zx._ptr(status), _zx._ptr(err), _zx._stream(stream))
+            if st != 0:
+                raise _zx.ZxError("zx_kv_encode_slots_fused", st)
             return status
         ws = self.workspace(k)
         st = _zx.lib().zx_kv_encode_slots(C.byref(self.pool), _zx._ptr(flat), k, _zx._ptr(slot_ids), int(max_len),

@@ -80,7 +80,7 @@ EXPORTS = ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "
            "zx_status_string", "zx_version", "zx_kv_slot_sizes", "zx_kv_workspace_bytes", "zx_kv_encode_slots",
            "zx_kv_slot_container", "zx_kv_decode_slots", "zx_zf_scan_workspace_bytes", "zx_zf_encode_size",
            "zx_zf_encode", "zx_zf_decode", "zx_histogram_accumulate", "zx_build_codebook_u64",
-           "zx_kv_encode_slots_noalloc", "zx_encode_plan")
+           "zx_kv_encode_slots_noalloc", "zx_encode_plan", "zx_kv_encode_slots_fused")
 
 
 def lib():
@@ -112,6 +112,7 @@ def lib():
         L.zx_kv_workspace_bytes.restype = C.c_size_t
         L.zx_kv_encode_slots.argtypes = [C.POINTER(zx_kv_pool), P, U32, P, U32, P, C.c_size_t, P, P, P]
         L.zx_kv_encode_slots_noalloc.argtypes = [C.POINTER(zx_kv_pool), P, U32, P, U32, P, P, P]
+        L.zx_kv_encode_slots_fused.argtypes = [C.POINTER(zx_kv_pool), P, U32, P, U32, P, P, P]
         L.zx_kv_slot_container.argtypes = [C.POINTER(zx_kv_pool), U32, C.POINTER(zx_container)]
         L.zx_kv_decode_slots.argtypes = [C.POINTER(zx_kv_pool), P, U32, P, P, P]
         L.zx_zf_scan_workspace_bytes.argtypes = [U64]
@@ -126,7 +127,7 @@ def lib():
                   "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_kv_slot_sizes",
                   "zx_kv_encode_slots", "zx_kv_slot_container", "zx_kv_decode_slots", "zx_zf_encode_size",
                   "zx_zf_encode", "zx_zf_decode", "zx_histogram_accumulate", "zx_build_codebook_u64",
-                  "zx_kv_encode_slots_noalloc", "zx_encode_plan"):
+                  "zx_kv_encode_slots_noalloc", "zx_encode_plan", "zx_kv_encode_slots_fused"):
             getattr(L, f).restype = I
         _lib = L
     return _lib

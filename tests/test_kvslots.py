@@ -223,3 +223,50 @@ def test_fp8_slots():
     y = pool.decode(slots)
     assert torch.equal(y.view(torch.uint8), x)
     assert torch.equal(pool.decode_containers(slots).view(torch.uint8), x)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,max_len", [(zx.BF16, 32), (zx.BF16, 12), (zx.FP8_E4M3FN, 15), (zx.FP8_E4M3FN, 6)])
+def test_fused_append_equals_workspace_append(dtype, max_len):
+    """zx_kv_encode_slots_fused (one launch: each block's histogram, codebook and size
+    in its workgroup) against zx_kv_encode_slots (separate launches, workspace): every
+    pool array, status and error word equal.  The blocks include ones that do not fit
+    their slot, a one-symbol block, and a slot id past the pool; max_len 12 / 6 force
+    length-limited codes."""
+    import workloads
+    say("kv fused append", dtype, max_len)
+    g = torch.Generator(device="cuda").manual_seed(17)
+    if dtype == zx.BF16:
+        x = torch.cat([kv_blocks(0, 4), kv_blocks(1, 9)[:2]])                           # 10 blocks, ~2.9 bits
+        one = torch.full((1, BLOCK), 0x3C00, dtype=torch.int16, device="cuda")
+        noise = torch.randint(-32768, 32767, (1, BLOCK), generator=g, device="cuda", dtype=torch.int32).to(torch.int16)
+    else:
+        q, _ = workloads.c4(device="cuda")
+        x = q.reshape(-1)[:10 * BLOCK].reshape(10, BLOCK)                                  # ~2.6 bits
+        one = torch.full((1, BLOCK), 0x38, dtype=torch.uint8, device="cuda")
+        noise = torch.randint(0, 255, (1, BLOCK), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+    blocks = torch.cat([x, noise, one]).contiguous()   # noise: 4+ bits per element, past any 3-bit slot
+    pools = [KVSlotPool(16, dtype=dtype, cap_words=6144) for _ in range(2)]
+    for p in pools:
+        for f in ("signmant", "stream", "gaps", "seg_desc", "lengths", "degenerate", "block_bitoff", "block_seg"):
+            getattr(p, f).zero_()
+    slots = torch.tensor([15, 3, 7, 0, 12, 9, 1, 4, 16, 2, 11, 6], dtype=torch.int32, device="cuda")   # 16: past the pool
+    errs = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(2)]
+    st_ws = pools[0].append(blocks, slots, err=errs[0], max_len=max_len, fused=False)
+    st_fu = pools[1].append(blocks, slots, err=errs[1], max_len=max_len)
+    torch.cuda.synchronize()
+    assert st_ws.tolist() == st_fu.tolist()
+    assert st_fu.tolist()[8] == 1 and st_fu.tolist()[10] == 6 and st_fu.tolist()[11] == 0   # bad id, noise, one symbol
+    assert st_fu.tolist().count(0) >= 6
+    # the error word keeps the first report, and the order in which workgroups report
+    # is not fixed: each holds one of the statuses reported
+    reported = {v for v in st_fu.tolist() if v}
+    assert int(errs[0].item()) in reported and int(errs[1].item()) in reported
+    for f in ("signmant", "stream", "gaps", "seg_desc", "lengths", "degenerate", "block_bitoff", "block_seg"):
+        assert torch.equal(getattr(pools[0], f), getattr(pools[1], f)), f
+    ok = [int(s) for s, st in zip(slots.tolist(), st_fu.tolist()) if st == 0]
+    y = pools[1].decode(ok)
+    torch.cuda.synchronize()
+    rows = [slots.tolist().index(s) for s in ok]
+    assert torch.equal(y.reshape(len(ok), -1).view(blocks.dtype if blocks.dtype != torch.bfloat16 else torch.int16),
+                       blocks[rows])

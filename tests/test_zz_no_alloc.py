@@ -65,7 +65,7 @@ def test_noalloc_append_equals_workspace_append(dtype):
         ids = rng.choice([s for s in range(n_slots) if s not in used], size=k, replace=False)
         used += ids.tolist()
         sid = torch.tensor(ids, dtype=torch.int32, device="cuda")
-        st_a = a.append(blocks, sid, err=err_a)
+        st_a = a.append(blocks, sid, err=err_a, fused=False)   # zx_kv_encode_slots, with a workspace
         st_b = b.append(blocks, sid, err=err_b, noalloc=True)
         torch.cuda.synchronize()
         assert torch.equal(st_a, st_b)
