@@ -11,6 +11,8 @@ zx_encode, zx_build_decode_table, zx_decode, zx_decode_block_batch).  `compress`
 from __future__ import annotations
 
 import ctypes as C
+import itertools
+import threading
 import os
 from dataclasses import dataclass
 from typing import List, Optional, Sequence
@@ -397,8 +399,9 @@ def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_sc
     return c
 
 
-_plan_tag = [0]
+_plan_tags = itertools.count(1)   # next() is atomic: concurrent compress() calls get distinct tags
 _plan_ring = {}   # device index -> pinned int64 [_PLAN_SLOTS, 4]: where zx_encode_plan publishes the totals
+_plan_ring_lock = threading.Lock()
 _PLAN_SLOTS = 256
 
 
@@ -407,9 +410,11 @@ def _plan_slot(dev):
     each call's unique tag tells its own publication from an older one)."""
     ring = _plan_ring.get(dev.index)
     if ring is None:
-        ring = _plan_ring[dev.index] = torch.full((_PLAN_SLOTS, 4), -1, dtype=torch.int64, pin_memory=True)
-    _plan_tag[0] += 1
-    tag = _plan_tag[0]
+        with _plan_ring_lock:
+            ring = _plan_ring.get(dev.index)
+            if ring is None:
+                ring = _plan_ring[dev.index] = torch.full((_PLAN_SLOTS, 4), -1, dtype=torch.int64, pin_memory=True)
+    tag = next(_plan_tags)
     return ring[tag % _PLAN_SLOTS], tag
 
 
