@@ -11,8 +11,11 @@
 // scanned into block offsets, and inside a block each round of 2048 elements scans
 // its per-thread code lengths.  Codes are ORed into an LDS staging area aligned to
 // global stream words; whole words are then written with plain stores.  The only
-// words two blocks can share are a block's first and last word; those are cleared
-// beforehand and combined with atomicOr, which gives the same bytes in any order.
+// words two blocks can share are a block's first and last word.  Each block owns the
+// stream bits from its first bit up to the next block's (the last block: up to the end
+// of the stream, padding included) and sets exactly those bits of a shared word with
+// two atomics (clear its bits, then OR its code bits in); the owners' bits are disjoint
+// and cover the word, so the word ends the same in any order, whatever it held before.
 #include <mutex>
 
 #include "zx_codebook.h"
@@ -160,20 +163,37 @@ __global__ __launch_bounds__(1024) void k_scan_blocks(uint64_t nblocks, uint64_t
     }
 }
 
-// Clear every stream word two blocks may share, and the tail padding.
-__global__ void k_clear_shared_words(uint64_t nblocks, const uint64_t *__restrict__ block_bitoff, uint64_t total_bits,
-                                     uint64_t stream_words, uint32_t *__restrict__ stream)
+// The stream of an empty tensor: padding only, all zero.
+__global__ void k_zero_stream(uint64_t stream_words, uint32_t *__restrict__ stream)
 {
-    const uint64_t i = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x;
-    if (i < nblocks) {
-        const uint64_t g0 = block_bitoff[i], g1 = block_bitoff[i + 1];
-        if (g1 > g0 && g1 <= total_bits) {
-            stream[g0 >> 5] = 0;
-            stream[(g1 - 1) >> 5] = 0;
-        }
+    for (uint64_t w = blockIdx.x * (uint64_t)blockDim.x + threadIdx.x; w < stream_words; w += (uint64_t)gridDim.x * blockDim.x)
+        stream[w] = 0;
+}
+
+// Stream word gw gets value v in the bits a block owns, global stream bits [own_lo,
+// own_hi) (bit 0 of a word is its most significant): a plain store when it owns the
+// whole word, otherwise its bits cleared and then ORed in, so that the other owner of
+// the word may do the same at any time.
+__device__ __forceinline__ void put_word(uint32_t *stream, uint64_t gw, uint32_t v, uint64_t own_lo, uint64_t own_hi)
+{
+    const uint64_t wb = gw * 32;
+    const uint32_t lo = own_lo > wb ? (uint32_t)(own_lo - wb) : 0u;              // < 32
+    const uint32_t hi = own_hi >= wb + 32 ? 32u : (uint32_t)(own_hi - wb);      // > lo
+    if (lo == 0 && hi == 32) {
+        stream[gw] = v;
+        return;
     }
-    const uint64_t tail = total_bits >> 5;
-    for (uint64_t w = tail + i; w < stream_words; w += (uint64_t)gridDim.x * blockDim.x) stream[w] = 0;
+    const uint32_t m = (0xFFFFFFFFu >> lo) & (hi == 32 ? 0xFFFFFFFFu : ~(0xFFFFFFFFu >> hi));
+    atomicAnd(&stream[gw], ~m);
+    atomicOr(&stream[gw], v & m);
+}
+
+// The last block of a stream also owns the words after its own, up to the stream's
+// end (its padding): they are cleared (the first of them only from the block's end on,
+// when the block ends inside it).
+__device__ __forceinline__ void zero_stream_tail(uint32_t *stream, uint64_t from_word, uint64_t zero_to, uint64_t own_lo)
+{
+    for (uint64_t w = from_word + threadIdx.x; w < zero_to; w += kEncThreads) put_word(stream, w, 0u, own_lo, ~0ull);
 }
 
 // -------------------------------------------------------------------- bit packing
@@ -231,7 +251,7 @@ __device__ __forceinline__ void load_block_in(const void *__restrict__ in, uint6
 template <int DT>
 __device__ __forceinline__ void encode_onepass(const BlockIn<DT> &x, uint64_t lo, uint64_t b, const Canon &c,
                                                uint32_t degen, uint64_t G, uint32_t bits, uint32_t s0, uint32_t nsb, uint32_t nch,
-                                               uint64_t w_first, uint64_t w_last, uint8_t *__restrict__ signmant,
+                                               uint64_t own_hi, uint64_t zero_to, uint8_t *__restrict__ signmant,
                                                uint32_t *__restrict__ stream, uint32_t *__restrict__ seg_desc,
                                                uint8_t *__restrict__ gaps, uint32_t *__restrict__ err, uint32_t *stage,
                                                uint8_t *symbuf, uint2 *ctab, uint8_t *gapbuf, uint32_t *segbuf,
@@ -403,13 +423,8 @@ __device__ __forceinline__ void encode_onepass(const BlockIn<DT> &x, uint64_t lo
     // ---- all stores
     const uint64_t W0 = G >> 5;
     const uint32_t nw = bits ? (a0 + bits + 31) >> 5 : 0;
-    for (uint32_t i = tid; i < nw; i += kEncThreads) {
-        const uint64_t gw = W0 + i;
-        if (gw == w_first || gw == w_last)
-            atomicOr(&stream[gw], stage[i]);
-        else
-            stream[gw] = stage[i];
-    }
+    for (uint32_t i = tid; i < nw; i += kEncThreads) put_word(stream, W0 + i, stage[i], G, own_hi);
+    if (zero_to) zero_stream_tail(stream, W0 + nw, zero_to, G);
     for (uint32_t ch = tid; ch < nsb * kSegChunks; ch += kEncThreads)
         gaps[(uint64_t)s0 * kSegChunks + ch] = ch < nch ? gapbuf[ch] : (uint8_t)ZX_NO_GAP;
     for (uint32_t j = tid; j < nsb; j += kEncThreads) {
@@ -427,7 +442,8 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
                                                         const uint32_t *__restrict__ block_seg,
                                                         uint8_t *__restrict__ signmant, uint32_t *__restrict__ stream,
                                                         uint32_t *__restrict__ seg_desc, uint8_t *__restrict__ gaps,
-                                                        uint64_t total_bits, uint64_t nsegs, uint32_t *__restrict__ err)
+                                                        uint64_t total_bits, uint64_t nsegs, uint64_t stream_words,
+                                                        uint32_t *__restrict__ err)
 {
     constexpr uint32_t A = alphabet_of(DT);
     __shared__ Canon c;
@@ -463,10 +479,13 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
         if (tid == 0) report(err, ZX_E_CORRUPT);
         return;
     }
-    const uint64_t w_first = G >> 5;
-    const uint64_t w_last = bits ? (G + bits - 1) >> 5 : w_first;
+    // the stream bits this block owns: up to the next block's first, or for the last
+    // block to the end of the stream, padding included
+    const bool last = lo + kBlock >= n;
+    const uint64_t own_hi = last ? ~0ull : G + bits;
+    const uint64_t zero_to = last ? stream_words : 0ull;
     if (nb == kBlock && (G & 31) + bits <= kOnePassBits) {
-        encode_onepass<DT>(x, lo, b, c, degen, G, (uint32_t)bits, s0, nsb, nch, w_first, w_last, signmant, stream, seg_desc,
+        encode_onepass<DT>(x, lo, b, c, degen, G, (uint32_t)bits, s0, nsb, nch, own_hi, zero_to, signmant, stream, seg_desc,
                            gaps, err, stage, symbuf, ctab, gapbuf, segbuf, part2, s_bad);
         return;
     }
@@ -632,14 +651,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
         __syncthreads();
         // ---- flush whole words, keep the partial last word as the next carry
         const uint32_t nw = (a0 + R) >> 5;
-        for (uint32_t i = tid; i < nw; i += kEncThreads) {
-            const uint64_t gw = W + i;
-            const uint32_t val = stage[i];
-            if (gw == w_first || gw == w_last)
-                atomicOr(&stream[gw], val);
-            else
-                stream[gw] = val;
-        }
+        for (uint32_t i = tid; i < nw; i += kEncThreads) put_word(stream, W + i, stage[i], G, own_hi);
         const uint32_t carry = stage[nw];
         __syncthreads();
         for (uint32_t i = tid; i < kStageWords; i += kEncThreads) stage[i] = (i == 0) ? carry : 0u;
@@ -648,7 +660,8 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
         a0 = (a0 + R) & 31;
         P += R;
     }
-    if (tid == 0 && bits && a0) atomicOr(&stream[W], stage[0]);
+    if (tid == 0 && bits && a0) put_word(stream, W, stage[0], G, own_hi);
+    if (zero_to) zero_stream_tail(stream, (bits && a0) ? W + 1 : W, zero_to, G);
     if (bad) s_bad = 1;
     __syncthreads();
     if (tid == 0 && s_bad) report(err, ZX_E_CODEBOOK);
@@ -738,7 +751,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_slots(KvSlots P, const v
         P.block_seg[2 * (uint64_t)slot + 1] = nsb;
     }
     const uint32_t nch = (uint32_t)((bits + kChunkBits - 1) / kChunkBits);
-    encode_onepass<DT>(x, 0, 0, c, degen, 0, (uint32_t)bits, 0, nsb, nch, ~0ull, ~0ull, sm, st, sd, gp, err, stage, symbuf,
+    encode_onepass<DT>(x, 0, 0, c, degen, 0, (uint32_t)bits, 0, nsb, nch, ~0ull, 0ull, sm, st, sd, gp, err, stage, symbuf,
                        ctab, gapbuf, segbuf, part2, s_bad);
     // the rest of the slot's stream, padding included, is zero
     const uint32_t nw = (uint32_t)((bits + 31) / 32);
@@ -854,7 +867,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_slots_fused(KvSlots P, c
         P.block_seg[2 * (uint64_t)slot] = 0;
         P.block_seg[2 * (uint64_t)slot + 1] = nsb;
     }
-    encode_onepass<DT>(x, 0, 0, c, degen, 0, (uint32_t)bits, 0, nsb, nch, ~0ull, ~0ull, sm, st, sd, gp, err, stage, symbuf,
+    encode_onepass<DT>(x, 0, 0, c, degen, 0, (uint32_t)bits, 0, nsb, nch, ~0ull, 0ull, sm, st, sd, gp, err, stage, symbuf,
                        ctab, gapbuf, segbuf, part2, s_bad);
     // the rest of the slot's stream, padding included, is zero
     const uint32_t nw = (uint32_t)((bits + 31) / 32);
@@ -1167,25 +1180,19 @@ extern "C" zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int p
     if (!aligned16(in) || !aligned16(signmant) || !aligned16(stream)) return ZX_E_INVAL;
     if (nsegs < nblocks) return ZX_E_INVAL;
     const uint64_t words = zx_stream_words(total_bits);
-    {
-        const uint32_t threads = 256;
-        uint64_t grid = (nblocks + threads - 1) / threads;
-        if (grid == 0) grid = 1;
-        if (grid > 65535) grid = 65535;
-        hipLaunchKernelGGL(k_clear_shared_words, dim3((uint32_t)grid), dim3(threads), 0, stream_, nblocks, block_bitoff, total_bits,
-                           words, stream);
-        if (hipGetLastError() != hipSuccess) return ZX_E_HIP;
+    if (nblocks == 0) {   // no block to clear the padding
+        hipLaunchKernelGGL(k_zero_stream, dim3(1), dim3(256), 0, stream_, words, stream);
+        return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
     }
-    if (nblocks == 0) return ZX_OK;
     if (dtype == ZX_BF16)
         hipLaunchKernelGGL(k_encode<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream_, in, n, per_block, lengths,
-                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, err);
+                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, words, err);
     else if (dtype == ZX_E8M0)
         hipLaunchKernelGGL(k_encode<ZX_E8M0>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream_, in, n, per_block, lengths,
-                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, err);
+                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, words, err);
     else
         hipLaunchKernelGGL(k_encode<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream_, in, n, per_block, lengths,
-                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, err);
+                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, words, err);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
 }
 
