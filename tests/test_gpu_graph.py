@@ -74,3 +74,39 @@ def test_single_and_per_block_decodes_in_one_graph(layer):
         zx.decompress(cs[0], out=outs[0], err=err)
         zx.decompress(cb, out=outs[1], err=err)
     replay_and_check(graph, [xs[0], x0], outs, err)
+
+
+def test_kv_append_and_slot_decode_in_a_graph():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lossless_float_compression_amd.kvslots import KVSlotPool
+    say("graph: K/V fused append + slot decode, new blocks before every replay")
+    k = 8
+    pool = KVSlotPool(32, zx.BF16, bits_per_elem=4.0)
+    slots = torch.arange(3, 3 + 2 * k, 2, dtype=torch.int32, device="cuda")
+    blocks = torch.empty((k, zx.BLOCK_ELEMS), dtype=torch.bfloat16, device="cuda")
+    status = torch.empty(k, dtype=torch.int32, device="cuda")
+    out = torch.empty((k, zx.BLOCK_ELEMS), dtype=torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(515)
+    blocks.copy_(torch.randn(blocks.shape, generator=g, device="cuda") * 0.5)
+    pool.append(blocks, slots, status=status, err=err)          # eager first
+    pool.decode(slots, out=out, err=err)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), blocks.view(torch.int16))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pool.append(blocks, slots, status=status, err=err)
+        pool.decode(slots, out=out, err=err)
+    for r in range(4):
+        # new K/V blocks (eager), then the captured append and decode
+        blocks.copy_(torch.randn(blocks.shape, generator=g, device="cuda") * (0.25 + r))
+        out.fill_(float("nan"))
+        status.fill_(-1)
+        err.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        assert torch.equal(status.cpu(), torch.zeros(k, dtype=torch.int32))
+        assert torch.equal(out.view(torch.int16), blocks.view(torch.int16))
