@@ -607,8 +607,9 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
         uint64_t acc = 0;
 #pragma unroll
         for (uint32_t k = 0; k < kEncPerThread; ++k) {
-            if (k >= have) break;
-            const uint32_t l = c.len[sym[k]];
+            // (elements past `have`, and symbols without a code, place nothing; the
+            // loop keeps a fixed trip count so that sym[] stays in registers)
+            const uint32_t l = k < have ? c.len[sym[k]] : 0u;
             if (l == 0) continue;
             const uint32_t cd = (p + kChunkBits - 1) / kChunkBits;   // first chunk boundary >= p
             if (cd * kChunkBits < p + l) {
