@@ -100,7 +100,17 @@ class KVSlotPool:
         By default one launch builds each block's histogram, codebook and stream
         (zx_kv_encode_slots_fused); fused=False takes the separate histogram, codebook
         and size launches with a workspace (zx_kv_encode_slots), noalloc=True those
-        launches with the library's fixed scratch.  All three write the same bytes."""
+        launches with the library's fixed scratch.  All three write the same bytes.
+        With a torch `stream` other than the current one, the append (and `status`,
+        when allocated here) runs on it after the work already enqueued on the current
+        stream, the producer of `blocks`.  Appends with fused=False share the pool's
+        workspace, and noalloc=True ones the device's scratch: such calls must not
+        overlap, on any stream."""
+        side = _zx._side_stream(stream)
+        if side is not None:
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                return self.append(blocks, slot_ids, status, err, max_len, None, noalloc, fused)
         dt, flat = _zx._as_bits(blocks)
         if dt != self.dtype:
             raise TypeError("blocks have another dtype than the pool")

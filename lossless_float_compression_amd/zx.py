@@ -337,9 +337,13 @@ def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_sc
     container's error word to ZX_E_CODEBOOK.
 
     `stream` (a torch stream; default the current one) carries every kernel, torch's
-    own fills and the synchronisation of the readback."""
-    if stream is not None:
-        with torch.cuda.stream(stream):
+    own fills and the synchronisation of the readback; a stream other than the current
+    one first waits for the work already enqueued on the current stream (the producer
+    of `x`)."""
+    side = _side_stream(stream)
+    if side is not None:
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
             return compress(x, per_block, max_len, fp8_scale, None, codebook)
     dtype, flat = _as_bits(x)
     if not flat.is_cuda:

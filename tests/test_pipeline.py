@@ -149,3 +149,39 @@ def test_decompress_rejects_wrong_outputs():
             zx.decompress(c, out=bad)
         with pytest.raises(ValueError):
             zx.decompress_batch([c], outs=[bad])
+
+
+@pytest.mark.gpu
+def test_side_stream_encodes_wait_for_the_producer_stream():
+    """compress(stream=side) and KVSlotPool.append(stream=side) read their input only
+    after what the current stream has queued: here the input itself is still being
+    written there, behind long matmuls."""
+    import lossless_float_compression_amd as zx
+    from lossless_float_compression_amd.kvslots import KVSlotPool
+    print("side-stream encodes wait for the producer", file=sys.stderr, flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(78)
+    x = (torch.randn((2000, 1000), generator=g, device="cuda") * 0.03).to(torch.bfloat16)
+    blocks = (torch.randn(3 * 65536, generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    a = torch.randn(4096, 4096, device="cuda")
+    b = torch.empty_like(a)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    for _ in range(6):
+        torch.mm(a, a, out=b)
+    x_late = x.clone()                       # written behind the matmuls
+    c = zx.compress(x_late, stream=side)
+    pool = KVSlotPool(4, zx.BF16, cap_words=8192)
+    for _ in range(6):
+        torch.mm(a, a, out=b)
+    blocks_late = blocks.clone()
+    ids = torch.tensor([3, 1, 0], dtype=torch.int32, device="cuda")
+    status = pool.append(blocks_late, ids, stream=side)
+    torch.cuda.synchronize()
+    assert int(c._err.item()) == 0
+    assert torch.equal(zx.decompress(c).view(torch.int16), x.view(torch.int16))
+    assert torch.equal(status.cpu(), torch.zeros(3, dtype=torch.int32))
+    rows = pool.decode(ids)
+    torch.cuda.synchronize()
+    assert torch.equal(rows.view(torch.int16), blocks.view(3, 65536).view(torch.int16))
