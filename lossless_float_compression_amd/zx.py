@@ -296,9 +296,12 @@ def build_shared_codebook(tensors, max_len: int = 32, stream=None) -> SharedCode
     """A model-wide codebook: the exponent counts of all `tensors` (any iterable, read
     once) summed in 64 bits (zx_histogram_accumulate), then one Huffman codebook and
     one decode table.  Everything runs on `stream` (a torch stream; default the
-    current one)."""
-    if stream is not None:
-        with torch.cuda.stream(stream):
+    current one), after the work already enqueued on the current stream (the producers
+    of the tensors) when it is another one."""
+    side = _side_stream(stream)
+    if side is not None:
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
             return build_shared_codebook(tensors, max_len, None)
     L = lib()
     s = _stream(None)
@@ -586,9 +589,13 @@ class ZfCompressed:
 def compress_zf(x: torch.Tensor, fp8_scale: Optional[float] = None, stream=None) -> ZfCompressed:
     """Encode a device tensor with the dominant-range codec: block parameters and
     record offsets, one 8-byte read of the record total, then planes and records.
-    Everything runs on `stream` (a torch stream; default the current one)."""
-    if stream is not None:
-        with torch.cuda.stream(stream):
+    Everything runs on `stream` (a torch stream; default the current one), after the
+    work already enqueued on the current stream (the producer of `x`) when it is
+    another one."""
+    side = _side_stream(stream)
+    if side is not None:
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
             return compress_zf(x, fp8_scale, None)
     dtype, flat = _as_bits(x)
     if dtype == E8M0:

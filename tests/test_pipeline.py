@@ -153,7 +153,8 @@ def test_decompress_rejects_wrong_outputs():
 
 @pytest.mark.gpu
 def test_side_stream_encodes_wait_for_the_producer_stream():
-    """compress(stream=side) and KVSlotPool.append(stream=side) read their input only
+    """compress, compress_zf, build_shared_codebook and KVSlotPool.append given
+    stream=side read their input only
     after what the current stream has queued: here the input itself is still being
     written there, behind long matmuls."""
     import lossless_float_compression_amd as zx
@@ -178,7 +179,17 @@ def test_side_stream_encodes_wait_for_the_producer_stream():
     blocks_late = blocks.clone()
     ids = torch.tensor([3, 1, 0], dtype=torch.int32, device="cuda")
     status = pool.append(blocks_late, ids, stream=side)
+    for _ in range(6):
+        torch.mm(a, a, out=b)
+    x_late2 = x.clone()
+    cz = zx.compress_zf(x_late2, stream=side)
+    for _ in range(6):
+        torch.mm(a, a, out=b)
+    x_late3 = x.clone()
+    cb = zx.build_shared_codebook([x_late3], stream=side)
     torch.cuda.synchronize()
+    assert torch.equal(zx.decompress_zf(cz).view(torch.int16), x.view(torch.int16))
+    assert torch.equal(cb.lengths.cpu(), c.lengths.cpu()), "one tensor's shared codebook is its own"
     assert int(c._err.item()) == 0
     assert torch.equal(zx.decompress(c).view(torch.int16), x.view(torch.int16))
     assert torch.equal(status.cpu(), torch.zeros(3, dtype=torch.int32))
