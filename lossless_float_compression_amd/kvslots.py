@@ -71,6 +71,18 @@ class KVSlotPool:
                                    self.block_bitoff.data_ptr(), self.block_seg.data_ptr())
         self._conts: Dict[int, _zx.zx_container] = {}
         self._ws: Optional[torch.Tensor] = None
+        self._streams = set()   # side streams the pool's arrays are recorded on
+
+    def _on_side(self, side: torch.cuda.Stream) -> None:
+        """Mark the pool's arrays as used on `side` (once per stream), so that their
+        memory is not handed out again before work there is done."""
+        key = side.cuda_stream
+        if key in self._streams:
+            return
+        self._streams.add(key)
+        for t in (self.signmant, self.stream, self.gaps, self.seg_desc, self.lengths, self.degenerate,
+                  self.block_bitoff, self.block_seg):
+            t.record_stream(side)
 
     # ---- sizes
     def nbytes(self) -> int:
@@ -109,6 +121,7 @@ class KVSlotPool:
         side = _zx._side_stream(stream)
         if side is not None:
             side.wait_stream(torch.cuda.current_stream())
+            self._on_side(side)
             with torch.cuda.stream(side):
                 return self.append(blocks, slot_ids, status, err, max_len, None, noalloc, fused)
         dt, flat = _zx._as_bits(blocks)
@@ -176,6 +189,7 @@ class KVSlotPool:
         side = _zx._side_stream(stream)
         if side is not None:
             side.wait_stream(torch.cuda.current_stream())
+            self._on_side(side)
             with torch.cuda.stream(side):
                 return self.decode(slots, out, err, None)
         if not torch.is_tensor(slots):
@@ -197,6 +211,7 @@ class KVSlotPool:
         side = _zx._side_stream(stream)
         if side is not None:
             side.wait_stream(torch.cuda.current_stream())
+            self._on_side(side)
             with torch.cuda.stream(side):
                 return self.decode_containers(slots, out, err, None)
         k = len(slots)

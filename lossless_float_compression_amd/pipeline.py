@@ -52,6 +52,11 @@ class LayerPipeline:
         # the containers (and the scratch buffers just allocated) were produced on the
         # current stream: the side stream's first decodes must come after that work
         self.side.wait_stream(torch.cuda.current_stream())
+        # the buffers are written on the side stream: their memory is not handed out
+        # again before the side stream's work on them is done, whenever they are freed
+        for bset in self.bufs:
+            for t in bset:
+                t.record_stream(self.side)
         self._ready = [torch.cuda.Event() for _ in range(depth)]
         self._free = [torch.cuda.Event() for _ in range(depth)]
         self._freed = [False] * depth     # a release was recorded for this set
