@@ -191,7 +191,8 @@ zx_status zx_encode_plan(zx_dtype dtype, const void *in, uint64_t n, uint32_t ma
  *   block_bitoff, block_seg                  from zx_encode_size
  *   total_bits, nsegs                        the totals read back
  *   signmant   u8 out [n] (BF16) or [ceil(n/2)] (FP8)
- *   stream     u32 out [zx_stream_words(total_bits)]
+ *   stream     u32 out [zx_stream_words(total_bits)]: every word is written (the padding
+ *              as zeros), whatever the buffer held, so it needs no clearing
  *   seg_desc   u32 out [nsegs][2];  gaps  u8 out [nsegs][64]
  *   err        optional: ZX_E_CODEBOOK if an element's exponent has no code. */
 zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int per_block,
