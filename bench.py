@@ -202,18 +202,33 @@ def cpu_baseline(x_cpu_bits: np.ndarray, dtype: int, seconds: float):
     """The oracle as it stands, on this host, on the same tensor: its bit-serial decode of
     the tensor's container on T threads over independent 65536-element blocks (the
     reported value), then on one thread, and its single-threaded encode."""
+    return cpu_baseline_parts([(x_cpu_bits, dtype, False)], seconds, f"full tensor ({x_cpu_bits.size} elements)")
+
+
+def cpu_baseline_parts(parts, seconds: float, sample: str):
+    """cpu_baseline over a sample of several tensors, each (raw bits, dtype, per_block)
+    with its own container: the times of the parts add up, and the rates are the
+    sample's raw bytes over those sums."""
     import oracle
     oracle.build(force=False)
     T = host_threads()
-    t_enc, n_enc, c = _timed_reps(lambda: oracle.encode(dtype, x_cpu_bits), seconds / 3)
-    t_dec1, n_dec1, y1 = _timed_reps(lambda: oracle.decode(c), seconds / 3)
-    t_decT, n_decT, yT = _timed_reps(lambda: oracle.decode_threaded(c, T), seconds / 3)
-    assert np.array_equal(y1, x_cpu_bits) and np.array_equal(yT, x_cpu_bits)
-    nb = x_cpu_bits.nbytes
+    share = seconds / 3 / max(len(parts), 1)
+    t_enc = t_dec1 = t_decT = 0.0
+    n_enc = n_dec1 = n_decT = 0
+    nb = nblk = 0
+    for bits, dtype, per_block in parts:
+        te, ne, c = _timed_reps(lambda: oracle.encode(dtype, bits, per_block=per_block), share, min_reps=1)
+        t1, n1, y1 = _timed_reps(lambda: oracle.decode(c), share, min_reps=1)
+        tT, nT, yT = _timed_reps(lambda: oracle.decode_threaded(c, T), share)
+        assert np.array_equal(y1, bits) and np.array_equal(yT, bits)
+        t_enc += te; t_dec1 += t1; t_decT += tT
+        n_enc += ne; n_dec1 += n1; n_decT += nT
+        nb += bits.nbytes
+        nblk += c.nblocks
     return {"value": round(nb / t_decT / 1e9, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
-            "sample": (f"full tensor ({x_cpu_bits.size} elements, {c.nblocks} blocks of 65536): bit-serial oracle "
-                       f"decode on {T} threads over contiguous block ranges, median of {n_decT} runs; single-thread "
-                       f"decode median of {n_dec1}, single-thread encode median of {n_enc}"),
+            "sample": (f"{sample}, {nblk} blocks of 65536: bit-serial oracle decode on {T} threads over contiguous "
+                       f"block ranges ({n_decT} timed runs, medians summed over the {len(parts)} container(s)); "
+                       f"single-thread decode ({n_dec1} runs) and encode ({n_enc} runs) likewise"),
             "decode_1thread_GBps": round(nb / t_dec1 / 1e9, 4),
             "encode_1thread_GBps": round(nb / t_enc / 1e9, 4),
             "cpu_model": cpu_model(), "host_threads_available": os.cpu_count()}

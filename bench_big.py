@@ -154,7 +154,26 @@ def run_c3(args):
                      "alg_bytes_per_launch": int(layer_alg)},
         "context_d2d_copy_GBps": copy_context_GBps(int(layer_alg)),
         "setup_s": round(setup_s, 1),
+        **({} if args.no_cpu else {"cpu_baseline": _c3_cpu_baseline(args)}),
     }
+
+
+def _c3_cpu_baseline(args):
+    """The oracle on layer 0 (its seven tensors, one codebook each): a bounded sample of
+    the set, copied from the device."""
+    from bench import cpu_baseline_parts
+    parts = [(workloads.c3_tensor(i).cpu().numpy().view(np.uint16).reshape(-1), 0, False)
+             for i in range(len(workloads.C3_SHAPES))]
+    return cpu_baseline_parts(parts, args.cpu_seconds, "layer 0 (7 tensors, 218,103,808 elements)")
+
+
+def _c5_cpu_baseline(args):
+    """The oracle on one (kv, layer) slab of the cache, one codebook per block: a bounded
+    sample of the cache, copied from the device."""
+    from bench import cpu_baseline_parts
+    x = workloads.c5_slab(0, 0).cpu().numpy().view(np.uint16).reshape(-1)
+    return cpu_baseline_parts([(x, 0, True)], args.cpu_seconds,
+                              f"one [8, 32768, 128] slab (kv 0, layer 0; {x.size} elements, one codebook per block)")
 
 
 def run_c5(args):
@@ -216,6 +235,7 @@ def run_c5(args):
                      "alg_bytes_per_launch": int(alg)},
         "context_d2d_copy_GBps": copy_context_GBps(int(alg)),
         "setup_s": round(setup_s, 1),
+        **({} if args.no_cpu else {"cpu_baseline": _c5_cpu_baseline(args)}),
     }
 
 
