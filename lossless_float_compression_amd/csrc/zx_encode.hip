@@ -200,13 +200,14 @@ __device__ __forceinline__ void zero_stream_tail(uint32_t *stream, uint64_t from
 // A full block whose bits fit the LDS stage (at most 8192 words: any mean code length
 // up to about 4 bits) is packed in one pass.  The whole block's input (8 loads per
 // thread) is requested at the kernel's start together with the code lengths, so it
-// arrives while the code table is built; it is then split at once: sign/mantissa
-// bytes (nibbles) go straight to memory and the exponent symbols to LDS, one byte
-// per element.  The rounds that follow read only LDS: each looks up its threads'
-// codes in a table of (code, length) pairs, scans their bit counts over the
-// workgroup and places the codes, gap bytes and segment entries in LDS; the stream
-// words, gaps and segment entries are stored at the end.  The rounds are bound by
-// vector-ALU issue (about 20 instructions per element), not by memory.  Other
+// arrives while the code table is built.  Round r splits its own 16 bytes per thread
+// (sign/mantissa bytes or nibbles straight to memory, exponent symbols kept in
+// registers) and so waits only for its own loads: the rounds start while the later
+// rounds' input is still arriving.  Each round looks up its threads' codes in a table
+// of (code, length) pairs, scans their bit counts over the workgroup and places the
+// codes, gap bytes and segment entries in LDS; the stream words a round completes
+// are stored during the next one, gaps and segment entries at the end.  The rounds
+// are bound by vector-ALU issue (about 20 instructions per element), not by memory.  Other
 // blocks (the last, partial block of a tensor, or very long codes) take the
 // round-by-round path in k_encode.
 constexpr uint32_t kOnePassBits = (kStageWords - 2) * 32;
@@ -223,73 +224,54 @@ struct BlockIn {
     uint32_t w[kRoundsPerBlock][RW];
 };
 
-// Request a full block's input for this thread.  A block that is not full requests
-// the same 16 bytes of `dummy` eight times instead, so the number of loads in
-// flight is the same on every path.
+// Request round r of a full block's input for this thread.  A block that is not full
+// requests the same 16 bytes of `dummy` instead, so the number of loads in flight is
+// the same on every path.
 template <int DT>
-__device__ __forceinline__ void load_block_in(const void *__restrict__ in, uint64_t lo, bool full, const void *dummy,
-                                              BlockIn<DT> &x)
+__device__ __forceinline__ void load_round(const void *__restrict__ in, uint64_t lo, bool full, const void *dummy, uint32_t r,
+                                           BlockIn<DT> &x)
 {
-    const uint32_t tid = threadIdx.x;
-#pragma unroll
-    for (uint32_t r = 0; r < kRoundsPerBlock; ++r) {
-        const uint64_t e = lo + (uint64_t)r * kRound + tid * kEncPerThread;
-        if (DT == ZX_BF16) {
-            const uint4 *a = full ? reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(in) + e)
-                                  : reinterpret_cast<const uint4 *>(dummy);
-            const uint4 q = *a;
-            x.w[r][0] = q.x; x.w[r][1] = q.y; x.w[r][2 % BlockIn<DT>::RW] = q.z; x.w[r][3 % BlockIn<DT>::RW] = q.w;
-        } else {
-            const uint2 *a = full ? reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(in) + e)
-                                  : reinterpret_cast<const uint2 *>(dummy);
-            const uint2 q = *a;
-            x.w[r][0] = q.x; x.w[r][1] = q.y;
-        }
+    const uint64_t e = lo + (uint64_t)r * kRound + threadIdx.x * kEncPerThread;
+    if (DT == ZX_BF16) {
+        const uint4 *a = full ? reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(in) + e)
+                              : reinterpret_cast<const uint4 *>(dummy);
+        const uint4 q = *a;
+        x.w[r][0] = q.x; x.w[r][1] = q.y; x.w[r][2 % BlockIn<DT>::RW] = q.z; x.w[r][3 % BlockIn<DT>::RW] = q.w;
+    } else {
+        const uint2 *a = full ? reinterpret_cast<const uint2 *>(reinterpret_cast<const uint8_t *>(in) + e)
+                              : reinterpret_cast<const uint2 *>(dummy);
+        const uint2 q = *a;
+        x.w[r][0] = q.x; x.w[r][1] = q.y;
     }
 }
 
-template <int DT>
-__device__ __forceinline__ void encode_onepass(const BlockIn<DT> &x, uint64_t lo, uint64_t b, const Canon &c,
+// Request the first NR rounds of a block's input.
+template <int DT, uint32_t NR>
+__device__ __forceinline__ void load_block_in(const void *__restrict__ in, uint64_t lo, bool full, const void *dummy,
+                                              BlockIn<DT> &x)
+{
+#pragma unroll
+    for (uint32_t r = 0; r < NR; ++r) load_round<DT>(in, lo, full, dummy, r, x);
+}
+
+// Rounds of input a workgroup has requested before its first round; each round then
+// requests the one this many rounds after it.  The whole block at once would keep
+// every round's input in registers through the rounds.
+constexpr uint32_t kEncAhead = 4;
+
+// D: rounds of input the caller requested (load_block_in<DT, D>) before the call; with
+// the whole block requested, every round is split at once.
+template <int DT, uint32_t D>
+__device__ __forceinline__ void encode_onepass(BlockIn<DT> &x, const void *__restrict__ blk_in, uint64_t lo, uint64_t b,
+                                               const Canon &c,
                                                uint32_t degen, uint64_t G, uint32_t bits, uint32_t s0, uint32_t nsb, uint32_t nch,
                                                uint64_t own_hi, uint64_t zero_to, uint8_t *__restrict__ signmant,
                                                uint32_t *__restrict__ stream, uint32_t *__restrict__ seg_desc,
                                                uint8_t *__restrict__ gaps, uint32_t *__restrict__ err, uint32_t *stage,
-                                               uint8_t *symbuf, uint2 *ctab, uint8_t *gapbuf, uint32_t *segbuf,
+                                               uint2 *ctab, uint8_t *gapbuf, uint32_t *segbuf,
                                                uint32_t (*part2)[kEncThreads / kWave], uint32_t &s_bad)
 {
     const uint32_t tid = threadIdx.x;
-    // ---- split every round: sign/mantissa bytes (nibbles) stored at once, exponent
-    //      symbols into LDS, one byte per element in block order
-#pragma unroll
-    for (uint32_t r = 0; r < kRoundsPerBlock; ++r) {
-        const uint32_t i0 = r * kRound + tid * kEncPerThread;
-        if (DT == ZX_E8M0) {
-            *reinterpret_cast<uint2 *>(symbuf + i0) = make_uint2(x.w[r][0], x.w[r][1]);
-        } else if (DT == ZX_BF16) {
-            uint32_t t[4];
-#pragma unroll
-            for (uint32_t w = 0; w < 4; ++w) {
-                const uint32_t v = x.w[r][w];
-                t[w] = (v & 0x007F007Fu) | ((v >> 8) & 0x00800080u);   // [sm, 0, sm, 0]
-            }
-            *reinterpret_cast<uint2 *>(signmant + lo + i0) =
-                make_uint2(__builtin_amdgcn_perm(t[1], t[0], 0x06040200u), __builtin_amdgcn_perm(t[3], t[2], 0x06040200u));
-            // x >> 7 holds the first element's exponent in byte 0 and the second's in byte 2
-            const uint32_t e01 = __builtin_amdgcn_perm(x.w[r][1] >> 7, x.w[r][0] >> 7, 0x06040200u);
-            const uint32_t e23 = __builtin_amdgcn_perm(x.w[r][3 % BlockIn<DT>::RW] >> 7, x.w[r][2 % BlockIn<DT>::RW] >> 7, 0x06040200u);
-            *reinterpret_cast<uint2 *>(symbuf + i0) = make_uint2(e01, e23);
-        } else {
-            uint32_t t[2];
-#pragma unroll
-            for (uint32_t w = 0; w < 2; ++w) {
-                const uint32_t v = x.w[r][w];
-                const uint32_t nb4 = (v & 0x07070707u) | ((v >> 4) & 0x08080808u);   // one nibble per byte
-                t[w] = (nb4 | (nb4 >> 4)) & 0x00FF00FFu;                              // two nibbles per half
-            }
-            *reinterpret_cast<uint32_t *>(signmant + (lo + i0) / 2) = __builtin_amdgcn_perm(t[1], t[0], 0x06040200u);
-            *reinterpret_cast<uint2 *>(symbuf + i0) = make_uint2((x.w[r][0] >> 3) & 0x0F0F0F0Fu, (x.w[r][1] >> 3) & 0x0F0F0F0Fu);
-        }
-    }
     for (uint32_t i = tid; i < kStageWords; i += kEncThreads) stage[i] = 0;
     if (tid == 0) s_bad = 0;
     // code table: the code, and its length with a flag for a symbol the block may not
@@ -301,9 +283,39 @@ __device__ __forceinline__ void encode_onepass(const BlockIn<DT> &x, uint64_t lo
     }
     __syncthreads();
 
+    // ---- split of round r, just before its lookups (so a round waits for its own
+    //      input only, and the rounds start while the later input is still arriving):
+    //      sign/mantissa bytes (nibbles) stored at once, the exponent symbols kept,
+    //      one byte per element
+    auto split = [&](uint32_t r) -> uint2 {
+        const uint32_t i0 = r * kRound + tid * kEncPerThread;
+        if (DT == ZX_E8M0) return make_uint2(x.w[r][0], x.w[r][1]);
+        if (DT == ZX_BF16) {
+            uint32_t t[4];
+#pragma unroll
+            for (uint32_t w = 0; w < 4; ++w) {
+                const uint32_t v = x.w[r][w];
+                t[w] = (v & 0x007F007Fu) | ((v >> 8) & 0x00800080u);   // [sm, 0, sm, 0]
+            }
+            *reinterpret_cast<uint2 *>(signmant + lo + i0) =
+                make_uint2(__builtin_amdgcn_perm(t[1], t[0], 0x06040200u), __builtin_amdgcn_perm(t[3], t[2], 0x06040200u));
+            // x >> 7 holds the first element's exponent in byte 0 and the second's in byte 2
+            return make_uint2(__builtin_amdgcn_perm(x.w[r][1] >> 7, x.w[r][0] >> 7, 0x06040200u),
+                              __builtin_amdgcn_perm(x.w[r][3 % BlockIn<DT>::RW] >> 7, x.w[r][2 % BlockIn<DT>::RW] >> 7, 0x06040200u));
+        }
+        uint32_t t[2];
+#pragma unroll
+        for (uint32_t w = 0; w < 2; ++w) {
+            const uint32_t v = x.w[r][w];
+            const uint32_t nb4 = (v & 0x07070707u) | ((v >> 4) & 0x08080808u);   // one nibble per byte
+            t[w] = (nb4 | (nb4 >> 4)) & 0x00FF00FFu;                              // two nibbles per half
+        }
+        *reinterpret_cast<uint32_t *>(signmant + (lo + i0) / 2) = __builtin_amdgcn_perm(t[1], t[0], 0x06040200u);
+        return make_uint2((x.w[r][0] >> 3) & 0x0F0F0F0Fu, (x.w[r][1] >> 3) & 0x0F0F0F0Fu);
+    };
+
     const uint32_t a0 = (uint32_t)(G & 31);
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    bool bad = false;
     // A round is split at its barrier: `pre` looks up the codes of the thread's 8
     // elements and publishes the wave's bit count; after the barrier `xscan` turns
     // the wave counts into this thread's offset; `post` places the codes and the
@@ -312,13 +324,25 @@ __device__ __forceinline__ void encode_onepass(const BlockIn<DT> &x, uint64_t lo
     struct Rd {
         uint64_t acc;      // the thread's codes, concatenated (exact while tb <= 64)
         uint64_t starts;   // bit j: a code starts j bits into them (exact while j < 64)
+        uint2 sv;          // the 8 symbols, one byte each
         uint32_t tb;       // their total length
         uint32_t o;        // bits before them in the round
         uint32_t R;        // bits in the round
     };
+    uint2 pres[D >= kRoundsPerBlock ? kRoundsPerBlock : 1];
+    if constexpr (D >= kRoundsPerBlock) {
+#pragma unroll
+        for (uint32_t r = 0; r < kRoundsPerBlock; ++r) pres[r] = split(r);
+    }
     auto pre = [&](uint32_t r, Rd &d) {
-        const uint32_t i0 = r * kRound + tid * kEncPerThread;
-        const uint2 sv = *reinterpret_cast<const uint2 *>(symbuf + i0);
+        uint2 sv;
+        if constexpr (D >= kRoundsPerBlock) {
+            sv = pres[r];
+        } else {
+            sv = split(r);
+            if (r + D < kRoundsPerBlock) load_round<DT>(blk_in, 0, true, nullptr, r + D, x);
+        }
+        d.sv = sv;
         uint32_t flags = 0;
         d.tb = 0;
         d.acc = 0;
@@ -332,7 +356,9 @@ __device__ __forceinline__ void encode_onepass(const BlockIn<DT> &x, uint64_t lo
             d.starts |= 1ull << (d.tb & 63u);
             d.tb += e.y & 0xFFu;
         }
-        if (flags & kEncBadFlag) bad = true;
+        // (a store, so that each round's flags are reduced in that round and not all
+        // kept for the end)
+        if (flags & kEncBadFlag) s_bad = 1;
         uint32_t wtot;
         d.o = wave_excl_scan(d.tb, wtot);
         if (lane_id() == 0) part2[r & 1][wave] = wtot;   // double-buffered by round
@@ -376,8 +402,8 @@ __device__ __forceinline__ void encode_onepass(const BlockIn<DT> &x, uint64_t lo
                     segbuf[bnd / (kChunkBits * kSegChunks)] = i0 + (uint32_t)__builtin_popcountll(d.starts & ((1ull << rel) - 1));
             }
         } else {
-            // ---- long codes: code by code, the symbols read again
-            const uint2 sv = *reinterpret_cast<const uint2 *>(symbuf + i0);
+            // ---- long codes: code by code
+            const uint2 sv = d.sv;
             uint32_t pk = p0;
 #pragma unroll
             for (uint32_t k = 0; k < kEncPerThread; ++k) {
@@ -403,12 +429,17 @@ __device__ __forceinline__ void encode_onepass(const BlockIn<DT> &x, uint64_t lo
             }
         }
     };
+    // Stream words are stored as soon as they are complete: after round r-1's codes
+    // are placed (the barrier of round r), every stage word below round r's first bit.
+    const uint64_t W0 = G >> 5;
+    uint32_t wdone = 0;   // stage words stored so far
     Rd cur, prev;
     uint32_t P = 0;    // block-relative bit of round r-1's first code
     pre(0, cur);
     __syncthreads();
     xscan(0, cur);
-#pragma unroll 1
+    // unrolled: each round names its own input registers, so it waits for its own loads only
+#pragma unroll
     for (uint32_t r = 1; r < kRoundsPerBlock; ++r) {
         prev = cur;
         pre(r, cur);
@@ -416,14 +447,15 @@ __device__ __forceinline__ void encode_onepass(const BlockIn<DT> &x, uint64_t lo
         P += prev.R;
         __syncthreads();
         xscan(r, cur);
+        const uint32_t wfin = (a0 + P) >> 5;
+        for (uint32_t i = wdone + tid; i < wfin; i += kEncThreads) put_word(stream, W0 + i, stage[i], G, own_hi);
+        wdone = wfin;
     }
     post(kRoundsPerBlock - 1, cur, P);
-    if (bad) s_bad = 1;
     __syncthreads();
-    // ---- all stores
-    const uint64_t W0 = G >> 5;
+    // ---- the remaining stores
     const uint32_t nw = bits ? (a0 + bits + 31) >> 5 : 0;
-    for (uint32_t i = tid; i < nw; i += kEncThreads) put_word(stream, W0 + i, stage[i], G, own_hi);
+    for (uint32_t i = wdone + tid; i < nw; i += kEncThreads) put_word(stream, W0 + i, stage[i], G, own_hi);
     if (zero_to) zero_stream_tail(stream, W0 + nw, zero_to, G);
     for (uint32_t ch = tid; ch < nsb * kSegChunks; ch += kEncThreads)
         gaps[(uint64_t)s0 * kSegChunks + ch] = ch < nch ? gapbuf[ch] : (uint8_t)ZX_NO_GAP;
@@ -453,7 +485,6 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
     __shared__ uint8_t gapbuf[kOnePassChunks];
     __shared__ uint32_t segbuf[kOnePassSegs];
     __shared__ uint32_t part2[2][kEncThreads / kWave];
-    __shared__ __align__(16) uint8_t symbuf[kBlock];
     __shared__ uint2 ctab[256];
 
     const uint32_t tid = threadIdx.x;
@@ -461,11 +492,13 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
     const uint64_t cb = per_block ? b : 0;
     // the code lengths and, for a full block, its first two rounds of input are
     // requested together, so the input arrives while the code table is built
+    // (every vector load that the code table needs goes before the input: loads
+    // complete in order, so waiting for one waits for all those issued before it)
     const uint32_t lsym = lengths[cb * A + (tid < A ? tid : A - 1)];
-    BlockIn<DT> x;
-    load_block_in<DT>(in, b * kBlock, (b + 1) * (uint64_t)kBlock <= n, block_bitoff, x);
-    canon_build_from(lsym, A, c);
     const uint32_t degen = degenerate[cb];
+    BlockIn<DT> x;
+    load_block_in<DT, kEncAhead>(in, b * kBlock, (b + 1) * (uint64_t)kBlock <= n, block_bitoff, x);
+    canon_build_from(lsym, A, c);
     const uint64_t G = block_bitoff[b];
     const uint64_t bits = block_bitoff[b + 1] - G;
     const uint32_t s0 = block_seg[b];
@@ -485,8 +518,9 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
     const uint64_t own_hi = last ? ~0ull : G + bits;
     const uint64_t zero_to = last ? stream_words : 0ull;
     if (nb == kBlock && (G & 31) + bits <= kOnePassBits) {
-        encode_onepass<DT>(x, lo, b, c, degen, G, (uint32_t)bits, s0, nsb, nch, own_hi, zero_to, signmant, stream, seg_desc,
-                           gaps, err, stage, symbuf, ctab, gapbuf, segbuf, part2, s_bad);
+        const void *blk_in = reinterpret_cast<const uint8_t *>(in) + lo * (DT == ZX_BF16 ? 2 : 1);
+        encode_onepass<DT, kEncAhead>(x, blk_in, lo, b, c, degen, G, (uint32_t)bits, s0, nsb, nch, own_hi, zero_to, signmant, stream, seg_desc,
+                           gaps, err, stage, ctab, gapbuf, segbuf, part2, s_bad);
         return;
     }
 
@@ -666,6 +700,10 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
     if (bad) s_bad = 1;
     __syncthreads();
     if (tid == 0 && s_bad) report(err, ZX_E_CODEBOOK);
+    // Nothing of this path is left in flight: the compiler joins its end with the
+    // one-pass path's entry, and a memory operation pending here would make the first
+    // round there wait for input it does not need yet.
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 // -------------------------------------------------------------------- K/V slots
@@ -707,19 +745,20 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_slots(KvSlots P, const v
     __shared__ uint8_t gapbuf[kOnePassChunks];
     __shared__ uint32_t segbuf[kOnePassSegs];
     __shared__ uint32_t part2[2][kEncThreads / kWave];
-    __shared__ __align__(16) uint8_t symbuf[kBlock];
     __shared__ uint2 ctab[256];
 
     const uint32_t tid = threadIdx.x;
     const uint64_t j = blockIdx.x;
+    // (the loads the code table and the sizes need go before the input, which
+    // completes in order after them)
     const uint32_t lsym = wlen[j * A + (tid < A ? tid : A - 1)];
-    BlockIn<DT> x;
-    load_block_in<DT>(src, j * kBlock, true, nullptr, x);
-    canon_build_from(lsym, A, c);
     const uint32_t slot = slot_ids[j];
     const uint32_t degen = wdeg[j];
     const uint64_t bits = wbits[j + 1];
     const uint32_t nsb = wnseg[j + 1];
+    BlockIn<DT> x;
+    load_block_in<DT, kEncAhead>(src, j * kBlock, true, nullptr, x);
+    canon_build_from(lsym, A, c);
     if (slot >= P.n_slots) {
         if (tid == 0) {
             status[j] = ZX_E_INVAL;
@@ -752,7 +791,8 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_slots(KvSlots P, const v
         P.block_seg[2 * (uint64_t)slot + 1] = nsb;
     }
     const uint32_t nch = (uint32_t)((bits + kChunkBits - 1) / kChunkBits);
-    encode_onepass<DT>(x, 0, 0, c, degen, 0, (uint32_t)bits, 0, nsb, nch, ~0ull, 0ull, sm, st, sd, gp, err, stage, symbuf,
+    const void *blk_in = reinterpret_cast<const uint8_t *>(src) + j * kBlock * (DT == ZX_BF16 ? 2 : 1);
+    encode_onepass<DT, kEncAhead>(x, blk_in, 0, 0, c, degen, 0, (uint32_t)bits, 0, nsb, nch, ~0ull, 0ull, sm, st, sd, gp, err, stage,
                        ctab, gapbuf, segbuf, part2, s_bad);
     // the rest of the slot's stream, padding included, is zero
     const uint32_t nw = (uint32_t)((bits + 31) / 32);
@@ -761,8 +801,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_slots(KvSlots P, const v
 }
 
 // The same append in one launch, with no workspace: each workgroup builds its block's
-// histogram from the input it holds in registers (32 lane copies in the symbol buffer,
-// which the split overwrites later), its code lengths in one wavefront (the codebook's
+// histogram from the input it holds in registers (32 lane copies in LDS), its code lengths in one wavefront (the codebook's
 // LDS in the stage, which the rounds overwrite later), and its bits and segment count,
 // then encodes exactly as k_encode_slots.
 constexpr uint32_t kFusedHistCopies = 32;
@@ -787,23 +826,22 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_slots_fused(KvSlots P, c
     __shared__ uint8_t gapbuf[kOnePassChunks];
     __shared__ uint32_t segbuf[kOnePassSegs];
     __shared__ uint32_t part2[2][kEncThreads / kWave];
-    __shared__ __align__(16) uint8_t symbuf[kBlock];
+    __shared__ uint32_t hbuf[kFusedHistCopies * (A + 1)];
     __shared__ uint2 ctab[256];
     __shared__ uint8_t lenbuf[256];
     __shared__ uint16_t degbuf;
     static_assert(sizeof(CodebookLds<uint32_t>) <= sizeof(stage), "the codebook's LDS fits the stage");
-    static_assert(kFusedHistCopies * (A + 1) * 4 <= kBlock, "the histogram copies fit the symbol buffer");
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid % kWave;
     const uint32_t wave = tid / kWave;
     const uint64_t j = blockIdx.x;
     BlockIn<DT> x;
-    load_block_in<DT>(src, j * kBlock, true, nullptr, x);
+    load_block_in<DT, kRoundsPerBlock>(src, j * kBlock, true, nullptr, x);
     const uint32_t slot = slot_ids[j];
     // histogram: lane l counts into copy l % 32 (stride A + 1: lanes l and l + 32 share
     // a copy, and the banks of one instruction's atomics differ but for those pairs)
-    uint32_t *h = reinterpret_cast<uint32_t *>(symbuf);
+    uint32_t *h = hbuf;
     for (uint32_t i = tid; i < kFusedHistCopies * (A + 1); i += kEncThreads) h[i] = 0;
     __syncthreads();
     uint32_t *mine = h + (lane % kFusedHistCopies) * (A + 1);
@@ -868,7 +906,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_slots_fused(KvSlots P, c
         P.block_seg[2 * (uint64_t)slot] = 0;
         P.block_seg[2 * (uint64_t)slot + 1] = nsb;
     }
-    encode_onepass<DT>(x, 0, 0, c, degen, 0, (uint32_t)bits, 0, nsb, nch, ~0ull, 0ull, sm, st, sd, gp, err, stage, symbuf,
+    encode_onepass<DT, kRoundsPerBlock>(x, nullptr, 0, 0, c, degen, 0, (uint32_t)bits, 0, nsb, nch, ~0ull, 0ull, sm, st, sd, gp, err, stage,
                        ctab, gapbuf, segbuf, part2, s_bad);
     // the rest of the slot's stream, padding included, is zero
     const uint32_t nw = (uint32_t)((bits + 31) / 32);
