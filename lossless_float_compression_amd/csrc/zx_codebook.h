@@ -27,6 +27,14 @@ __device__ __forceinline__ uint64_t read_u64(uint64_t v, uint32_t i)
     return ((uint64_t)hi << 32) | lo;
 }
 
+// 64-bit value of lane (lane ^ o).
+__device__ __forceinline__ uint64_t read_u64_xor(uint64_t v, int o)
+{
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o, kWave);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // LDS of one codebook build.
 template <typename H>
 struct CodebookLds {
@@ -108,36 +116,50 @@ __device__ void codebook_wave(CodebookLds<H> &L, uint32_t max_len, uint8_t *__re
         bool wide = sizeof(H) != 4;
         if constexpr (sizeof(H) == 4) {
             // 32-bit counts: node weights fit 32 bits unless the counts sum to 2^32 or
-            // more (then the merge runs again below in 64 bits).  The queue heads live
+            // more (then the merge runs below in 64 bits instead).  The queue heads live
             // in scalar registers; a step compares them with scalar instructions and
             // refills the consumed head with one readlane; the new node's weight and the
             // parents go to their lanes by a lane-index select.
             const uint32_t lw = lane < k ? (uint32_t)w[lane] : 0u;
+            // a node weight overflows 32 bits exactly when the counts summed do
+            uint64_t total = lw;
+            for (int o = 32; o >= 1; o >>= 1) total += read_u64_xor(total, o);
+            wide = __builtin_amdgcn_readfirstlane((uint32_t)(total >> 32)) != 0;
             uint32_t nw = 0;                   // weight of internal node `lane`
             uint32_t ha = __builtin_amdgcn_readlane(lw, 0), hb = 0;
-            uint32_t ovf = 0;
-            for (uint32_t step = 0; step + 1 < k; ++step) {
+            const uint32_t nsteps = wide ? 0u : k - 1;
+            for (uint32_t step = 0; step < nsteps; ++step) {
                 uint32_t val[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    // the leaf queue wins weight ties (no branch: every value here is
-                    // wavefront-uniform and stays in scalar registers)
-                    const bool tl = q1 < k && (q2 >= made || ha <= hb);
-                    val[t] = tl ? ha : hb;
-                    lpar = (tl && lane == q1) ? made : lpar;
-                    npar = (!tl && lane == q2) ? made : npar;
-                    q1 = __builtin_amdgcn_readfirstlane(q1 + (tl ? 1u : 0u));
-                    q2 = __builtin_amdgcn_readfirstlane(q2 + (tl ? 0u : 1u));
-                    ha = __builtin_amdgcn_readlane(lw, q1 < k ? q1 : 0u);
-                    hb = __builtin_amdgcn_readlane(nw, q2 < made ? q2 : 0u);
+                    // the leaf queue wins weight ties.  Every value here is wavefront-
+                    // uniform; the comparisons are the signs of differences and the choice
+                    // a mask, so that everything stays in scalar registers (a boolean
+                    // choice was widened to a lane mask and read back through a vector
+                    // register).  Each pick takes from exactly one queue, so the node
+                    // queue's head is the picks so far less the leaves taken.
+                    const uint32_t lt = (q1 - k) >> 31;                                       // q1 < k
+                    const uint32_t ge = 1u - ((q2 - made) >> 31);                            // q2 >= made
+                    const uint32_t le = 1u - (uint32_t)(((uint64_t)hb - (uint64_t)ha) >> 63);  // ha <= hb
+                    const uint32_t tl = lt & (ge | le);                                      // take the leaf
+                    const uint32_t keep_a = 0u - tl;                                         // all ones if tl
+                    val[t] = (ha & keep_a) | (hb & ~keep_a);
+                    const uint32_t leaf_at = q1 | ~keep_a;    // the leaf taken, or no lane
+                    const uint32_t node_at = q2 | keep_a;     // the node taken, or no lane
+                    lpar = lane == leaf_at ? made : lpar;
+                    npar = lane == node_at ? made : npar;
+                    q1 += tl;
+                    q2 = 2u * step + (uint32_t)t + 1u - q1;
+                    // (a head read past the end of its queue is never chosen: lt or ge
+                    // decides then)
+                    ha = __builtin_amdgcn_readlane(lw, q1 & (kWave - 1));
+                    hb = __builtin_amdgcn_readlane(nw, q2 & (kWave - 1));
                 }
-                const uint32_t sum = __builtin_amdgcn_readfirstlane(val[0] + val[1]);
-                ovf |= sum < val[0] ? 1u : 0u;
+                const uint32_t sum = val[0] + val[1];
                 nw = lane == made ? sum : nw;
                 hb = q2 == made ? sum : hb;    // the node queue was empty: the new node heads it
-                made = __builtin_amdgcn_readfirstlane(made + 1u);
+                ++made;
             }
-            wide = ovf != 0;
         }
         if (wide) {
             lpar = npar = 0;

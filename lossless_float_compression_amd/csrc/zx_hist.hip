@@ -14,7 +14,6 @@
 namespace zxk {
 
 constexpr int kHistThreads = 1024;
-constexpr uint32_t kHistUnroll = 8;   // 16-byte loads in flight per lane (a whole BF16 block in one step)
 
 template <int DT>
 __global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restrict__ in, uint64_t n,
@@ -28,59 +27,47 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restri
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid % kWave;
     const uint64_t b = blockIdx.x;
-    for (uint32_t i = tid; i < kWave * S; i += kHistThreads) h[i] = 0;
-    __syncthreads();
     uint32_t *const mine = h + lane * S;
     const uint64_t lo = b * kBlock;
-    const uint64_t hi = (lo + kBlock < n) ? lo + kBlock : n;
-    const uint32_t nb = (uint32_t)(hi - lo);
-    // 16 bytes per lane per step: 8 BF16 or 16 FP8 elements
-    constexpr uint32_t EPV = DT == ZX_BF16 ? 8 : 16;
-    const uint32_t nvec = (nb + EPV - 1) / EPV;
-    const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(in) + lo * (DT == ZX_BF16 ? 2 : 1));
-    constexpr uint32_t kStep = kHistThreads * kHistUnroll;
-    for (uint32_t base = 0; base < nvec; base += kStep) {
-        uint32_t words[kHistUnroll][4];
-        uint32_t have[kHistUnroll];
-        // issue every load of this step before counting
+    const uint32_t nb = (uint32_t)(((lo + kBlock < n) ? lo + kBlock : n) - lo);
+    auto exp_of = [](uint32_t word, uint32_t k) -> uint32_t {   // k-th element of a 32-bit word
+        if (DT == ZX_BF16) return (word >> (16 * (k & 1) + 7)) & 0xFFu;
+        if (DT == ZX_E8M0) return (word >> (8 * (k & 3))) & 0xFFu;
+        return (word >> (8 * (k & 3) + 3)) & 0xFu;
+    };
+    if (nb == kBlock) {
+        // a full block: every 16-byte load of the thread in flight at once (straight-line
+        // code, so that no wait falls between them), issued before the copies are
+        // cleared so that the clearing and its barrier overlap them
+        constexpr uint32_t kVecs = kBlock * (DT == ZX_BF16 ? 2 : 1) / 16 / kHistThreads;   // 8 or 4
+        constexpr uint32_t EPW = DT == ZX_BF16 ? 2 : 4;                                    // elements per word
+        const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(in) + lo * (DT == ZX_BF16 ? 2 : 1));
+        // (the scheduling barriers keep the loads in this order and everything that
+        // reads them below the workgroup barrier: each vector is then counted as soon as
+        // it arrives, and the barrier waits for none of them)
+        uint4 q[kVecs];
 #pragma unroll
-        for (uint32_t u = 0; u < kHistUnroll; ++u) {
-            const uint32_t v = base + u * kHistThreads + tid;
-            words[u][0] = words[u][1] = words[u][2] = words[u][3] = 0;
-            have[u] = 0;
-            if (v < nvec) {
-                const uint32_t first = v * EPV;
-                have[u] = (nb - first < EPV) ? nb - first : EPV;
-                if (have[u] == EPV) {
-                    const uint4 q = src[v];
-                    words[u][0] = q.x; words[u][1] = q.y; words[u][2] = q.z; words[u][3] = q.w;
-                } else {
-                    const uint8_t *bytes = reinterpret_cast<const uint8_t *>(src) + (uint64_t)first * (DT == ZX_BF16 ? 2 : 1);
-                    const uint32_t nbytes = have[u] * (DT == ZX_BF16 ? 2 : 1);
-                    for (uint32_t k = 0; k < nbytes; ++k) words[u][k >> 2] |= (uint32_t)bytes[k] << (8 * (k & 3));
-                }
-            }
+        for (uint32_t u = 0; u < kVecs; ++u) {
+            q[u] = src[u * kHistThreads + tid];
+            __builtin_amdgcn_sched_barrier(0);
         }
+        for (uint32_t i = tid; i < kWave * S; i += kHistThreads) h[i] = 0;
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (uint32_t u = 0; u < kHistUnroll; ++u) {
-            if (have[u] == EPV) {
+        for (uint32_t u = 0; u < kVecs; ++u) {
+            const uint32_t wv[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
 #pragma unroll
-                for (uint32_t k = 0; k < EPV; ++k) {
-                    uint32_t e;
-                    if (DT == ZX_BF16) e = (words[u][k >> 1] >> (16 * (k & 1) + 7)) & 0xFFu;
-                    else if (DT == ZX_E8M0) e = (words[u][k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                    else e = (words[u][k >> 2] >> (8 * (k & 3) + 3)) & 0xFu;
-                    atomicAdd(&mine[e], 1u);
-                }
-            } else {
-                for (uint32_t k = 0; k < have[u]; ++k) {
-                    uint32_t e;
-                    if (DT == ZX_BF16) e = (words[u][k >> 1] >> (16 * (k & 1) + 7)) & 0xFFu;
-                    else if (DT == ZX_E8M0) e = (words[u][k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                    else e = (words[u][k >> 2] >> (8 * (k & 3) + 3)) & 0xFu;
-                    atomicAdd(&mine[e], 1u);
-                }
-            }
+            for (uint32_t k = 0; k < 4 * EPW; ++k) atomicAdd(&mine[exp_of(wv[k / EPW], k)], 1u);
+        }
+    } else {
+        // the last, partial block of a tensor: element by element
+        for (uint32_t i = tid; i < kWave * S; i += kHistThreads) h[i] = 0;
+        __syncthreads();
+        for (uint32_t i = tid; i < nb; i += kHistThreads) {
+            const uint32_t word = DT == ZX_BF16 ? (uint32_t)reinterpret_cast<const uint16_t *>(in)[lo + i]
+                                                : (uint32_t)reinterpret_cast<const uint8_t *>(in)[lo + i];
+            atomicAdd(&mine[exp_of(word, 0)], 1u);
         }
     }
     __syncthreads();

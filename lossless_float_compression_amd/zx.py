@@ -407,22 +407,27 @@ def compress(x: torch.Tensor, per_block: bool = False, max_len: int = 32, fp8_sc
 
 
 _plan_tags = itertools.count(1)   # next() is atomic: concurrent compress() calls get distinct tags
-_plan_ring = {}   # device index -> pinned int64 [_PLAN_SLOTS, 4]: where zx_encode_plan publishes the totals
+# device index -> (pinned int64 [_PLAN_SLOTS, 4] where zx_encode_plan publishes the totals,
+# its numpy view, its address)
+_plan_ring = {}
 _plan_ring_lock = threading.Lock()
 _PLAN_SLOTS = 256
 
 
 def _plan_slot(dev):
-    """A pinned 4-word host slot for one compress() call (slots are reused round-robin;
-    each call's unique tag tells its own publication from an older one)."""
+    """A pinned 4-word host slot for one compress() call, as (address, numpy view, tag)
+    (slots are reused round-robin; each call's unique tag tells its own publication
+    from an older one)."""
     ring = _plan_ring.get(dev.index)
     if ring is None:
         with _plan_ring_lock:
             ring = _plan_ring.get(dev.index)
             if ring is None:
-                ring = _plan_ring[dev.index] = torch.full((_PLAN_SLOTS, 4), -1, dtype=torch.int64, pin_memory=True)
+                t = torch.full((_PLAN_SLOTS, 4), -1, dtype=torch.int64, pin_memory=True)
+                ring = _plan_ring[dev.index] = (t, t.numpy(), t.data_ptr())
     tag = next(_plan_tags)
-    return ring[tag % _PLAN_SLOTS], tag
+    i = tag % _PLAN_SLOTS
+    return ring[2] + 32 * i, ring[1][i], tag
 
 
 def _layout(sizes):
@@ -451,14 +456,13 @@ def _compress_planned(x, dtype, flat, n, A, nb, max_len, fp8_scale, stream):
     arena = torch.empty(total, **u8)
     base, wsp = arena.data_ptr(), ws.data_ptr()
     o_dtab, o_bo, o_bs, o_tot, o_err, o_len, o_deg = offs
-    host, tag = _plan_slot(dev)
+    host_ptr, hv, tag = _plan_slot(dev)
     _check("zx_encode_plan", L.zx_encode_plan(dtype, flat.data_ptr(), n, max_len, wsp, wsp + 4 * nbw * A, base + o_len,
-                                              base + o_deg, base + o_bo, base + o_bs, base + o_tot, host.data_ptr(), tag,
+                                              base + o_deg, base + o_bo, base + o_bs, base + o_tot, host_ptr, tag,
                                               base + o_dtab, base + o_err, stream))
     signmant = torch.empty(n if dtype == BF16 else (n + 1) // 2 if dtype == FP8_E4M3FN else 0, **u8)
     dtab, block_bitoff, block_seg, totals, err, lengths, degenerate = (
         arena[o:o + nbytes].view(dt) for o, (nbytes, dt) in zip(offs, sizes))
-    hv = host.numpy()
     spins = 0
     while hv[2] != tag:
         spins += 1
@@ -468,18 +472,21 @@ def _compress_planned(x, dtype, flat, n, A, nb, max_len, fp8_scale, stream):
                 raise RuntimeError("zx_encode_plan did not publish its totals")
     total_bits, nsegs = int(hv[0]), int(hv[1])
     nwords = zx_stream_words(total_bits)
-    out_sizes = [(4 * nwords, torch.int32), (8 * nsegs, torch.int32), (SEG_CHUNKS * nsegs, torch.uint8)]
-    ooffs, ototal = _layout(out_sizes)
-    out = torch.empty(ototal, **u8)
+    # one allocation: stream words, segment table, gaps (16-byte aligned pieces)
+    o_sd = (4 * nwords + 15) // 16 * 16
+    o_gp = o_sd + (8 * nsegs + 15) // 16 * 16
+    out = torch.empty(o_gp + SEG_CHUNKS * nsegs, **u8)
     ob = out.data_ptr()
     _check("zx_encode", L.zx_encode(dtype, flat.data_ptr(), n, 0, base + o_len, base + o_deg, base + o_bo, base + o_bs,
-                                    total_bits, nsegs, signmant.data_ptr(), ob + ooffs[0], ob + ooffs[1], ob + ooffs[2],
-                                    base + o_err, stream))
-    words, seg_desc, gaps = (out[o:o + nbytes].view(dt) for o, (nbytes, dt) in zip(ooffs, out_sizes))
+                                    total_bits, nsegs, signmant.data_ptr(), ob, ob + o_sd, ob + o_gp, base + o_err, stream))
+    # the container's views of it, made while the encode runs (as few tensor operations
+    # as possible: this is the host's share of back-to-back calls)
+    out32 = out.view(torch.int32)
     c = Compressed(dtype=dtype, per_block=0, n=n, shape=tuple(x.shape), total_bits=total_bits,
-                   nsegs=nsegs, lengths=lengths.view(1, A), degenerate=degenerate, signmant=signmant, stream=words,
-                   block_bitoff=block_bitoff, block_seg=block_seg, seg_desc=seg_desc.view(nsegs, 2),
-                   gaps=gaps.view(nsegs, SEG_CHUNKS), dtab=dtab, fp8_scale=fp8_scale)
+                   nsegs=nsegs, lengths=lengths.view(1, A), degenerate=degenerate, signmant=signmant,
+                   stream=out32[:nwords], block_bitoff=block_bitoff, block_seg=block_seg,
+                   seg_desc=out32.as_strided((nsegs, 2), (2, 1), o_sd // 4),
+                   gaps=out.as_strided((nsegs, SEG_CHUNKS), (SEG_CHUNKS, 1), o_gp), dtab=dtab, fp8_scale=fp8_scale)
     c._err = err
     return c
 
