@@ -268,7 +268,7 @@ def median_launch_ms(launch, n_per_rep: int, reps: int = 25, warmup: int = 5):
 
 def encode_chain(cs, xs):
     """A launcher for the device-side encode chain of copy k: zx_encode_plan (histogram,
-    codebook, block sizes, totals, decode table) and zx_encode, through the C ABI into
+    codebook, block sizes, totals, canonical codes, decode table) and zx_encode_coded, through the C ABI into
     preallocated buffers with the sizes already known (the same work compress() does,
     without its one host wait for the totals and without allocation)."""
     import ctypes
@@ -283,6 +283,7 @@ def encode_chain(cs, xs):
         nb = zx.nblocks_of(c.n)
         A = zx.alphabet(c.dtype)
         d = dict(flat=flat, th=torch.empty(A, dtype=torch.int32, device="cuda"),
+                 cd=torch.empty(A, dtype=torch.int32, device="cuda"),
                  bh=torch.empty((max(nb, 1), A), dtype=torch.int32, device="cuda"),
                  ln=torch.empty((1, A), dtype=torch.uint8, device="cuda"),
                  dg=torch.empty(1, dtype=torch.int16, device="cuda"),
@@ -298,9 +299,9 @@ def encode_chain(cs, xs):
         c, p, _ = bufs[k % len(bufs)]
         st = 0
         st |= L.zx_encode_plan(c.dtype, p["flat"], c.n, 32, p["bh"], p["th"], p["ln"], p["dg"], p["bo"], p["bs"],
-                               p["tot"], None, 0, p["dt"], p["err"], sptr)
-        st |= L.zx_encode(c.dtype, p["flat"], c.n, 0, p["ln"], p["dg"], p["bo"], p["bs"], c.total_bits, c.nsegs,
-                          p["sm"], p["st"], p["sd"], p["gp"], p["err"], sptr)
+                               p["tot"], None, 0, p["dt"], p["cd"], p["err"], sptr)
+        st |= L.zx_encode_coded(c.dtype, p["flat"], c.n, p["ln"], p["cd"], p["dg"], p["bo"], p["bs"], c.total_bits,
+                                c.nsegs, p["sm"], p["st"], p["sd"], p["gp"], p["err"], sptr)
         assert st == 0, "encode chain call failed"
 
     def check():

@@ -176,6 +176,8 @@ zx_status zx_encode_size(zx_dtype dtype, const void *in, uint64_t n, int per_blo
  *                 the decode table), so a host thread may wait for the tag instead of
  *                 the stream
  *   dtab          NULL, or zx_decode_table_bytes() device bytes: the decode table
+ *   codes         NULL, or u32[A] device out: the canonical code of each symbol
+ *                 (right-aligned, 0 for a symbol without a code), for zx_encode_coded
  *   err           NULL, or a device word set to 0 (the error word zx_encode reports to)
  * Errors: ZX_E_UNSUPPORTED (dtype), ZX_E_CODEBOOK (max_len out of range), ZX_E_INVAL
  * (null or misaligned buffers, n >= 2^32), ZX_E_HIP (launch). */
@@ -183,7 +185,7 @@ zx_status zx_encode_plan(zx_dtype dtype, const void *in, uint64_t n, uint32_t ma
                          uint32_t *block_hist, uint32_t *tensor_hist, uint8_t *lengths,
                          uint16_t *degenerate, uint64_t *block_bitoff, uint32_t *block_seg,
                          uint64_t *totals, uint64_t *totals_host, uint64_t tag, uint32_t *dtab,
-                         uint32_t *err, hipStream_t stream);
+                         uint32_t *codes, uint32_t *err, hipStream_t stream);
 
 /* Encode: split fields, bit-pack exponent codes, write gaps and segment table
  * (Intel summary, 方法论; DFloat11, 方法介绍 Fig. 2).
@@ -201,6 +203,20 @@ zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int per_block,
                     uint64_t total_bits, uint64_t nsegs,
                     uint8_t *signmant, uint32_t *stream, uint32_t *seg_desc, uint8_t *gaps,
                     uint32_t *err, hipStream_t stream_);
+
+/* zx_encode of a per-tensor codebook whose canonical codes are already known, as
+ * zx_encode_plan writes them (the codes of RFC 1951, section 3.2.2, that zx_encode
+ * would derive from the lengths in every workgroup).  Same outputs and errors as
+ * zx_encode with per_block = 0.
+ *   codes  u32[A] device: the canonical code of each symbol for these lengths (the
+ *          caller guarantees they match; other codes make an undecodable stream);
+ *          NULL or misaligned: ZX_E_INVAL. */
+zx_status zx_encode_coded(zx_dtype dtype, const void *in, uint64_t n, const uint8_t *lengths,
+                          const uint32_t *codes, const uint16_t *degenerate,
+                          const uint64_t *block_bitoff, const uint32_t *block_seg,
+                          uint64_t total_bits, uint64_t nsegs,
+                          uint8_t *signmant, uint32_t *stream, uint32_t *seg_desc, uint8_t *gaps,
+                          uint32_t *err, hipStream_t stream_);
 
 /* Decode table for one codebook (per-tensor scope): the small lookup tables the
  * decoder keeps in LDS (DFloat11, 方法介绍: one large prefix-free table split into

@@ -475,7 +475,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
                                                         uint8_t *__restrict__ signmant, uint32_t *__restrict__ stream,
                                                         uint32_t *__restrict__ seg_desc, uint8_t *__restrict__ gaps,
                                                         uint64_t total_bits, uint64_t nsegs, uint64_t stream_words,
-                                                        uint32_t *__restrict__ err)
+                                                        const uint32_t *__restrict__ codes, uint32_t *__restrict__ err)
 {
     constexpr uint32_t A = alphabet_of(DT);
     __shared__ Canon c;
@@ -495,10 +495,21 @@ __global__ __launch_bounds__(kEncThreads) void k_encode(const void *__restrict__
     // (every vector load that the code table needs goes before the input: loads
     // complete in order, so waiting for one waits for all those issued before it)
     const uint32_t lsym = lengths[cb * A + (tid < A ? tid : A - 1)];
+    const uint32_t lcode = codes ? codes[tid < A ? tid : A - 1] : 0u;
     const uint32_t degen = degenerate[cb];
     BlockIn<DT> x;
     load_block_in<DT, kEncAhead>(in, b * kBlock, (b + 1) * (uint64_t)kBlock <= n, block_bitoff, x);
-    canon_build_from(lsym, A, c);
+    if (codes) {
+        // the canonical codes came with the lengths: only the two arrays the encoder
+        // reads are filled (each thread's own symbol; a barrier follows before any
+        // thread reads another's)
+        if (tid < A) {
+            c.len[tid] = (uint8_t)lsym;
+            c.code[tid] = lcode;
+        }
+    } else {
+        canon_build_from(lsym, A, c);
+    }
     const uint64_t G = block_bitoff[b];
     const uint64_t bits = block_bitoff[b + 1] - G;
     const uint32_t s0 = block_seg[b];
@@ -947,7 +958,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const uint32_t *__restric
                                                        uint16_t *__restrict__ degenerate, uint64_t *__restrict__ block_bitoff,
                                                        uint32_t *__restrict__ block_seg, uint64_t *__restrict__ totals,
                                                        uint64_t *totals_host, uint64_t tag, DTab *__restrict__ dtab,
-                                                       uint32_t *__restrict__ err)
+                                                       uint32_t *__restrict__ codes, uint32_t *__restrict__ err)
 {
     constexpr uint32_t A = alphabet_of(DT);
     struct TableLds {
@@ -1109,10 +1120,20 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(const uint32_t *__restric
         block_seg[0] = 0;
         publish_totals(total_b, total_s, totals, totals_host, tag, err);
     }
-    if (!dtab) return;
-    // the decode table, once the totals are out
+    if (!dtab && !codes) return;
+    // the canonical codes and the decode table, once the totals are out
     canon_build_from(mylen, A, u.tb.c);
-    dtab_fill(u.tb.c, A, *dtab, u.tb.t1);
+    if (codes && tid < A) codes[tid] = u.tb.c.code[tid];
+    if (dtab) dtab_fill(u.tb.c, A, *dtab, u.tb.t1);
+}
+
+// The canonical code of each symbol, for zx_encode_coded (the larger-tensor planning
+// path; k_plan writes them itself).
+__global__ __launch_bounds__(1024) void k_canon_codes(const uint8_t *__restrict__ lengths, uint32_t A, uint32_t *__restrict__ codes)
+{
+    __shared__ Canon c;
+    canon_build(lengths, A, c);
+    if (threadIdx.x < A) codes[threadIdx.x] = c.code[threadIdx.x];
 }
 
 // The planning steps' last one for larger tensors (after k_scan_blocks).
@@ -1168,7 +1189,7 @@ extern "C" zx_status zx_encode_plan(zx_dtype dtype, const void *in, uint64_t n, 
                                     uint32_t *block_hist, uint32_t *tensor_hist, uint8_t *lengths,
                                     uint16_t *degenerate, uint64_t *block_bitoff, uint32_t *block_seg,
                                     uint64_t *totals, uint64_t *totals_host, uint64_t tag, uint32_t *dtab,
-                                    uint32_t *err, hipStream_t stream)
+                                    uint32_t *codes, uint32_t *err, hipStream_t stream)
 {
     if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN && dtype != ZX_E8M0) return ZX_E_UNSUPPORTED;
     const uint32_t A = alphabet_of(dtype);
@@ -1176,7 +1197,7 @@ extern "C" zx_status zx_encode_plan(zx_dtype dtype, const void *in, uint64_t n, 
     if (!block_hist || !tensor_hist || !lengths || !degenerate || !block_bitoff || !block_seg || !totals) return ZX_E_INVAL;
     if ((n && !in) || n >= (1ull << 32)) return ZX_E_INVAL;
     if (!aligned16(in) || !aligned16(block_hist) || !aligned16(tensor_hist) || !aligned16(dtab) ||
-        ((uintptr_t)totals & 7u) || ((uintptr_t)block_bitoff & 7u) || ((uintptr_t)totals_host & 7u))
+        ((uintptr_t)totals & 7u) || ((uintptr_t)block_bitoff & 7u) || ((uintptr_t)totals_host & 7u) || ((uintptr_t)codes & 3u))
         return ZX_E_INVAL;
     const uint64_t nblocks = (n + kBlock - 1) / kBlock;
     zx_status st;
@@ -1186,10 +1207,10 @@ extern "C" zx_status zx_encode_plan(zx_dtype dtype, const void *in, uint64_t n, 
         DTab *t = reinterpret_cast<DTab *>(dtab);
         if (A == 256)
             hipLaunchKernelGGL(k_plan<ZX_BF16>, dim3(1), dim3(kPlanThreads), 0, stream, block_hist, (uint32_t)nblocks, max_len,
-                               lengths, degenerate, block_bitoff, block_seg, totals, totals_host, tag, t, err);
+                               lengths, degenerate, block_bitoff, block_seg, totals, totals_host, tag, t, codes, err);
         else
             hipLaunchKernelGGL(k_plan<ZX_FP8_E4M3FN>, dim3(1), dim3(kPlanThreads), 0, stream, block_hist, (uint32_t)nblocks,
-                               max_len, lengths, degenerate, block_bitoff, block_seg, totals, totals_host, tag, t, err);
+                               max_len, lengths, degenerate, block_bitoff, block_seg, totals, totals_host, tag, t, codes, err);
         return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
     }
     // larger tensors: the separate steps, then the totals published and the table built
@@ -1199,16 +1220,18 @@ extern "C" zx_status zx_encode_plan(zx_dtype dtype, const void *in, uint64_t n, 
         return st;
     hipLaunchKernelGGL(k_publish, dim3(1), dim3(64), 0, stream, totals, totals_host, tag, err);
     if (hipGetLastError() != hipSuccess) return ZX_E_HIP;
+    if (codes) {
+        hipLaunchKernelGGL(k_canon_codes, dim3(1), dim3(1024), 0, stream, lengths, A, codes);
+        if (hipGetLastError() != hipSuccess) return ZX_E_HIP;
+    }
     if (dtab) return zx_build_decode_table(dtype, lengths, dtab, stream);
     return ZX_OK;
 }
 
-extern "C" zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int per_block,
-                               const uint8_t *lengths, const uint16_t *degenerate,
-                               const uint64_t *block_bitoff, const uint32_t *block_seg,
-                               uint64_t total_bits, uint64_t nsegs,
-                               uint8_t *signmant, uint32_t *stream, uint32_t *seg_desc, uint8_t *gaps,
-                               uint32_t *err, hipStream_t stream_)
+static zx_status encode_impl(zx_dtype dtype, const void *in, uint64_t n, int per_block, const uint8_t *lengths,
+                             const uint16_t *degenerate, const uint64_t *block_bitoff, const uint32_t *block_seg,
+                             uint64_t total_bits, uint64_t nsegs, uint8_t *signmant, uint32_t *stream, uint32_t *seg_desc,
+                             uint8_t *gaps, const uint32_t *codes, uint32_t *err, hipStream_t stream_)
 {
     if (dtype != ZX_BF16 && dtype != ZX_FP8_E4M3FN && dtype != ZX_E8M0) return ZX_E_UNSUPPORTED;
     const uint64_t nblocks = (n + kBlock - 1) / kBlock;
@@ -1225,14 +1248,37 @@ extern "C" zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int p
     }
     if (dtype == ZX_BF16)
         hipLaunchKernelGGL(k_encode<ZX_BF16>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream_, in, n, per_block, lengths,
-                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, words, err);
+                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, words, codes, err);
     else if (dtype == ZX_E8M0)
         hipLaunchKernelGGL(k_encode<ZX_E8M0>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream_, in, n, per_block, lengths,
-                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, words, err);
+                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, words, codes, err);
     else
         hipLaunchKernelGGL(k_encode<ZX_FP8_E4M3FN>, dim3((uint32_t)nblocks), dim3(kEncThreads), 0, stream_, in, n, per_block, lengths,
-                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, words, err);
+                           degenerate, block_bitoff, block_seg, signmant, stream, seg_desc, gaps, total_bits, nsegs, words, codes, err);
     return hipGetLastError() == hipSuccess ? ZX_OK : ZX_E_HIP;
+}
+
+extern "C" zx_status zx_encode(zx_dtype dtype, const void *in, uint64_t n, int per_block,
+                               const uint8_t *lengths, const uint16_t *degenerate,
+                               const uint64_t *block_bitoff, const uint32_t *block_seg,
+                               uint64_t total_bits, uint64_t nsegs,
+                               uint8_t *signmant, uint32_t *stream, uint32_t *seg_desc, uint8_t *gaps,
+                               uint32_t *err, hipStream_t stream_)
+{
+    return encode_impl(dtype, in, n, per_block, lengths, degenerate, block_bitoff, block_seg, total_bits, nsegs, signmant,
+                       stream, seg_desc, gaps, nullptr, err, stream_);
+}
+
+extern "C" zx_status zx_encode_coded(zx_dtype dtype, const void *in, uint64_t n, const uint8_t *lengths,
+                                     const uint32_t *codes, const uint16_t *degenerate,
+                                     const uint64_t *block_bitoff, const uint32_t *block_seg,
+                                     uint64_t total_bits, uint64_t nsegs,
+                                     uint8_t *signmant, uint32_t *stream, uint32_t *seg_desc, uint8_t *gaps,
+                                     uint32_t *err, hipStream_t stream_)
+{
+    if (!codes || ((uintptr_t)codes & 3u)) return ZX_E_INVAL;
+    return encode_impl(dtype, in, n, 0, lengths, degenerate, block_bitoff, block_seg, total_bits, nsegs, signmant, stream,
+                       seg_desc, gaps, codes, err, stream_);
 }
 
 // ---- K/V slot pool

@@ -82,7 +82,7 @@ EXPORTS = ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "
            "zx_status_string", "zx_version", "zx_kv_slot_sizes", "zx_kv_workspace_bytes", "zx_kv_encode_slots",
            "zx_kv_slot_container", "zx_kv_decode_slots", "zx_zf_scan_workspace_bytes", "zx_zf_encode_size",
            "zx_zf_encode", "zx_zf_decode", "zx_histogram_accumulate", "zx_build_codebook_u64",
-           "zx_kv_encode_slots_noalloc", "zx_encode_plan", "zx_kv_encode_slots_fused")
+           "zx_kv_encode_slots_noalloc", "zx_encode_plan", "zx_kv_encode_slots_fused", "zx_encode_coded")
 
 
 def lib():
@@ -124,12 +124,13 @@ def lib():
         L.zx_zf_decode.argtypes = [C.POINTER(zx_zf_container), P, P, P]
         L.zx_histogram_accumulate.argtypes = [I, P, U64, P, P]
         L.zx_build_codebook_u64.argtypes = [I, P, U32, U32, P, P, P]
-        L.zx_encode_plan.argtypes = [I, P, U64, U32, P, P, P, P, P, P, P, P, U64, P, P, P]
+        L.zx_encode_plan.argtypes = [I, P, U64, U32, P, P, P, P, P, P, P, P, U64, P, P, P, P]
+        L.zx_encode_coded.argtypes = [I, P, U64, P, P, P, P, P, U64, U64, P, P, P, P, P, P]
         for f in ("zx_histogram", "zx_build_codebook", "zx_encode_size", "zx_encode", "zx_build_decode_table",
                   "zx_decode", "zx_decode_block_batch", "zx_decode_block_batch_wg", "zx_kv_slot_sizes",
                   "zx_kv_encode_slots", "zx_kv_slot_container", "zx_kv_decode_slots", "zx_zf_encode_size",
                   "zx_zf_encode", "zx_zf_decode", "zx_histogram_accumulate", "zx_build_codebook_u64",
-                  "zx_kv_encode_slots_noalloc", "zx_encode_plan", "zx_kv_encode_slots_fused"):
+                  "zx_kv_encode_slots_noalloc", "zx_encode_plan", "zx_kv_encode_slots_fused", "zx_encode_coded"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -183,12 +184,13 @@ def zx_encode_size(dtype, inp, n, per_block, lengths, block_hist, block_bitoff, 
 
 
 def zx_encode_plan(dtype, inp, n, max_len, block_hist, tensor_hist, lengths, degenerate, block_bitoff, block_seg,
-                   totals, totals_host=None, tag=0, dtab=None, err=None, stream=None):
-    """totals_host: a pinned host int64 tensor of at least 3 entries, or None."""
+                   totals, totals_host=None, tag=0, dtab=None, err=None, stream=None, codes=None):
+    """totals_host: a pinned host int64 tensor of at least 3 entries, or None; codes: an
+    int32 device tensor of A entries that receives the canonical codes, or None."""
     _check("zx_encode_plan", lib().zx_encode_plan(dtype, _ptr(inp), n, max_len, _ptr(block_hist), _ptr(tensor_hist),
                                                   _ptr(lengths), _ptr(degenerate), _ptr(block_bitoff), _ptr(block_seg),
-                                                  _ptr(totals), _ptr(totals_host), int(tag), _ptr(dtab), _ptr(err),
-                                                  _stream(stream)))
+                                                  _ptr(totals), _ptr(totals_host), int(tag), _ptr(dtab), _ptr(codes),
+                                                  _ptr(err), _stream(stream)))
 
 
 def zx_encode(dtype, inp, n, per_block, lengths, degenerate, block_bitoff, block_seg, total_bits, nsegs,
@@ -196,6 +198,14 @@ def zx_encode(dtype, inp, n, per_block, lengths, degenerate, block_bitoff, block
     _check("zx_encode", lib().zx_encode(dtype, _ptr(inp), n, int(per_block), _ptr(lengths), _ptr(degenerate),
                                         _ptr(block_bitoff), _ptr(block_seg), total_bits, nsegs, _ptr(signmant),
                                         _ptr(stream_words), _ptr(seg_desc), _ptr(gaps), _ptr(err), _stream(stream)))
+
+
+def zx_encode_coded(dtype, inp, n, lengths, codes, degenerate, block_bitoff, block_seg, total_bits, nsegs,
+                    signmant, stream_words, seg_desc, gaps, err=None, stream=None):
+    _check("zx_encode_coded", lib().zx_encode_coded(dtype, _ptr(inp), n, _ptr(lengths), _ptr(codes), _ptr(degenerate),
+                                                    _ptr(block_bitoff), _ptr(block_seg), total_bits, nsegs,
+                                                    _ptr(signmant), _ptr(stream_words), _ptr(seg_desc), _ptr(gaps),
+                                                    _ptr(err), _stream(stream)))
 
 
 def zx_build_decode_table(dtype, lengths, dtab, stream=None):
@@ -441,8 +451,9 @@ def _layout(sizes):
 
 def _compress_planned(x, dtype, flat, n, A, nb, max_len, fp8_scale, stream):
     """Per-tensor codebook: zx_encode_plan (histogram, codebook, sizes and totals in
-    as few launches as the tensor allows; the decode table after the totals), a wait
-    for the totals on a pinned host word instead of the stream, then zx_encode.  The
+    as few launches as the tensor allows; the canonical codes and the decode table
+    after the totals), a wait for the totals on a pinned host word instead of the
+    stream, then zx_encode_coded with those codes.  The
     launches take raw addresses in one arena; the container's tensor views of it are
     made while the kernels run."""
     dev = flat.device
@@ -452,14 +463,14 @@ def _compress_planned(x, dtype, flat, n, A, nb, max_len, fp8_scale, stream):
     sizes = [(zx_decode_table_bytes(), torch.uint8), (8 * (nb + 1), torch.int64), (4 * (nb + 1), torch.int32),
              (16, torch.int64), (4, torch.int32), (A, torch.uint8), (2, torch.int16)]
     offs, total = _layout(sizes)
-    ws = torch.empty(nbw * A + A, dtype=torch.int32, device=dev)   # block histograms, tensor histogram
+    ws = torch.empty(nbw * A + 2 * A, dtype=torch.int32, device=dev)   # block histograms, tensor histogram, codes
     arena = torch.empty(total, **u8)
     base, wsp = arena.data_ptr(), ws.data_ptr()
     o_dtab, o_bo, o_bs, o_tot, o_err, o_len, o_deg = offs
     host_ptr, hv, tag = _plan_slot(dev)
     _check("zx_encode_plan", L.zx_encode_plan(dtype, flat.data_ptr(), n, max_len, wsp, wsp + 4 * nbw * A, base + o_len,
                                               base + o_deg, base + o_bo, base + o_bs, base + o_tot, host_ptr, tag,
-                                              base + o_dtab, base + o_err, stream))
+                                              base + o_dtab, wsp + 4 * (nbw * A + A), base + o_err, stream))
     signmant = torch.empty(n if dtype == BF16 else (n + 1) // 2 if dtype == FP8_E4M3FN else 0, **u8)
     dtab, block_bitoff, block_seg, totals, err, lengths, degenerate = (
         arena[o:o + nbytes].view(dt) for o, (nbytes, dt) in zip(offs, sizes))
@@ -477,8 +488,9 @@ def _compress_planned(x, dtype, flat, n, A, nb, max_len, fp8_scale, stream):
     o_gp = o_sd + (8 * nsegs + 15) // 16 * 16
     out = torch.empty(o_gp + SEG_CHUNKS * nsegs, **u8)
     ob = out.data_ptr()
-    _check("zx_encode", L.zx_encode(dtype, flat.data_ptr(), n, 0, base + o_len, base + o_deg, base + o_bo, base + o_bs,
-                                    total_bits, nsegs, signmant.data_ptr(), ob, ob + o_sd, ob + o_gp, base + o_err, stream))
+    _check("zx_encode_coded", L.zx_encode_coded(dtype, flat.data_ptr(), n, base + o_len, wsp + 4 * (nbw * A + A),
+                                                base + o_deg, base + o_bo, base + o_bs, total_bits, nsegs,
+                                                signmant.data_ptr(), ob, ob + o_sd, ob + o_gp, base + o_err, stream))
     # the container's views of it, made while the encode runs (as few tensor operations
     # as possible: this is the host's share of back-to-back calls)
     out32 = out.view(torch.int32)

@@ -84,14 +84,20 @@ def test_argument_errors_return_before_any_launch(zx):
     assert lib.zx_decode(C.byref(c), P(0x20000), None, None) == 1
     # the encode plan: dtype, length limit, missing workspace, n >= 2^32, misaligned host word
     ok = [P(0x1000 * (k + 1)) for k in range(8)]   # in, block_hist, tensor_hist, lengths, degenerate, bitoff, seg, totals
-    def plan(dtype=0, n=10, max_len=32, bufs=ok, host=None):
+    def plan(dtype=0, n=10, max_len=32, bufs=ok, host=None, codes=None):
         return lib.zx_encode_plan(dtype, bufs[0], n, max_len, bufs[1], bufs[2], bufs[3], bufs[4], bufs[5], bufs[6],
-                                  bufs[7], host, 0, None, None, None)
+                                  bufs[7], host, 0, None, codes, None, None)
     assert plan(dtype=5) == 2
     assert plan(max_len=7) == 3 and plan(dtype=1, max_len=3) == 3 and plan(max_len=33) == 3
     assert plan(bufs=ok[:1] + [None] + ok[2:]) == 1
     assert plan(n=1 << 32) == 1
     assert plan(host=P(0x5004)) == 1
+    assert plan(codes=P(0x6002)) == 1          # the codes must be u32-aligned
+    # zx_encode_coded: the codes are required and u32-aligned
+    def coded(codes):
+        return lib.zx_encode_coded(0, P(0x1000), 10, P(0x2000), codes, P(0x3000), P(0x4000), P(0x5000), 20, 1,
+                                   P(0x6000), P(0x7000), P(0x8000), P(0x9000), None, None)
+    assert coded(None) == 1 and coded(P(0xA002)) == 1
     # the K/V append without allocation takes at most ZX_KV_NOALLOC_MAX_BLOCKS blocks
     pool = zx.zx.zx_kv_pool()
     assert zx.zx.KV_NOALLOC_MAX_BLOCKS == 1024
