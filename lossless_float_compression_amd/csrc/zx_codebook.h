@@ -120,45 +120,68 @@ __device__ void codebook_wave(CodebookLds<H> &L, uint32_t max_len, uint8_t *__re
             // in scalar registers; a step compares them with scalar instructions and
             // refills the consumed head with one readlane; the new node's weight and the
             // parents go to their lanes by a lane-index select.
-            const uint32_t lw = lane < k ? (uint32_t)w[lane] : 0u;
             // a node weight overflows 32 bits exactly when the counts summed do
-            uint64_t total = lw;
+            uint64_t total = lane < k ? (uint32_t)w[lane] : 0u;
             for (int o = 32; o >= 1; o >>= 1) total += read_u64_xor(total, o);
             wide = __builtin_amdgcn_readfirstlane((uint32_t)(total >> 32)) != 0;
-            uint32_t nw = 0;                   // weight of internal node `lane`
-            uint32_t ha = __builtin_amdgcn_readlane(lw, 0), hb = 0;
+            // Lanes past the last leaf, and nodes not made yet, weigh kEmpty, which no
+            // queue head compared here can reach (the counts sum below 2^32, and only
+            // the root, never compared, weighs the whole sum): an exhausted queue then
+            // loses every comparison by itself.
+            constexpr uint32_t kEmpty = 0xFFFFFFFFu;
+            const uint32_t lw = lane < k ? (uint32_t)w[lane] : kEmpty;
+            uint32_t nw = kEmpty;              // weight of internal node `lane`
+            uint32_t ha = __builtin_amdgcn_readlane(lw, 0), hb = kEmpty;
             const uint32_t nsteps = wide ? 0u : k - 1;
-            for (uint32_t step = 0; step < nsteps; ++step) {
-                uint32_t val[2];
+            // lane s records which queues step s took from (bit t: its pick t was a
+            // leaf); the parents are rebuilt from these bits after the merge, so that a
+            // step is scalar instructions, four readlanes and two lane selects
+            uint32_t picks = 0;
+            for (uint32_t step = 0; step < nsteps; ++step) {   // (step == made)
+                uint32_t val[2], took[2];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     // the leaf queue wins weight ties.  Every value here is wavefront-
-                    // uniform; the comparisons are the signs of differences and the choice
-                    // a mask, so that everything stays in scalar registers (a boolean
-                    // choice was widened to a lane mask and read back through a vector
-                    // register).  Each pick takes from exactly one queue, so the node
-                    // queue's head is the picks so far less the leaves taken.
-                    const uint32_t lt = (q1 - k) >> 31;                                       // q1 < k
-                    const uint32_t ge = 1u - ((q2 - made) >> 31);                            // q2 >= made
-                    const uint32_t le = 1u - (uint32_t)(((uint64_t)hb - (uint64_t)ha) >> 63);  // ha <= hb
-                    const uint32_t tl = lt & (ge | le);                                      // take the leaf
-                    const uint32_t keep_a = 0u - tl;                                         // all ones if tl
-                    val[t] = (ha & keep_a) | (hb & ~keep_a);
-                    const uint32_t leaf_at = q1 | ~keep_a;    // the leaf taken, or no lane
-                    const uint32_t node_at = q2 | keep_a;     // the node taken, or no lane
-                    lpar = lane == leaf_at ? made : lpar;
-                    npar = lane == node_at ? made : npar;
+                    // uniform and stays in scalar registers (the choice is an integer, not
+                    // a boolean, which was widened to a lane mask and read back through a
+                    // vector register).  Each pick takes from exactly one queue, so the
+                    // node queue's head is the picks so far less the leaves taken.
+                    const uint32_t tl = ha <= hb ? 1u : 0u;   // take the leaf
+                    val[t] = tl ? ha : hb;
+                    took[t] = tl;
                     q1 += tl;
                     q2 = 2u * step + (uint32_t)t + 1u - q1;
-                    // (a head read past the end of its queue is never chosen: lt or ge
-                    // decides then)
-                    ha = __builtin_amdgcn_readlane(lw, q1 & (kWave - 1));
-                    hb = __builtin_amdgcn_readlane(nw, q2 & (kWave - 1));
+                    const uint32_t la = __builtin_amdgcn_readlane(lw, q1 & (kWave - 1));
+                    ha = q1 < k ? la : kEmpty;
+                    hb = __builtin_amdgcn_readlane(nw, q2);   // (q2 <= made < 64)
                 }
                 const uint32_t sum = val[0] + val[1];
-                nw = lane == made ? sum : nw;
+                const bool here = lane == made;
+                nw = here ? sum : nw;
+                picks = here ? (took[0] | (took[1] << 1)) : picks;
                 hb = q2 == made ? sum : hb;    // the node queue was empty: the new node heads it
                 ++made;
+            }
+            if (!wide) {
+                // step s made node s from its two picks; a leaf pick took the leaf whose
+                // index is the number of leaf picks before it, a node pick the node whose
+                // index is the number of node picks before it
+                uint16_t *const leafpar = parent;          // [0, 64): parent of leaf i
+                uint16_t *const nodepar = parent + kWave;  // [64, 128): parent of node i
+                const uint32_t mine = lane < nsteps ? picks : 0u;
+                const uint32_t b0 = mine & 1u, b1 = mine >> 1;
+                uint32_t nleaf;
+                const uint32_t l0 = wave_excl_scan(b0 + b1, nleaf);   // leaf picks before step `lane`
+                if (lane < nsteps) {
+                    if (b0) leafpar[l0] = (uint16_t)lane;
+                    else nodepar[2 * lane - l0] = (uint16_t)lane;
+                    const uint32_t l1 = l0 + b0;
+                    if (b1) leafpar[l1] = (uint16_t)lane;
+                    else nodepar[2 * lane + 1 - l1] = (uint16_t)lane;
+                }
+                wave_sync();
+                lpar = lane < k ? leafpar[lane] : 0u;
+                npar = lane + 1 < made ? nodepar[lane] : 0u;
             }
         }
         if (wide) {
