@@ -816,6 +816,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_slots(KvSlots P, const v
 // LDS in the stage, which the rounds overwrite later), and its bits and segment count,
 // then encodes exactly as k_encode_slots.
 constexpr uint32_t kFusedHistCopies = 32;
+static_assert((kFusedHistCopies & (kFusedHistCopies - 1)) == 0 && kFusedHistCopies <= kWave, "copies: a power of two, at most a wavefront");
 
 template <int DT>
 __device__ __forceinline__ uint32_t block_exp(const BlockIn<DT> &x, uint32_t r, uint32_t e)
@@ -837,7 +838,7 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_slots_fused(KvSlots P, c
     __shared__ uint8_t gapbuf[kOnePassChunks];
     __shared__ uint32_t segbuf[kOnePassSegs];
     __shared__ uint32_t part2[2][kEncThreads / kWave];
-    __shared__ uint32_t hbuf[kFusedHistCopies * (A + 1)];
+    __shared__ uint32_t hbuf[A * kFusedHistCopies];
     __shared__ uint2 ctab[256];
     __shared__ uint8_t lenbuf[256];
     __shared__ uint16_t degbuf;
@@ -850,22 +851,25 @@ __global__ __launch_bounds__(kEncThreads) void k_encode_slots_fused(KvSlots P, c
     BlockIn<DT> x;
     load_block_in<DT, kRoundsPerBlock>(src, j * kBlock, true, nullptr, x);
     const uint32_t slot = slot_ids[j];
-    // histogram: lane l counts into copy l % 32 (stride A + 1: lanes l and l + 32 share
-    // a copy, and the banks of one instruction's atomics differ but for those pairs)
+    // histogram: lane l counts into copy l % 32, laid out bin-major (copy k's count of
+    // value v at 32 v + k), so the bank of a counter depends on the lane alone and
+    // lanes l and l + 32 are the only ones an instruction's atomics pair up
     uint32_t *h = hbuf;
-    for (uint32_t i = tid; i < kFusedHistCopies * (A + 1); i += kEncThreads) h[i] = 0;
+    for (uint32_t i = tid; i < A * kFusedHistCopies; i += kEncThreads) h[i] = 0;
     __syncthreads();
-    uint32_t *mine = h + (lane % kFusedHistCopies) * (A + 1);
+    uint32_t *mine = h + lane % kFusedHistCopies;
 #pragma unroll
     for (uint32_t r = 0; r < kRoundsPerBlock; ++r) {
 #pragma unroll
-        for (uint32_t e = 0; e < kEncPerThread; ++e) atomicAdd(&mine[block_exp<DT>(x, r, e)], 1u);
+        for (uint32_t e = 0; e < kEncPerThread; ++e) atomicAdd(&mine[block_exp<DT>(x, r, e) * kFusedHistCopies], 1u);
     }
     __syncthreads();
     CodebookLds<uint32_t> &L = *reinterpret_cast<CodebookLds<uint32_t> *>(stage);
     if (tid < A) {
+        // the copies of value tid, read rotated by tid so that a wavefront's reads fall
+        // in distinct banks
         uint32_t t = 0;
-        for (uint32_t k = 0; k < kFusedHistCopies; ++k) t += h[k * (A + 1) + tid];
+        for (uint32_t k = 0; k < kFusedHistCopies; ++k) t += h[tid * kFusedHistCopies + ((k + tid) & (kFusedHistCopies - 1))];
         L.cnt[tid] = t;
     }
     __syncthreads();

@@ -6,9 +6,11 @@
 // wavefront mostly hold the same handful of values: a single shared histogram would
 // serialise its atomics on those few bins.  Each lane therefore owns a private copy
 // of the histogram in LDS (shared by the lane of the same index in every wavefront
-// of the workgroup), laid out with a stride of A + 1 words so that lane l's bin v
-// sits in bank (l + v) mod 64: the 64 LDS atomics of one instruction fall in 64
-// distinct banks whatever the values.  The 64 copies are summed at the end.
+// of the workgroup), laid out bin-major: lane l's count of value v is word 64 v + l.
+// The bank of a lane's counter then depends on the lane alone, so the atomics of
+// one instruction never meet in a bank because of the values the lanes hold (a
+// lane-major layout with an odd stride spreads one value over the banks, but two
+// lanes holding neighbouring values collide).  The 64 copies are summed at the end.
 #include "zx_common.h"
 
 namespace zxk {
@@ -22,12 +24,11 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restri
                                                             unsigned long long *__restrict__ hist64)
 {
     constexpr uint32_t A = alphabet_of(DT);
-    constexpr uint32_t S = A + 1;                 // copy stride in words
-    __shared__ uint32_t h[kWave * S];
+    __shared__ uint32_t h[A * kWave];             // lane l's count of value v at 64 v + l
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid % kWave;
     const uint64_t b = blockIdx.x;
-    uint32_t *const mine = h + lane * S;
+    uint32_t *const mine = h + lane;
     const uint64_t lo = b * kBlock;
     const uint32_t nb = (uint32_t)(((lo + kBlock < n) ? lo + kBlock : n) - lo);
     auto exp_of = [](uint32_t word, uint32_t k) -> uint32_t {   // k-th element of a 32-bit word
@@ -51,41 +52,43 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const void *__restri
             q[u] = src[u * kHistThreads + tid];
             __builtin_amdgcn_sched_barrier(0);
         }
-        for (uint32_t i = tid; i < kWave * S; i += kHistThreads) h[i] = 0;
+        for (uint32_t i = tid; i < A * kWave; i += kHistThreads) h[i] = 0;
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (uint32_t u = 0; u < kVecs; ++u) {
             const uint32_t wv[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
 #pragma unroll
-            for (uint32_t k = 0; k < 4 * EPW; ++k) atomicAdd(&mine[exp_of(wv[k / EPW], k)], 1u);
+            for (uint32_t k = 0; k < 4 * EPW; ++k) atomicAdd(&mine[exp_of(wv[k / EPW], k) * kWave], 1u);
         }
     } else {
         // the last, partial block of a tensor: element by element
-        for (uint32_t i = tid; i < kWave * S; i += kHistThreads) h[i] = 0;
+        for (uint32_t i = tid; i < A * kWave; i += kHistThreads) h[i] = 0;
         __syncthreads();
         for (uint32_t i = tid; i < nb; i += kHistThreads) {
             const uint32_t word = DT == ZX_BF16 ? (uint32_t)reinterpret_cast<const uint16_t *>(in)[lo + i]
                                                 : (uint32_t)reinterpret_cast<const uint8_t *>(in)[lo + i];
-            atomicAdd(&mine[exp_of(word, 0)], 1u);
+            atomicAdd(&mine[exp_of(word, 0) * kWave], 1u);
         }
     }
     __syncthreads();
-    // sum the 64 copies: thread t adds copies t/A, t/A + 1024/A, ... of bin t % A
-    constexpr uint32_t kGroups = kHistThreads / A;          // 4 (BF16) or 64 (FP8)
-    const uint32_t bin = tid % A;
-    const uint32_t grp = tid / A;
+    // sum the 64 copies: G threads per value, each adding C of its copies (rotated by
+    // the value, so that a wavefront's reads fall in distinct banks), then the G
+    // partial sums of a value are added across neighbouring lanes
+    constexpr uint32_t G = kHistThreads / A;                // 4 (alphabet 256) or 64 (alphabet 16)
+    constexpr uint32_t C = kWave / G;                       // 16 or 1
+    static_assert(G * A == kHistThreads && C * G == kWave, "histogram sum shape");
+    const uint32_t v = tid / G;
+    const uint32_t g = tid % G;
     uint32_t c = 0;
-    for (uint32_t cp = grp; cp < kWave; cp += kGroups) c += h[cp * S + bin];
-    __syncthreads();
-    h[grp * S + bin] = c;
-    __syncthreads();
-    if (tid < A) {
-        uint32_t t = 0;
-        for (uint32_t g = 0; g < kGroups; ++g) t += h[g * S + tid];
-        if (block_hist) block_hist[b * A + tid] = t;
-        if (tensor_hist && t) atomicAdd(&tensor_hist[tid], t);
-        if (hist64 && t) atomicAdd(&hist64[tid], (unsigned long long)t);
+#pragma unroll
+    for (uint32_t j = 0; j < C; ++j) c += h[v * kWave + g * C + ((j + v) & (C - 1))];
+#pragma unroll
+    for (uint32_t o = 1; o < G; o <<= 1) c += __shfl_xor(c, o);
+    if (g == 0) {
+        if (block_hist) block_hist[b * A + v] = c;
+        if (tensor_hist && c) atomicAdd(&tensor_hist[v], c);
+        if (hist64 && c) atomicAdd(&hist64[v], (unsigned long long)c);
     }
 }
 
