@@ -90,6 +90,52 @@ def test_histogram(dtype, n):
         assert np.array_equal(np_u(bh[b], np.uint32), np.bincount(e[b * 65536:(b + 1) * 65536], minlength=A))
 
 
+@pytest.mark.parametrize("dtype", [zx.BF16, zx.FP8_E4M3FN, zx.E8M0])
+@pytest.mark.parametrize("pattern", ["one value", "lane-shifted sweep", "random bits"])
+def test_histogram_value_layouts(dtype, pattern):
+    """Counts per block, per tensor and accumulated in 64 bits, for value patterns that
+    stress the per-lane LDS counters: every lane on one value, and a sweep of every
+    value shifted by the lane (neighbouring lanes on neighbouring values); three full
+    blocks and a ragged tail."""
+    say("hist layouts", dtype, pattern)
+    n = 3 * 65536 + 4101
+    A = zx.alphabet(dtype)
+    i = np.arange(n, dtype=np.int64)
+    g = np.random.default_rng(5)
+    if pattern == "one value":
+        sym = np.full(n, A // 2 + 1, dtype=np.int64)
+    elif pattern == "lane-shifted sweep":
+        sym = (i + i // 64) % A
+    else:
+        sym = g.integers(0, A, n)
+    other = g.integers(0, 1 << 16, n)          # the bits outside the exponent field, at random
+    if dtype == zx.BF16:
+        words = ((other & 0x807F) | (sym << 7)).astype(np.uint16)
+        x = torch.from_numpy(words.view(np.int16))
+    elif dtype == zx.FP8_E4M3FN:
+        words = ((other & 0x87) | (sym << 3)).astype(np.uint8)
+        x = torch.from_numpy(words)
+    else:
+        words = sym.astype(np.uint8)
+        x = torch.from_numpy(words)
+    want = np.bincount(sym, minlength=A)
+    nb = (n + 65535) // 65536
+    xd = x.cuda()
+    th = torch.empty(A, dtype=torch.int32, device="cuda")
+    bh = torch.empty((nb, A), dtype=torch.int32, device="cuda")
+    zx.zx_histogram(dtype, xd, n, th, bh)
+    h64 = torch.zeros(A, dtype=torch.int64, device="cuda")
+    L = zx.lib()
+    s = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        assert L.zx_histogram_accumulate(dtype, xd.data_ptr(), n, h64.data_ptr(), s) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(np_u(th, np.uint32), want)
+    for b in range(nb):
+        assert np.array_equal(np_u(bh[b], np.uint32), np.bincount(sym[b * 65536:(b + 1) * 65536], minlength=A))
+    assert np.array_equal(h64.cpu().numpy(), 2 * want)
+
+
 # ------------------------------------------------------------------ codebook
 
 @pytest.mark.parametrize("dtype", [0, 1])
