@@ -12,8 +12,11 @@ R copies of the input and its containers (>= 1 GiB of traffic in flight): step i
 encodes copy i % R and decodes copy (i + R/2) % R, which was encoded half a
 rotation earlier and has been evicted since.
 
-After the K steps, max(K, 100) decodes run back to back over the rotation between
-two events; their average launch time is `decode_ms`, the time the roofline uses.
+After the K steps, decodes run back to back over the rotation between two events,
+at least 20 times; the median per-launch time is `decode_ms`, the time the roofline
+uses.
+The device-side encode chain is timed the same way (`encode_chain_ms`), and so are
+whole compress() calls, host share included (`compress_ms_back_to_back`).
 The JSON line reports decode throughput (BF16 bytes out / decode time) as `value`,
 with encode throughput, compression ratio, the decode kernel's HBM roofline and
 the CPU oracle's decode throughput on the host as extra fields.
@@ -429,6 +432,13 @@ def bench_single(args):
     enc_launch, enc_check = encode_chain(cs, xs)
     enc_med, _ = median_launch_ms(enc_launch, R, reps=reps)
     enc_check()
+
+    # whole compress() calls back to back over the rotation (each waits for its own
+    # totals on the host, so this includes the host's share of every call)
+    def compress_launch(i):
+        cs[i % R] = zx.compress(xs[i % R], fp8_scale=scale)
+
+    cmp_med, _ = median_launch_ms(compress_launch, R, reps=reps)
     # correctness at full size, outside the timed region
     assert int(err.item()) == 0, "decoder reported a corrupt container"
     for k in range(R):
@@ -477,6 +487,7 @@ def bench_single(args):
         "decode_ms_in_step": round(float(step_dec_ms.mean()), 5),
         "encode_ms": round(enc_e2e_ms, 5),
         "encode_GBps": round(raw_bytes / (enc_e2e_ms * 1e-3) / 1e9, 2),
+        "compress_ms_back_to_back": round(cmp_med, 5),
         "encode_chain_ms": round(enc_med, 5),
         "encode_chain_GBps": round(raw_bytes / (enc_med * 1e-3) / 1e9, 2),
         "encode_roofline": {"bound": "hbm", "alg_bytes": enc_alg, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
